@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cache quantization hot path on one MI355X.
+
+One step = quantize the K and V of one batch (every tile and kv head of the
+workload) and run quantized decode attention over the cache just written.
+Inputs are seeded synthetic data already resident in device memory; a ring of
+independent copies (inputs and caches) larger than the 256 MB last-level cache
+makes every step read from and write to HBM.
+
+Prints one JSON line: whole-step throughput in GB/s of algorithmic bytes
+(inputs read + codes and side data written by the quantizer; codes and side data
+of every attended page + queries + outputs for decode), the quantizer's roofline
+position, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantize GB/s (fp16 in) + quantized decode-attn GB/s, % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+ESIZE = {"f32": 4, "bf16": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def block_bytes(f, with_rope=True):
+    T, D = f.tile_tokens, f.head_dim
+    return T * D * f.bits // 8 + T * (D // f.group) * 4 + 2 * D + (T * f.rope_dim * 2 if with_rope else 0)
+
+
+def quantize_bytes(cfg, f, width):
+    """Algorithmic bytes of one quantizer launch: source read + cache written."""
+    read = cfg.total_tokens * cfg.num_kv_heads * width * ESIZE[cfg.src_dtype]
+    write = cfg.num_pages * cfg.num_kv_heads * block_bytes(f)
+    return read, write
+
+
+def decode_bytes(cfg, seqs=None):
+    """Algorithmic bytes of one decode call: every attended page of K and V
+    (codes, scale/zero, normalizer, rope), the queries and the fp32 outputs."""
+    T = cfg.fk.tile_tokens
+    lens = cfg.seq_lens if seqs is None else cfg.seq_lens[seqs]
+    pages = int(sum((int(L) + T - 1) // T for L in lens)) * cfg.num_kv_heads
+    per_page = block_bytes(cfg.fk) + (block_bytes(cfg.fv) if cfg.fv is not None else 0)
+    q = len(lens) * cfg.num_q_heads * cfg.width * ESIZE[cfg.src_dtype]
+    out = len(lens) * cfg.num_q_heads * cfg.dv * 4
+    return pages * per_page + q + out
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for name in ("quantize.hip", "common.h"):
+        with open(os.path.join(ROOT, "kv_cache_quantization_04_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload_key):
+    """HBM bytes per quantizer launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"quantize_kernel_{workload_key}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_digest():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(cfg, ks, vs, q, nseq):
+    import oracle as O
+
+    threads = os.cpu_count() or 1
+    seqs = list(range(min(nseq, cfg.num_seqs)))
+    sel = np.nonzero(np.isin(cfg.tile_seq, seqs))[0]
+    Hkv = cfg.num_kv_heads
+    t0 = time.perf_counter()
+    kc = O.HostCache(cfg.fk, cfg.num_pages, Hkv)
+    O.quantize_cache(kc, ks, O.F32 if cfg.src_dtype == "f32" else O.BF16, cfg.tile_src_token[sel],
+                     cfg.tile_valid[sel], cfg.tile_page[sel], nthreads=threads)
+    vc = None
+    if cfg.fv is not None:
+        vc = O.HostCache(cfg.fv, cfg.num_pages, Hkv)
+        O.quantize_cache(vc, vs, O.F32 if cfg.src_dtype == "f32" else O.BF16, cfg.tile_src_token[sel],
+                         cfg.tile_valid[sel], cfg.tile_page[sel], nthreads=threads)
+    tq = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    O.decode_attn(q[seqs], O.F32 if cfg.src_dtype == "f32" else O.BF16, kc, vc, cfg.block_table[seqs],
+                  cfg.seq_lens[seqs], cfg.sm_scale, folded=False, nthreads=threads)
+    td = time.perf_counter() - t1
+    tokens = int(cfg.seq_lens[seqs].sum())
+    W = cfg.width
+    qb = tokens * Hkv * W * ESIZE[cfg.src_dtype] + sel.size * Hkv * block_bytes(cfg.fk)
+    if cfg.fv is not None:
+        qb += tokens * Hkv * cfg.dv * ESIZE[cfg.src_dtype] + sel.size * Hkv * block_bytes(cfg.fv)
+    db = decode_bytes(cfg, seqs)
+    return {"value": round((qb + db) / (tq + td) / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(seqs)} of {cfg.num_seqs} sequences ({tokens} tokens x {Hkv} kv heads): fp64 "
+                      f"oracle quantize of their K and V tiles ({tq:.2f} s) and dequantize-then-softmax decode for "
+                      f"all {cfg.num_q_heads} query heads ({td:.2f} s), {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 = GQA decode, the headline)")
+    ap.add_argument("--ring-mb", type=int, default=2048, help="live bytes of the copy ring")
+    ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures a single GPU: the quantizer and decode shard by sequence and kv head with no "
+              "exchange, so no multi-GPU figure is produced; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_quantization_04_amd as K
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    cfg = W.config(args.config)
+    log(f"workload: {cfg.name}")
+    ks = W.gen_k(cfg)
+    vs = W.gen_v(cfg) if cfg.fv is not None else None
+    q = W.gen_q(cfg)
+
+    def to_dev(a):
+        if cfg.src_dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def kfmt(f):
+        return K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+    tst, tv, tp = i32(cfg.tile_src_token), i32(cfg.tile_valid), i32(cfg.tile_page)
+    bt, sl = i32(cfg.block_table), i32(cfg.seq_lens)
+    qd = to_dev(q)
+    kin_r, kout_w = quantize_bytes(cfg, cfg.fk, cfg.width)
+    vin_r, vout_w = quantize_bytes(cfg, cfg.fv, cfg.dv) if cfg.fv is not None else (0, 0)
+    qbytes = kin_r + kout_w + vin_r + vout_w
+    dbytes = decode_bytes(cfg)
+    per_copy = qbytes
+    ring = max(2, math.ceil(args.ring_mb * 1e6 / per_copy))
+    log(f"ring of {ring} copies ({ring * per_copy / 1e6:.0f} MB live)")
+    ksrc0 = to_dev(ks)
+    vsrc0 = to_dev(vs) if vs is not None else None
+    ksrc = [ksrc0] + [ksrc0.clone() for _ in range(ring - 1)]
+    vsrc = ([vsrc0] + [vsrc0.clone() for _ in range(ring - 1)]) if vs is not None else [None] * ring
+    kcache = [K.DeviceCache(kfmt(cfg.fk), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
+    vcache = ([K.DeviceCache(kfmt(cfg.fv), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
+              if cfg.fv is not None else [None] * ring)
+    max_len = int(cfg.seq_lens.max())
+    splits = K.kv_decode_attn_default_splits(cfg.num_seqs, cfg.num_kv_heads, max_len, cfg.fk.tile_tokens)
+    ws = torch.empty(K.kv_decode_attn_workspace_bytes(cfg.num_seqs, cfg.num_q_heads, cfg.dv, splits),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.num_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device=dev)
+    # a plain device copy of known size: the reference kernel for scaling HBM counters
+    calib = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    torch.empty_like(calib).copy_(calib)
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        j = i % ring
+        if evs:
+            evs[0].record(stream)
+        K.kv_quantize(kcache[j], ksrc[j], tst, tv, tp, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        if vsrc[j] is not None:
+            K.kv_quantize(vcache[j], vsrc[j], tst, tv, tp, stream=stream)
+        if evs:
+            evs[2].record(stream)
+        K.kv_decode_attn(qd, kcache[j], vcache[j], bt, sl, max_len, cfg.sm_scale, num_splits=splits, workspace=ws,
+                         out=out, stream=stream)
+        if evs:
+            evs[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    tk = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    tvq = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    td = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms on device, {wall * 1e3:.3f} ms wall")
+
+    value = (qbytes + dbytes) / (ms_step * 1e-3) / 1e9
+    nq = 2 if cfg.fv is not None else 1
+    q_gbs = qbytes / ((tk + tvq) * 1e-3) / 1e9
+    d_gbs = dbytes / (td * 1e-3) / 1e9
+    per_launch = qbytes / nq
+    avg_launch_ms = (tk + tvq) / nq
+    traffic = profiled_traffic(f"config{args.config}")
+    positions = int(cfg.seq_lens.sum())
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "kv_layout": "K token-major, V channel-major, fp16 side data",
+                   "decode_splits": splits, "copy_ring": ring},
+        "roofline": {"bound": "hbm", "kernel": "quantize_kernel", "achieved": round(per_launch / (avg_launch_ms * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(per_launch / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": per_launch,
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 3)},
+        "detail": {
+            "quantize_GBps": round(q_gbs, 2), "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+            "quantize_input_GBps": round((kin_r + vin_r) / ((tk + tvq) * 1e-3) / 1e9, 2),
+            "quantize_tokens_per_s": round(nq * cfg.total_tokens * cfg.num_kv_heads / ((tk + tvq) * 1e-3), 1),
+            "quantize_us": round((tk + tvq) * 1e3, 3),
+            "decode_GBps": round(d_gbs, 2), "decode_frac_hbm": round(d_gbs / HBM_PEAK_GBS, 4),
+            "decode_us": round(td * 1e3, 3), "decode_positions_per_s": round(positions / (td * 1e-3), 1),
+            "decode_bytes": dbytes, "quantize_bytes": qbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, ks, vs, q, args.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

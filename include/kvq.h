@@ -1,0 +1,167 @@
+/*
+ * kvq: KVarN-style KV-cache quantization and quantized decode attention for
+ * AMD Instinct MI355X (gfx950). C ABI of libkvq.so.
+ *
+ * The method (as described by the "KVarN" project review, section Key
+ * Features, "Variance-Normalized Quantization Pipeline"; and by the KVarN item
+ * of the "KV-Cache" tag page): each KV tile of T tokens x D channels is
+ *   1. rotated along its channels by a block Sylvester Hadamard matrix
+ *      Q = blockdiag(H_h / sqrt(h)) to spread channel outliers,
+ *   2. put through `iters` Sinkhorn-like rounds that set every row, then every
+ *      column, of X Q / (r c) to unit RMS (dual-axis variance equalization over
+ *      the tile, computed on the fly: no calibration data),
+ *   3. quantized per token and per group of `group` channels by asymmetric
+ *      round-to-nearest: code = clamp(rne((y - Z) / S), 0, 2^bits - 1) with
+ *      y = (X Q)_j / c_j, S = (max y - min y) / (2^bits - 1), Z = min y.
+ * Stored per (page, head): packed codes, fp16 (S, Z) per token and group,
+ * fp16 c per channel. The per-token row factors r are not stored: per-token
+ * min-max quantization is exactly invariant to them.
+ * The consumer (decode attention) never rebuilds K or V: it rotates and
+ * scales the query, q' = (q Q) o c_K, takes scores from the codes with the
+ * per-token (S, Z), accumulates values as sum_t p_t (S_t code_t + Z_t) o c_V
+ * and rotates the result back once.
+ *
+ * Conventions
+ *  - Every pointer inside kvq_cache and every array argument named "device"
+ *    is device memory owned by the caller; kvq_cache and kvq_format structs
+ *    themselves are host memory, read during the call only.
+ *  - Each call validates its arguments on the host, returns a negative
+ *    kvq_status without enqueuing anything when they are invalid, and otherwise
+ *    enqueues its kernels on `stream` and returns KVQ_OK without synchronizing.
+ *  - Data conditions found on the device (non-finite input, fp16 overflow of a
+ *    scale, zero point or normalizer) set bits in *status_flags; they never
+ *    abort a launch.
+ *  - The library allocates no device memory and keeps no mutable global state;
+ *    calls on different streams may run concurrently.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 } kvq_dtype;
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_EINVAL = -1,       /* null pointer, bad size, shape mismatch          */
+    KVQ_EUNSUPPORTED = -2, /* valid but not built: head_dim, tile, bits, align */
+    KVQ_EWORKSPACE = -3,   /* decode workspace smaller than required          */
+    KVQ_ELAUNCH = -4       /* the HIP runtime refused a launch                */
+} kvq_status;
+
+/* Order of the codes inside one (page, head) block. */
+enum { KVQ_TOKEN_MAJOR = 0, KVQ_CHANNEL_MAJOR = 1 };
+
+/* Bits of *status_flags. */
+enum { KVQ_FLAG_NONFINITE = 1u, KVQ_FLAG_SIDE_OVERFLOW = 2u };
+
+typedef struct {
+    int32_t head_dim;    /* D: quantized channels (MLA: the latent width)                */
+    int32_t rope_dim;    /* R: channels after D kept as bf16 unrotated (MLA rope), else 0 */
+    int32_t tile_tokens; /* T: tokens per tile = tokens per page                         */
+    int32_t hadamard_n;  /* h: Hadamard block size; power of two dividing D              */
+    int32_t group;       /* G: channels per (S, Z) pair; multiple of 8 dividing D        */
+    int32_t bits;        /* code width: 2, 3, 4 or 8                                     */
+    int32_t iters;       /* normalization rounds (row step then column step), >= 0       */
+    int32_t layout;      /* KVQ_TOKEN_MAJOR (keys) or KVQ_CHANNEL_MAJOR (values)          */
+} kvq_format;
+
+/* One paged quantized cache (K, V, or the MLA latent). Byte layout, per
+ * physical page p and head h (P = num_pages, H = num_heads):
+ *   codes  [P][H][T*D*bits/8] bytes. The block is one little-endian bitstream
+ *          (bit k is bit k%8 of byte k/8); code i of the stream occupies bits
+ *          [bits*i, bits*i + bits). Token-major: i = t*D + j. Channel-major:
+ *          i = j*T + t.
+ *   sz     [P][H][T][D/G][2] fp16: (S, Z) of token t, channel group g.
+ *   cnorm  [P][H][D] fp16: normalizer c_j of the tile.
+ *   rope   [P][H][T][R] bf16: unrotated copy of channels D..D+R-1; NULL if R == 0.
+ * Rows t >= the tile's valid count hold zero codes, S = Z = 0 and zero rope. */
+typedef struct {
+    kvq_format fmt;
+    int32_t num_pages, num_heads;
+    uint8_t *codes;
+    uint16_t *sz;
+    uint16_t *cnorm;
+    uint16_t *rope;
+} kvq_cache;
+
+/* Parses "kvarn_k{bk}v{bv}_g{T}" (the KVarN preset string, e.g.
+ * kvarn_k4v2_g128: 4-bit keys, 2-bit values, 128-token tiles; "KVarN"
+ * project review, Key Features, "4-bit Keys, 2-bit Values Preset"). Sets
+ * head_dim, tile_tokens and bits; hadamard_n = group = head_dim, iters = 4,
+ * rope_dim = 0; keys token-major, values channel-major.
+ * Returns KVQ_EINVAL for a malformed string or null pointers. */
+kvq_status kvq_format_from_preset(const char *preset, int32_t head_dim, kvq_format *k, kvq_format *v);
+
+/* Bytes of codes, sz, cnorm and rope for one cache (the four arrays' sizes
+ * summed), or 0 for an invalid format. */
+size_t kvq_cache_bytes(const kvq_format *fmt, int32_t num_pages, int32_t num_heads);
+
+/* Quantizes num_tiles tiles for every head into dst.
+ * src (device): element (token tau, head h, channel c) is at
+ *   src[tau * stride_token + h * stride_head + c], c < D + R, in src_dtype;
+ *   strides in elements, multiples of 8, src 16-byte aligned.
+ * Tile i reads tokens tile_src_token[i] .. + tile_valid[i] - 1
+ *   (0 <= tile_valid[i] <= T) and writes page tile_dst_page[i] of every head;
+ *   the three arrays are device int32 [num_tiles]. Statistics use the valid rows
+ *   only; the rest of the page is zeroed.
+ * status_flags (device, nullable): KVQ_FLAG_* bits are OR-ed in.
+ * Supported: D in {64, 128, 256, 512}, T in {16, 32, 64, 128}, bits in
+ *   {2, 3, 4, 8}, G a multiple of 8 dividing D, h a power of two in [8, D]
+ *   or h = 1; R = 0, or R a multiple of 8 with bf16/f16/f32 input.
+ * Errors: KVQ_EINVAL (nulls, negative counts, H != dst->num_heads ...),
+ *   KVQ_EUNSUPPORTED (outside the list above), KVQ_ELAUNCH. */
+kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+                       int64_t stride_head, int32_t num_tiles, const int32_t *tile_src_token,
+                       const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
+                       hipStream_t stream);
+
+/* Rebuilds tiles from the cache: x_hat = ((S code + Z) o c) Q, rope copied.
+ * dst (device): [num_tiles][H][T][D + R] in dst_dtype (f32, f16 or bf16); rows
+ * t >= tile_valid[i] are written as zero. tile_page, tile_valid: device int32. */
+kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t *tile_page,
+                         const int32_t *tile_valid, void *dst, kvq_dtype dst_dtype, hipStream_t stream);
+
+/* Number of split-K partitions kv_decode_attn uses when num_splits == 0. */
+int32_t kv_decode_attn_default_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                      int32_t tile_tokens);
+
+/* Workspace bytes kv_decode_attn needs for these sizes (num_splits >= 1). */
+size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,
+                                      int32_t num_splits);
+
+/* Decode attention of one new query per sequence over the paged quantized
+ * cache: out[s][hq] = softmax_t(sm_scale <q[s][hq], k_t>) applied to v_t, over
+ * t < seq_lens[s], with k_t, v_t the dequantized rows reached through
+ * block_table[s][t / T] (row t % T). Query head hq reads kv head
+ * hq / (num_q_heads / H). When v == NULL (MLA), k's latent (first D channels
+ * of each dequantized row) is also the value and k's rope channels take part
+ * in the score only.
+ *   q (device): [num_seqs][num_q_heads][D + R] in q_dtype.
+ *   block_table (device int32): [num_seqs][block_table_stride].
+ *   seq_lens (device int32): [num_seqs], each in [0, max_seq_len].
+ *   out (device fp32): [num_seqs][num_q_heads][Dv], Dv = (v ? v : k)->fmt.head_dim.
+ *   workspace (device): at least kv_decode_attn_workspace_bytes(...) bytes.
+ * The score rotation and normalizer fold is exact in real arithmetic; in fp32
+ * the result differs from fp64 dequantize-then-attention by rounding only.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (layouts: K token-major, V channel-major,
+ * MLA latent token-major; T in {16, 32, 64, 128}), KVQ_EWORKSPACE, KVQ_ELAUNCH. */
+kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                          const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
+                          int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
+                          float sm_scale, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                          float *out, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *kvq_status_str(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

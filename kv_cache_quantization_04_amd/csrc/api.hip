@@ -1,0 +1,198 @@
+// C ABI of libkvq.so: host-side validation and launch.
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+#include "launch.h"
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+kvq_status check_format(const kvq_format *f) {
+    if (!f) return KVQ_EINVAL;
+    const int D = f->head_dim, T = f->tile_tokens;
+    if (D <= 0 || T <= 0 || f->bits <= 0 || f->group <= 0 || f->hadamard_n <= 0 || f->iters < 0 ||
+        f->rope_dim < 0)
+        return KVQ_EINVAL;
+    if (f->layout != KVQ_TOKEN_MAJOR && f->layout != KVQ_CHANNEL_MAJOR) return KVQ_EINVAL;
+    if (D % f->group != 0 || D % f->hadamard_n != 0 || !is_pow2(f->hadamard_n)) return KVQ_EINVAL;
+    if (!(D == 64 || D == 128 || D == 256 || D == 512)) return KVQ_EUNSUPPORTED;
+    if (!(T == 16 || T == 32 || T == 64 || T == 128)) return KVQ_EUNSUPPORTED;
+    if (!(f->bits == 2 || f->bits == 3 || f->bits == 4 || f->bits == 8)) return KVQ_EUNSUPPORTED;
+    if (f->group % 8 != 0) return KVQ_EUNSUPPORTED;
+    if (f->rope_dim % 8 != 0) return KVQ_EUNSUPPORTED;
+    if (f->iters > 64) return KVQ_EUNSUPPORTED;
+    return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_cache *c) {
+    if (!c) return KVQ_EINVAL;
+    kvq_status st = check_format(&c->fmt);
+    if (st != KVQ_OK) return st;
+    if (c->num_pages < 0 || c->num_heads <= 0) return KVQ_EINVAL;
+    if (!c->codes || !c->sz || !c->cnorm) return KVQ_EINVAL;
+    if (c->fmt.rope_dim > 0 && !c->rope) return KVQ_EINVAL;
+    if (((uintptr_t)c->codes & 3) || ((uintptr_t)c->sz & 3)) return KVQ_EUNSUPPORTED;
+    return KVQ_OK;
+}
+
+bool valid_dtype(int d) { return d == KVQ_F32 || d == KVQ_F16 || d == KVQ_BF16; }
+
+kvq_status launched() { return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_str(kvq_status s) {
+    switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_EUNSUPPORTED: return "unsupported configuration";
+    case KVQ_EWORKSPACE: return "workspace too small";
+    case KVQ_ELAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+kvq_status kvq_format_from_preset(const char *preset, int32_t head_dim, kvq_format *k, kvq_format *v) {
+    if (!preset || !k || !v || head_dim <= 0) return KVQ_EINVAL;
+    int bk = 0, bv = 0, T = 0, used = 0;
+    if (std::sscanf(preset, "kvarn_k%dv%d_g%d%n", &bk, &bv, &T, &used) != 3 || preset[used] != '\0')
+        return KVQ_EINVAL;
+    if (bk <= 0 || bv <= 0 || T <= 0) return KVQ_EINVAL;
+    *k = kvq_format{head_dim, 0, T, head_dim, head_dim, bk, 4, KVQ_TOKEN_MAJOR};
+    *v = kvq_format{head_dim, 0, T, head_dim, head_dim, bv, 4, KVQ_CHANNEL_MAJOR};
+    return KVQ_OK;
+}
+
+size_t kvq_cache_bytes(const kvq_format *f, int32_t num_pages, int32_t num_heads) {
+    if (check_format(f) != KVQ_OK || num_pages < 0 || num_heads <= 0) return 0;
+    const size_t ph = (size_t)num_pages * num_heads;
+    const size_t T = f->tile_tokens, D = f->head_dim;
+    return ph * (T * D * f->bits / 8 + T * (D / f->group) * 4 + D * 2 + T * f->rope_dim * 2);
+}
+
+kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+                       int64_t stride_head, int32_t num_tiles, const int32_t *tile_src_token,
+                       const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
+                       hipStream_t stream) {
+    kvq_status st = check_cache(dst);
+    if (st != KVQ_OK) return st;
+    if (!src || num_tiles < 0 || !valid_dtype(src_dtype)) return KVQ_EINVAL;
+    if (num_tiles > 0 && (!tile_src_token || !tile_valid || !tile_dst_page)) return KVQ_EINVAL;
+    if (stride_token < 0 || stride_head < 0) return KVQ_EINVAL;
+    if (((uintptr_t)src & 15) || (stride_token % 8) || (stride_head % 8)) return KVQ_EUNSUPPORTED;
+    if (num_tiles == 0) return KVQ_OK;
+    const kvq_format &f = dst->fmt;
+    kvq::QuantArgs a{src, (int)src_dtype, stride_token, stride_head, tile_src_token, tile_valid, tile_dst_page,
+                     dst->codes, dst->sz, dst->cnorm, dst->rope, dst->num_heads, f.hadamard_n, f.group, f.bits,
+                     f.iters, f.layout, f.rope_dim, dst->num_pages, status_flags};
+    if (!kvq::launch_quantize(f.head_dim, f.tile_tokens, num_tiles, a, stream)) return KVQ_EUNSUPPORTED;
+    return launched();
+}
+
+kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t *tile_page, const int32_t *tile_valid,
+                         void *dst, kvq_dtype dst_dtype, hipStream_t stream) {
+    kvq_status st = check_cache(src);
+    if (st != KVQ_OK) return st;
+    if (!dst || num_tiles < 0 || !valid_dtype(dst_dtype)) return KVQ_EINVAL;
+    if (num_tiles > 0 && (!tile_page || !tile_valid)) return KVQ_EINVAL;
+    if (num_tiles == 0) return KVQ_OK;
+    const kvq_format &f = src->fmt;
+    kvq::DequantArgs a{src->codes, src->sz, src->cnorm, src->rope, tile_page, tile_valid, dst, (int)dst_dtype,
+                       src->num_heads, f.hadamard_n, f.group, f.bits, f.layout, f.rope_dim, src->num_pages};
+    if (!kvq::launch_dequant(f.head_dim, f.tile_tokens, num_tiles, a, stream)) return KVQ_EUNSUPPORTED;
+    return launched();
+}
+
+int32_t kv_decode_attn_default_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                      int32_t tile_tokens) {
+    if (num_seqs <= 0 || num_kv_heads <= 0 || tile_tokens <= 0 || max_seq_len <= 0) return 1;
+    const int64_t pages = (max_seq_len + tile_tokens - 1) / tile_tokens;
+    const int64_t target = 2048;  // workgroups in flight: 8 per compute unit
+    int64_t sp = (target + (int64_t)num_seqs * num_kv_heads - 1) / ((int64_t)num_seqs * num_kv_heads);
+    if (sp > pages) sp = pages;
+    if (sp < 1) sp = 1;
+    return (int32_t)sp;
+}
+
+size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,
+                                      int32_t num_splits) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim_v <= 0 || num_splits <= 0) return 0;
+    return (size_t)num_seqs * num_q_heads * num_splits * (head_dim_v + 2) * sizeof(float);
+}
+
+kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads, const kvq_cache *k,
+                          const kvq_cache *v, const int32_t *block_table, int32_t block_table_stride,
+                          const int32_t *seq_lens, int32_t max_seq_len, float sm_scale, int32_t num_splits,
+                          void *workspace, size_t workspace_bytes, float *out, hipStream_t stream) {
+    kvq_status st = check_cache(k);
+    if (st != KVQ_OK) return st;
+    if (v && (st = check_cache(v)) != KVQ_OK) return st;
+    if (!q || !valid_dtype(q_dtype) || num_seqs < 0 || num_q_heads <= 0 || !out || max_seq_len < 0) return KVQ_EINVAL;
+    if (num_seqs == 0) return KVQ_OK;
+    if (!block_table || !seq_lens || block_table_stride <= 0 || num_splits < 0) return KVQ_EINVAL;
+    const kvq_format &fk = k->fmt;
+    const kvq_format &fv = v ? v->fmt : k->fmt;
+    if (num_q_heads % k->num_heads != 0) return KVQ_EINVAL;
+    if (v) {
+        if (v->num_heads != k->num_heads || fv.tile_tokens != fk.tile_tokens || v->num_pages != k->num_pages)
+            return KVQ_EINVAL;
+        if (fk.rope_dim != 0 || fv.rope_dim != 0) return KVQ_EUNSUPPORTED;
+        if (fk.layout != KVQ_TOKEN_MAJOR || fv.layout != KVQ_CHANNEL_MAJOR) return KVQ_EUNSUPPORTED;
+    } else {
+        if (fk.layout != KVQ_TOKEN_MAJOR) return KVQ_EUNSUPPORTED;
+    }
+    if ((int64_t)block_table_stride * fk.tile_tokens < max_seq_len) return KVQ_EINVAL;
+    const int splits = num_splits > 0 ? num_splits
+                                      : kv_decode_attn_default_splits(num_seqs, k->num_heads, max_seq_len, fk.tile_tokens);
+    if (!workspace || workspace_bytes < kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, fv.head_dim, splits))
+        return KVQ_EWORKSPACE;
+
+    kvq::DecodeArgs a{};
+    a.q = q;
+    a.q_dtype = (int)q_dtype;
+    a.B = num_seqs;
+    a.Hq = num_q_heads;
+    a.Hkv = k->num_heads;
+    a.grp = num_q_heads / k->num_heads;
+    a.hc = a.grp < 16 ? a.grp : 16;
+    if (a.grp % a.hc != 0) return KVQ_EUNSUPPORTED;
+    a.nhc = a.grp / a.hc;
+    a.kcodes = k->codes;
+    a.ksz = k->sz;
+    a.kcn = k->cnorm;
+    a.krope = k->rope;
+    a.D = fk.head_dim;
+    a.R = fk.rope_dim;
+    a.kG = fk.group;
+    a.kbits = fk.bits;
+    a.kh = fk.hadamard_n;
+    a.klayout = fk.layout;
+    const kvq_cache *vc = v ? v : k;
+    a.vcodes = vc->codes;
+    a.vsz = vc->sz;
+    a.vcn = vc->cnorm;
+    a.Dv = fv.head_dim;
+    a.vG = fv.group;
+    a.vbits = fv.bits;
+    a.vh = fv.hadamard_n;
+    a.vlayout = fv.layout;
+    a.vH = vc->num_heads;
+    a.T = fk.tile_tokens;
+    a.num_pages = k->num_pages;
+    a.bt = block_table;
+    a.bt_stride = block_table_stride;
+    a.seq_lens = seq_lens;
+    a.sm = sm_scale;
+    a.splits = splits;
+    a.ws = (float *)workspace;
+    a.out = out;
+    if (!kvq::launch_decode(a, stream)) return KVQ_EUNSUPPORTED;
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,220 @@
+// Split-K decode attention over the paged quantized cache (gfx950), generic path.
+//
+// Folded evaluation (the dequantized K and V are never formed):
+//   score_t = sm * ( sum_g S_tg * <q'_g, code_tg> + Z_tg * sum_{j in g} q'_j ) [+ <q_rope, k_rope_t>]
+//     with q' = (q Q) o c_K (per page: c is per tile),
+//   o'      = sum_t p_t (S_tg code_tj + Z_tg) c_V,j     accumulated per page,
+//   out     = (o' / sum_t p_t) Q                         in the reduce kernel.
+// Grid: (split, kv head x head chunk, sequence); each workgroup walks its page
+// range through the block table and writes (m, l, o') to the workspace.
+#include "common.h"
+#include "launch.h"
+
+namespace kvq {
+
+__device__ __forceinline__ uint32_t get_code(const uint8_t *blk, int i, int bits, int blockbytes) {
+    const int bit = bits * i;
+    const int bo = bit >> 3;
+    uint32_t win = blk[bo];
+    if (bo + 1 < blockbytes) win |= (uint32_t)blk[bo + 1] << 8;
+    return (win >> (bit & 7)) & ((1u << bits) - 1);
+}
+
+// In-place Walsh-Hadamard transform of `rows` LDS rows of length n, blocks of h.
+__device__ void lds_fwht(float *buf, int rows, int n, int h) {
+    for (int len = 1; len < h; len <<= 1) {
+        for (int e = threadIdx.x; e < rows * n / 2; e += blockDim.x) {
+            const int r = e / (n / 2), pe = e % (n / 2);
+            const int i = (pe / len) * 2 * len + pe % len;
+            float *row = buf + r * n;
+            const float x = row[i], y = row[i + len];
+            row[i] = x + y;
+            row[i + len] = x - y;
+        }
+        __syncthreads();
+    }
+}
+
+constexpr int DEC_NT = 256;
+constexpr int DEC_MAXO = 32;  // owned (head, channel) outputs per thread
+
+__global__ void __launch_bounds__(DEC_NT) decode_generic_kernel(DecodeArgs a) {
+    extern __shared__ float smem[];
+    const int hc = a.hc, D = a.D, R = a.R, Dv = a.Dv, T = a.T;
+    float *qbar = smem;                    // [hc][D]
+    float *qt = qbar + hc * D;             // [hc][D]
+    float *qsum = qt + hc * D;             // [hc][D/kG]
+    float *qrope = qsum + hc * (D / a.kG); // [hc][R]
+    float *logit = qrope + hc * R;         // [hc][T]
+    float *mrow = logit + hc * T;          // [hc]
+    float *lrow = mrow + hc;               // [hc]
+    float *srow = lrow + hc;               // [hc]
+
+    const int tid = threadIdx.x;
+    const int split = blockIdx.x;
+    const int hk = blockIdx.y / a.nhc, chunk = blockIdx.y % a.nhc;
+    const int s = blockIdx.z;
+    const int h0 = hk * a.grp + chunk * hc;
+    const int L = a.seq_lens[s];
+    const int npages = min((L + T - 1) / T, a.bt_stride);
+    const int pps = (npages + a.splits - 1) / a.splits;
+    const int p0 = split * pps, p1 = min(npages, p0 + pps);
+
+    // rotated query (unnormalized transform; 1/sqrt(h) applied below)
+    for (int e = tid; e < hc * D; e += DEC_NT) {
+        const int hh = e / D, j = e % D;
+        qbar[e] = load_as_float(a.q, a.q_dtype, ((int64_t)s * a.Hq + h0 + hh) * (D + R) + j);
+    }
+    for (int e = tid; e < hc * R; e += DEC_NT) {
+        const int hh = e / R, j = e % R;
+        qrope[e] = load_as_float(a.q, a.q_dtype, ((int64_t)s * a.Hq + h0 + hh) * (D + R) + D + j);
+    }
+    if (tid < hc) {
+        mrow[tid] = -INFINITY;
+        lrow[tid] = 0.f;
+    }
+    __syncthreads();
+    lds_fwht(qbar, hc, D, a.kh);
+    const float qscale = 1.0f / sqrtf((float)a.kh);
+    for (int e = tid; e < hc * D; e += DEC_NT) qbar[e] *= qscale;
+
+    float o[DEC_MAXO];
+#pragma unroll
+    for (int i = 0; i < DEC_MAXO; ++i) o[i] = 0.f;
+    const int nown = hc * Dv;
+    const int kblockbytes = T * D * a.kbits / 8;
+    const int vblockbytes = T * Dv * a.vbits / 8;
+    const int kng = D / a.kG, vng = Dv / a.vG;
+    __syncthreads();
+
+    for (int pi = p0; pi < p1; ++pi) {
+        const int page = a.bt[(int64_t)s * a.bt_stride + pi];
+        if (page < 0 || page >= a.num_pages) continue;  // invalid block-table entry: page skipped
+        const int rows = min(T, L - pi * T);
+        const int64_t kblk = (int64_t)page * a.Hkv + hk;
+        for (int e = tid; e < hc * D; e += DEC_NT) qt[e] = qbar[e] * half_bits_to_float(a.kcn[kblk * D + e % D]);
+        __syncthreads();
+        for (int e = tid; e < hc * kng; e += DEC_NT) {
+            const int hh = e / kng, g = e % kng;
+            float acc = 0.f;
+            for (int j = g * a.kG; j < (g + 1) * a.kG; ++j) acc += qt[hh * D + j];
+            qsum[e] = acc;
+        }
+        __syncthreads();
+        const uint8_t *kb = a.kcodes + kblk * kblockbytes;
+        for (int e = tid; e < hc * T; e += DEC_NT) {
+            const int hh = e / T, t = e % T;
+            float acc = -INFINITY;
+            if (t < rows) {
+                acc = 0.f;
+                for (int g = 0; g < kng; ++g) {
+                    float dot = 0.f;
+                    for (int j = g * a.kG; j < (g + 1) * a.kG; ++j) {
+                        const int i = a.klayout == KVQ_TOKEN_MAJOR ? t * D + j : j * T + t;
+                        dot = __builtin_fmaf(qt[hh * D + j], (float)get_code(kb, i, a.kbits, kblockbytes), dot);
+                    }
+                    const uint32_t szw = reinterpret_cast<const uint32_t *>(a.ksz)[(kblk * T + t) * kng + g];
+                    acc += half_bits_to_float(szw & 0xffffu) * dot + half_bits_to_float(szw >> 16) * qsum[hh * kng + g];
+                }
+                for (int j = 0; j < R; ++j)
+                    acc += qrope[hh * R + j] * bf16_bits_to_float(a.krope[(kblk * T + t) * R + j]);
+                acc *= a.sm;
+            }
+            logit[e] = acc;
+        }
+        __syncthreads();
+        if (tid < hc) {
+            float mx = mrow[tid];
+            for (int t = 0; t < rows; ++t) mx = fmaxf(mx, logit[tid * T + t]);
+            const float sc = __expf(mrow[tid] - mx);
+            float l = lrow[tid] * sc;
+            for (int t = 0; t < rows; ++t) {
+                const float pv = __expf(logit[tid * T + t] - mx);
+                logit[tid * T + t] = pv;
+                l += pv;
+            }
+            mrow[tid] = mx;
+            lrow[tid] = l;
+            srow[tid] = sc;
+        }
+        __syncthreads();
+        const int64_t vblk = (int64_t)page * a.vH + hk;
+        const uint8_t *vb = a.vcodes + vblk * vblockbytes;
+#pragma unroll
+        for (int i = 0; i < DEC_MAXO; ++i) {
+            const int e = tid + i * DEC_NT;
+            if (e < nown) {
+                const int hh = e / Dv, j = e % Dv;
+                const int g = j / a.vG;
+                float acc = 0.f;
+                for (int t = 0; t < rows; ++t) {
+                    const int ci = a.vlayout == KVQ_TOKEN_MAJOR ? t * Dv + j : j * T + t;
+                    const uint32_t szw = reinterpret_cast<const uint32_t *>(a.vsz)[(vblk * T + t) * vng + g];
+                    const float xv = __builtin_fmaf(half_bits_to_float(szw & 0xffffu),
+                                                    (float)get_code(vb, ci, a.vbits, vblockbytes),
+                                                    half_bits_to_float(szw >> 16));
+                    acc = __builtin_fmaf(logit[hh * T + t], xv, acc);
+                }
+                o[i] = __builtin_fmaf(o[i], srow[hh], acc * half_bits_to_float(a.vcn[vblk * Dv + j]));
+            }
+        }
+        __syncthreads();
+    }
+
+    // partial result of this split: o' (unnormalized), m, l
+#pragma unroll
+    for (int i = 0; i < DEC_MAXO; ++i) {
+        const int e = tid + i * DEC_NT;
+        if (e < nown) {
+            const int hh = e / Dv, j = e % Dv;
+            a.ws[(((int64_t)s * a.Hq + h0 + hh) * a.splits + split) * (Dv + 2) + j] = o[i];
+        }
+    }
+    if (tid < hc) {
+        float *w = a.ws + (((int64_t)s * a.Hq + h0 + tid) * a.splits + split) * (Dv + 2) + Dv;
+        w[0] = mrow[tid];
+        w[1] = lrow[tid];
+    }
+}
+
+// Merge the split partials of one (sequence, query head), normalize, rotate back.
+__global__ void __launch_bounds__(DEC_NT) decode_reduce_kernel(DecodeArgs a) {
+    extern __shared__ float buf[];  // [Dv]
+    const int hq = blockIdx.x, s = blockIdx.y;
+    const int Dv = a.Dv;
+    const float *w = a.ws + ((int64_t)s * a.Hq + hq) * a.splits * (Dv + 2);
+    float M = -INFINITY;
+    for (int i = 0; i < a.splits; ++i) M = fmaxf(M, w[i * (Dv + 2) + Dv]);
+    float l = 0.f;
+    for (int i = 0; i < a.splits; ++i) {
+        const float mi = w[i * (Dv + 2) + Dv];
+        if (mi != -INFINITY) l += __expf(mi - M) * w[i * (Dv + 2) + Dv + 1];
+    }
+    const float invl = l > 0.f ? 1.0f / l : 0.f;
+    for (int j = threadIdx.x; j < Dv; j += DEC_NT) {
+        float acc = 0.f;
+        for (int i = 0; i < a.splits; ++i) {
+            const float mi = w[i * (Dv + 2) + Dv];
+            if (mi != -INFINITY) acc = __builtin_fmaf(__expf(mi - M), w[i * (Dv + 2) + j], acc);
+        }
+        buf[j] = acc * invl;
+    }
+    __syncthreads();
+    lds_fwht(buf, 1, Dv, a.vh);
+    const float sc = 1.0f / sqrtf((float)a.vh);
+    for (int j = threadIdx.x; j < Dv; j += DEC_NT) a.out[((int64_t)s * a.Hq + hq) * Dv + j] = buf[j] * sc;
+}
+
+bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    const size_t smem = sizeof(float) * (2 * a.hc * a.D + a.hc * (a.D / a.kG) + a.hc * a.R + a.hc * a.T + 3 * a.hc);
+    if (a.hc * a.Dv > DEC_NT * DEC_MAXO) return false;
+    if (smem > 64 * 1024 &&
+        hipFuncSetAttribute((const void *)decode_generic_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) !=
+            hipSuccess)
+        return false;
+    hipLaunchKernelGGL(decode_generic_kernel, dim3(a.splits, a.Hkv * a.nhc, a.B), dim3(DEC_NT), smem, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * a.Dv, stream, a);
+    return true;
+}
+
+}  // namespace kvq

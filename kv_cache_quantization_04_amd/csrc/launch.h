@@ -1,0 +1,55 @@
+// Argument blocks and launchers shared by the host API and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct QuantArgs {
+    const void *src;
+    int dtype;
+    int64_t stride_token, stride_head;
+    const int32_t *tile_src_token, *tile_valid, *tile_dst_page;
+    uint8_t *codes;
+    uint16_t *sz, *cnorm, *rope;
+    int H, h, G, bits, iters, layout, R, num_pages;
+    uint32_t *flags;
+};
+
+struct DequantArgs {
+    const uint8_t *codes;
+    const uint16_t *sz, *cnorm, *rope;
+    const int32_t *tile_page, *tile_valid;
+    void *dst;
+    int dtype;
+    int H, h, G, bits, layout, R, num_pages;
+};
+
+struct DecodeArgs {
+    const void *q;
+    int q_dtype;
+    int B, Hq, Hkv, grp, hc, nhc;
+    // K (or MLA latent) cache
+    const uint8_t *kcodes;
+    const uint16_t *ksz, *kcn, *krope;
+    int D, R, kG, kbits, kh, klayout;
+    // V cache (the K cache itself for MLA)
+    const uint8_t *vcodes;
+    const uint16_t *vsz, *vcn;
+    int Dv, vG, vbits, vh, vlayout, vH;
+    int T, num_pages;
+    const int32_t *bt;
+    int bt_stride;
+    const int32_t *seq_lens;
+    float sm;
+    int splits;
+    float *ws;
+    float *out;
+};
+
+bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
+bool launch_dequant(int D, int T, int num_tiles, const DequantArgs &a, hipStream_t stream);
+bool launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kvq

@@ -380,22 +380,25 @@ void orc_decode_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t n
     const int Hkv = k->num_heads, grp = num_q_heads / Hkv, Wq = D + R;
     /* one work item = (sequence, kv head): its pages are dequantized (or read) once
      * and shared by the query heads of the group */
-    parallel_for((int64_t)num_seqs * Hkv, nthreads, [&](int64_t w) {
+    const int64_t units = (int64_t)num_seqs * Hkv;
+    const int inner = (int)std::max<int64_t>(1, nthreads / std::max<int64_t>(units, 1));
+    parallel_for(units, nthreads, [&](int64_t w) {
         const int s = (int)(w / Hkv), hk = (int)(w % Hkv);
         const int L = seq_lens[s];
         const int npages = (L + T - 1) / T;
-        std::vector<double> logits(std::max(L, 1));
         if (!folded) {
             /* softmax(q K^T * scale) V over explicitly dequantized K and V */
             std::vector<double> K((size_t)npages * T * D), V((size_t)npages * T * Dv);
-            for (int pi = 0; pi < npages; ++pi) {
+            parallel_for(npages, inner, [&](int64_t pi) {
                 const int page = block_table[(size_t)s * block_table_stride + pi];
                 dequant_block(k, page, hk, K.data() + (size_t)pi * T * D);
                 if (v) dequant_block(v, page, hk, V.data() + (size_t)pi * T * Dv);
-            }
+            });
             if (!v) V = K; /* the MLA latent doubles as the value */
-            for (int hq = hk * grp; hq < (hk + 1) * grp; ++hq) {
+            parallel_for(grp, inner, [&](int64_t gi) {
+                const int hq = hk * grp + (int)gi;
                 const int64_t qoff = ((int64_t)s * num_q_heads + hq) * Wq;
+                std::vector<double> logits(std::max(L, 1));
                 double mx = -INFINITY;
                 for (int t = 0; t < L; ++t) {
                     const int pi = t / T, row = t % T;
@@ -417,14 +420,16 @@ void orc_decode_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t n
                     for (int j = 0; j < Dv; ++j) o[j] += p * V[(size_t)t * Dv + j];
                 }
                 for (int j = 0; j < Dv; ++j) out[((size_t)s * num_q_heads + hq) * Dv + j] = L > 0 ? o[j] / l : 0.0;
-            }
+            });
         } else {
             /* the folded evaluation: q' = (q Q) o c_K per page, scores use the
              * per-token scale and zero directly, values accumulate in the rotated
              * and normalized domain and are mapped back once at the end */
             const int Gk = fk->group, Gv = fv->group;
-            std::vector<uint16_t> kc((size_t)T * D), vcodes((size_t)T * Dv);
-            for (int hq = hk * grp; hq < (hk + 1) * grp; ++hq) {
+            parallel_for(grp, inner, [&](int64_t gi) {
+                const int hq = hk * grp + (int)gi;
+                std::vector<uint16_t> kc((size_t)T * D), vcodes((size_t)T * Dv);
+                std::vector<double> logits(std::max(L, 1));
                 const int64_t qoff = ((int64_t)s * num_q_heads + hq) * Wq;
                 std::vector<double> qin(D), qbar(D);
                 for (int j = 0; j < D; ++j) qin[j] = load_elem(q, q_dtype, qoff + j);
@@ -480,7 +485,7 @@ void orc_decode_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t n
                 for (int j = 0; j < Dv; ++j) o[j] = L > 0 ? o[j] / l : 0.0;
                 rotate_rows(o.data(), 1, Dv, fv->hadamard_n, ob.data());
                 for (int j = 0; j < Dv; ++j) out[((size_t)s * num_q_heads + hq) * Dv + j] = ob[j];
-            }
+            });
         }
     });
 }

@@ -1,0 +1,139 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and
+the CPU oracle on the same seeded inputs, and compare element by element.
+
+Parity bars (derivations in the design notes):
+  codes     |gpu - oracle| <= 1 everywhere, and != on at most code_flip_max(bits) of elements:
+            1e-4 for the 2/3/4-bit formats; for wider test formats the rate of
+            rounding ties grows with the number of levels, so 1e-4 (2^b - 1) / 15
+  S, Z, c   fp16 bit patterns equal, except 1-ulp differences on at most SIDE_ULP_MAX
+  dequant   per row ||x_gpu - x_orc||_inf <= 1e-3 ||x_orc||_inf  (same stored cache)
+  decode    per (seq, head) ||o_gpu - o_orc||_inf <= 2e-3 ||o_orc||_inf (same stored cache)
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import kv_cache_quantization_04_amd as K
+import oracle as O
+import workloads as W
+
+CODE_FLIP_MAX = 1e-4
+
+
+def code_flip_max(bits: int) -> float:
+    return CODE_FLIP_MAX * max(1.0, (2 ** bits - 1) / 15.0)
+
+SIDE_ULP_MAX = 2e-3
+DEQUANT_RTOL = 1e-3
+DECODE_RTOL = 2e-3
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+ORC_DT = {"f32": O.F32, "bf16": O.BF16, "f16": O.F16}
+
+
+def kfmt(f: W.Fmt) -> K.kvq_format:
+    return K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
+
+
+def to_dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Host array (float32, or uint16 bit patterns for 16-bit types) -> device tensor."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).to(device)
+    return t.view(TORCH_DT[dtype])
+
+
+def i32(a, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)
+
+
+def host_copy(dc: K.DeviceCache, f: W.Fmt) -> O.HostCache:
+    """Download a device cache into an oracle HostCache (for comparison only)."""
+    hc = O.HostCache(f, dc.num_pages, dc.num_heads)
+    hc.codes[...] = dc.codes.cpu().numpy()
+    hc.sz[...] = dc.sz.cpu().numpy().view(np.uint16)
+    hc.cnorm[...] = dc.cnorm.cpu().numpy().view(np.uint16)
+    if hc.rope is not None:
+        hc.rope[...] = dc.rope.cpu().numpy().view(np.uint16)
+    return hc
+
+
+def upload(hc: O.HostCache, dc: K.DeviceCache, pages=None):
+    """Write oracle cache blocks into a device cache (all pages, or the given ones)."""
+    if pages is None:
+        pages = np.arange(hc.num_pages)
+    idx = torch.from_numpy(np.asarray(pages, np.int64)).to(dc.codes.device)
+    dc.codes[idx] = torch.from_numpy(hc.codes[pages]).to(dc.codes.device)
+    dc.sz[idx] = torch.from_numpy(hc.sz[pages].view(np.int16)).to(dc.codes.device)
+    dc.cnorm[idx] = torch.from_numpy(hc.cnorm[pages].view(np.int16)).to(dc.codes.device)
+    if hc.rope is not None:
+        dc.rope[idx] = torch.from_numpy(hc.rope[pages].view(np.int16)).to(dc.codes.device)
+
+
+def half_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in fp16 units in the last place between bit patterns (same sign)."""
+    def key(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x & 0x7FFF)
+
+    return np.abs(key(a) - key(b))
+
+
+def compare_blocks(gpu: O.HostCache, orc: O.HostCache, pages, heads=None, stats=None):
+    """Compare codes, (S, Z) and c of the given pages; returns accumulated stats."""
+    f = orc.f
+    heads = range(orc.num_heads) if heads is None else heads
+    st = stats if stats is not None else dict(codes=0, flips=0, maxdiff=0, side=0, side_ulp1=0, side_bad=0,
+                                              bits=f.bits)
+    for p in pages:
+        for h in heads:
+            cg = O.unpack(gpu.codes[p, h], f).astype(np.int32)
+            co = O.unpack(orc.codes[p, h], f).astype(np.int32)
+            d = np.abs(cg - co)
+            st["codes"] += d.size
+            st["flips"] += int((d != 0).sum())
+            st["maxdiff"] = max(st["maxdiff"], int(d.max()))
+            for a, b in ((gpu.sz[p, h], orc.sz[p, h]), (gpu.cnorm[p, h], orc.cnorm[p, h])):
+                u = half_ulp_diff(a.reshape(-1), b.reshape(-1))
+                st["side"] += u.size
+                st["side_ulp1"] += int((u == 1).sum())
+                st["side_bad"] += int((u > 1).sum())
+            if orc.rope is not None:
+                assert np.array_equal(gpu.rope[p, h], orc.rope[p, h])
+    return st
+
+
+def assert_block_parity(st, where=""):
+    msg = f"{where} {st}"
+    assert st["maxdiff"] <= 1, msg
+    assert st["flips"] <= code_flip_max(st["bits"]) * st["codes"], msg
+    assert st["side_bad"] == 0, msg
+    assert st["side_ulp1"] <= max(SIDE_ULP_MAX * st["side"], 0), msg
+
+
+def gpu_quantize(f: W.Fmt, src: np.ndarray, dtype: str, tile_src_token, tile_valid, tile_page, num_pages: int,
+                 flags=None) -> K.DeviceCache:
+    H = src.shape[1]
+    dc = K.DeviceCache(kfmt(f), num_pages, H)
+    K.kv_quantize(dc, to_dev(src, dtype), i32(tile_src_token), i32(tile_valid), i32(tile_page), status_flags=flags)
+    return dc
+
+
+def orc_quantize(f: W.Fmt, src: np.ndarray, dtype: str, tile_src_token, tile_valid, tile_page, num_pages: int):
+    hc = O.HostCache(f, num_pages, src.shape[1])
+    fl = O.quantize_cache(hc, src, ORC_DT[dtype], tile_src_token, tile_valid, tile_page, nthreads=16)
+    return hc, fl
+
+
+def rel_rowwise(a: np.ndarray, b: np.ndarray) -> float:
+    """max over rows of ||a - b||_inf / ||b||_inf (rows = last axis); zero rows skipped."""
+    a2 = a.reshape(-1, a.shape[-1])
+    b2 = b.reshape(-1, b.shape[-1])
+    den = np.abs(b2).max(axis=1)
+    num = np.abs(a2 - b2).max(axis=1)
+    keep = den > 0
+    if not keep.any():
+        return float(num.max()) if num.size else 0.0
+    assert np.all(num[~keep] == 0)
+    return float((num[keep] / den[keep]).max())

@@ -1,0 +1,322 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases compare every element; the full-size workloads run in the launch
+configuration of bench.py and compare sampled tiles and sampled decode outputs,
+each recomputed by the oracle from the same seeded inputs.  Decode and
+dequantize are fed the identical stored cache (oracle blocks uploaded).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_quantization_04_amd as K
+import oracle as O
+import workloads as W
+from harness import (DECODE_RTOL, DEQUANT_RTOL, ORC_DT, assert_block_parity, compare_blocks, gpu_quantize, host_copy,
+                     i32, kfmt, orc_quantize, rel_rowwise, to_dev, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f16_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def make_src(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, np.float32)
+    return bf16_bits(x) if dtype == "bf16" else f16_bits(x)
+
+
+def heavy(rng, tokens, H, D, outliers=3):
+    s = np.exp(rng.standard_normal((H, D)))
+    for h in range(H):
+        s[h, rng.choice(D, outliers, replace=False)] *= 20
+    return rng.standard_normal((tokens, H, D)) * s[None]
+
+
+def tiles_for(lens, T, rng=None):
+    src, valid, page = [], [], []
+    tok = 0
+    for L in lens:
+        npg = max(1, (L + T - 1) // T) if L > 0 else 1
+        for p in range(npg):
+            src.append(tok + p * T)
+            valid.append(max(0, min(T, L - p * T)))
+        tok += L
+    P = len(src)
+    page = rng.permutation(P) if rng is not None else np.arange(P)
+    return np.array(src), np.array(valid), np.array(page), tok
+
+
+# ----------------------------------------------------------------------------- quantizer, every element
+SMALL = [
+    # D, T, bits, G, h, iters, dtype, layout, R
+    (64, 64, 4, 64, 64, 4, "f32", 0, 0),
+    (64, 16, 2, 32, 64, 2, "bf16", 1, 0),
+    (128, 128, 4, 128, 128, 4, "bf16", 0, 0),
+    (128, 128, 2, 128, 128, 4, "bf16", 1, 0),
+    (128, 16, 3, 128, 128, 2, "bf16", 0, 0),
+    (128, 16, 3, 128, 128, 2, "bf16", 1, 0),
+    (128, 32, 8, 64, 32, 1, "f16", 0, 0),
+    (128, 64, 4, 16, 128, 0, "f32", 1, 0),
+    (256, 32, 4, 256, 256, 3, "bf16", 0, 0),
+    (512, 128, 4, 512, 512, 4, "bf16", 0, 64),
+    (512, 16, 3, 128, 512, 2, "bf16", 0, 64),
+    (128, 128, 4, 128, 1, 4, "bf16", 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "D{}T{}b{}G{}h{}N{}{}L{}R{}".format(*c))
+def test_quantize_every_element(gpu, case):
+    D, T, bits, G, h, iters, dtype, layout, R = case
+    log("quantize case", case)
+    rng = np.random.default_rng(hash(case) % 2 ** 32)
+    f = W.Fmt(D, R, T, h, G, bits, iters, layout)
+    H = 2
+    lens = [3 * T + T // 2 + 1, 1, T, 0] if T <= 64 else [2 * T + 37, 1, T]
+    tst, tv, tp, tok = tiles_for(lens, T, rng)
+    x = np.concatenate([heavy(rng, tok, H, D), rng.standard_normal((tok, H, R))], axis=2) if R else heavy(rng, tok, H, D)
+    src = make_src(x, dtype)
+    P = len(tp)
+    flags = torch.zeros(1, dtype=torch.int32, device=gpu)
+    dc = gpu_quantize(f, src, dtype, tst, tv, tp, P, flags=flags)
+    torch.cuda.synchronize()
+    hc, fl = orc_quantize(f, src, dtype, tst, tv, tp, P)
+    st = compare_blocks(host_copy(dc, f), hc, range(P))
+    log("  stats", st)
+    assert_block_parity(st, str(case))
+    assert int(flags.item()) == fl == 0
+
+
+def test_quantize_is_deterministic(gpu):
+    cfg = W.config(1)
+    rng = np.random.default_rng(5)
+    f = cfg.fk
+    src = make_src(heavy(rng, 1024, 8, 128), "bf16")
+    tst, tv, tp, _ = tiles_for([1024], 128)
+    a = gpu_quantize(f, src, "bf16", tst, tv, tp, len(tp))
+    b = gpu_quantize(f, src, "bf16", tst, tv, tp, len(tp))
+    torch.cuda.synchronize()
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.sz, b.sz) and torch.equal(a.cnorm, b.cnorm)
+
+
+def test_flags_nonfinite_and_overflow(gpu):
+    f = W.Fmt(128, 0, 16, 128, 128, 4, 2, 0)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((48, 1, 128)).astype(np.float32)
+    x[3, 0, 7] = np.nan        # tile 0: non-finite input
+    x[20:32, 0, :] *= 1e6      # tile 1: scales and zero points overflow fp16
+    tst, tv, tp, _ = tiles_for([48], 16)
+    flags = torch.zeros(1, dtype=torch.int32, device=gpu)
+    gpu_quantize(f, x, "f32", tst, tv, tp, 3, flags=flags)
+    _, fl = orc_quantize(f, x, "f32", tst, tv, tp, 3)
+    assert int(flags.item()) == fl == (O.FLAG_NONFINITE | O.FLAG_SIDE_OVERFLOW)
+
+
+# ----------------------------------------------------------------------------- dequantize and decode, small
+def small_paged(seed, D=128, T=16, Hq=8, Hkv=2, lens=(300, 1, 77, 16), kbits=4, vbits=3, iters=2, G=None, mla=False,
+                R=0, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    G = G or D
+    fk = W.Fmt(D, R, T, D, G, kbits, iters, 0)
+    fv = None if mla else W.Fmt(D, 0, T, D, G, vbits, iters, 1)
+    tst, tv, tp, tok = tiles_for(list(lens), T, rng)
+    P = len(tp)
+    kx = heavy(rng, tok, Hkv, D)
+    if R:
+        kx = np.concatenate([kx, rng.standard_normal((tok, Hkv, R))], axis=2)
+    ks = make_src(kx, dtype)
+    vs = None if mla else make_src(rng.standard_normal((tok, Hkv, D)), dtype)
+    q = make_src(rng.standard_normal((len(lens), Hq, D + R)), dtype)
+    npg = [max(1, (L + T - 1) // T) for L in lens]
+    bt = np.zeros((len(lens), max(npg)), np.int32)
+    k = 0
+    for s, n in enumerate(npg):
+        bt[s, :n] = tp[k:k + n]
+        k += n
+    return dict(fk=fk, fv=fv, tst=tst, tv=tv, tp=tp, P=P, ks=ks, vs=vs, q=q, bt=bt, lens=np.array(lens), dtype=dtype,
+                Hq=Hq, Hkv=Hkv)
+
+
+def run_decode_case(gpu, w, sm, splits=0):
+    kc, _ = orc_quantize(w["fk"], w["ks"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
+    vc = None
+    if w["fv"] is not None:
+        vc, _ = orc_quantize(w["fv"], w["vs"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
+    ref = O.decode_attn(w["q"], ORC_DT[w["dtype"]], kc, vc, w["bt"], w["lens"], sm, folded=False, nthreads=16)
+    dk = K.DeviceCache(kfmt(w["fk"]), w["P"], w["Hkv"])
+    upload(kc, dk)
+    dv = None
+    if vc is not None:
+        dv = K.DeviceCache(kfmt(w["fv"]), w["P"], w["Hkv"])
+        upload(vc, dv)
+    out = K.kv_decode_attn(to_dev(w["q"], w["dtype"]), dk, dv, i32(w["bt"]), i32(w["lens"]), int(w["lens"].max()), sm,
+                           num_splits=splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), ref, kc, vc, dk, dv
+
+
+DEC_SMALL = [
+    dict(),
+    dict(T=128, lens=(1000, 129, 5), kbits=4, vbits=2, iters=4),
+    dict(T=64, D=64, lens=(256,), kbits=4, vbits=4, iters=4, Hq=2, Hkv=2, dtype="f32"),
+    dict(G=32, lens=(100, 33)),
+    dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(700, 128, 1), iters=4),
+    dict(mla=True, D=512, R=64, T=128, Hq=128, Hkv=1, lens=(300,), iters=4),
+]
+
+
+@pytest.mark.parametrize("kw", DEC_SMALL, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) or "default")
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_small(gpu, kw, splits):
+    log("decode case", kw, "splits", splits)
+    w = small_paged(11 + len(kw), **kw)
+    out, ref, *_ = run_decode_case(gpu, w, 1.0 / math.sqrt(w["fk"].head_dim + w["fk"].rope_dim), splits)
+    err = rel_rowwise(out, ref)
+    log("  decode rel err", err)
+    assert err <= DECODE_RTOL
+
+
+def test_decode_closed_forms(gpu):
+    """q = 0 averages the values; sequence length 0 gives zeros."""
+    w = small_paged(3, lens=(50, 0, 17))
+    w["q"] = np.zeros_like(w["q"])
+    out, ref, *_ = run_decode_case(gpu, w, 0.1)
+    assert rel_rowwise(out[[0, 2]], ref[[0, 2]]) <= DECODE_RTOL
+    assert np.all(out[1] == 0)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(T=128, lens=(300, 5), kbits=4, vbits=2, iters=4),
+                                dict(mla=True, D=512, R=64, T=128, Hkv=1, Hq=4, lens=(260,), iters=4)])
+def test_dequantize_same_cache(gpu, kw):
+    w = small_paged(21, **kw)
+    for f, srcs in ((w["fk"], w["ks"]), (w["fv"], w["vs"])):
+        if f is None:
+            continue
+        hc, _ = orc_quantize(f, srcs, w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
+        dc = K.DeviceCache(kfmt(f), w["P"], w["Hkv"])
+        upload(hc, dc)
+        ref = O.dequantize_cache(hc, w["tp"], w["tv"], nthreads=16)
+        out = K.kv_dequantize(dc, i32(w["tp"]), i32(w["tv"])).cpu().numpy().astype(np.float64)
+        err = rel_rowwise(out, ref)
+        log("dequant rel err", err)
+        assert err <= DEQUANT_RTOL
+
+
+# ----------------------------------------------------------------------------- full-size workloads, sampled
+def full_gpu_caches(cfg, gpu):
+    """Quantize the whole workload on the GPU exactly as bench.py does."""
+    ks = W.gen_k(cfg)
+    dk = gpu_quantize(cfg.fk, ks, cfg.src_dtype, cfg.tile_src_token, cfg.tile_valid, cfg.tile_page, cfg.num_pages)
+    del ks
+    dv = None
+    if cfg.fv is not None:
+        vs = W.gen_v(cfg)
+        dv = gpu_quantize(cfg.fv, vs, cfg.src_dtype, cfg.tile_src_token, cfg.tile_valid, cfg.tile_page, cfg.num_pages)
+        del vs
+    torch.cuda.synchronize()
+    return dk, dv
+
+
+def tile_sample(cfg, n, seed):
+    rng = np.random.default_rng(seed)
+    tiles = rng.choice(cfg.num_pages, size=min(n, cfg.num_pages), replace=False)
+    # always include a partial tile when there is one
+    partial = np.nonzero(cfg.tile_valid < cfg.fk.tile_tokens)[0]
+    if partial.size:
+        tiles[0] = partial[0]
+    heads = rng.integers(0, cfg.num_kv_heads, size=tiles.size)
+    return tiles, heads
+
+
+def oracle_tile(cfg, f, tile, head, which):
+    T = f.tile_tokens
+    t0 = int(cfg.tile_src_token[tile])
+    n = int(cfg.tile_valid[tile])
+    x = (W.gen_k if which == "k" else W.gen_v)(cfg, t0, t0 + T if t0 + T <= cfg.total_tokens else cfg.total_tokens)
+    x = np.ascontiguousarray(x[:, head:head + 1])
+    hc = O.HostCache(f, 1, 1)
+    O.quantize_cache(hc, x, ORC_DT[cfg.src_dtype], [0], [n], [0], nthreads=1)
+    return hc
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4])
+def test_full_workload_sampled(gpu, ci):
+    cfg = W.config(ci)
+    log("full workload", ci, cfg.name)
+    dk, dv = full_gpu_caches(cfg, gpu)
+    # ---- quantizer: sampled tiles, every element of each
+    tiles, heads = tile_sample(cfg, 24, ci)
+    for which, f, dc in (("k", cfg.fk, dk), ("v", cfg.fv, dv)):
+        if f is None:
+            continue
+        st = None
+        for tile, head in zip(tiles, heads):
+            orc = oracle_tile(cfg, f, tile, head, which)
+            page = int(cfg.tile_page[tile])
+            g = O.HostCache(f, 1, 1)
+            g.codes[0, 0] = dc.codes[page, head].cpu().numpy()
+            g.sz[0, 0] = dc.sz[page, head].cpu().numpy().view(np.uint16)
+            g.cnorm[0, 0] = dc.cnorm[page, head].cpu().numpy().view(np.uint16)
+            if g.rope is not None:
+                g.rope[0, 0] = dc.rope[page, head].cpu().numpy().view(np.uint16)
+            st = compare_blocks(g, orc, [0], stats=st)
+        log("  quantize", which, st)
+        assert_block_parity(st, f"config {ci} {which}")
+
+    # ---- decode on the bench launch configuration: one sequence and kv head get
+    # the oracle's own blocks, and their outputs are compared
+    rng = np.random.default_rng(100 + ci)
+    s = int(rng.integers(cfg.num_seqs))
+    hk = int(rng.integers(cfg.num_kv_heads))
+    grp = cfg.num_q_heads // cfg.num_kv_heads
+    nq = min(grp, 8)
+    T = cfg.fk.tile_tokens
+    L = int(cfg.seq_lens[s])
+    tsel = np.nonzero(cfg.tile_seq == s)[0]
+    t0, t1 = int(cfg.seq_start[s]), int(cfg.seq_start[s]) + L
+    ks = np.ascontiguousarray(W.gen_k(cfg, t0, t1)[:, hk:hk + 1])
+    loc_src = cfg.tile_src_token[tsel] - t0
+    loc_valid = cfg.tile_valid[tsel]
+    loc_page = np.arange(tsel.size)
+    kc, _ = orc_quantize(cfg.fk, ks, cfg.src_dtype, loc_src, loc_valid, loc_page, tsel.size)
+    vc = None
+    if cfg.fv is not None:
+        vs = np.ascontiguousarray(W.gen_v(cfg, t0, t1)[:, hk:hk + 1])
+        vc, _ = orc_quantize(cfg.fv, vs, cfg.src_dtype, loc_src, loc_valid, loc_page, tsel.size)
+    q = W.gen_q(cfg)
+    qh = np.ascontiguousarray(q[s:s + 1, hk * grp: hk * grp + nq])
+    if nq < grp:  # oracle evaluates a subset of the group's query heads
+        pass
+    ref = O.decode_attn(qh, ORC_DT[cfg.src_dtype], kc, vc, loc_page[None, :], np.array([L]), cfg.sm_scale,
+                        folded=False, nthreads=16)
+    phys = cfg.tile_page[tsel]
+    for hc, dc in ((kc, dk), (vc, dv)):
+        if hc is None:
+            continue
+        idx = torch.from_numpy(phys.astype(np.int64)).to(gpu)
+        dc.codes[idx, hk] = torch.from_numpy(hc.codes[:, 0]).to(gpu)
+        dc.sz[idx, hk] = torch.from_numpy(hc.sz[:, 0].view(np.int16)).to(gpu)
+        dc.cnorm[idx, hk] = torch.from_numpy(hc.cnorm[:, 0].view(np.int16)).to(gpu)
+        if hc.rope is not None:
+            dc.rope[idx, hk] = torch.from_numpy(hc.rope[:, 0].view(np.int16)).to(gpu)
+    out = K.kv_decode_attn(to_dev(q, cfg.src_dtype), dk, dv, i32(cfg.block_table), i32(cfg.seq_lens),
+                           int(cfg.seq_lens.max()), cfg.sm_scale)
+    torch.cuda.synchronize()
+    got = out[s, hk * grp: hk * grp + nq].cpu().numpy().astype(np.float64)
+    err = rel_rowwise(got, ref[0])
+    log("  decode seq", s, "kv head", hk, "rel err", err)
+    assert err <= DECODE_RTOL
