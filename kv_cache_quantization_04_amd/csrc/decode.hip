@@ -205,7 +205,15 @@ __global__ void __launch_bounds__(DEC_NT) decode_reduce_kernel(DecodeArgs a) {
     for (int j = threadIdx.x; j < Dv; j += DEC_NT) a.out[((int64_t)s * a.Hq + hq) * Dv + j] = buf[j] * sc;
 }
 
+bool decode_mfma_supported(const DecodeArgs &a);
+bool launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+
 bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    if (decode_mfma_supported(a)) {
+        if (!launch_decode_mfma(a, stream)) return false;
+        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * a.Dv, stream, a);
+        return true;
+    }
     const size_t smem = sizeof(float) * (2 * a.hc * a.D + a.hc * (a.D / a.kG) + a.hc * a.R + a.hc * a.T + 3 * a.hc);
     if (a.hc * a.Dv > DEC_NT * DEC_MAXO) return false;
     if (smem > 64 * 1024 &&

@@ -1,0 +1,405 @@
+// Split-K decode attention over the paged quantized cache with MFMA (gfx950),
+// head_dim 128, grouped-query attention with up to 16 query heads per kv head.
+//
+// Scores and value accumulation are dense contractions per page:
+//   scores^T [tokens x heads]  = A_K [tokens x channels] . qbar^T [channels x heads]
+//   o'^T     [channels x heads] = A_V [channels x tokens] . P~^T [tokens x heads]
+// run as v_mfma_f32_16x16x32_f16 tiles with fp32 accumulation. The codes enter
+// exactly, centred (code - 2^(b-1)); the K normalizer is folded into the query
+// per page, q'_j = qbar_j c_K,j in fp32. Query and probability operands are
+// split into fp16 hi + lo parts (two MFMAs each), about 22 significant bits,
+// after a per-page power-of-two scaling that puts their largest value near 2^14
+// (clear of fp16 overflow, and of the subnormal range where lo would lose bits).
+//   score_t = sm * ( S_t * [A_K . q']_t + (Z_t + 2^(b-1) S_t) * sum_j q'_j )
+//   o'_j   += c_V,j * ( [A_V . P~]_j + sum_t p_t (Z_t + 2^(b-1) S_t) ),  P~_t = p_t S_t
+// Each wave walks its own pages (online softmax per wave); the four waves of a
+// workgroup merge before writing the split partial. Token order inside a page
+// is permuted so that the score tile of two 16-token M-tiles lands, lane for
+// lane, in the layout of the 32-token operand of the value product.
+#include "common.h"
+#include "launch.h"
+
+namespace kvq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int MD = 128;      // head_dim of this kernel
+constexpr int MNT = 256;     // threads per workgroup (4 waves)
+
+__device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+__device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Eight codes of one lane chunk -> half8 in MFMA element order kk, where element
+// kk holds chunk position e(kk) = (kk >> 1) + 4 (kk & 1), centred by 2^(b-1).
+// `lo` holds the chunk's bits starting at bit 0 (b * 8 bits used).
+template <int B>
+__device__ __forceinline__ half8 unpack8(uint32_t lo) {
+    constexpr uint32_t MAGIC = 0x64006400u;  // fp16 1024 in both halves
+    constexpr _Float16 BIAS = (_Float16)(1024 + (1 << (B - 1)));
+    uint32_t p[4];
+    if constexpr (B == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = ((lo >> (4 * i)) & 0x000F000Fu) | MAGIC;
+    } else if constexpr (B == 2) {
+        // codes 0..3 in bits 0..7, 4..7 in bits 8..15: move the second byte to bit 16
+        const uint32_t s = (lo & 0xFFu) | ((lo & 0xFF00u) << 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = ((s >> (2 * i)) & 0x00030003u) | MAGIC;
+    } else {  // B == 3: codes 0..3 in bits 0..11, 4..7 in bits 12..23
+        const uint32_t s = (lo & 0xFFFu) | ((lo & 0xFFF000u) << 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = ((s >> (3 * i)) & 0x00070007u) | MAGIC;
+    }
+    half8 r;
+    const half2v bias = {BIAS, BIAS};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2v h = as_h2(p[i]) - bias;
+        r[2 * i] = h[0];
+        r[2 * i + 1] = h[1];
+    }
+    return r;
+}
+
+// 2^(14 - floor(log2 m)) for m > 0 (1 for m == 0 or not finite): scales values
+// with maximum magnitude m into [2^14, 2^15).
+__device__ __forceinline__ float pow2_scale_for(float m) {
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xffu);
+    if (e == 0 || e == 0xff) return 1.f;
+    const int se = min(254, 268 - e);  // biased exponent of 2^(14 - (e - 127))
+    return __uint_as_float((uint32_t)se << 23);
+}
+
+// fp32 -> fp16 hi + lo split of one value.
+__device__ __forceinline__ void split_h(float x, _Float16 &hi, _Float16 &lo) {
+    hi = (_Float16)x;
+    lo = (_Float16)(x - (float)hi);
+}
+
+__device__ __forceinline__ float xlane_sum_q(float v) {  // sum over the 4 lanes sharing lane & 15
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+__device__ __forceinline__ float xlane_max_q(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// The 24 bits of eight 3-bit codes starting at byte-aligned bit `bit0`
+// (three byte loads: never reads past the chunk).
+__device__ __forceinline__ uint32_t load_bits3(const uint8_t *base, int64_t bit0) {
+    const uint8_t *p = base + (bit0 >> 3);
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+}
+
+template <int T, int KB, int VB>
+__global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
+    constexpr int MT = T / 16;                 // 16-token M-tiles of the score product
+    constexpr int KSV = T >= 32 ? T / 32 : 1;  // 32-token K-steps of the value product
+    constexpr int KCB = 32 * KB / 8;           // bytes of one lane's 32-channel K chunk
+    __shared__ float qs[16][MD];
+    __shared__ float red_o[4][16][MD + 1];
+    __shared__ float red_ml[4][16][2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
+    const int g = a.grp;
+    const int L = a.seq_lens[s];
+    const int npages = min((L + T - 1) / T, a.bt_stride);
+    const int pps = (npages + a.splits - 1) / a.splits;
+    const int p0 = split * pps, p1 = min(npages, p0 + pps);
+
+    // ---- rotated query qbar = q Q for the g heads of this kv head (rows >= g zero)
+    for (int e = tid; e < 16 * MD; e += MNT) {
+        const int hh = e / MD, j = e % MD;
+        qs[hh][j] = hh < g ? load_as_float(a.q, a.q_dtype, ((int64_t)s * a.Hq + hk * g + hh) * MD + j) : 0.f;
+    }
+    __syncthreads();
+    for (int len = 1; len < a.kh; len <<= 1) {
+        for (int e = tid; e < 16 * MD / 2; e += MNT) {
+            const int hh = e / (MD / 2), pe = e % (MD / 2);
+            const int i = (pe / len) * 2 * len + pe % len;
+            const float x = qs[hh][i], y = qs[hh][i + len];
+            qs[hh][i] = x + y;
+            qs[hh][i + len] = x - y;
+        }
+        __syncthreads();
+    }
+    const float qscale = 1.0f / sqrtf((float)a.kh);
+    // B operand of the score product: lane (head l16, chunk lq), K-step st covers
+    // channels lq*32 + st*8 + e(kk); qv holds qbar of those channels in (st, e) order.
+    float qv[32];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[st * 8 + e] = qs[l16][lq * 32 + st * 8 + e] * qscale;
+
+    const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
+    constexpr float KC = (float)(1 << (KB - 1)), VC = (float)(1 << (VB - 1));
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[8];
+#pragma unroll
+    for (int mc = 0; mc < 8; ++mc) o[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int pi = p0 + wave; pi < p1; pi += 4) {
+        const int page = a.bt[(int64_t)s * a.bt_stride + pi];
+        if (page < 0 || page >= a.num_pages) continue;
+        const int rows = min(T, L - pi * T);
+        const int64_t kblk = (int64_t)page * a.Hkv + hk;
+
+        // c_K of the lane's 32 channels (lq*32 ..)
+        const uint4 *cp = reinterpret_cast<const uint4 *>(a.kcn + kblk * MD + lq * 32);
+        uint32_t cw[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = cp[i];
+            cw[4 * i] = v.x; cw[4 * i + 1] = v.y; cw[4 * i + 2] = v.z; cw[4 * i + 3] = v.w;
+        }
+        // q' = qbar o c_K for this page, scaled by 2^sq, as fp16 hi + lo in MFMA element order
+        float qt[32];
+        float qc = 0.f, qmax = 0.f;  // sum_j q'_j and max |q'_j| over the lane's channels
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w = cw[st * 4 + (e >> 1)];
+                const float x = qv[st * 8 + e] * half_bits_to_float((e & 1) ? (w >> 16) : (w & 0xffffu));
+                qt[st * 8 + e] = x;
+                qc += x;
+                qmax = fmaxf(qmax, fabsf(x));
+            }
+        qc = xlane_sum_q(qc);
+        const float qsc = pow2_scale_for(xlane_max_q(qmax));
+        const float qinv = 1.0f / qsc;
+        half8 qhi[4], qlo[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const int e = (kk >> 1) + 4 * (kk & 1);
+                _Float16 hi, lo;
+                split_h(qt[st * 8 + e] * qsc, hi, lo);
+                qhi[st][kk] = hi;
+                qlo[st][kk] = lo;
+            }
+
+        // ---- scores: one MFMA chain per 16-token M-tile
+        const uint8_t *kbase = a.kcodes + kblk * (T * MD * KB / 8);
+        f32x4 sc[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            int tok;
+            if constexpr (T >= 32) tok = 32 * (j >> 1) + 8 * (l16 >> 2) + 4 * (j & 1) + (l16 & 3);
+            else tok = 8 * ((l16 >> 2) & 1) + 4 * (l16 >> 3) + (l16 & 3);
+            const uint8_t *row = kbase + tok * (MD * KB / 8) + lq * KCB;
+            uint32_t kw[KB];
+#pragma unroll
+            for (int i = 0; i < KB; ++i) kw[i] = reinterpret_cast<const uint32_t *>(row)[i];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                // 8 codes of K-step st start at bit st*8*KB of the chunk
+                const int bit = st * 8 * KB;
+                uint32_t bitsv;
+                if (bit % 32 == 0) bitsv = kw[bit / 32];
+                else bitsv = __builtin_amdgcn_alignbit(kw[bit / 32 + 1 < KB ? bit / 32 + 1 : bit / 32], kw[bit / 32], bit % 32);
+                const half8 ak = unpack8<KB>(bitsv);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[st], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[st], acc, 0, 0, 0);
+            }
+            sc[j] = acc;
+        }
+
+        // ---- online softmax over this page (per head l16; lanes hold tokens)
+        float pmax = -INFINITY;
+        uint4 vzq[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            int tok0;
+            if constexpr (T >= 32) tok0 = 32 * (j >> 1) + 8 * lq + 4 * (j & 1);
+            else tok0 = 8 * (lq & 1) + 4 * (lq >> 1);
+            const uint4 kz = *reinterpret_cast<const uint4 *>(a.ksz + (kblk * T + tok0) * 2);
+            vzq[j] = *reinterpret_cast<const uint4 *>(a.vsz + (kblk * T + tok0) * 2);
+            const uint32_t kzw[4] = {kz.x, kz.y, kz.z, kz.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float S = half_bits_to_float(kzw[i] & 0xffffu), Z = half_bits_to_float(kzw[i] >> 16);
+                float x = sml2 * __builtin_fmaf(S * qinv, sc[j][i], (Z + KC * S) * qc);
+                if (tok0 + i >= rows) x = -INFINITY;
+                sc[j][i] = x;
+                pmax = fmaxf(pmax, x);
+            }
+        }
+        pmax = xlane_max_q(pmax);
+        const float m_new = fmaxf(m_run, pmax);
+        const float alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+        // P~ = p S_V scaled by 2^sp with max_t S_V,t near 2^14 (p <= 1)
+        float smax = 0.f;
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            const uint32_t vzw[4] = {vzq[j].x, vzq[j].y, vzq[j].z, vzq[j].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) smax = fmaxf(smax, fabsf(half_bits_to_float(vzw[i] & 0xffffu)));
+        }
+        const float psc = pow2_scale_for(xlane_max_q(smax));
+        float psum = 0.f, zs = 0.f;
+        _Float16 phi[MT][4], plo[MT][4];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            const uint32_t vzw[4] = {vzq[j].x, vzq[j].y, vzq[j].z, vzq[j].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float SV = half_bits_to_float(vzw[i] & 0xffffu), ZV = half_bits_to_float(vzw[i] >> 16);
+                const float p = exp2f(sc[j][i] - m_new);
+                psum += p;
+                zs = __builtin_fmaf(p, ZV + VC * SV, zs);
+                split_h(p * SV * psc, phi[j][i], plo[j][i]);
+            }
+        }
+        const float pinv = 1.0f / psc;
+        l_run = __builtin_fmaf(l_run, alpha, psum);
+        zs = xlane_sum_q(zs);
+
+        // ---- P~ as the B operand of the value product: K-step sv, lane (head, lq)
+        // element kk <-> token 32 sv + 8 lq + e(kk), e < 4 from M-tile 2sv, e >= 4 from 2sv+1
+        half8 pbh[KSV], pbl[KSV];
+        if constexpr (T >= 32) {
+#pragma unroll
+            for (int sv = 0; sv < KSV; ++sv)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pbh[sv][2 * i] = phi[2 * sv][i];
+                    pbh[sv][2 * i + 1] = phi[2 * sv + 1][i];
+                    pbl[sv][2 * i] = plo[2 * sv][i];
+                    pbl[sv][2 * i + 1] = plo[2 * sv + 1][i];
+                }
+        } else {
+            // T = 16: lanes lq = 0, 1 take tokens 8 lq + e; the upper four come from lane + 32
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float hu = __shfl_xor((float)phi[0][i], 32, 64);
+                const float lu = __shfl_xor((float)plo[0][i], 32, 64);
+                const bool act = lq < 2;
+                pbh[0][2 * i] = act ? phi[0][i] : (_Float16)0.f;
+                pbh[0][2 * i + 1] = act ? (_Float16)hu : (_Float16)0.f;
+                pbl[0][2 * i] = act ? plo[0][i] : (_Float16)0.f;
+                pbl[0][2 * i + 1] = act ? (_Float16)lu : (_Float16)0.f;
+            }
+        }
+
+        // ---- values: channel tiles mc; lane (channel 16 mc + l16, tokens 32 sv + 8 lq ..)
+        const uint8_t *vbase = a.vcodes + kblk * (T * MD * VB / 8);
+        const uint16_t *vcn = a.vcn + kblk * MD;
+#pragma unroll
+        for (int mc = 0; mc < 8; ++mc) {
+            const int ch = 16 * mc + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sv = 0; sv < KSV; ++sv) {
+                half8 av;
+                if (T >= 32 || lq < 2) {
+                    const int64_t bit0 = ((int64_t)ch * T + 32 * sv + 8 * lq) * VB;
+                    uint32_t bitsv;
+                    if constexpr (VB == 4) bitsv = reinterpret_cast<const uint32_t *>(vbase)[bit0 >> 5];
+                    else if constexpr (VB == 2) bitsv = reinterpret_cast<const uint16_t *>(vbase)[bit0 >> 4];
+                    else bitsv = load_bits3(vbase, bit0);
+                    av = unpack8<VB>(bitsv);
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) av[kk] = (_Float16)0.f;
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbh[sv], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbl[sv], acc, 0, 0, 0);
+            }
+            // fold: o' = alpha o' + c_V (acc + zs); rows 4 lq + i of tile mc are channels
+            const uint2 cv2 = *reinterpret_cast<const uint2 *>(vcn + 16 * mc + 4 * lq);
+            const float cvv[4] = {half_bits_to_float(cv2.x & 0xffffu), half_bits_to_float(cv2.x >> 16),
+                                  half_bits_to_float(cv2.y & 0xffffu), half_bits_to_float(cv2.y >> 16)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf(o[mc][i], alpha, cvv[i] * __builtin_fmaf(acc[i], pinv, zs));
+        }
+    }
+
+    // ---- merge the four waves, write the split partial (m, l in log2 units -> natural)
+    l_run = xlane_sum_q(l_run);
+    if (lq == 0) {
+        red_ml[wave][l16][0] = m_run;
+        red_ml[wave][l16][1] = l_run;
+    }
+#pragma unroll
+    for (int mc = 0; mc < 8; ++mc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_o[wave][l16][16 * mc + 4 * lq + i] = o[mc][i];
+    __syncthreads();
+    for (int e = tid; e < g * MD; e += MNT) {
+        const int hh = e / MD, j = e % MD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[w][hh][0]);
+        float acc = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float mw = red_ml[w][hh][0];
+            if (mw != -INFINITY) {
+                const float f = exp2f(mw - M);
+                acc = __builtin_fmaf(f, red_o[w][hh][j], acc);
+                lsum = __builtin_fmaf(f, red_ml[w][hh][1], lsum);
+            }
+        }
+        float *wsr = a.ws + (((int64_t)s * a.Hq + hk * g + hh) * a.splits + split) * (MD + 2);
+        wsr[j] = acc;
+        if (j == 0) {
+            // partial max stored in natural-log units for the merge kernel
+            wsr[MD] = M == -INFINITY ? -INFINITY : M * 0.6931471805599453f;
+            wsr[MD + 1] = lsum;
+        }
+    }
+}
+
+bool decode_mfma_supported(const DecodeArgs &a) {
+    if (a.D != MD || a.R != 0 || a.Dv != MD) return false;
+    if (a.kG != MD || a.vG != MD) return false;
+    if (a.grp > 16 || 16 % a.grp != 0 || a.hc != a.grp) return false;
+    if (a.klayout != KVQ_TOKEN_MAJOR || a.vlayout != KVQ_CHANNEL_MAJOR || a.vH != a.Hkv) return false;
+    if (!(a.kbits >= 2 && a.kbits <= 4) || !(a.vbits >= 2 && a.vbits <= 4)) return false;
+    return a.T == 16 || a.T == 32 || a.T == 64 || a.T == 128;
+}
+
+template <int T, int KB>
+static bool launch_vb(const DecodeArgs &a, hipStream_t stream) {
+    const dim3 grid(a.splits, a.Hkv, a.B);
+    switch (a.vbits) {
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 2>), grid, dim3(MNT), 0, stream, a); return true;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 3>), grid, dim3(MNT), 0, stream, a); return true;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 4>), grid, dim3(MNT), 0, stream, a); return true;
+    }
+    return false;
+}
+
+template <int T>
+static bool launch_kb(const DecodeArgs &a, hipStream_t stream) {
+    switch (a.kbits) {
+    case 2: return launch_vb<T, 2>(a, stream);
+    case 3: return launch_vb<T, 3>(a, stream);
+    case 4: return launch_vb<T, 4>(a, stream);
+    }
+    return false;
+}
+
+bool launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+    switch (a.T) {
+    case 16: return launch_kb<16>(a, stream);
+    case 32: return launch_kb<32>(a, stream);
+    case 64: return launch_kb<64>(a, stream);
+    case 128: return launch_kb<128>(a, stream);
+    }
+    return false;
+}
+
+}  // namespace kvq

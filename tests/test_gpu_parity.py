@@ -128,7 +128,7 @@ def test_flags_nonfinite_and_overflow(gpu):
 
 # ----------------------------------------------------------------------------- dequantize and decode, small
 def small_paged(seed, D=128, T=16, Hq=8, Hkv=2, lens=(300, 1, 77, 16), kbits=4, vbits=3, iters=2, G=None, mla=False,
-                R=0, dtype="bf16"):
+                R=0, dtype="bf16", qscale=1.0):
     rng = np.random.default_rng(seed)
     G = G or D
     fk = W.Fmt(D, R, T, D, G, kbits, iters, 0)
@@ -140,7 +140,7 @@ def small_paged(seed, D=128, T=16, Hq=8, Hkv=2, lens=(300, 1, 77, 16), kbits=4, 
         kx = np.concatenate([kx, rng.standard_normal((tok, Hkv, R))], axis=2)
     ks = make_src(kx, dtype)
     vs = None if mla else make_src(rng.standard_normal((tok, Hkv, D)), dtype)
-    q = make_src(rng.standard_normal((len(lens), Hq, D + R)), dtype)
+    q = make_src(rng.standard_normal((len(lens), Hq, D + R)) * qscale, dtype)
     npg = [max(1, (L + T - 1) // T) for L in lens]
     bt = np.zeros((len(lens), max(npg)), np.int32)
     k = 0
@@ -171,6 +171,13 @@ def run_decode_case(gpu, w, sm, splits=0):
 
 DEC_SMALL = [
     dict(),
+    dict(T=128, lens=(600, 131), kbits=4, vbits=4, iters=4),
+    dict(T=32, lens=(250, 33, 31), kbits=2, vbits=4, iters=3),
+    dict(T=64, lens=(500, 64, 1), kbits=3, vbits=2, iters=2, Hq=16, Hkv=1),
+    dict(T=16, lens=(1000, 17), kbits=3, vbits=3, Hq=16, Hkv=2),
+    # nearly flat softmax over a long context: many tiny probabilities
+    dict(T=128, lens=(4096,), kbits=4, vbits=4, iters=4, qscale=0.01),
+    dict(T=16, lens=(3000,), kbits=3, vbits=3, qscale=0.01),
     dict(T=128, lens=(1000, 129, 5), kbits=4, vbits=2, iters=4),
     dict(T=64, D=64, lens=(256,), kbits=4, vbits=4, iters=4, Hq=2, Hkv=2, dtype="f32"),
     dict(G=32, lens=(100, 33)),
