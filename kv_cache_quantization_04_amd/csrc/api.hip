@@ -112,9 +112,13 @@ int32_t kv_decode_attn_default_splits(int32_t num_seqs, int32_t num_kv_heads, in
                                       int32_t tile_tokens) {
     if (num_seqs <= 0 || num_kv_heads <= 0 || tile_tokens <= 0 || max_seq_len <= 0) return 1;
     const int64_t pages = (max_seq_len + tile_tokens - 1) / tile_tokens;
-    const int64_t target = 2048;  // workgroups in flight: 8 per compute unit
-    int64_t sp = (target + (int64_t)num_seqs * num_kv_heads - 1) / ((int64_t)num_seqs * num_kv_heads);
-    if (sp > pages) sp = pages;
+    // about 4 workgroups per compute unit, and at least 4 pages per split (the
+    // four waves of a workgroup walk pages independently)
+    const int64_t target = 1024;
+    const int64_t units = (int64_t)num_seqs * num_kv_heads;
+    int64_t sp = (target + units - 1) / units;
+    const int64_t cap = (pages + 3) / 4;
+    if (sp > cap) sp = cap;
     if (sp < 1) sp = 1;
     return (int32_t)sp;
 }

@@ -178,40 +178,60 @@ __global__ void __launch_bounds__(DEC_NT) decode_generic_kernel(DecodeArgs a) {
 }
 
 // Merge the split partials of one (sequence, query head), normalize, rotate back.
+// The split weights exp(m_i - M) / l are formed once in LDS, then every output
+// channel is one pass of fused multiply-adds over the splits.
+constexpr int RED_MAX_SPLITS = 1024;
+
 __global__ void __launch_bounds__(DEC_NT) decode_reduce_kernel(DecodeArgs a) {
-    extern __shared__ float buf[];  // [Dv]
+    extern __shared__ float buf[];  // [Dv] outputs, then [splits] weights
+    __shared__ float red[DEC_NT / 64];
     const int hq = blockIdx.x, s = blockIdx.y;
-    const int Dv = a.Dv;
+    const int Dv = a.Dv, tid = threadIdx.x;
+    float *wgt = buf + Dv;
     const float *w = a.ws + ((int64_t)s * a.Hq + hq) * a.splits * (Dv + 2);
+    // M = max_i m_i
     float M = -INFINITY;
-    for (int i = 0; i < a.splits; ++i) M = fmaxf(M, w[i * (Dv + 2) + Dv]);
+    for (int i = tid; i < a.splits; i += DEC_NT) M = fmaxf(M, w[(int64_t)i * (Dv + 2) + Dv]);
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = red[0];
+    for (int i = 1; i < DEC_NT / 64; ++i) M = fmaxf(M, red[i]);
+    __syncthreads();
+    // weights e_i = exp(m_i - M) and l = sum_i e_i l_i
     float l = 0.f;
-    for (int i = 0; i < a.splits; ++i) {
-        const float mi = w[i * (Dv + 2) + Dv];
-        if (mi != -INFINITY) l += __expf(mi - M) * w[i * (Dv + 2) + Dv + 1];
+    for (int i = tid; i < a.splits; i += DEC_NT) {
+        const float mi = w[(int64_t)i * (Dv + 2) + Dv];
+        const float e = mi == -INFINITY ? 0.f : __expf(mi - M);
+        wgt[i] = e;
+        l = __builtin_fmaf(e, w[(int64_t)i * (Dv + 2) + Dv + 1], l);
     }
+    for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = l;
+    __syncthreads();
+    l = 0.f;
+    for (int i = 0; i < DEC_NT / 64; ++i) l += red[i];
     const float invl = l > 0.f ? 1.0f / l : 0.f;
-    for (int j = threadIdx.x; j < Dv; j += DEC_NT) {
+    for (int j = tid; j < Dv; j += DEC_NT) {
         float acc = 0.f;
-        for (int i = 0; i < a.splits; ++i) {
-            const float mi = w[i * (Dv + 2) + Dv];
-            if (mi != -INFINITY) acc = __builtin_fmaf(__expf(mi - M), w[i * (Dv + 2) + j], acc);
-        }
+        for (int i = 0; i < a.splits; ++i) acc = __builtin_fmaf(wgt[i], w[(int64_t)i * (Dv + 2) + j], acc);
         buf[j] = acc * invl;
     }
     __syncthreads();
     lds_fwht(buf, 1, Dv, a.vh);
     const float sc = 1.0f / sqrtf((float)a.vh);
-    for (int j = threadIdx.x; j < Dv; j += DEC_NT) a.out[((int64_t)s * a.Hq + hq) * Dv + j] = buf[j] * sc;
+    for (int j = tid; j < Dv; j += DEC_NT) a.out[((int64_t)s * a.Hq + hq) * Dv + j] = buf[j] * sc;
 }
 
 bool decode_mfma_supported(const DecodeArgs &a);
 bool launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 
 bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    if (a.splits > RED_MAX_SPLITS) return false;
     if (decode_mfma_supported(a)) {
         if (!launch_decode_mfma(a, stream)) return false;
-        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * a.Dv, stream, a);
+        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * (a.Dv + a.splits),
+                           stream, a);
         return true;
     }
     const size_t smem = sizeof(float) * (2 * a.hc * a.D + a.hc * (a.D / a.kG) + a.hc * a.R + a.hc * a.T + 3 * a.hc);
@@ -221,7 +241,8 @@ bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
             hipSuccess)
         return false;
     hipLaunchKernelGGL(decode_generic_kernel, dim3(a.splits, a.Hkv * a.nhc, a.B), dim3(DEC_NT), smem, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * a.Dv, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * (a.Dv + a.splits), stream,
+                       a);
     return true;
 }
 

@@ -344,7 +344,14 @@ __global__ void __launch_bounds__(2 * D) dequant_kernel(DequantArgs a) {
     default: return false;                       \
     }
 
+bool quantize_d128_supported(int D, int T, const QuantArgs &a);
+void launch_quantize_d128(int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
+
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream) {
+    if (quantize_d128_supported(D, T, a)) {
+        launch_quantize_d128(T, num_tiles, a, stream);
+        return true;
+    }
 #define KVQ_LQ(D_, T_) \
     hipLaunchKernelGGL((quantize_kernel<D_, T_>), dim3(num_tiles, a.H), dim3(2 * D_), 0, stream, a)
     KVQ_DISPATCH(KVQ_LQ)

@@ -1,0 +1,417 @@
+// Tile quantizer specialised for head_dim 128, Hadamard block 128, one scale
+// group per token (gfx950). Same method and results as the generic kernel; all
+// cross-lane traffic stays in the VALU (DPP, permlane swaps) or the LDS
+// crossbar without memory (ds_swizzle), and the codes are packed in registers.
+//
+// Workgroup = one (tile, head): 256 threads. Lane l of wave w holds the 8
+// consecutive channels 8 (l & 15) .. + 7 of the R = T/16 consecutive rows
+// starting at 16-row-group rg = 4 w + (l >> 4). The 16 lanes of a DPP row
+// therefore cover one token's 128 channels: the Hadamard butterflies on channel
+// bits 3..6 and every per-token reduction are DPP row operations.
+//
+// Method: "KVarN" project review, Key Features ("Variance-Normalized
+// Quantization Pipeline"): rotate, run row/column RMS normalization rounds,
+// asymmetric round-to-nearest with fp16 scale, zero point and normalizer.
+#include "common.h"
+#include "launch.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int QD = 128;
+constexpr int QNT = 256;
+#ifndef KVQ_QUANT_KEEP_SQUARES
+#define KVQ_QUANT_KEEP_SQUARES 1
+#endif
+#ifndef KVQ_QUANT_MIN_BLOCKS
+#define KVQ_QUANT_MIN_BLOCKS 2
+#endif
+#ifndef KVQ_QUANT_FWHT_DPP
+#define KVQ_QUANT_FWHT_DPP 0
+#endif
+constexpr bool KEEP_SQ = KVQ_QUANT_KEEP_SQUARES != 0;
+
+// DPP controls (gfx9 encoding)
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_ROR4 = 0x124;      // lane i <- lane (i - 4) mod 16
+constexpr int DPP_ROR8 = 0x128;      // lane i <- lane (i - 8) mod 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Partner value across lanes, lane ^ M within 32-lane groups, through the LDS
+// crossbar (ds_swizzle bit mode; no LDS memory, no VALU slot).
+template <int M>
+__device__ __forceinline__ float swz_xor(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
+}
+
+// Sum / min / max over the 16 lanes of a DPP row; every lane gets the same bits.
+__device__ __forceinline__ float row_sum16(float s) {
+    s += dpp<DPP_ROR8>(s);
+    s += dpp<DPP_ROR4>(s);
+    s += dpp<DPP_QUAD_XOR2>(s);
+    s += dpp<DPP_QUAD_XOR1>(s);
+    return s;
+}
+__device__ __forceinline__ float row_min16(float s) {
+    s = fminf(s, dpp<DPP_ROR8>(s));
+    s = fminf(s, dpp<DPP_ROR4>(s));
+    s = fminf(s, dpp<DPP_QUAD_XOR2>(s));
+    return fminf(s, dpp<DPP_QUAD_XOR1>(s));
+}
+__device__ __forceinline__ float row_max16(float s) {
+    s = fmaxf(s, dpp<DPP_ROR8>(s));
+    s = fmaxf(s, dpp<DPP_ROR4>(s));
+    s = fmaxf(s, dpp<DPP_QUAD_XOR2>(s));
+    return fmaxf(s, dpp<DPP_QUAD_XOR1>(s));
+}
+
+__device__ __forceinline__ void load8_bf16(const uint16_t *p, float (&v)[8]) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// Pack eight byte codes c[0..7] (< 2^BITS) of consecutive stream positions into
+// the little-endian bitstream word(s): returns the low 8*BITS bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack8(const float (&u)[8]) {
+    // u are rounded-to-be codes in fp32; v_cvt_pk_u8_f32 rounds to nearest even
+    // and clamps below at 0 (the upper clamp is applied by the caller)
+    if constexpr (BITS == 4) {
+        uint32_t x = 0, y = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            x = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * b], b, x);
+            y = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * b + 1], b, y);
+        }
+        return x | (y << 4);
+    } else {  // BITS == 2
+        uint32_t d[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[i] = __builtin_amdgcn_cvt_pk_u8_f32(u[i], 0, d[i]);
+            d[i] = __builtin_amdgcn_cvt_pk_u8_f32(u[i + 4], 1, d[i]);
+        }
+        return d[0] | (d[1] << 2) | (d[2] << 4) | (d[3] << 6);
+    }
+}
+
+}  // namespace
+
+template <int T, int BITS, int LAYOUT>
+__global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kernel(QuantArgs a, int num_items) {
+    constexpr int R = T / 16;  // rows per thread
+    constexpr float LEVELS = (float)((1 << BITS) - 1);
+    __shared__ float colsum[2][4][QD];  // [buffer][wave][channel]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cc = lane & 15, rr = lane >> 4;
+    const int rg = wave * 4 + rr;
+    const uint16_t *srcbase = reinterpret_cast<const uint16_t *>(a.src) + cc * 8;
+
+    // Persistent workgroups: item = tile * H + head, strided by the grid. The
+    // next item's source rows are copied HBM -> LDS by direct-to-LDS loads while
+    // the current item is processed in registers. Each wave load instruction
+    // moves 4 rows (1 KB): lane l -> row 4 b + (l >> 4), 16-byte chunk l & 15.
+    __shared__ uint4 stage[T * QD * 2 / 16];
+    auto fetch = [&](int itm) {
+        const int tl = itm / a.H, hd = itm % a.H;
+        const int nv = a.tile_valid[tl];
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src) + hd * a.stride_head +
+                              (int64_t)a.tile_src_token[tl] * a.stride_token + (lane & 15) * 8;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int b = wave * R + i;
+            const int row = 4 * b + (lane >> 4);
+            if (row < nv)
+                __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)row * a.stride_token),
+                                                 (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
+        }
+    };
+    int item = blockIdx.x;
+    if (item < num_items) fetch(item);
+    for (; item < num_items; item += gridDim.x) {
+    const int tile = item / a.H, head = item % a.H;
+    const int dst_page = a.tile_dst_page[tile];
+    const int n = a.tile_valid[tile];
+    const int64_t blk = (int64_t)dst_page * a.H + head;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into LDS have landed
+    __syncthreads();                // and every other wave's
+    float y[R][8];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int row = rg * R + k;
+        const uint4 v = row < n ? stage[row * 16 + cc] : uint4{0, 0, 0, 0};
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[k][2 * i] = __uint_as_float(w4[i] << 16);
+            y[k][2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+        }
+    }
+    __syncthreads();  // the staging buffer is free again
+    if (item + (int)gridDim.x < num_items) fetch(item + gridDim.x);
+    if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
+
+    // ---- unnormalized Walsh-Hadamard transform along the 128 channels -------
+#pragma unroll
+    for (int s = 1; s < 8; s <<= 1)
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (!(j & s)) {
+                    const float p = y[k][j], q = y[k][j | s];
+                    y[k][j] = p + q;
+                    y[k][j | s] = p - q;
+                }
+    // Cross-lane stages (lane bit b <-> channel bit 3 + b) in the sign-deferred
+    // form t' = t + s_b * partner(t), s_b = -1 on lanes with bit b set: one fused
+    // multiply-add per value, the partner read through ds_swizzle. After
+    // the four stages t = sigma * Y with sigma = s_1 s_2 s_4 s_8 per lane; the
+    // squares ignore sigma and it is folded into the per-channel multiplier.
+    const float s1 = (cc & 1) ? -1.f : 1.f, s2 = (cc & 2) ? -1.f : 1.f;
+    const float s4 = (cc & 4) ? -1.f : 1.f, s8 = (cc & 8) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = y[k][j];
+#if KVQ_QUANT_FWHT_DPP
+            v = __builtin_fmaf(dpp<DPP_QUAD_XOR1>(v), s1, v);
+            v = __builtin_fmaf(dpp<DPP_QUAD_XOR2>(v), s2, v);
+            v = __builtin_fmaf(swz_xor<4>(v), s4, v);
+            v = __builtin_fmaf(dpp<DPP_ROR8>(v), s8, v);
+#else
+            v = __builtin_fmaf(swz_xor<1>(v), s1, v);
+            v = __builtin_fmaf(swz_xor<2>(v), s2, v);
+            v = __builtin_fmaf(swz_xor<4>(v), s4, v);
+            v = __builtin_fmaf(swz_xor<8>(v), s8, v);
+#endif
+            y[k][j] = v;
+        }
+    const float sigma = s1 * s2 * s4 * s8;
+
+    // ---- normalization rounds on A = Y^2: u = 1/r^2 per row, w = 1/c^2 per channel
+    // A = Y^2, kept in registers (KEEP_SQ) or recomputed where used
+    float A[KEEP_SQ ? R : 1][8];
+    if constexpr (KEEP_SQ) {
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) A[k][j] = y[k][j] * y[k][j];
+    }
+    auto sq = [&](int k, int j) -> float {
+        if constexpr (KEEP_SQ) return A[k][j];
+        else return y[k][j] * y[k][j];
+    };
+    // non-finite detector: a row's sum of squares is finite iff the row is
+    // (first round below; computed here when there is no round)
+    uint32_t bad = 0;
+    if (a.iters == 0) {
+        float ssq = 0.f;
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ssq += y[k][j] * y[k][j];
+        if (!isfinite(ssq)) bad |= KVQ_FLAG_NONFINITE;
+    }
+    float w[8], u[R], csq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        w[j] = 1.f;
+        csq[j] = 1.f;
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) u[k] = 1.f;
+    const float fD = (float)QD, fn = (float)n;
+
+    for (int it = 0; it < a.iters; ++it) {
+        // row step: r^2 = mean_j A_ij w_j over the 128 channels
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s = __builtin_fmaf(sq(k, j), w[j], s);
+            s = row_sum16(s);
+            if (it == 0 && !isfinite(s)) bad |= KVQ_FLAG_NONFINITE;
+            if (s > 0.f && s < INFINITY) u[k] = fD * __builtin_amdgcn_rcpf(s);
+        }
+        // column step: c^2 = mean_i A_ij u_i over the n valid rows
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int k = 0; k < R; ++k) acc = __builtin_fmaf(sq(k, j), u[k], acc);
+            t[j] = acc;
+        }
+        // across the four row groups of the wave: permlane swaps pair up halves
+        float h4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[j]), __float_as_uint(t[j + 4]), false, false);
+            h4[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // ch j (lanes < 32) / j + 4 (lanes >= 32)
+        }
+        float h2[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
+            h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 cc + 2 rr + j
+        }
+        float *cs = colsum[it & 1][wave];
+        *reinterpret_cast<float2 *>(cs + cc * 8 + 2 * rr) = float2{h2[0], h2[1]};
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const float4 p0 = *reinterpret_cast<const float4 *>(&colsum[it & 1][ww][cc * 8]);
+            const float4 p1 = *reinterpret_cast<const float4 *>(&colsum[it & 1][ww][cc * 8 + 4]);
+            t[0] += p0.x; t[1] += p0.y; t[2] += p0.z; t[3] += p0.w;
+            t[4] += p1.x; t[5] += p1.y; t[6] += p1.z; t[7] += p1.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (n > 0 && t[j] > 0.f && t[j] < INFINITY) {
+                csq[j] = t[j] * __builtin_amdgcn_rcpf(fn);
+                w[j] = fn * __builtin_amdgcn_rcpf(t[j]);
+            }
+    }
+
+    // ---- fp16 normalizer c16 and per-channel multiplier 1 / (sqrt(128) c16) --
+    float mult[8];
+    uint32_t cpk[4];
+    constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint16_t c16 = float_to_half_bits(sqrtf(csq[j]));
+        const float cv = half_bits_to_float(c16);
+        if (!(cv > 0.f && cv < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
+        mult[j] = (sigma * INV_SQRT_H) / cv;
+        if (j & 1) cpk[j >> 1] |= (uint32_t)c16 << 16;
+        else cpk[j >> 1] = c16;
+    }
+    if (rg == 0) *reinterpret_cast<uint4 *>(a.cnorm + blk * QD + cc * 8) = uint4{cpk[0], cpk[1], cpk[2], cpk[3]};
+
+    // ---- per token: asymmetric RTN with fp16 (S, Z), codes packed in registers
+    // channel-major: two byte-accumulators per channel (4-bit: even / odd rows,
+    // 2-bit: rows 0..3 / 4..7) assembled into the channel's bitstream at the end
+    uint32_t cma[8], cmb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cma[j] = cmb[j] = 0;
+    uint8_t *cbase = a.codes + blk * (T * QD * BITS / 8);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int row = rg * R + k;
+        float yy[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) yy[j] = y[k][j] * mult[j];
+        float mn = yy[0], mx = yy[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+            mn = fminf(mn, yy[j]);
+            mx = fmaxf(mx, yy[j]);
+        }
+        mn = row_min16(mn);
+        mx = row_max16(mx);
+        uint16_t S16 = 0, Z16 = 0;
+        if (row < n) {
+            S16 = float_to_half_bits((mx - mn) * (1.0f / LEVELS));
+            Z16 = float_to_half_bits(mn);
+        }
+        const float Sv = half_bits_to_float(S16), Zv = half_bits_to_float(Z16);
+        if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
+        const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
+        const float zi = -Zv * inv;
+        float q[8];  // (y - Z) / S, clamped above; rounding and the lower clamp in cvt_pk_u8
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = fminf(__builtin_fmaf(yy[j], inv, zi), LEVELS);
+        if (cc == 0) reinterpret_cast<uint32_t *>(a.sz)[blk * T + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
+        if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
+            const uint32_t word = pack8<BITS>(q);
+            if constexpr (BITS == 4) reinterpret_cast<uint32_t *>(cbase)[row * (QD / 8) + cc] = word;
+            else reinterpret_cast<uint16_t *>(cbase)[row * (QD / 8) + cc] = (uint16_t)word;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (BITS == 4) {
+                    if (k & 1) cmb[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], (k >> 1) & 3, cmb[j]);
+                    else cma[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], (k >> 1) & 3, cma[j]);
+                } else {
+                    if (k < 4) cma[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k, cma[j]);
+                    else cmb[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k - 4, cmb[j]);
+                }
+            }
+        }
+    }
+    if constexpr (LAYOUT == KVQ_CHANNEL_MAJOR) {
+        // channel ch: rows rg*R .. rg*R + R - 1 are stream positions ch * T + rg * R + k
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int pos = (cc * 8 + j) * T + rg * R;
+            if constexpr (BITS == 4) {
+                const uint32_t word = cma[j] | (cmb[j] << 4);
+                if constexpr (R == 8) reinterpret_cast<uint32_t *>(cbase)[pos / 8] = word;
+                else reinterpret_cast<uint16_t *>(cbase)[pos / 4] = (uint16_t)word;
+            } else {
+                auto squeeze = [](uint32_t x) {  // four byte codes (< 4) -> one byte, LE 2-bit fields
+                    return (x & 0x03u) | ((x >> 6) & 0x0Cu) | ((x >> 12) & 0x30u) | ((x >> 18) & 0xC0u);
+                };
+                if constexpr (R == 8) reinterpret_cast<uint16_t *>(cbase)[pos / 8] = (uint16_t)(squeeze(cma[j]) | (squeeze(cmb[j]) << 8));
+                else cbase[pos / 4] = (uint8_t)squeeze(cma[j]);
+            }
+        }
+    }
+    if (a.flags) {
+        const int nf = __syncthreads_or((int)(bad & KVQ_FLAG_NONFINITE));
+        const int so = __syncthreads_or((int)(bad & KVQ_FLAG_SIDE_OVERFLOW));
+        if (tid == 0 && (nf || so))
+            atomicOr(a.flags, (nf ? (uint32_t)KVQ_FLAG_NONFINITE : 0u) | (so ? (uint32_t)KVQ_FLAG_SIDE_OVERFLOW : 0u));
+    }
+    }
+}
+
+bool quantize_d128_supported(int D, int T, const QuantArgs &a) {
+    return D == QD && (T == 64 || T == 128) && a.h == QD && a.G == QD && a.R == 0 && a.dtype == KVQ_BF16 &&
+           (a.bits == 2 || a.bits == 4) && (a.layout == KVQ_TOKEN_MAJOR || a.layout == KVQ_CHANNEL_MAJOR);
+}
+
+template <int T, int BITS, int LAYOUT>
+static void launch_one(int num_tiles, const QuantArgs &a, hipStream_t stream) {
+    const int items = num_tiles * a.H;
+    int dev = 0, cus = 256, per_cu = 2;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_d128_kernel<T, BITS, LAYOUT>, QNT, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const int grid = items < cus * per_cu ? items : cus * per_cu;
+    hipLaunchKernelGGL((quantize_d128_kernel<T, BITS, LAYOUT>), dim3(grid), dim3(QNT), 0, stream, a, items);
+}
+
+template <int T, int BITS>
+static void launch_l(int num_tiles, const QuantArgs &a, hipStream_t stream) {
+    if (a.layout == KVQ_TOKEN_MAJOR) launch_one<T, BITS, KVQ_TOKEN_MAJOR>(num_tiles, a, stream);
+    else launch_one<T, BITS, KVQ_CHANNEL_MAJOR>(num_tiles, a, stream);
+}
+
+void launch_quantize_d128(int T, int num_tiles, const QuantArgs &a, hipStream_t stream) {
+    if (T == 128) {
+        if (a.bits == 4) launch_l<128, 4>(num_tiles, a, stream);
+        else launch_l<128, 2>(num_tiles, a, stream);
+    } else {
+        if (a.bits == 4) launch_l<64, 4>(num_tiles, a, stream);
+        else launch_l<64, 2>(num_tiles, a, stream);
+    }
+}
+
+}  // namespace kvq

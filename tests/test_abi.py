@@ -100,6 +100,6 @@ def test_decode_argument_errors():
 
 def test_default_splits():
     # long context, one sequence: at least 256 partitions over the 8 kv heads
-    assert 8 * K.kv_decode_attn_default_splits(1, 8, 131072, 128) >= 256
+    assert 8 * K.kv_decode_attn_default_splits(1, 8, 131072, 128) >= 256  # the long-context workload: >= 256 partitions
     assert K.kv_decode_attn_default_splits(8, 8, 4096, 128) <= 32
     assert K.kv_decode_attn_default_splits(1, 1, 5, 16) == 1
