@@ -30,6 +30,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantize GB/s (fp16 in) + quantized decode-attn GB/s, % of HBM peak"
 HBM_PEAK_GBS = 8000.0
+# fp32 VALU lane-operations per second with packed FP32 disabled (the build's flag):
+# 256 CUs x 64 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 ESIZE = {"f32": 4, "bf16": 2}
 
 
@@ -49,6 +52,14 @@ def quantize_bytes(cfg, f, width):
     return read, write
 
 
+def quantize_valu_ops(cfg, f, width):
+    """Algorithmic VALU lane-operations of one quantizer launch: per element log2(h)
+    butterfly add/sub + 2 N row/column FMAs + 7 (square, scale, min, max, code FMA,
+    clamp, round-and-pack)."""
+    elements = cfg.total_tokens * cfg.num_kv_heads * f.head_dim
+    return elements * (int(math.log2(f.hadamard_n)) + 2 * f.iters + 7)
+
+
 def decode_bytes(cfg, seqs=None):
     """Algorithmic bytes of one decode call: every attended page of K and V
     (codes, scale/zero, normalizer, rope), the queries and the fp32 outputs."""
@@ -63,7 +74,7 @@ def decode_bytes(cfg, seqs=None):
 
 def source_digest():
     h = hashlib.sha256()
-    for name in ("quantize.hip", "common.h"):
+    for name in ("quantize_d128.hip", "common.h"):
         with open(os.path.join(ROOT, "kv_cache_quantization_04_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -72,7 +83,7 @@ def source_digest():
 def profiled_traffic(workload_key):
     """HBM bytes per quantizer launch from the committed rocprofv3 counter summary,
     or None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"quantize_kernel_{workload_key}_hbm_counters.md")
+    path = os.path.join(ROOT, "profiles", f"quantize_d128_kernel_{workload_key}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -227,6 +238,7 @@ def main():
     per_launch = qbytes / nq
     avg_launch_ms = (tk + tvq) / nq
     traffic = profiled_traffic(f"config{args.config}")
+    qops = quantize_valu_ops(cfg, cfg.fk, cfg.width) + (quantize_valu_ops(cfg, cfg.fv, cfg.dv) if cfg.fv is not None else 0)
     positions = int(cfg.seq_lens.sum())
     res = {
         "metric": METRIC,
@@ -243,11 +255,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "kv_layout": "K token-major, V channel-major, fp16 side data",
                    "decode_splits": splits, "copy_ring": ring},
-        "roofline": {"bound": "hbm", "kernel": "quantize_kernel", "achieved": round(per_launch / (avg_launch_ms * 1e-3) / 1e9, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(per_launch / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": per_launch,
-                     "avg_launch_us": round(avg_launch_ms * 1e3, 3)},
+        "roofline": {"bound": "alu", "kernel": "quantize_d128_kernel",
+                     "achieved": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                     "unit": "T VALU lane-ops/s", "frac": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
+                     "traffic": traffic, "algorithmic_ops_per_launch": qops / nq,
+                     "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                     "hbm": {"achieved": round(per_launch / (avg_launch_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(per_launch / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}},
         "detail": {
             "quantize_GBps": round(q_gbs, 2), "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
             "quantize_input_GBps": round((kin_r + vin_r) / ((tk + tvq) * 1e-3) / 1e9, 2),

@@ -111,7 +111,11 @@ template <int T, int BITS, int LAYOUT>
 __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kernel(QuantArgs a, int num_items) {
     constexpr int R = T / 16;  // rows per thread
     constexpr float LEVELS = (float)((1 << BITS) - 1);
-    __shared__ float colsum[2][4][QD];  // [buffer][wave][channel]
+    __shared__ float colsum[2][QD][4];  // [buffer][channel][wave]
+    __shared__ float wsh[2][QD];        // 1 / c^2 per channel, per round
+    __shared__ float multsh[QD];
+    __shared__ uint32_t outbuf[T * QD * BITS / 32];
+    __shared__ uint32_t szbuf[T];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cc = lane & 15, rr = lane >> 4;
@@ -127,13 +131,16 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
         const int tl = itm / a.H, hd = itm % a.H;
         const int nv = a.tile_valid[tl];
         const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src) + hd * a.stride_head +
-                              (int64_t)a.tile_src_token[tl] * a.stride_token + (lane & 15) * 8;
+                              (int64_t)a.tile_src_token[tl] * a.stride_token;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const int b = wave * R + i;
             const int row = 4 * b + (lane >> 4);
+            // LDS slot (lane & 15) of the row holds chunk slot ^ swz(row): the four
+            // row groups of a wave then read different banks
+            const int chunk = (lane & 15) ^ ((row / R) & 3);
             if (row < nv)
-                __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)row * a.stride_token),
+                __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)row * a.stride_token + chunk * 8),
                                                  (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
         }
     };
@@ -150,7 +157,7 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
 #pragma unroll
     for (int k = 0; k < R; ++k) {
         const int row = rg * R + k;
-        const uint4 v = row < n ? stage[row * 16 + cc] : uint4{0, 0, 0, 0};
+        const uint4 v = row < n ? stage[row * 16 + (cc ^ rr)] : uint4{0, 0, 0, 0};
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -225,18 +232,19 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
             for (int j = 0; j < 8; ++j) ssq += y[k][j] * y[k][j];
         if (!isfinite(ssq)) bad |= KVQ_FLAG_NONFINITE;
     }
-    float w[8], u[R], csq[8];
+    float w[8], u[R];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        w[j] = 1.f;
-        csq[j] = 1.f;
-    }
+    for (int j = 0; j < 8; ++j) w[j] = 1.f;
 #pragma unroll
     for (int k = 0; k < R; ++k) u[k] = 1.f;
     const float fD = (float)QD, fn = (float)n;
+    // owner of channel tid (tid < 128): column sum of the last round
+    float t_own = 0.f;
+    constexpr float TINY = 1e-30f;
 
     for (int it = 0; it < a.iters; ++it) {
-        // row step: r^2 = mean_j A_ij w_j over the 128 channels
+        // row step: r^2 = mean_j A_ij w_j over the 128 channels. A zero row keeps a
+        // large finite u and contributes 0 * u = 0 below, as with an unchanged factor.
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             float s = 0.f;
@@ -244,7 +252,7 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
             for (int j = 0; j < 8; ++j) s = __builtin_fmaf(sq(k, j), w[j], s);
             s = row_sum16(s);
             if (it == 0 && !isfinite(s)) bad |= KVQ_FLAG_NONFINITE;
-            if (s > 0.f && s < INFINITY) u[k] = fD * __builtin_amdgcn_rcpf(s);
+            u[k] = fD * __builtin_amdgcn_rcpf(fmaxf(s, TINY));
         }
         // column step: c^2 = mean_i A_ij u_i over the n valid rows
         float t[8];
@@ -268,40 +276,42 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
             const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
             h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 cc + 2 rr + j
         }
-        float *cs = colsum[it & 1][wave];
-        *reinterpret_cast<float2 *>(cs + cc * 8 + 2 * rr) = float2{h2[0], h2[1]};
+        colsum[it & 1][cc * 8 + 2 * rr][wave] = h2[0];
+        colsum[it & 1][cc * 8 + 2 * rr + 1][wave] = h2[1];
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t[j] = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-            const float4 p0 = *reinterpret_cast<const float4 *>(&colsum[it & 1][ww][cc * 8]);
-            const float4 p1 = *reinterpret_cast<const float4 *>(&colsum[it & 1][ww][cc * 8 + 4]);
-            t[0] += p0.x; t[1] += p0.y; t[2] += p0.z; t[3] += p0.w;
-            t[4] += p1.x; t[5] += p1.y; t[6] += p1.z; t[7] += p1.w;
+        if (tid < QD) {
+            const float4 p = *reinterpret_cast<const float4 *>(colsum[it & 1][tid]);
+            t_own = (p.x + p.y) + (p.z + p.w);
+            // a zero column keeps a large finite w (its A entries are all zero)
+            wsh[it & 1][tid] = fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (n > 0 && t[j] > 0.f && t[j] < INFINITY) {
-                csq[j] = t[j] * __builtin_amdgcn_rcpf(fn);
-                w[j] = fn * __builtin_amdgcn_rcpf(t[j]);
-            }
+        __syncthreads();
+        const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[it & 1][cc * 8]);
+        const float4 w1 = *reinterpret_cast<const float4 *>(&wsh[it & 1][cc * 8 + 4]);
+        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
     }
 
-    // ---- fp16 normalizer c16 and per-channel multiplier 1 / (sqrt(128) c16) --
-    float mult[8];
-    uint32_t cpk[4];
+    // ---- fp16 normalizer c16 (owner threads) and the per-channel multiplier
+    // sigma / (sqrt(128) c16); a column whose sum of squares is 0 or not finite
+    // keeps c = 1
     constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint16_t c16 = float_to_half_bits(sqrtf(csq[j]));
+    if (tid < QD) {
+        const float csq = (a.iters > 0 && n > 0 && t_own > 0.f && t_own < INFINITY) ? t_own / fn : 1.f;
+        const uint16_t c16 = float_to_half_bits(sqrtf(csq));
         const float cv = half_bits_to_float(c16);
         if (!(cv > 0.f && cv < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
-        mult[j] = (sigma * INV_SQRT_H) / cv;
-        if (j & 1) cpk[j >> 1] |= (uint32_t)c16 << 16;
-        else cpk[j >> 1] = c16;
+        multsh[tid] = INV_SQRT_H / cv;
+        a.cnorm[blk * QD + tid] = c16;
     }
-    if (rg == 0) *reinterpret_cast<uint4 *>(a.cnorm + blk * QD + cc * 8) = uint4{cpk[0], cpk[1], cpk[2], cpk[3]};
+    __syncthreads();
+    float mult[8];
+    {
+        const float4 m0 = *reinterpret_cast<const float4 *>(&multsh[cc * 8]);
+        const float4 m1 = *reinterpret_cast<const float4 *>(&multsh[cc * 8 + 4]);
+        mult[0] = m0.x * sigma; mult[1] = m0.y * sigma; mult[2] = m0.z * sigma; mult[3] = m0.w * sigma;
+        mult[4] = m1.x * sigma; mult[5] = m1.y * sigma; mult[6] = m1.z * sigma; mult[7] = m1.w * sigma;
+    }
 
     // ---- per token: asymmetric RTN with fp16 (S, Z), codes packed in registers
     // channel-major: two byte-accumulators per channel (4-bit: even / odd rows,
@@ -309,7 +319,7 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
     uint32_t cma[8], cmb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) cma[j] = cmb[j] = 0;
-    uint8_t *cbase = a.codes + blk * (T * QD * BITS / 8);
+    uint8_t *cbase = reinterpret_cast<uint8_t *>(outbuf);  // LDS image of the code block
 #pragma unroll
     for (int k = 0; k < R; ++k) {
         const int row = rg * R + k;
@@ -336,7 +346,7 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
         float q[8];  // (y - Z) / S, clamped above; rounding and the lower clamp in cvt_pk_u8
 #pragma unroll
         for (int j = 0; j < 8; ++j) q[j] = fminf(__builtin_fmaf(yy[j], inv, zi), LEVELS);
-        if (cc == 0) reinterpret_cast<uint32_t *>(a.sz)[blk * T + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
+        if (cc == 0) szbuf[row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
             const uint32_t word = pack8<BITS>(q);
             if constexpr (BITS == 4) reinterpret_cast<uint32_t *>(cbase)[row * (QD / 8) + cc] = word;
@@ -371,6 +381,17 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
                 else cbase[pos / 4] = (uint8_t)squeeze(cma[j]);
             }
         }
+    }
+    // ---- coalesced stores of the code block and the (S, Z) words --------------
+    __syncthreads();
+    {
+        constexpr int NW = T * QD * BITS / 32;  // 32-bit words of the code block
+        uint4 *gcodes = reinterpret_cast<uint4 *>(a.codes + blk * (T * QD * BITS / 8));
+        const uint4 *lcodes = reinterpret_cast<const uint4 *>(outbuf);
+#pragma unroll
+        for (int i = tid; i < NW / 4; i += QNT) gcodes[i] = lcodes[i];
+        if (tid < T / 4)
+            reinterpret_cast<uint4 *>(a.sz + blk * T * 2)[tid] = reinterpret_cast<const uint4 *>(szbuf)[tid];
     }
     if (a.flags) {
         const int nf = __syncthreads_or((int)(bad & KVQ_FLAG_NONFINITE));
