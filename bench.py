@@ -237,7 +237,7 @@ def main():
     d_gbs = dbytes / (td * 1e-3) / 1e9
     per_launch = qbytes / nq
     avg_launch_ms = (tk + tvq) / nq
-    traffic = profiled_traffic(f"config{args.config}")
+    traffic = profiled_traffic(W.NAMES[args.config])
     qops = quantize_valu_ops(cfg, cfg.fk, cfg.width) + (quantize_valu_ops(cfg, cfg.fv, cfg.dv) if cfg.fv is not None else 0)
     positions = int(cfg.seq_lens.sum())
     res = {

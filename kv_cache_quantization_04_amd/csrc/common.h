@@ -31,6 +31,21 @@ __device__ __forceinline__ float load_as_float(const void *p, int dtype, int64_t
     return bf16_bits_to_float(((const uint16_t *)p)[idx]);
 }
 
+// Workgroup barrier that orders LDS accesses only: this wave's LDS operations
+// complete, then all waves meet. Global loads in flight (direct-to-LDS
+// prefetches included) are not waited for, unlike __syncthreads(), whose fence
+// drains the vector memory counter. The memory clobber keeps the compiler from
+// moving memory accesses across it. A direct-to-LDS copy must be waited for
+// explicitly (s_waitcnt vmcnt) before the barrier that publishes it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Read-only kernel input read through the constant address space, so that a
+// wave-uniform index becomes a scalar load (the kernel never writes these).
+template <typename V>
+__device__ __forceinline__ V load_const(const V *p, int64_t i) {
+    return ((const __attribute__((address_space(4))) V *)(uintptr_t)p)[i];
+}
+
 // Butterfly partner exchange inside a group of lanes (xor pattern).
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, WAVE); }
 

@@ -107,40 +107,51 @@ __device__ __forceinline__ uint32_t pack8(const float (&u)[8]) {
 
 }  // namespace
 
-template <int T, int BITS, int LAYOUT>
-__global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kernel(QuantArgs a, int num_items) {
+// The LDS buffers come in as restrict pointers: after inlining, the compiler
+// knows that the direct-to-LDS prefetch into `stage` touches none of the others
+// and lets the prefetch stay in flight across their accesses.
+//   stage  [T * 128 * 2 / 16] source rows of the next item (bf16, swizzled chunks)
+//   colsum0/1 [128][4]  per-channel column partial sums, [channel][wave]; even/odd rounds
+//   wsh0/1    [128]     1 / c^2 per channel; even/odd rounds
+//   multsh [128]        per-channel output multiplier
+//   outbuf [T * 128 * BITS / 32] LDS image of the code block
+//   szbuf  [T]          (S, Z) fp16 pairs per token
+template <int T, int BITS, int LAYOUT, int NIT>
+__device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_items, uint4 *__restrict__ stage,
+                                                   float (*__restrict__ colsum0)[4], float (*__restrict__ colsum1)[4],
+                                                   float *__restrict__ wsh0, float *__restrict__ wsh1,
+                                                   float *__restrict__ multsh, uint32_t *__restrict__ outbuf,
+                                                   uint32_t *__restrict__ szbuf) {
     constexpr int R = T / 16;  // rows per thread
     constexpr float LEVELS = (float)((1 << BITS) - 1);
-    __shared__ float colsum[2][QD][4];  // [buffer][channel][wave]
-    __shared__ float wsh[2][QD];        // 1 / c^2 per channel, per round
-    __shared__ float multsh[QD];
-    __shared__ uint32_t outbuf[T * QD * BITS / 32];
-    __shared__ uint32_t szbuf[T];
+    // rounds: a compile-time count (fully unrolled) or, with NIT < 0, the runtime one
+    const int iters = NIT >= 0 ? NIT : a.iters;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cc = lane & 15, rr = lane >> 4;
     const int rg = wave * 4 + rr;
-    const uint16_t *srcbase = reinterpret_cast<const uint16_t *>(a.src) + cc * 8;
 
     // Persistent workgroups: item = tile * H + head, strided by the grid. The
     // next item's source rows are copied HBM -> LDS by direct-to-LDS loads while
-    // the current item is processed in registers. Each wave load instruction
-    // moves 4 rows (1 KB): lane l -> row 4 b + (l >> 4), 16-byte chunk l & 15.
-    __shared__ uint4 stage[T * QD * 2 / 16];
+    // the current item is processed in registers; only LDS-ordering barriers are
+    // used until the next item starts, so the copies stay in flight. Each wave
+    // load instruction moves 4 rows (1 KB): lane l -> row 4 b + (l >> 4), 16-byte
+    // chunk l & 15. LDS slot (l & 15) of a row holds chunk slot ^ ((row / R) & 3),
+    // so the four row groups of a wave read different banks; for a fixed b that
+    // swizzle is the constant ((4 i) / R) & 3.
+    const uint32_t lane_row_bytes = (uint32_t)rr * (uint32_t)a.stride_token * 2u;
     auto fetch = [&](int itm) {
         const int tl = itm / a.H, hd = itm % a.H;
-        const int nv = a.tile_valid[tl];
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src) + hd * a.stride_head +
-                              (int64_t)a.tile_src_token[tl] * a.stride_token;
+        const int nv = load_const(a.tile_valid, tl);
+        const char *src = reinterpret_cast<const char *>(a.src) +
+                          2 * (hd * a.stride_head + (int64_t)load_const(a.tile_src_token, tl) * a.stride_token);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const int b = wave * R + i;
-            const int row = 4 * b + (lane >> 4);
-            // LDS slot (lane & 15) of the row holds chunk slot ^ swz(row): the four
-            // row groups of a wave then read different banks
-            const int chunk = (lane & 15) ^ ((row / R) & 3);
-            if (row < nv)
-                __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)row * a.stride_token + chunk * 8),
+            const uint32_t off = lane_row_bytes + 16u * (uint32_t)(cc ^ (((4 * i) / R) & 3));
+            if (4 * b + rr < nv)
+                __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)(4 * b) * a.stride_token * 2 + off),
                                                  (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
         }
     };
@@ -148,11 +159,11 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
     if (item < num_items) fetch(item);
     for (; item < num_items; item += gridDim.x) {
     const int tile = item / a.H, head = item % a.H;
-    const int dst_page = a.tile_dst_page[tile];
-    const int n = a.tile_valid[tile];
+    const int dst_page = load_const(a.tile_dst_page, tile);
+    const int n = load_const(a.tile_valid, tile);
     const int64_t blk = (int64_t)dst_page * a.H + head;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into LDS have landed
-    __syncthreads();                // and every other wave's
+    lds_barrier();                  // and every other wave's
     float y[R][8];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
@@ -165,7 +176,7 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
             y[k][2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
         }
     }
-    __syncthreads();  // the staging buffer is free again
+    lds_barrier();  // the staging buffer is free again
     if (item + (int)gridDim.x < num_items) fetch(item + gridDim.x);
     if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
 
@@ -224,7 +235,7 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
     // non-finite detector: a row's sum of squares is finite iff the row is
     // (first round below; computed here when there is no round)
     uint32_t bad = 0;
-    if (a.iters == 0) {
+    if (iters == 0) {
         float ssq = 0.f;
 #pragma unroll
         for (int k = 0; k < R; ++k)
@@ -242,7 +253,8 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
     float t_own = 0.f;
     constexpr float TINY = 1e-30f;
 
-    for (int it = 0; it < a.iters; ++it) {
+#pragma unroll
+    for (int it = 0; it < iters; ++it) {
         // row step: r^2 = mean_j A_ij w_j over the 128 channels. A zero row keeps a
         // large finite u and contributes 0 * u = 0 below, as with an unchanged factor.
 #pragma unroll
@@ -276,18 +288,20 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
             const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
             h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 cc + 2 rr + j
         }
-        colsum[it & 1][cc * 8 + 2 * rr][wave] = h2[0];
-        colsum[it & 1][cc * 8 + 2 * rr + 1][wave] = h2[1];
-        __syncthreads();
+        float(*colsum)[4] = (it & 1) ? colsum1 : colsum0;
+        float *wsh = (it & 1) ? wsh1 : wsh0;
+        colsum[cc * 8 + 2 * rr][wave] = h2[0];
+        colsum[cc * 8 + 2 * rr + 1][wave] = h2[1];
+        lds_barrier();
         if (tid < QD) {
-            const float4 p = *reinterpret_cast<const float4 *>(colsum[it & 1][tid]);
+            const float4 p = *reinterpret_cast<const float4 *>(colsum[tid]);
             t_own = (p.x + p.y) + (p.z + p.w);
             // a zero column keeps a large finite w (its A entries are all zero)
-            wsh[it & 1][tid] = fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
+            wsh[tid] = fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
         }
-        __syncthreads();
-        const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[it & 1][cc * 8]);
-        const float4 w1 = *reinterpret_cast<const float4 *>(&wsh[it & 1][cc * 8 + 4]);
+        lds_barrier();
+        const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[cc * 8]);
+        const float4 w1 = *reinterpret_cast<const float4 *>(&wsh[cc * 8 + 4]);
         w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
         w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
     }
@@ -297,14 +311,14 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
     // keeps c = 1
     constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
     if (tid < QD) {
-        const float csq = (a.iters > 0 && n > 0 && t_own > 0.f && t_own < INFINITY) ? t_own / fn : 1.f;
+        const float csq = (iters > 0 && n > 0 && t_own > 0.f && t_own < INFINITY) ? t_own / fn : 1.f;
         const uint16_t c16 = float_to_half_bits(sqrtf(csq));
         const float cv = half_bits_to_float(c16);
         if (!(cv > 0.f && cv < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
         multsh[tid] = INV_SQRT_H / cv;
         a.cnorm[blk * QD + tid] = c16;
     }
-    __syncthreads();
+    lds_barrier();
     float mult[8];
     {
         const float4 m0 = *reinterpret_cast<const float4 *>(&multsh[cc * 8]);
@@ -383,7 +397,7 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
         }
     }
     // ---- coalesced stores of the code block and the (S, Z) words --------------
-    __syncthreads();
+    lds_barrier();
     {
         constexpr int NW = T * QD * BITS / 32;  // 32-bit words of the code block
         uint4 *gcodes = reinterpret_cast<uint4 *>(a.codes + blk * (T * QD * BITS / 8));
@@ -393,36 +407,58 @@ __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kerne
         if (tid < T / 4)
             reinterpret_cast<uint4 *>(a.sz + blk * T * 2)[tid] = reinterpret_cast<const uint4 *>(szbuf)[tid];
     }
-    if (a.flags) {
-        const int nf = __syncthreads_or((int)(bad & KVQ_FLAG_NONFINITE));
-        const int so = __syncthreads_or((int)(bad & KVQ_FLAG_SIDE_OVERFLOW));
-        if (tid == 0 && (nf || so))
+    if (a.flags) {  // one atomic per wave that saw a condition; no barrier
+        const bool nf = __ballot((bad & KVQ_FLAG_NONFINITE) != 0) != 0;
+        const bool so = __ballot((bad & KVQ_FLAG_SIDE_OVERFLOW) != 0) != 0;
+        if (lane == 0 && (nf || so))
             atomicOr(a.flags, (nf ? (uint32_t)KVQ_FLAG_NONFINITE : 0u) | (so ? (uint32_t)KVQ_FLAG_SIDE_OVERFLOW : 0u));
     }
     }
 }
 
+template <int T, int BITS, int LAYOUT, int NIT>
+__global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kernel(QuantArgs a, int num_items) {
+    __shared__ uint4 stage[T * QD * 2 / 16];
+    __shared__ float colsum0[QD][4], colsum1[QD][4];
+    __shared__ float wsh0[QD], wsh1[QD];
+    __shared__ float multsh[QD];
+    __shared__ uint32_t outbuf[T * QD * BITS / 32];
+    __shared__ uint32_t szbuf[T];
+    quantize_d128_body<T, BITS, LAYOUT, NIT>(a, num_items, stage, colsum0, colsum1, wsh0, wsh1, multsh, outbuf,
+                                             szbuf);
+}
+
 bool quantize_d128_supported(int D, int T, const QuantArgs &a) {
+    // the per-lane source offset (up to 3 token strides) is kept in 32 bits
     return D == QD && (T == 64 || T == 128) && a.h == QD && a.G == QD && a.R == 0 && a.dtype == KVQ_BF16 &&
+           a.stride_token < (int64_t(1) << 28) &&
            (a.bits == 2 || a.bits == 4) && (a.layout == KVQ_TOKEN_MAJOR || a.layout == KVQ_CHANNEL_MAJOR);
 }
 
-template <int T, int BITS, int LAYOUT>
+template <int T, int BITS, int LAYOUT, int NIT>
 static void launch_one(int num_tiles, const QuantArgs &a, hipStream_t stream) {
     const int items = num_tiles * a.H;
     int dev = 0, cus = 256, per_cu = 2;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_d128_kernel<T, BITS, LAYOUT>, QNT, 0) != hipSuccess ||
-        per_cu < 1)
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_d128_kernel<T, BITS, LAYOUT, NIT>, QNT, 0) !=
+            hipSuccess || per_cu < 1)
         per_cu = 1;
     const int grid = items < cus * per_cu ? items : cus * per_cu;
-    hipLaunchKernelGGL((quantize_d128_kernel<T, BITS, LAYOUT>), dim3(grid), dim3(QNT), 0, stream, a, items);
+    hipLaunchKernelGGL((quantize_d128_kernel<T, BITS, LAYOUT, NIT>), dim3(grid), dim3(QNT), 0, stream, a, items);
+}
+
+template <int T, int BITS, int LAYOUT>
+static void launch_n(int num_tiles, const QuantArgs &a, hipStream_t stream) {
+    if (a.iters == 4) launch_one<T, BITS, LAYOUT, 4>(num_tiles, a, stream);
+    else if (a.iters == 2) launch_one<T, BITS, LAYOUT, 2>(num_tiles, a, stream);
+    else launch_one<T, BITS, LAYOUT, -1>(num_tiles, a, stream);
 }
 
 template <int T, int BITS>
 static void launch_l(int num_tiles, const QuantArgs &a, hipStream_t stream) {
-    if (a.layout == KVQ_TOKEN_MAJOR) launch_one<T, BITS, KVQ_TOKEN_MAJOR>(num_tiles, a, stream);
-    else launch_one<T, BITS, KVQ_CHANNEL_MAJOR>(num_tiles, a, stream);
+    if (a.layout == KVQ_TOKEN_MAJOR) launch_n<T, BITS, KVQ_TOKEN_MAJOR>(num_tiles, a, stream);
+    else launch_n<T, BITS, KVQ_CHANNEL_MAJOR>(num_tiles, a, stream);
 }
 
 void launch_quantize_d128(int T, int num_tiles, const QuantArgs &a, hipStream_t stream) {
