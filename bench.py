@@ -183,7 +183,7 @@ def main():
     vcache = ([K.DeviceCache(kfmt(cfg.fv), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
               if cfg.fv is not None else [None] * ring)
     max_len = int(cfg.seq_lens.max())
-    splits = K.kv_decode_attn_default_splits(cfg.num_seqs, cfg.num_kv_heads, max_len, cfg.fk.tile_tokens)
+    splits = K.kv_decode_attn_default_splits(kcache[0], vcache[0], cfg.num_seqs, cfg.num_q_heads, max_len)
     ws = torch.empty(K.kv_decode_attn_workspace_bytes(cfg.num_seqs, cfg.num_q_heads, cfg.dv, splits),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.num_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device=dev)

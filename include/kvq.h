@@ -128,9 +128,14 @@ kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtyp
 kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t *tile_page,
                          const int32_t *tile_valid, void *dst, kvq_dtype dst_dtype, hipStream_t stream);
 
-/* Number of split-K partitions kv_decode_attn uses when num_splits == 0. */
-int32_t kv_decode_attn_default_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
-                                      int32_t tile_tokens);
+/* Number of split-K partitions kv_decode_attn uses when num_splits == 0 for
+ * these caches (k, v as passed to kv_decode_attn; host structs, device arrays
+ * not read) and sizes. The count depends on the kernel the call selects: the
+ * pages of each (sequence, kv head) are divided into this many ranges, each
+ * producing a partial softmax state that a second pass merges. Returns 1 for
+ * invalid arguments. */
+int32_t kv_decode_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_seq_len);
 
 /* Workspace bytes kv_decode_attn needs for these sizes (num_splits >= 1). */
 size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,

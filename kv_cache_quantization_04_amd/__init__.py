@@ -60,7 +60,7 @@ _sig = {
     "kvq_cache_bytes": (_sz, [ctypes.POINTER(kvq_format), _i32, _i32]),
     "kv_quantize": (_i32, [ctypes.POINTER(kvq_cache), _vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
     "kv_dequantize": (_i32, [ctypes.POINTER(kvq_cache), _i32, _vp, _vp, _vp, _i32, _vp]),
-    "kv_decode_attn_default_splits": (_i32, [_i32, _i32, _i32, _i32]),
+    "kv_decode_attn_default_splits": (_i32, [ctypes.c_void_p, ctypes.c_void_p, _i32, _i32, _i32]),
     "kv_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "kv_decode_attn": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _vp, _i32,
                               _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
@@ -163,8 +163,10 @@ def kv_dequantize(src: DeviceCache, tile_page, tile_valid, out=None, dtype=None,
     return out
 
 
-def kv_decode_attn_default_splits(num_seqs: int, num_kv_heads: int, max_seq_len: int, tile_tokens: int) -> int:
-    return int(_lib.kv_decode_attn_default_splits(num_seqs, num_kv_heads, max_seq_len, tile_tokens))
+def kv_decode_attn_default_splits(k: DeviceCache, v: Optional[DeviceCache], num_seqs: int, num_q_heads: int,
+                                  max_seq_len: int) -> int:
+    return int(_lib.kv_decode_attn_default_splits(ctypes.byref(k.struct), ctypes.byref(v.struct) if v is not None else None,
+                                                  num_seqs, num_q_heads, max_seq_len))
 
 
 def kv_decode_attn_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim_v: int, num_splits: int) -> int:
@@ -177,7 +179,7 @@ def kv_decode_attn(q, k: DeviceCache, v: Optional[DeviceCache], block_table, seq
     B, Hq = q.shape[0], q.shape[1]
     dv = (v or k).fmt.head_dim
     if num_splits <= 0:
-        num_splits = kv_decode_attn_default_splits(B, k.num_heads, max_seq_len, k.fmt.tile_tokens)
+        num_splits = kv_decode_attn_default_splits(k, v, B, Hq, max_seq_len)
     need = kv_decode_attn_workspace_bytes(B, Hq, dv, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)

@@ -42,6 +42,51 @@ bool valid_dtype(int d) { return d == KVQ_F32 || d == KVQ_F16 || d == KVQ_BF16; 
 
 kvq_status launched() { return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ELAUNCH; }
 
+// Format-dependent fields of a decode call over validated caches: GQA grouping,
+// the K (or MLA latent) cache and the V cache (the latent itself when v is NULL).
+kvq_status decode_layout(const kvq_cache *k, const kvq_cache *v, int32_t num_q_heads, kvq::DecodeArgs &a) {
+    const kvq_format &fk = k->fmt;
+    const kvq_format &fv = v ? v->fmt : k->fmt;
+    if (num_q_heads <= 0 || num_q_heads % k->num_heads != 0) return KVQ_EINVAL;
+    if (v) {
+        if (v->num_heads != k->num_heads || fv.tile_tokens != fk.tile_tokens || v->num_pages != k->num_pages)
+            return KVQ_EINVAL;
+        if (fk.rope_dim != 0 || fv.rope_dim != 0) return KVQ_EUNSUPPORTED;
+        if (fk.layout != KVQ_TOKEN_MAJOR || fv.layout != KVQ_CHANNEL_MAJOR) return KVQ_EUNSUPPORTED;
+    } else {
+        if (fk.layout != KVQ_TOKEN_MAJOR) return KVQ_EUNSUPPORTED;
+    }
+    a.Hq = num_q_heads;
+    a.Hkv = k->num_heads;
+    a.grp = num_q_heads / k->num_heads;
+    a.hc = a.grp < 16 ? a.grp : 16;
+    if (a.grp % a.hc != 0) return KVQ_EUNSUPPORTED;
+    a.nhc = a.grp / a.hc;
+    a.kcodes = k->codes;
+    a.ksz = k->sz;
+    a.kcn = k->cnorm;
+    a.krope = k->rope;
+    a.D = fk.head_dim;
+    a.R = fk.rope_dim;
+    a.kG = fk.group;
+    a.kbits = fk.bits;
+    a.kh = fk.hadamard_n;
+    a.klayout = fk.layout;
+    const kvq_cache *vc = v ? v : k;
+    a.vcodes = vc->codes;
+    a.vsz = vc->sz;
+    a.vcn = vc->cnorm;
+    a.Dv = fv.head_dim;
+    a.vG = fv.group;
+    a.vbits = fv.bits;
+    a.vh = fv.hadamard_n;
+    a.vlayout = fv.layout;
+    a.vH = vc->num_heads;
+    a.T = fk.tile_tokens;
+    a.num_pages = k->num_pages;
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,19 +153,14 @@ kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t 
     return launched();
 }
 
-int32_t kv_decode_attn_default_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
-                                      int32_t tile_tokens) {
-    if (num_seqs <= 0 || num_kv_heads <= 0 || tile_tokens <= 0 || max_seq_len <= 0) return 1;
-    const int64_t pages = (max_seq_len + tile_tokens - 1) / tile_tokens;
-    // about 4 workgroups per compute unit, and at least 4 pages per split (the
-    // four waves of a workgroup walk pages independently)
-    const int64_t target = 1024;
-    const int64_t units = (int64_t)num_seqs * num_kv_heads;
-    int64_t sp = (target + units - 1) / units;
-    const int64_t cap = (pages + 3) / 4;
-    if (sp > cap) sp = cap;
-    if (sp < 1) sp = 1;
-    return (int32_t)sp;
+int32_t kv_decode_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_seq_len) {
+    kvq::DecodeArgs a{};
+    if (num_seqs <= 0 || max_seq_len <= 0 || check_cache(k) != KVQ_OK || (v && check_cache(v) != KVQ_OK) ||
+        decode_layout(k, v, num_q_heads, a) != KVQ_OK)
+        return 1;
+    a.B = num_seqs;
+    return kvq::decode_default_splits(a, max_seq_len);
 }
 
 size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,
@@ -139,55 +179,15 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
     if (!q || !valid_dtype(q_dtype) || num_seqs < 0 || num_q_heads <= 0 || !out || max_seq_len < 0) return KVQ_EINVAL;
     if (num_seqs == 0) return KVQ_OK;
     if (!block_table || !seq_lens || block_table_stride <= 0 || num_splits < 0) return KVQ_EINVAL;
-    const kvq_format &fk = k->fmt;
-    const kvq_format &fv = v ? v->fmt : k->fmt;
-    if (num_q_heads % k->num_heads != 0) return KVQ_EINVAL;
-    if (v) {
-        if (v->num_heads != k->num_heads || fv.tile_tokens != fk.tile_tokens || v->num_pages != k->num_pages)
-            return KVQ_EINVAL;
-        if (fk.rope_dim != 0 || fv.rope_dim != 0) return KVQ_EUNSUPPORTED;
-        if (fk.layout != KVQ_TOKEN_MAJOR || fv.layout != KVQ_CHANNEL_MAJOR) return KVQ_EUNSUPPORTED;
-    } else {
-        if (fk.layout != KVQ_TOKEN_MAJOR) return KVQ_EUNSUPPORTED;
-    }
-    if ((int64_t)block_table_stride * fk.tile_tokens < max_seq_len) return KVQ_EINVAL;
-    const int splits = num_splits > 0 ? num_splits
-                                      : kv_decode_attn_default_splits(num_seqs, k->num_heads, max_seq_len, fk.tile_tokens);
-    if (!workspace || workspace_bytes < kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, fv.head_dim, splits))
-        return KVQ_EWORKSPACE;
-
     kvq::DecodeArgs a{};
+    if ((st = decode_layout(k, v, num_q_heads, a)) != KVQ_OK) return st;
+    if ((int64_t)block_table_stride * a.T < max_seq_len) return KVQ_EINVAL;
+    a.B = num_seqs;
+    const int splits = num_splits > 0 ? num_splits : kvq::decode_default_splits(a, max_seq_len);
+    if (!workspace || workspace_bytes < kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, a.Dv, splits))
+        return KVQ_EWORKSPACE;
     a.q = q;
     a.q_dtype = (int)q_dtype;
-    a.B = num_seqs;
-    a.Hq = num_q_heads;
-    a.Hkv = k->num_heads;
-    a.grp = num_q_heads / k->num_heads;
-    a.hc = a.grp < 16 ? a.grp : 16;
-    if (a.grp % a.hc != 0) return KVQ_EUNSUPPORTED;
-    a.nhc = a.grp / a.hc;
-    a.kcodes = k->codes;
-    a.ksz = k->sz;
-    a.kcn = k->cnorm;
-    a.krope = k->rope;
-    a.D = fk.head_dim;
-    a.R = fk.rope_dim;
-    a.kG = fk.group;
-    a.kbits = fk.bits;
-    a.kh = fk.hadamard_n;
-    a.klayout = fk.layout;
-    const kvq_cache *vc = v ? v : k;
-    a.vcodes = vc->codes;
-    a.vsz = vc->sz;
-    a.vcn = vc->cnorm;
-    a.Dv = fv.head_dim;
-    a.vG = fv.group;
-    a.vbits = fv.bits;
-    a.vh = fv.hadamard_n;
-    a.vlayout = fv.layout;
-    a.vH = vc->num_heads;
-    a.T = fk.tile_tokens;
-    a.num_pages = k->num_pages;
     a.bt = block_table;
     a.bt_stride = block_table_stride;
     a.seq_lens = seq_lens;

@@ -225,9 +225,42 @@ __global__ void __launch_bounds__(DEC_NT) decode_reduce_kernel(DecodeArgs a) {
 
 bool decode_mfma_supported(const DecodeArgs &a);
 bool launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+bool decode_mla_supported(const DecodeArgs &a);
+int decode_mla_head_groups(const DecodeArgs &a);
+bool launch_decode_mla(const DecodeArgs &a, hipStream_t stream);
+
+int decode_default_splits(const DecodeArgs &a, int max_seq_len) {
+    const int64_t pages = (max_seq_len + a.T - 1) / a.T;
+    int64_t units, target, min_pages;
+    if (decode_mla_supported(a)) {
+        // one 256-thread workgroup per compute unit (its registers fill the SIMDs),
+        // per (sequence, kv head, 64 query heads, split); at least 2 pages per split
+        units = (int64_t)a.B * a.Hkv * decode_mla_head_groups(a);
+        target = 256;
+        min_pages = 2;
+    } else {
+        // about 4 workgroups per compute unit, and at least 4 pages per split (the
+        // four waves of a workgroup walk pages independently)
+        units = (int64_t)a.B * a.Hkv;
+        target = 1024;
+        min_pages = 4;
+    }
+    int64_t sp = (target + units - 1) / units;
+    const int64_t cap = (pages + min_pages - 1) / min_pages;
+    if (sp > cap) sp = cap;
+    if (sp > RED_MAX_SPLITS) sp = RED_MAX_SPLITS;
+    if (sp < 1) sp = 1;
+    return (int)sp;
+}
 
 bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.splits > RED_MAX_SPLITS) return false;
+    if (decode_mla_supported(a)) {
+        if (!launch_decode_mla(a, stream)) return false;
+        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * (a.Dv + a.splits),
+                           stream, a);
+        return true;
+    }
     if (decode_mfma_supported(a)) {
         if (!launch_decode_mfma(a, stream)) return false;
         hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * (a.Dv + a.splits),

@@ -363,6 +363,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 }
 
 bool decode_mfma_supported(const DecodeArgs &a) {
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    if (!al16(a.kcodes) || !al16(a.ksz) || !al16(a.kcn) || !al16(a.vcodes) || !al16(a.vsz) || !al16(a.vcn)) return false;
     if (a.D != MD || a.R != 0 || a.Dv != MD) return false;
     if (a.kG != MD || a.vG != MD) return false;
     if (a.grp > 16 || 16 % a.grp != 0 || a.hc != a.grp) return false;

@@ -51,5 +51,8 @@ struct DecodeArgs {
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
 bool launch_dequant(int D, int T, int num_tiles, const DequantArgs &a, hipStream_t stream);
 bool launch_decode(const DecodeArgs &a, hipStream_t stream);
+// split-K partitions for a decode call whose fields other than q, block table,
+// lengths, splits and buffers are filled in
+int decode_default_splits(const DecodeArgs &a, int max_seq_len);
 
 }  // namespace kvq

@@ -98,8 +98,27 @@ def test_decode_argument_errors():
     assert st(splits=3, ws_bytes=need - 1) == K.KVQ_EWORKSPACE
 
 
+def default_splits(fk, fv, num_seqs, num_q_heads, num_kv_heads, max_len, pages=1 << 16):
+    kc = cache_struct(fk, pages=pages, heads=num_kv_heads, rope=FAKE if fk.rope_dim else None)
+    vc = cache_struct(fv, pages=pages, heads=num_kv_heads) if fv is not None else None
+    return K._lib.kv_decode_attn_default_splits(ctypes.byref(kc), ctypes.byref(vc) if vc is not None else None,
+                                                num_seqs, num_q_heads, max_len)
+
+
 def test_default_splits():
+    fk = K.make_format(128, 0, 128, 128, 128, 4, 4, K.KVQ_TOKEN_MAJOR)
+    fv = K.make_format(128, 0, 128, 128, 128, 2, 4, K.KVQ_CHANNEL_MAJOR)
     # long context, one sequence: at least 256 partitions over the 8 kv heads
-    assert 8 * K.kv_decode_attn_default_splits(1, 8, 131072, 128) >= 256  # the long-context workload: >= 256 partitions
-    assert K.kv_decode_attn_default_splits(8, 8, 4096, 128) <= 32
-    assert K.kv_decode_attn_default_splits(1, 1, 5, 16) == 1
+    assert 8 * default_splits(fk, fv, 1, 32, 8, 131072) >= 256
+    assert default_splits(fk, fv, 8, 32, 8, 4096) <= 32
+    f16k = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_TOKEN_MAJOR)
+    f16v = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_CHANNEL_MAJOR)
+    assert default_splits(f16k, f16v, 1, 8, 1, 5) == 1
+    # MLA latent (512 + 64 rope, 4-bit): one workgroup per compute unit over
+    # (sequence, 64 query heads, split): 32 sequences x 2 head groups x 4 splits
+    fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)
+    assert default_splits(fm, None, 32, 128, 1, 32768) == 4
+    assert default_splits(fm, None, 1, 128, 1, 256) == 1      # 2 pages: at least 2 per split
+    # invalid arguments give 1
+    assert default_splits(fk, fv, 0, 32, 8, 4096) == 1
+    assert default_splits(fk, fv, 8, 30, 8, 4096) == 1
