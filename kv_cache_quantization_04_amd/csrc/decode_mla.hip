@@ -8,9 +8,9 @@
 // and normalizers into query and output and the per-token scales into scores.
 //
 // Per page, with qbar = q Q over the latent, q'_j = qbar_j c_j (c of this page):
-//   score_t = sm * ( S_t * [A . q']_t + (Z_t + 8 S_t) * sum_j q'_j + <q_rope, k_rope_t> )
-//   o'_j   += c_j * ( [A^T . P~]_j + sum_t p_t (Z_t + 8 S_t) ),  P~_t = p_t S_t
-// with A the centred codes (code - 8), exact in fp16. Both products run as
+//   score_t = sm * ( S_t * [A . q']_t + Z_t * sum_j q'_j + <q_rope, k_rope_t> )
+//   o'_j   += c_j * ( [A^T . P~]_j + sum_t p_t Z_t ),  P~_t = p_t S_t
+// with A the codes, exact in fp16 (as subnormals n 2^-24). Both products run as
 // v_mfma_f32_16x16x32_f16 with q' and P~ split into fp16 hi + lo parts after a
 // power-of-two scaling; the rope product runs as v_mfma_f32_16x16x32_bf16 with
 // the query's rope part split into bf16 hi + lo.
@@ -46,7 +46,7 @@ constexpr int XNT = 512;   // threads per workgroup (8 waves)
 constexpr int XHG = 64;    // query heads per workgroup
 
 // LDS image of one page (bytes). Codes: token row r (256 B) holds its 16-byte
-// chunk g at slot g ^ swz(r); rope: row r (128 B) holds chunk g at slot g ^ (r & 7);
+// chunk g at slot g ^ swz(r); rope: row r (128 B) holds chunk g at slot g ^ rswz(r);
 // (S, Z) pairs and the normalizer in natural order.
 constexpr int L_CODES = 0;
 constexpr int L_ROPE = XT * XD / 2;             // 32768
@@ -54,33 +54,34 @@ constexpr int L_SZ = L_ROPE + XT * XR * 2;      // 49152
 constexpr int L_CN = L_SZ + XT * 4;             // 49664
 constexpr int L_BYTES = L_CN + XD * 2;          // 50688
 constexpr int NCHUNK = L_BYTES / 16;            // 3168 16-byte chunks per page
-constexpr int PRE = (NCHUNK + XNT - 1) / XNT;   // 7 per thread
-// score exchange between the two waves of a pair: [wave][33][64] floats
-constexpr int L_XCH = L_BYTES;
+constexpr int CPT = (NCHUNK + XNT - 1) / XNT;   // 7 chunks per thread in the staging copy
+constexpr int NDMA = (NCHUNK + 63) / 64;        // 50 wave-wide direct-to-LDS copies per page
+// shared memory: staging image (natural chunk order, written by direct-to-LDS
+// copies), working image (swizzled), score exchange [pair][33][64] floats, and
+// each wave's rope query (bf16 hi / lo words, lane-major): 151552 bytes
 constexpr int XCH_WORDS = 33 * 64;
-constexpr int L_TOTAL = L_XCH + 8 * XCH_WORDS * 4;  // 118272
 
 // Slot swizzle of a code row: the 16 rows read together by either product land
 // in 16 different 16-byte slots (rows 4b + i + 16 q of a score tile, and rows
 // 16 lq + i of a transposed read).
 __device__ __forceinline__ int swz(int r) { return (r & 15) ^ ((r >> 2) & 12); }
+// Rope rows are 128 B, two to a bank window: the 16 rows of a score tile (rows
+// 4 b + i + 16 q) differ in (r & 1, rswz(r)).
+__device__ __forceinline__ int rswz(int r) { return ((r >> 1) & 1) | ((r >> 3) & 6); }
 
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
 // Eight 4-bit codes of one dword -> half8 in MFMA element order kk, element kk
-// holding nibble e(kk) = (kk >> 1) + 4 (kk & 1), centred by 8.
+// holding nibble e(kk) = (kk >> 1) + 4 (kk & 1). Each code n becomes the fp16 bit
+// pattern n, the subnormal n * 2^-24, which the matrix cores take exactly; the
+// factor 2^24 goes into the fp32 scale of the product.
 __device__ __forceinline__ half8 unpack8_4(uint32_t w) {
-    constexpr uint32_t MAGIC = 0x64006400u;  // fp16 1024 in both halves
-    const half2v bias = {(_Float16)1032.f, (_Float16)1032.f};
-    half8 r;
+    uint32_t p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const half2v h = as_h2(((w >> (4 * i)) & 0x000F000Fu) | MAGIC) - bias;
-        r[2 * i] = h[0];
-        r[2 * i + 1] = h[1];
-    }
-    return r;
+    for (int i = 0; i < 4; ++i) p[i] = (w >> (4 * i)) & 0x000F000Fu;
+    return __builtin_bit_cast(half8, uint4{p[0], p[1], p[2], p[3]});
 }
+constexpr float TWO24 = 16777216.f;
 
 // 2^(14 - floor(log2 m)) for m > 0 (1 for m == 0 or not finite).
 __device__ __forceinline__ float pow2_scale(float m) {
@@ -88,6 +89,11 @@ __device__ __forceinline__ float pow2_scale(float m) {
     if (e == 0 || e == 0xff) return 1.f;
     const int se = min(254, 268 - e);
     return __uint_as_float((uint32_t)se << 23);
+}
+
+// 2^24 / x for x a power of two from pow2_scale (exact)
+__device__ __forceinline__ float two24_over(float x) {
+    return __uint_as_float((uint32_t)min(254, 254 + 24 - (int)(__float_as_uint(x) >> 23)) << 23);
 }
 
 __device__ __forceinline__ float lq_sum(float v) {  // over the 4 lanes sharing lane & 15
@@ -116,10 +122,14 @@ __device__ __forceinline__ float load_q(const void *q, int64_t i) {
     else return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(q)[i]);
 }
 
+// One workgroup's pages. The three shared-memory regions come in as restrict
+// pointers: after inlining, the compiler knows that the direct-to-LDS copies
+// into `stage` touch neither `work` nor `xch`, and lets them stay in flight while
+// the current page is processed.
 template <int QDT>
-__global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int units, int nhg) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // L_TOTAL bytes
-
+__device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg, uint8_t *__restrict__ stage,
+                                         uint8_t *__restrict__ work, float *__restrict__ xch,
+                                         uint32_t *__restrict__ qrl_lds) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hs = wave & 3, half = wave >> 2;
@@ -145,39 +155,24 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
     const bool hq_ok = active && hl0 + l16 < a.grp;
     const int hq = hk * a.grp + hl0 + l16;                  // this lane's head (columns of every tile)
 
-    // ---- page prefetch: thread t moves chunks t + 512 k of the page image
-    uint4 pre[PRE];
+    // ---- page copy HBM -> staging image: wave w issues wave-wide copies w, w + 8, ...;
+    // lane l of copy k moves chunk 64 k + l
     auto fetch = [&](int pi) {
         const int page = load_const(a.bt, (int64_t)s * a.bt_stride + pi);
         const int64_t blk = (int64_t)page * a.Hkv + hk;
-        const uint4 *gcodes = reinterpret_cast<const uint4 *>(a.kcodes + blk * (XT * XD / 2));
-        const uint4 *grope = reinterpret_cast<const uint4 *>(a.krope + blk * (XT * XR));
-        const uint4 *gsz = reinterpret_cast<const uint4 *>(a.ksz + blk * (XT * 2));
-        const uint4 *gcn = reinterpret_cast<const uint4 *>(a.kcn + blk * XD);
-#pragma unroll
-        for (int k = 0; k < PRE; ++k) {
-            const int c = tid + XNT * k;
-            if (c < 2048) pre[k] = gcodes[c];
-            else if (c < 3072) pre[k] = grope[c - 2048];
-            else if (c < 3104) pre[k] = gsz[c - 3072];
-            else if (c < NCHUNK) pre[k] = gcn[c - 3104];
-        }
-    };
-    auto stash = [&]() {  // registers -> LDS image, swizzled
-#pragma unroll
-        for (int k = 0; k < PRE; ++k) {
-            const int c = tid + XNT * k;
-            int off;
-            if (c < 2048) {
-                const int r = c >> 4, g = c & 15;
-                off = L_CODES + r * 256 + 16 * (g ^ swz(r));
-            } else if (c < 3072) {
-                const int r = (c - 2048) >> 3, g = (c - 2048) & 7;
-                off = L_ROPE + r * 128 + 16 * (g ^ (r & 7));
-            } else {
-                off = L_SZ + 16 * (c - 3072);  // (S, Z) then normalizer, contiguous
-            }
-            if (c < NCHUNK) *reinterpret_cast<uint4 *>(lds + off) = pre[k];
+        const uint8_t *gcodes = a.kcodes + blk * (XT * XD / 2);
+        const uint8_t *grope = reinterpret_cast<const uint8_t *>(a.krope + blk * (XT * XR));
+        const uint8_t *gsz = reinterpret_cast<const uint8_t *>(a.ksz + blk * (XT * 2));
+        const uint8_t *gcn = reinterpret_cast<const uint8_t *>(a.kcn + blk * XD);
+        for (int k = wave; k < NDMA; k += 8) {
+            const int c = 64 * k + lane;
+            const uint8_t *src = c < 2048 ? gcodes + 16 * c
+                               : c < 3072 ? grope + 16 * (c - 2048)
+                               : c < 3104 ? gsz + 16 * (c - 3072)
+                                          : gcn + 16 * (c - 3104);
+            if (c < NCHUNK)
+                __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(stage + 1024 * k),
+                                                 16, 0, 0);
         }
     };
     auto page_ok = [&](int pi) {
@@ -191,7 +186,7 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
     // ---- rotated query of the lane's head over all 512 channels (c = 32 st + 8 lq + e);
     // the wave keeps its half: qv[st'][e] = qbar[256 half + 32 st' + 8 lq + e] / sqrt(512)
     float qv[8][8];
-    uint32_t qrh[4], qrl[4];  // rope dims 32 half + 8 lq + 0..7 as bf16 hi / lo pairs
+    uint32_t *qr = qrl_lds + wave * 8 * 64 + lane;  // rope dims 32 half + 8 lq + 0..7: bf16 hi words 0..3, lo 4..7
     float qmax = 0.f;
     {
         const int64_t qb = ((int64_t)s * a.Hq + hq) * (XD + XR);
@@ -211,8 +206,8 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
                 hw |= (uint32_t)hb << (16 * h);
                 lw |= (uint32_t)lb << (16 * h);
             }
-            qrh[e2] = hw;
-            qrl[e2] = lw;
+            qr[e2 * 64] = hw;
+            qr[(4 + e2) * 64] = lw;
         }
         // Walsh-Hadamard transform: bits of e and st in registers, bits of lq
         // across lanes (lane bits 4 and 5)
@@ -263,24 +258,56 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
     f32x4 o[16];
 #pragma unroll
     for (int mc = 0; mc < 16; ++mc) o[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float *xmine = reinterpret_cast<float *>(lds + L_XCH) + wave * XCH_WORDS;
-    const float *xpart = reinterpret_cast<const float *>(lds + L_XCH) + (wave ^ 4) * XCH_WORDS;
+    float *xp = xch + hs * XCH_WORDS;  // this pair's exchange slot
+    const uint16_t *cn = reinterpret_cast<const uint16_t *>(work + L_CN);
 
     while (pi < p1) {
         const int cur = pi;
-        lds_barrier();  // every wave is done with the previous page image
-        stash();
-        lds_barrier();  // the page image is complete
-        ++pi;
-        while (pi < p1 && !page_ok(pi)) ++pi;
-        if (pi < p1) fetch(pi);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into the staging image have landed
+        lds_barrier();                  // every wave's, and every wave is done with the working image
+        // staging -> working image, swizzled
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int c = tid + XNT * k;
+            if (c < NCHUNK) {
+                int off;
+                if (c < 2048) {
+                    const int r = c >> 4, g = c & 15;
+                    off = L_CODES + r * 256 + 16 * (g ^ swz(r));
+                } else if (c < 3072) {
+                    const int r = (c - 2048) >> 3, g = (c - 2048) & 7;
+                    off = L_ROPE + r * 128 + 16 * (g ^ rswz(r));
+                } else {
+                    off = L_SZ + 16 * (c - 3072);  // (S, Z) then normalizer, contiguous
+                }
+                *reinterpret_cast<uint4 *>(work + off) = *reinterpret_cast<const uint4 *>(stage + 16 * c);
+            }
+        }
+        lds_barrier();  // working image complete, staging image free
         const int rows = min(XT, L - cur * XT);
+        // Per-lane byte addresses of the code rows this lane reads, made opaque here
+        // so that the per-K-step addresses below are formed next to their reads
+        // rather than hoisted out of the page loop (64 live registers otherwise).
+        // Score tile j reads row r = 64 pi2 + 16 q + 4 b + i: address r * 256 + 4 lq,
+        // XOR 16 (chunk ^ swz(r)); the transposed reads use rows 64 pi2 + 16 lq + l16.
+        int lo = lane;  // the lane id, opaque: addresses derived from it stay inside the loop
+        asm volatile("" : "+v"(lo));
+        const int ol16 = lo & 15, olq = lo >> 4;
+        // rows 64 apart share the swizzle, so the second half of the page is a
+        // constant 16 KB further (an immediate offset of the read)
+        int sbase[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int r = 16 * (ol16 >> 2) + 4 * b + (ol16 & 3);
+            sbase[b] = L_CODES + r * 256 + 16 * swz(r) + 4 * olq;
+        }
+        const int tr0 = 16 * olq + ol16;
+        const int tbase = L_CODES + tr0 * 256 + 16 * swz(tr0);
 
         // page-wide bound of the query-side scaling: max c
-        const uint16_t *cn = reinterpret_cast<const uint16_t *>(lds + L_CN);
         float cmax = 0.f;
         {
-            const uint4 cw = *reinterpret_cast<const uint4 *>(lds + L_CN + 16 * lane);
+            const uint4 cw = *reinterpret_cast<const uint4 *>(work + L_CN + 16 * lane);
             const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -289,7 +316,11 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
             for (int m = 1; m < 64; m <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, m, 64));
         }
         const float qsc = pow2_scale(qmax * cmax);
-        const float qinv = 1.0f / qsc;
+        const float qinv = two24_over(qsc);  // undoes the query scaling and the codes' 2^-24
+        // the next valid page, copied into the staging image while this one is processed
+        ++pi;
+        while (pi < p1 && !page_ok(pi)) ++pi;
+        if (pi < p1) fetch(pi);
 
         // ---- partial scores^T over this wave's latent half: tile j = (pi2 = j >> 2, b = j & 3)
         // holds tokens 64 pi2 + 16 q + 4 b + i (row 4 q + i); A rows come from lane l16 = 4 q + i
@@ -301,7 +332,7 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
                 const int chunk = 8 * half + st;  // 16-byte chunk of a code row: channels 32 chunk ..
-                const uint4 cw = *reinterpret_cast<const uint4 *>(lds + L_CN + 2 * (32 * chunk + 8 * lq));
+                const uint4 cw = *reinterpret_cast<const uint4 *>(work + L_CN + 2 * (32 * chunk + 8 * lq));
                 const uint32_t c4[4] = {cw.x, cw.y, cw.z, cw.w};
                 half8 bh, bl;
 #pragma unroll
@@ -317,55 +348,76 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int r = 64 * (j >> 2) + 16 * (l16 >> 2) + 4 * (j & 3) + (l16 & 3);
                     const uint32_t w =
-                        *reinterpret_cast<const uint32_t *>(lds + L_CODES + r * 256 + 16 * (chunk ^ swz(r)) + 4 * lq);
+                        *reinterpret_cast<const uint32_t *>(work + (sbase[j & 3] ^ (16 * chunk)) + 16384 * (j >> 2));
                     const half8 av = unpack8_4(w);
                     sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, sc[j], 0, 0, 0);
                     sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, sc[j], 0, 0, 0);
                 }
+                // keep the next K-step's operands from being hoisted here (register pressure)
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // rope half, then y = S qinv sc + rope, published for the partner wave
-            const bf16x8 bh = __builtin_bit_cast(bf16x8, uint4{qrh[0], qrh[1], qrh[2], qrh[3]});
-            const bf16x8 bl = __builtin_bit_cast(bf16x8, uint4{qrl[0], qrl[1], qrl[2], qrl[3]});
+            // rope half, then y = S qinv sc + rope
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, uint4{qr[0], qr[64], qr[128], qr[192]});
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, uint4{qr[256], qr[320], qr[384], qr[448]});
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int r = 64 * (j >> 2) + 16 * (l16 >> 2) + 4 * (j & 3) + (l16 & 3);
-                const uint4 rw = *reinterpret_cast<const uint4 *>(lds + L_ROPE + r * 128 + 16 * ((4 * half + lq) ^ (r & 7)));
+                const int r = 64 * (j >> 2) + 16 * (ol16 >> 2) + 4 * (j & 3) + (ol16 & 3);
+                const uint4 rw = *reinterpret_cast<const uint4 *>(work + L_ROPE + r * 128 + 16 * ((4 * half + olq) ^ rswz(r)));
                 const bf16x8 av = __builtin_bit_cast(bf16x8, rw);
                 f32x4 rp = {0.f, 0.f, 0.f, 0.f};
                 rp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, rp, 0, 0, 0);
                 rp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, rp, 0, 0, 0);
-                const int t0 = 64 * (j >> 2) + 16 * lq + 4 * (j & 3);
-                const uint4 zw = *reinterpret_cast<const uint4 *>(lds + L_SZ + 4 * t0);
+                const int t0 = 64 * (j >> 2) + 16 * olq + 4 * (j & 3);
+                const uint4 zw = *reinterpret_cast<const uint4 *>(work + L_SZ + 4 * t0);
                 const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float S = half_bits_to_float(z4[i] & 0xffffu);
-                    sc[j][i] = __builtin_fmaf(S * qinv, sc[j][i], rp[i]);
-                    xmine[(4 * j + i) * 64 + lane] = sc[j][i];
-                }
+                for (int i = 0; i < 4; ++i) sc[j][i] = __builtin_fmaf(half_bits_to_float(z4[i] & 0xffffu) * qinv, sc[j][i], rp[i]);
             }
-            xmine[32 * 64 + lane] = qc;
+            // the low half publishes its partial sums
+            if (half == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xp[(4 * j + i) * 64 + lane] = sc[j][i];
+                xp[32 * 64 + lane] = qc;
+            }
         }
-        lds_barrier();  // partial scores of both halves published
+        lds_barrier();
+        if (active && half == 1) {  // the high half completes the sums and publishes them
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sc[j][i] += xp[(4 * j + i) * 64 + lane];
+                    xp[(4 * j + i) * 64 + lane] = sc[j][i];
+                }
+            qc += xp[32 * 64 + lane];
+            xp[32 * 64 + lane] = qc;
+        }
+        lds_barrier();
         if (!active) continue;
-        qc += xpart[32 * 64 + lane];
+        if (half == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[j][i] = xp[(4 * j + i) * 64 + lane];
+            qc = xp[32 * 64 + lane];
+        }
         qc = lq_sum(qc);
 
         // ---- online softmax; lane (head l16, lq) holds tokens 64 pi2 + 16 lq + 4 b + i of tile (pi2, b)
         float smax = 0.f, pmax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int t0 = 64 * (j >> 2) + 16 * lq + 4 * (j & 3);
-            const uint4 zw = *reinterpret_cast<const uint4 *>(lds + L_SZ + 4 * t0);
+            const int t0 = 64 * (j >> 2) + 16 * olq + 4 * (j & 3);
+            const uint4 zw = *reinterpret_cast<const uint4 *>(work + L_SZ + 4 * t0);
             const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float S = half_bits_to_float(z4[i] & 0xffffu), Z = half_bits_to_float(z4[i] >> 16);
                 smax = fmaxf(smax, fabsf(S));
-                const float y = sc[j][i] + xpart[(4 * j + i) * 64 + lane];
-                float x = sml2 * __builtin_fmaf(__builtin_fmaf(8.f, S, Z), qc, y);
+                float x = sml2 * __builtin_fmaf(Z, qc, sc[j][i]);
                 if (t0 + i >= rows) x = -INFINITY;
                 sc[j][i] = x;
                 pmax = fmaxf(pmax, x);
@@ -376,7 +428,7 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
         const float m_new = fmaxf(m_run, pmax);
         const float alpha = exp2f(m_run - m_new);
         m_run = m_new;
-        const float psc = pow2_scale(smax), pinv = 1.0f / psc;
+        const float psc = pow2_scale(smax), pinv = two24_over(psc);
         float psum = 0.f, zs = 0.f;
         // P~ = p S psc straight into the B operand of the value product: K-step
         // kap = 2 pi2 + beta covers tokens 64 pi2 + 16 lq + 8 beta + e(kk); element
@@ -384,16 +436,16 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
         half8 pbh[4], pbl[4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int t0 = 64 * (j >> 2) + 16 * lq + 4 * (j & 3);
+            const int t0 = 64 * (j >> 2) + 16 * olq + 4 * (j & 3);
             const int kap = 2 * (j >> 2) + ((j >> 1) & 1);
-            const uint4 zw = *reinterpret_cast<const uint4 *>(lds + L_SZ + 4 * t0);
+            const uint4 zw = *reinterpret_cast<const uint4 *>(work + L_SZ + 4 * t0);
             const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float S = half_bits_to_float(z4[i] & 0xffffu), Z = half_bits_to_float(z4[i] >> 16);
                 const float p = exp2f(sc[j][i] - m_new);
                 psum += p;
-                zs = __builtin_fmaf(p, __builtin_fmaf(8.f, S, Z), zs);
+                zs = __builtin_fmaf(p, Z, zs);
                 const float xs = p * S * psc;
                 const _Float16 hi = (_Float16)xs;
                 pbh[kap][2 * i + (j & 1)] = hi;
@@ -411,9 +463,8 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p2 = 0; p2 < 2; ++p2) {
-                const int r = 64 * p2 + 16 * lq + l16;  // row addressed by this lane for the group's read
-                const int off = L_CODES + r * 256 + 16 * ((mc >> 1) ^ swz(r)) + 8 * (mc & 1);
-                const v2i tw = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(lds + off));
+                const int off = (tbase ^ (16 * (mc >> 1))) + 16384 * p2 + 8 * (mc & 1);  // this lane's row of the group's read
+                const v2i tw = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(work + off));
 #pragma unroll
                 for (int beta = 0; beta < 2; ++beta) {
                     const half8 av = unpack8_4((uint32_t)tw[beta]);
@@ -427,6 +478,7 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
                                   half_bits_to_float(cv2.y & 0xffffu), half_bits_to_float(cv2.y >> 16)};
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[m2][i] = __builtin_fmaf(o[m2][i], alpha, cvv[i] * __builtin_fmaf(acc[i], pinv, zs));
+            if (m2 & 1) __builtin_amdgcn_sched_barrier(0);  // at most two tiles' operands in flight
         }
     }
 
@@ -443,6 +495,18 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
     }
 }
 
+template <int QDT>
+__global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int units, int nhg) {
+    // Separate LDS variables: each gets its own alias scope, which lets the
+    // compiler keep the direct-to-LDS copies into `stage` in flight across the
+    // accesses to the others.
+    __shared__ __attribute__((aligned(16))) uint8_t stage[L_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t work[L_BYTES];
+    __shared__ float xch[4 * XCH_WORDS];
+    __shared__ uint32_t qr[8 * 8 * 64];
+    mla_body<QDT>(a, units, nhg, stage, work, xch, qr);
+}
+
 bool decode_mla_supported(const DecodeArgs &a) {
     auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
     return al16(a.kcodes) && al16(a.ksz) && al16(a.kcn) && al16(a.krope) && a.D == XD && a.R == XR && a.Dv == XD && a.T == XT && a.kbits == 4 && a.kG == XD && a.kh == XD &&
@@ -457,10 +521,7 @@ bool launch_decode_mla(const DecodeArgs &a, hipStream_t stream) {
     const int units = a.B * a.Hkv * a.splits;
     const int grid = ((units + 7) / 8) * 8 * nhg;
     auto go = [&](auto kern) {
-        // the LDS image plus the score exchange exceed the default 64 KB
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L_TOTAL) != hipSuccess)
-            return false;
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(XNT), L_TOTAL, stream, a, units, nhg);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(XNT), 0, stream, a, units, nhg);
         return true;
     };
     switch (a.q_dtype) {
