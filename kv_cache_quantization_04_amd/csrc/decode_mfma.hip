@@ -5,13 +5,15 @@
 //   scores^T [tokens x heads]  = A_K [tokens x channels] . qbar^T [channels x heads]
 //   o'^T     [channels x heads] = A_V [channels x tokens] . P~^T [tokens x heads]
 // run as v_mfma_f32_16x16x32_f16 tiles with fp32 accumulation. The codes enter
-// exactly, centred (code - 2^(b-1)); the K normalizer is folded into the query
-// per page, q'_j = qbar_j c_K,j in fp32. Query and probability operands are
-// split into fp16 hi + lo parts (two MFMAs each), about 22 significant bits,
-// after a per-page power-of-two scaling that puts their largest value near 2^14
-// (clear of fp16 overflow, and of the subnormal range where lo would lose bits).
-//   score_t = sm * ( S_t * [A_K . q']_t + (Z_t + 2^(b-1) S_t) * sum_j q'_j )
-//   o'_j   += c_V,j * ( [A_V . P~]_j + sum_t p_t (Z_t + 2^(b-1) S_t) ),  P~_t = p_t S_t
+// exactly: code n becomes the fp16 subnormal n 2^-(14+b), which the matrix cores
+// take as is (the power of two goes into the fp32 scale factors); the
+// K normalizer is folded into the query per page, q'_j = qbar_j c_K,j in fp32.
+// Query and probability operands are split into fp16 hi + lo parts (two MFMAs
+// each), about 22 significant bits, after a per-page power-of-two scaling that
+// puts their largest value near 2^14 (clear of fp16 overflow, and of the
+// subnormal range where lo would lose bits).
+//   score_t = sm * ( S_t * [A_K . q']_t + Z_t * sum_j q'_j )
+//   o'_j   += c_V,j * ( [A_V . P~]_j + sum_t p_t Z_t ),  P~_t = p_t S_t
 // Each wave walks its own pages (online softmax per wave); the four waves of a
 // workgroup merge before writing the split partial. Token order inside a page
 // is permuted so that the score tile of two 16-token M-tiles lands, lane for
@@ -32,36 +34,27 @@ __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(
 __device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
 // Eight codes of one lane chunk -> half8 in MFMA element order kk, where element
-// kk holds chunk position e(kk) = (kk >> 1) + 4 (kk & 1), centred by 2^(b-1).
-// `lo` holds the chunk's bits starting at bit 0 (b * 8 bits used).
+// kk holds chunk position e(kk) = (kk >> 1) + 4 (kk & 1) as the fp16 bit pattern
+// code << (10 - B): the subnormal code * 2^(-14 - B), exact in the matrix cores.
+// (The top of the subnormal range: accumulating products of the bare bit pattern,
+// code * 2^-24, loses low-order bits.) The power of two goes into the fp32 scale
+// factors. `lo` holds the chunk's bits starting at bit 0 (b * 8 bits used).
 template <int B>
 __device__ __forceinline__ half8 unpack8(uint32_t lo) {
-    constexpr uint32_t MAGIC = 0x64006400u;  // fp16 1024 in both halves
-    constexpr _Float16 BIAS = (_Float16)(1024 + (1 << (B - 1)));
+    constexpr int K = 10 - B;
+    constexpr uint32_t M = ((1u << B) - 1u) * 0x00010001u << K;
+    uint32_t s = lo;
+    if constexpr (B == 2) s = (lo & 0xFFu) | ((lo & 0xFF00u) << 8);   // codes 4..7 to bits 16..
+    if constexpr (B == 3) s = (lo & 0xFFFu) | ((lo & 0xFFF000u) << 4);  // codes 4..7 to bits 16..
     uint32_t p[4];
-    if constexpr (B == 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = ((lo >> (4 * i)) & 0x000F000Fu) | MAGIC;
-    } else if constexpr (B == 2) {
-        // codes 0..3 in bits 0..7, 4..7 in bits 8..15: move the second byte to bit 16
-        const uint32_t s = (lo & 0xFFu) | ((lo & 0xFF00u) << 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = ((s >> (2 * i)) & 0x00030003u) | MAGIC;
-    } else {  // B == 3: codes 0..3 in bits 0..11, 4..7 in bits 12..23
-        const uint32_t s = (lo & 0xFFFu) | ((lo & 0xFFF000u) << 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = ((s >> (3 * i)) & 0x00070007u) | MAGIC;
-    }
-    half8 r;
-    const half2v bias = {BIAS, BIAS};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const half2v h = as_h2(p[i]) - bias;
-        r[2 * i] = h[0];
-        r[2 * i + 1] = h[1];
+        const int sh = K - B * i;  // compile-time after unrolling
+        p[i] = (sh >= 0 ? (s << sh) : (s >> -sh)) & M;
     }
-    return r;
+    return __builtin_bit_cast(half8, uint4{p[0], p[1], p[2], p[3]});
 }
+template <int B> constexpr int CODE_EXP = 14 + B;  // unpacked code n is n * 2^-CODE_EXP
 
 // 2^(14 - floor(log2 m)) for m > 0 (1 for m == 0 or not finite): scales values
 // with maximum magnitude m into [2^14, 2^15).
@@ -70,6 +63,12 @@ __device__ __forceinline__ float pow2_scale_for(float m) {
     if (e == 0 || e == 0xff) return 1.f;
     const int se = min(254, 268 - e);  // biased exponent of 2^(14 - (e - 127))
     return __uint_as_float((uint32_t)se << 23);
+}
+
+// 2^E / x for x a power of two from pow2_scale_for (exact; saturates at 2^127)
+template <int E>
+__device__ __forceinline__ float pow2_over(float x) {
+    return __uint_as_float((uint32_t)min(254, 254 + E - (int)(__float_as_uint(x) >> 23)) << 23);
 }
 
 // fp32 -> fp16 hi + lo split of one value.
@@ -101,7 +100,6 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = T / 16;                 // 16-token M-tiles of the score product
     constexpr int KSV = T >= 32 ? T / 32 : 1;  // 32-token K-steps of the value product
     constexpr int KCB = 32 * KB / 8;           // bytes of one lane's 32-channel K chunk
-    __shared__ float qs[16][MD];
     __shared__ float red_o[4][16][MD + 1];
     __shared__ float red_ml[4][16][2];
 
@@ -114,33 +112,72 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     const int pps = (npages + a.splits - 1) / a.splits;
     const int p0 = split * pps, p1 = min(npages, p0 + pps);
 
-    // ---- rotated query qbar = q Q for the g heads of this kv head (rows >= g zero)
-    for (int e = tid; e < 16 * MD; e += MNT) {
-        const int hh = e / MD, j = e % MD;
-        qs[hh][j] = hh < g ? load_as_float(a.q, a.q_dtype, ((int64_t)s * a.Hq + hk * g + hh) * MD + j) : 0.f;
-    }
-    __syncthreads();
-    for (int len = 1; len < a.kh; len <<= 1) {
-        for (int e = tid; e < 16 * MD / 2; e += MNT) {
-            const int hh = e / (MD / 2), pe = e % (MD / 2);
-            const int i = (pe / len) * 2 * len + pe % len;
-            const float x = qs[hh][i], y = qs[hh][i + len];
-            qs[hh][i] = x + y;
-            qs[hh][i + len] = x - y;
-        }
-        __syncthreads();
-    }
-    const float qscale = 1.0f / sqrtf((float)a.kh);
-    // B operand of the score product: lane (head l16, chunk lq), K-step st covers
-    // channels lq*32 + st*8 + e(kk); qv holds qbar of those channels in (st, e) order.
+    // ---- rotated query qbar = q Q of head l16 (< g; other lanes hold zeros) in the
+    // B-operand layout: lane (head l16, chunk lq), K-step st covers channels
+    // lq*32 + st*8 + e(kk); qv[st*8 + e] = qbar[lq*32 + st*8 + e] / sqrt(h). The
+    // Walsh-Hadamard butterflies on channel bits 0..4 run in registers, bits 5 and 6
+    // across lanes 16 and 32 apart; blocks of h channels rotate separately.
     float qv[32];
+    {
+        const bool hv = l16 < g;
+        const int64_t qb = ((int64_t)s * a.Hq + hk * g + (hv ? l16 : 0)) * MD + lq * 32;
+        // 32 consecutive channels: 16-byte loads under one (uniform) dtype branch
+        if (a.q_dtype == KVQ_F32) {
+            const float4 *p4 = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qb);
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = p4[i];
+                qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+            }
+        } else {
+            const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
+            uint32_t w[16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[st * 8 + e] = qs[l16][lq * 32 + st * 8 + e] * qscale;
+            for (int i = 0; i < 4; ++i) {
+                const uint4 v = p4[i];
+                w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+            }
+            if (a.q_dtype == KVQ_BF16) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    qv[2 * k] = __uint_as_float(w[k] << 16);
+                    qv[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    qv[2 * k] = half_bits_to_float(w[k] & 0xffffu);
+                    qv[2 * k + 1] = half_bits_to_float(w[k] >> 16);
+                }
+            }
+        }
+        if (!hv)
+#pragma unroll
+            for (int i = 0; i < 32; ++i) qv[i] = 0.f;
+#pragma unroll
+        for (int b = 1; b < 32; b <<= 1)
+            if (b < a.kh)
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    if (!(i & b)) {
+                        const float x = qv[i], y = qv[i | b];
+                        qv[i] = x + y;
+                        qv[i | b] = x - y;
+                    }
+        const float s16 = (lq & 1) ? -1.f : 1.f, s32 = (lq & 2) ? -1.f : 1.f;
+        const float qscale = 1.0f / sqrtf((float)a.kh);
+        const bool x16 = a.kh > 32, x32 = a.kh > 64;
+        if (x16)
+#pragma unroll
+            for (int i = 0; i < 32; ++i) qv[i] = __builtin_fmaf(s16, qv[i], __shfl_xor(qv[i], 16, 64));
+        if (x32)
+#pragma unroll
+            for (int i = 0; i < 32; ++i) qv[i] = __builtin_fmaf(s32, qv[i], __shfl_xor(qv[i], 32, 64));
+#pragma unroll
+        for (int i = 0; i < 32; ++i) qv[i] *= qscale;
+    }
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
-    constexpr float KC = (float)(1 << (KB - 1)), VC = (float)(1 << (VB - 1));
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[8];
 #pragma unroll
@@ -175,7 +212,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
         qc = xlane_sum_q(qc);
         const float qsc = pow2_scale_for(xlane_max_q(qmax));
-        const float qinv = 1.0f / qsc;
+        const float qinv = pow2_over<CODE_EXP<KB>>(qsc);  // undoes the query scaling and the code unit
         half8 qhi[4], qlo[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st)
@@ -229,7 +266,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float S = half_bits_to_float(kzw[i] & 0xffffu), Z = half_bits_to_float(kzw[i] >> 16);
-                float x = sml2 * __builtin_fmaf(S * qinv, sc[j][i], (Z + KC * S) * qc);
+                float x = sml2 * __builtin_fmaf(S * qinv, sc[j][i], Z * qc);
                 if (tok0 + i >= rows) x = -INFINITY;
                 sc[j][i] = x;
                 pmax = fmaxf(pmax, x);
@@ -258,11 +295,11 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                 const float SV = half_bits_to_float(vzw[i] & 0xffffu), ZV = half_bits_to_float(vzw[i] >> 16);
                 const float p = exp2f(sc[j][i] - m_new);
                 psum += p;
-                zs = __builtin_fmaf(p, ZV + VC * SV, zs);
+                zs = __builtin_fmaf(p, ZV, zs);
                 split_h(p * SV * psc, phi[j][i], plo[j][i]);
             }
         }
-        const float pinv = 1.0f / psc;
+        const float pinv = pow2_over<CODE_EXP<VB>>(psc);
         l_run = __builtin_fmaf(l_run, alpha, psum);
         zs = xlane_sum_q(zs);
 
@@ -364,7 +401,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 
 bool decode_mfma_supported(const DecodeArgs &a) {
     auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
-    if (!al16(a.kcodes) || !al16(a.ksz) || !al16(a.kcn) || !al16(a.vcodes) || !al16(a.vsz) || !al16(a.vcn)) return false;
+    if (!al16(a.q) || !al16(a.kcodes) || !al16(a.ksz) || !al16(a.kcn) || !al16(a.vcodes) || !al16(a.vsz) || !al16(a.vcn))
+        return false;
     if (a.D != MD || a.R != 0 || a.Dv != MD) return false;
     if (a.kG != MD || a.vG != MD) return false;
     if (a.grp > 16 || 16 % a.grp != 0 || a.hc != a.grp) return false;

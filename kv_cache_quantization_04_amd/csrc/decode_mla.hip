@@ -10,7 +10,7 @@
 // Per page, with qbar = q Q over the latent, q'_j = qbar_j c_j (c of this page):
 //   score_t = sm * ( S_t * [A . q']_t + Z_t * sum_j q'_j + <q_rope, k_rope_t> )
 //   o'_j   += c_j * ( [A^T . P~]_j + sum_t p_t Z_t ),  P~_t = p_t S_t
-// with A the codes, exact in fp16 (as subnormals n 2^-24). Both products run as
+// with A the codes, exact in fp16 (as subnormals n 2^-18). Both products run as
 // v_mfma_f32_16x16x32_f16 with q' and P~ split into fp16 hi + lo parts after a
 // power-of-two scaling; the rope product runs as v_mfma_f32_16x16x32_bf16 with
 // the query's rope part split into bf16 hi + lo.
@@ -73,15 +73,15 @@ __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(
 
 // Eight 4-bit codes of one dword -> half8 in MFMA element order kk, element kk
 // holding nibble e(kk) = (kk >> 1) + 4 (kk & 1). Each code n becomes the fp16 bit
-// pattern n, the subnormal n * 2^-24, which the matrix cores take exactly; the
-// factor 2^24 goes into the fp32 scale of the product.
+// pattern n << 6, the subnormal n * 2^-18, which the matrix cores take exactly
+// (with the bare pattern n * 2^-24 their accumulation loses low-order bits); the
+// factor 2^18 goes into the fp32 scale of the product.
 __device__ __forceinline__ half8 unpack8_4(uint32_t w) {
-    uint32_t p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = (w >> (4 * i)) & 0x000F000Fu;
-    return __builtin_bit_cast(half8, uint4{p[0], p[1], p[2], p[3]});
+    constexpr uint32_t M = 0x000F000Fu << 6;
+    const uint32_t p0 = (w << 6) & M, p1 = (w << 2) & M, p2 = (w >> 2) & M, p3 = (w >> 6) & M;
+    return __builtin_bit_cast(half8, uint4{p0, p1, p2, p3});
 }
-constexpr float TWO24 = 16777216.f;
+constexpr int CODE_EXP = 18;  // unpacked code n is n * 2^-18
 
 // 2^(14 - floor(log2 m)) for m > 0 (1 for m == 0 or not finite).
 __device__ __forceinline__ float pow2_scale(float m) {
@@ -91,9 +91,9 @@ __device__ __forceinline__ float pow2_scale(float m) {
     return __uint_as_float((uint32_t)se << 23);
 }
 
-// 2^24 / x for x a power of two from pow2_scale (exact)
-__device__ __forceinline__ float two24_over(float x) {
-    return __uint_as_float((uint32_t)min(254, 254 + 24 - (int)(__float_as_uint(x) >> 23)) << 23);
+// 2^CODE_EXP / x for x a power of two from pow2_scale (exact; saturates at 2^127)
+__device__ __forceinline__ float code_over(float x) {
+    return __uint_as_float((uint32_t)min(254, 254 + CODE_EXP - (int)(__float_as_uint(x) >> 23)) << 23);
 }
 
 __device__ __forceinline__ float lq_sum(float v) {  // over the 4 lanes sharing lane & 15
@@ -316,7 +316,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             for (int m = 1; m < 64; m <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, m, 64));
         }
         const float qsc = pow2_scale(qmax * cmax);
-        const float qinv = two24_over(qsc);  // undoes the query scaling and the codes' 2^-24
+        const float qinv = code_over(qsc);  // undoes the query scaling and the code unit
         // the next valid page, copied into the staging image while this one is processed
         ++pi;
         while (pi < p1 && !page_ok(pi)) ++pi;
@@ -428,7 +428,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         const float m_new = fmaxf(m_run, pmax);
         const float alpha = exp2f(m_run - m_new);
         m_run = m_new;
-        const float psc = pow2_scale(smax), pinv = two24_over(psc);
+        const float psc = pow2_scale(smax), pinv = code_over(psc);
         float psum = 0.f, zs = 0.f;
         // P~ = p S psc straight into the B operand of the value product: K-step
         // kap = 2 pi2 + beta covers tokens 64 pi2 + 16 lq + 8 beta + e(kk); element
