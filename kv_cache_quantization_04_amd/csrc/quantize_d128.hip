@@ -105,20 +105,46 @@ __device__ __forceinline__ uint32_t pack8(const float (&u)[8]) {
     }
 }
 
+// LDS image of a code block: 16-byte slot U of the global layout lives at slot
+// code_slot(U). The stores that run together (one row, or one channel, of every
+// lane) then fall in distinct 16-byte bank windows, and the coalesced copy-out
+// reads slot code_slot(i) for global slot i (the map is its own inverse).
+//   token-major: the four row groups of a wave (rg & 3) spread over the slots of a
+//     row, rg = row / R, row = U / BITS;
+//   channel-major: the 16 channel groups (cc) spread over the 16 low slot bits.
+template <int T, int BITS, int LAYOUT>
+__device__ __forceinline__ int code_slot(int U) {
+    constexpr int R = T / 16;
+    if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
+        constexpr int L = BITS == 4 ? 2 : 1;   // log2 of slots per token row
+        constexpr int S = L + (R == 8 ? 3 : 2);  // log2 of slots per row group
+        return U ^ (((U >> S) & 3) << L);
+    } else {
+        constexpr int CR = T * BITS / 128;      // slots per channel row
+        constexpr int S = CR == 4 ? 5 : CR == 2 ? 4 : 3;  // log2 of slots per channel group (8 channels)
+        constexpr int M = CR == 1 ? 7 : 15;
+        return U ^ ((U >> S) & M);
+    }
+}
+template <int T, int BITS, int LAYOUT>
+__device__ __forceinline__ int code_byte(int b) {
+    return (code_slot<T, BITS, LAYOUT>(b >> 4) << 4) | (b & 15);
+}
+
 }  // namespace
 
 // The LDS buffers come in as restrict pointers: after inlining, the compiler
 // knows that the direct-to-LDS prefetch into `stage` touches none of the others
 // and lets the prefetch stay in flight across their accesses.
 //   stage  [T * 128 * 2 / 16] source rows of the next item (bf16, swizzled chunks)
-//   colsum0/1 [128][4]  per-channel column partial sums, [channel][wave]; even/odd rounds
+//   colsum0/1 [4][128]  per-channel column partial sums, [wave][channel]; even/odd rounds
 //   wsh0/1    [128]     1 / c^2 per channel; even/odd rounds
 //   multsh [128]        per-channel output multiplier
 //   outbuf [T * 128 * BITS / 32] LDS image of the code block
 //   szbuf  [T]          (S, Z) fp16 pairs per token
 template <int T, int BITS, int LAYOUT, int NIT>
 __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_items, uint4 *__restrict__ stage,
-                                                   float (*__restrict__ colsum0)[4], float (*__restrict__ colsum1)[4],
+                                                   float (*__restrict__ colsum0)[QD], float (*__restrict__ colsum1)[QD],
                                                    float *__restrict__ wsh0, float *__restrict__ wsh1,
                                                    float *__restrict__ multsh, uint32_t *__restrict__ outbuf,
                                                    uint32_t *__restrict__ szbuf) {
@@ -288,14 +314,13 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
             const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
             h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 cc + 2 rr + j
         }
-        float(*colsum)[4] = (it & 1) ? colsum1 : colsum0;
+        float(*colsum)[QD] = (it & 1) ? colsum1 : colsum0;
         float *wsh = (it & 1) ? wsh1 : wsh0;
-        colsum[cc * 8 + 2 * rr][wave] = h2[0];
-        colsum[cc * 8 + 2 * rr + 1][wave] = h2[1];
+        colsum[wave][cc * 8 + 2 * rr] = h2[0];
+        colsum[wave][cc * 8 + 2 * rr + 1] = h2[1];
         lds_barrier();
         if (tid < QD) {
-            const float4 p = *reinterpret_cast<const float4 *>(colsum[tid]);
-            t_own = (p.x + p.y) + (p.z + p.w);
+            t_own = (colsum[0][tid] + colsum[1][tid]) + (colsum[2][tid] + colsum[3][tid]);
             // a zero column keeps a large finite w (its A entries are all zero)
             wsh[tid] = fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
         }
@@ -363,8 +388,10 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         if (cc == 0) szbuf[row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
             const uint32_t word = pack8<BITS>(q);
-            if constexpr (BITS == 4) reinterpret_cast<uint32_t *>(cbase)[row * (QD / 8) + cc] = word;
-            else reinterpret_cast<uint16_t *>(cbase)[row * (QD / 8) + cc] = (uint16_t)word;
+            if constexpr (BITS == 4)
+                *reinterpret_cast<uint32_t *>(cbase + code_byte<T, BITS, LAYOUT>(4 * (row * (QD / 8) + cc))) = word;
+            else
+                *reinterpret_cast<uint16_t *>(cbase + code_byte<T, BITS, LAYOUT>(2 * (row * (QD / 8) + cc))) = (uint16_t)word;
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -385,14 +412,16 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
             const int pos = (cc * 8 + j) * T + rg * R;
             if constexpr (BITS == 4) {
                 const uint32_t word = cma[j] | (cmb[j] << 4);
-                if constexpr (R == 8) reinterpret_cast<uint32_t *>(cbase)[pos / 8] = word;
-                else reinterpret_cast<uint16_t *>(cbase)[pos / 4] = (uint16_t)word;
+                if constexpr (R == 8) *reinterpret_cast<uint32_t *>(cbase + code_byte<T, BITS, LAYOUT>(pos / 2)) = word;
+                else *reinterpret_cast<uint16_t *>(cbase + code_byte<T, BITS, LAYOUT>(pos / 2)) = (uint16_t)word;
             } else {
                 auto squeeze = [](uint32_t x) {  // four byte codes (< 4) -> one byte, LE 2-bit fields
                     return (x & 0x03u) | ((x >> 6) & 0x0Cu) | ((x >> 12) & 0x30u) | ((x >> 18) & 0xC0u);
                 };
-                if constexpr (R == 8) reinterpret_cast<uint16_t *>(cbase)[pos / 8] = (uint16_t)(squeeze(cma[j]) | (squeeze(cmb[j]) << 8));
-                else cbase[pos / 4] = (uint8_t)squeeze(cma[j]);
+                if constexpr (R == 8)
+                    *reinterpret_cast<uint16_t *>(cbase + code_byte<T, BITS, LAYOUT>(pos / 4)) =
+                        (uint16_t)(squeeze(cma[j]) | (squeeze(cmb[j]) << 8));
+                else cbase[code_byte<T, BITS, LAYOUT>(pos / 4)] = (uint8_t)squeeze(cma[j]);
             }
         }
     }
@@ -403,7 +432,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         uint4 *gcodes = reinterpret_cast<uint4 *>(a.codes + blk * (T * QD * BITS / 8));
         const uint4 *lcodes = reinterpret_cast<const uint4 *>(outbuf);
 #pragma unroll
-        for (int i = tid; i < NW / 4; i += QNT) gcodes[i] = lcodes[i];
+        for (int i = tid; i < NW / 4; i += QNT) gcodes[i] = lcodes[code_slot<T, BITS, LAYOUT>(i)];
         if (tid < T / 4)
             reinterpret_cast<uint4 *>(a.sz + blk * T * 2)[tid] = reinterpret_cast<const uint4 *>(szbuf)[tid];
     }
@@ -419,7 +448,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 template <int T, int BITS, int LAYOUT, int NIT>
 __global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kernel(QuantArgs a, int num_items) {
     __shared__ uint4 stage[T * QD * 2 / 16];
-    __shared__ float colsum0[QD][4], colsum1[QD][4];
+    __shared__ float colsum0[4][QD], colsum1[4][QD];
     __shared__ float wsh0[QD], wsh1[QD];
     __shared__ float multsh[QD];
     __shared__ uint32_t outbuf[T * QD * BITS / 32];
