@@ -95,19 +95,70 @@ __device__ __forceinline__ uint32_t load_bits3(const uint8_t *base, int64_t bit0
     return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
 }
 
+// Page image of one (page, kv head) for the staged path (small pages): K codes,
+// K (S, Z), K normalizer, V codes, V (S, Z), V normalizer, as laid out in HBM.
+// 3-bit V codes are also re-aligned into a second buffer: the 24 bits of each
+// 8-token chunk of a channel get a 32-bit word of their own.
+template <int T, int KB, int VB>
+struct PageImage {
+    static constexpr int KC = T * MD * KB / 8, SZ = T * 4, CN = MD * 2, VC = T * MD * VB / 8;
+    static constexpr int O_KC = 0, O_KSZ = KC, O_KCN = KC + SZ, O_VC = KC + SZ + CN;
+    static constexpr int O_VSZ = O_VC + VC, O_VCN = O_VSZ + SZ, BYTES = O_VCN + CN;
+    static constexpr int NPRE = (BYTES / 16 + 63) / 64;         // 16-byte chunks per lane
+    static constexpr int VCW = VB == 3 ? MD * (T / 8) * 4 : 16;  // re-aligned V codes
+};
+
+template <int N>
+struct Chunks {
+    uint4 v[N];
+};
+
+// This lane's 16-byte chunks lane + 64 k of the page image of block `blk`
+// (branch-free sources; lanes past the image re-read its last chunk, unused).
+template <int T, int KB, int VB>
+__device__ __forceinline__ Chunks<PageImage<T, KB, VB>::NPRE> fetch_page(const DecodeArgs &a, int64_t blk, int lane) {
+    using PI = PageImage<T, KB, VB>;
+    const uint8_t *kc = a.kcodes + blk * PI::KC, *vc = a.vcodes + blk * PI::VC;
+    const uint8_t *ksz = reinterpret_cast<const uint8_t *>(a.ksz) + blk * PI::SZ;
+    const uint8_t *vsz = reinterpret_cast<const uint8_t *>(a.vsz) + blk * PI::SZ;
+    const uint8_t *kcn = reinterpret_cast<const uint8_t *>(a.kcn) + blk * PI::CN;
+    const uint8_t *vcn = reinterpret_cast<const uint8_t *>(a.vcn) + blk * PI::CN;
+    Chunks<PI::NPRE> r;
+#pragma unroll
+    for (int k = 0; k < PI::NPRE; ++k) {
+        const int off = min(1024 * k + 16 * lane, PI::BYTES - 16);
+        uintptr_t src = (uintptr_t)(kc + off);
+        src = off >= PI::O_KSZ ? (uintptr_t)(ksz + (off - PI::O_KSZ)) : src;
+        src = off >= PI::O_KCN ? (uintptr_t)(kcn + (off - PI::O_KCN)) : src;
+        src = off >= PI::O_VC ? (uintptr_t)(vc + (off - PI::O_VC)) : src;
+        src = off >= PI::O_VSZ ? (uintptr_t)(vsz + (off - PI::O_VSZ)) : src;
+        src = off >= PI::O_VCN ? (uintptr_t)(vcn + (off - PI::O_VCN)) : src;
+        r.v[k] = *reinterpret_cast<const uint4 *>(src);
+    }
+    return r;
+}
+
 template <int T, int KB, int VB>
 __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = T / 16;                 // 16-token M-tiles of the score product
     constexpr int KSV = T >= 32 ? T / 32 : 1;  // 32-token K-steps of the value product
     constexpr int KCB = 32 * KB / 8;           // bytes of one lane's 32-channel K chunk
+    // 16-token pages are staged: each lane loads its share of the wave's next page into
+    // registers while the current page is processed from the wave's LDS image (`stg`,
+    // plus `wrk` for re-aligned 3-bit V codes).
+    constexpr bool STAGED = T == 16;
+    using PI = PageImage<T, KB, VB>;
+    __shared__ __attribute__((aligned(16))) uint8_t stg[4][STAGED ? PI::BYTES : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t wrk[4][STAGED ? PI::VCW : 16];
     __shared__ float red_o[4][16][MD + 1];
     __shared__ float red_ml[4][16][2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
     const int g = a.grp;
-    const int L = a.seq_lens[s];
+    const int L = load_const(a.seq_lens, s);
     const int npages = min((L + T - 1) / T, a.bt_stride);
     const int pps = (npages + a.splits - 1) / a.splits;
     const int p0 = split * pps, p1 = min(npages, p0 + pps);
@@ -183,14 +234,47 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mc = 0; mc < 8; ++mc) o[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int pi = p0 + wave; pi < p1; pi += 4) {
-        const int page = a.bt[(int64_t)s * a.bt_stride + pi];
-        if (page < 0 || page >= a.num_pages) continue;
-        const int rows = min(T, L - pi * T);
+    auto page_of = [&](int q) { return load_const(a.bt, (int64_t)s * a.bt_stride + q); };
+    auto valid = [&](int q) {
+        const int page = page_of(q);
+        return page >= 0 && page < a.num_pages;
+    };
+    // staged path: the next page's image chunks, in registers
+    Chunks<STAGED ? PI::NPRE : 1> pre{};
+    int pi = p0 + wave;
+    while (pi < p1 && !valid(pi)) pi += 4;
+    if constexpr (STAGED)
+        if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);
+    while (pi < p1) {
+        const int cur = pi;
+        const int page = page_of(cur);
+        pi += 4;
+        while (pi < p1 && !valid(pi)) pi += 4;
+        if constexpr (STAGED) {
+            // registers -> this wave's LDS image (LDS operations of a wave stay in order)
+#pragma unroll
+            for (int k = 0; k < PI::NPRE; ++k) {
+                const int off = 1024 * k + 16 * lane;
+                if (off < PI::BYTES) *reinterpret_cast<uint4 *>(&stg[wave][off]) = pre.v[k];
+            }
+            if constexpr (VB == 3) {  // four 3-byte chunks per lane -> four words
+#pragma unroll
+                for (int c4 = lane; c4 < MD * (T / 8) / 4; c4 += 64) {
+                    const uint32_t *sw = reinterpret_cast<const uint32_t *>(&stg[wave][PI::O_VC + 12 * c4]);
+                    const uint32_t w0 = sw[0], w1 = sw[1], w2 = sw[2];
+                    const uint4 r = {w0 & 0xFFFFFFu, (w0 >> 24) | ((w1 & 0xFFFFu) << 8), (w1 >> 16) | ((w2 & 0xFFu) << 16),
+                                     w2 >> 8};
+                    *reinterpret_cast<uint4 *>(&wrk[wave][16 * c4]) = r;
+                }
+            }
+            if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);  // travels meanwhile
+        }
+        const int rows = min(T, L - cur * T);
         const int64_t kblk = (int64_t)page * a.Hkv + hk;
 
         // c_K of the lane's 32 channels (lq*32 ..)
-        const uint4 *cp = reinterpret_cast<const uint4 *>(a.kcn + kblk * MD + lq * 32);
+        const uint4 *cp = STAGED ? reinterpret_cast<const uint4 *>(&stg[wave][PI::O_KCN + 64 * lq])
+                                 : reinterpret_cast<const uint4 *>(a.kcn + kblk * MD + lq * 32);
         uint32_t cw[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -226,7 +310,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
 
         // ---- scores: one MFMA chain per 16-token M-tile
-        const uint8_t *kbase = a.kcodes + kblk * (T * MD * KB / 8);
+        const uint8_t *kbase = STAGED ? &stg[wave][PI::O_KC] : a.kcodes + kblk * (T * MD * KB / 8);
         f32x4 sc[MT];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
@@ -260,8 +344,10 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             int tok0;
             if constexpr (T >= 32) tok0 = 32 * (j >> 1) + 8 * lq + 4 * (j & 1);
             else tok0 = 8 * (lq & 1) + 4 * (lq >> 1);
-            const uint4 kz = *reinterpret_cast<const uint4 *>(a.ksz + (kblk * T + tok0) * 2);
-            vzq[j] = *reinterpret_cast<const uint4 *>(a.vsz + (kblk * T + tok0) * 2);
+            const uint4 kz = STAGED ? *reinterpret_cast<const uint4 *>(&stg[wave][PI::O_KSZ + 4 * tok0])
+                                    : *reinterpret_cast<const uint4 *>(a.ksz + (kblk * T + tok0) * 2);
+            vzq[j] = STAGED ? *reinterpret_cast<const uint4 *>(&stg[wave][PI::O_VSZ + 4 * tok0])
+                            : *reinterpret_cast<const uint4 *>(a.vsz + (kblk * T + tok0) * 2);
             const uint32_t kzw[4] = {kz.x, kz.y, kz.z, kz.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -331,8 +417,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
 
         // ---- values: channel tiles mc; lane (channel 16 mc + l16, tokens 32 sv + 8 lq ..)
-        const uint8_t *vbase = a.vcodes + kblk * (T * MD * VB / 8);
-        const uint16_t *vcn = a.vcn + kblk * MD;
+        const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &stg[wave][PI::O_VC]) : a.vcodes + kblk * (T * MD * VB / 8);
+        const uint16_t *vcn = STAGED ? reinterpret_cast<const uint16_t *>(&stg[wave][PI::O_VCN]) : a.vcn + kblk * MD;
 #pragma unroll
         for (int mc = 0; mc < 8; ++mc) {
             const int ch = 16 * mc + l16;
@@ -345,6 +431,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                     uint32_t bitsv;
                     if constexpr (VB == 4) bitsv = reinterpret_cast<const uint32_t *>(vbase)[bit0 >> 5];
                     else if constexpr (VB == 2) bitsv = reinterpret_cast<const uint16_t *>(vbase)[bit0 >> 4];
+                    else if constexpr (STAGED) bitsv = reinterpret_cast<const uint32_t *>(vbase)[bit0 / 24];  // re-aligned
                     else bitsv = load_bits3(vbase, bit0);
                     av = unpack8<VB>(bitsv);
                 } else {
