@@ -14,6 +14,7 @@
 // asymmetric round-to-nearest with fp16 scale, zero point and normalizer.
 #include "common.h"
 #include "launch.h"
+#include "xlane.h"
 
 namespace kvq {
 
@@ -31,44 +32,6 @@ constexpr int QNT = 256;
 #define KVQ_QUANT_FWHT_DPP 0
 #endif
 constexpr bool KEEP_SQ = KVQ_QUANT_KEEP_SQUARES != 0;
-
-// DPP controls (gfx9 encoding)
-constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int DPP_ROR4 = 0x124;      // lane i <- lane (i - 4) mod 16
-constexpr int DPP_ROR8 = 0x128;      // lane i <- lane (i - 8) mod 16
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-// Partner value across lanes, lane ^ M within 32-lane groups, through the LDS
-// crossbar (ds_swizzle bit mode; no LDS memory, no VALU slot).
-template <int M>
-__device__ __forceinline__ float swz_xor(float v) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
-}
-
-// Sum / min / max over the 16 lanes of a DPP row; every lane gets the same bits.
-__device__ __forceinline__ float row_sum16(float s) {
-    s += dpp<DPP_ROR8>(s);
-    s += dpp<DPP_ROR4>(s);
-    s += dpp<DPP_QUAD_XOR2>(s);
-    s += dpp<DPP_QUAD_XOR1>(s);
-    return s;
-}
-__device__ __forceinline__ float row_min16(float s) {
-    s = fminf(s, dpp<DPP_ROR8>(s));
-    s = fminf(s, dpp<DPP_ROR4>(s));
-    s = fminf(s, dpp<DPP_QUAD_XOR2>(s));
-    return fminf(s, dpp<DPP_QUAD_XOR1>(s));
-}
-__device__ __forceinline__ float row_max16(float s) {
-    s = fmaxf(s, dpp<DPP_ROR8>(s));
-    s = fmaxf(s, dpp<DPP_ROR4>(s));
-    s = fmaxf(s, dpp<DPP_QUAD_XOR2>(s));
-    return fmaxf(s, dpp<DPP_QUAD_XOR1>(s));
-}
 
 __device__ __forceinline__ void load8_bf16(const uint16_t *p, float (&v)[8]) {
     const uint4 a = *reinterpret_cast<const uint4 *>(p);

@@ -70,6 +70,10 @@ SMALL = [
     (128, 128, 2, 128, 128, 4, "bf16", 1, 0),
     (128, 16, 3, 128, 128, 2, "bf16", 0, 0),
     (128, 16, 3, 128, 128, 2, "bf16", 1, 0),
+    (128, 16, 4, 128, 128, 4, "bf16", 0, 0),
+    (128, 16, 2, 128, 128, 3, "bf16", 1, 0),
+    (128, 16, 4, 128, 128, 0, "bf16", 1, 0),
+    (128, 64, 2, 128, 128, 2, "bf16", 0, 0),
     (128, 32, 8, 64, 32, 1, "f16", 0, 0),
     (128, 64, 4, 16, 128, 0, "f32", 1, 0),
     (256, 32, 4, 256, 256, 3, "bf16", 0, 0),
@@ -113,16 +117,18 @@ def test_quantize_is_deterministic(gpu):
     assert torch.equal(a.codes, b.codes) and torch.equal(a.sz, b.sz) and torch.equal(a.cnorm, b.cnorm)
 
 
-def test_flags_nonfinite_and_overflow(gpu):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_flags_nonfinite_and_overflow(gpu, dtype):
     f = W.Fmt(128, 0, 16, 128, 128, 4, 2, 0)
     rng = np.random.default_rng(9)
     x = rng.standard_normal((48, 1, 128)).astype(np.float32)
     x[3, 0, 7] = np.nan        # tile 0: non-finite input
     x[20:32, 0, :] *= 1e6      # tile 1: scales and zero points overflow fp16
+    x = make_src(x, dtype)
     tst, tv, tp, _ = tiles_for([48], 16)
     flags = torch.zeros(1, dtype=torch.int32, device=gpu)
-    gpu_quantize(f, x, "f32", tst, tv, tp, 3, flags=flags)
-    _, fl = orc_quantize(f, x, "f32", tst, tv, tp, 3)
+    gpu_quantize(f, x, dtype, tst, tv, tp, 3, flags=flags)
+    _, fl = orc_quantize(f, x, dtype, tst, tv, tp, 3)
     assert int(flags.item()) == fl == (O.FLAG_NONFINITE | O.FLAG_SIDE_OVERFLOW)
 
 
