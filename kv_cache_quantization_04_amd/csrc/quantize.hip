@@ -348,6 +348,8 @@ bool quantize_d128_supported(int D, int T, const QuantArgs &a);
 void launch_quantize_d128(int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
 bool quantize_t16_supported(int D, int T, const QuantArgs &a);
 void launch_quantize_t16(int num_tiles, const QuantArgs &a, hipStream_t stream);
+bool quantize_d512_supported(int D, int T, const QuantArgs &a);
+void launch_quantize_d512(int num_tiles, const QuantArgs &a, hipStream_t stream);
 
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream) {
     if (quantize_d128_supported(D, T, a)) {
@@ -356,6 +358,10 @@ bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_
     }
     if (quantize_t16_supported(D, T, a)) {
         launch_quantize_t16(num_tiles, a, stream);
+        return true;
+    }
+    if (quantize_d512_supported(D, T, a)) {
+        launch_quantize_d512(num_tiles, a, stream);
         return true;
     }
 #define KVQ_LQ(D_, T_) \

@@ -78,6 +78,9 @@ SMALL = [
     (128, 64, 4, 16, 128, 0, "f32", 1, 0),
     (256, 32, 4, 256, 256, 3, "bf16", 0, 0),
     (512, 128, 4, 512, 512, 4, "bf16", 0, 64),
+    (512, 128, 2, 512, 512, 4, "bf16", 0, 64),
+    (512, 128, 4, 512, 512, 2, "bf16", 0, 0),
+    (512, 128, 2, 512, 512, 0, "bf16", 0, 64),
     (512, 16, 3, 128, 512, 2, "bf16", 0, 64),
     (128, 128, 4, 128, 1, 4, "bf16", 0, 0),
 ]
@@ -130,6 +133,23 @@ def test_flags_nonfinite_and_overflow(gpu, dtype):
     gpu_quantize(f, x, dtype, tst, tv, tp, 3, flags=flags)
     _, fl = orc_quantize(f, x, dtype, tst, tv, tp, 3)
     assert int(flags.item()) == fl == (O.FLAG_NONFINITE | O.FLAG_SIDE_OVERFLOW)
+
+
+def test_flags_latent_tile_rope_nonfinite(gpu):
+    # 512-channel latent tiles with a 64-channel rope part: a NaN in the rope part
+    # of one token and in the latent part of another tile
+    f = W.Fmt(512, 64, 128, 512, 512, 4, 4, 0)
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((300, 1, 576)).astype(np.float32)
+    x[5, 0, 512 + 3] = np.nan
+    x[200, 0, 17] = np.inf
+    x = make_src(x, "bf16")
+    tst, tv, tp, _ = tiles_for([300], 128)
+    flags = torch.zeros(1, dtype=torch.int32, device=gpu)
+    gpu_quantize(f, x, "bf16", tst, tv, tp, len(tp), flags=flags)
+    _, fl = orc_quantize(f, x, "bf16", tst, tv, tp, len(tp))
+    assert fl & O.FLAG_NONFINITE
+    assert int(flags.item()) == fl
 
 
 # ----------------------------------------------------------------------------- dequantize and decode, small
