@@ -33,6 +33,8 @@ HBM_PEAK_GBS = 8000.0
 # fp32 VALU lane-operations per second with packed FP32 disabled (the build's flag):
 # 256 CUs x 64 lanes x 2.4 GHz
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# dense f16 / bf16 MFMA, MI355X published
+MFMA_F16_PEAK_TFLOPS = 2500.0
 ESIZE = {"f32": 4, "bf16": 2}
 
 
@@ -72,24 +74,44 @@ def decode_bytes(cfg, seqs=None):
     return pages * per_page + q + out
 
 
-def source_digest():
+CSRC = os.path.join(ROOT, "kv_cache_quantization_04_amd", "csrc")
+KERNEL_FILE = {"quantize_d128_kernel": "quantize_d128.hip", "quantize_t16_kernel": "quantize_t16.hip",
+               "quantize_d512_kernel": "quantize_d512.hip", "quantize_kernel": "quantize.hip",
+               "decode_mfma_kernel": "decode_mfma.hip", "decode_mla_kernel": "decode_mla.hip",
+               "decode_generic_kernel": "decode.hip"}
+
+
+def source_files(kernel):
+    """The kernel's source file and the local headers it includes, transitively."""
+    todo, seen = [KERNEL_FILE[kernel]], []
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(CSRC, name)):
+            continue
+        seen.append(name)
+        todo += re.findall(r'^#include "([^"]+)"', open(os.path.join(CSRC, name)).read(), re.M)
+    return sorted(seen)
+
+
+def source_digest(kernel):
+    """First 16 hex digits of sha256 over the kernel's source files (sorted by name)."""
     h = hashlib.sha256()
-    for name in ("quantize_d128.hip", "common.h"):
-        with open(os.path.join(ROOT, "kv_cache_quantization_04_amd", "csrc", name), "rb") as fh:
+    for name in source_files(kernel):
+        with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(workload_key):
-    """HBM bytes per quantizer launch from the committed rocprofv3 counter summary,
-    or None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"quantize_d128_kernel_{workload_key}_hbm_counters.md")
+def profiled_traffic(kernel, workload_key):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_key}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != source_digest():
+    if not m or not t or m.group(1) != source_digest(kernel):
         return None
     return float(t.group(1))
 
@@ -237,9 +259,37 @@ def main():
     d_gbs = dbytes / (td * 1e-3) / 1e9
     per_launch = qbytes / nq
     avg_launch_ms = (tk + tvq) / nq
-    traffic = profiled_traffic(W.NAMES[args.config])
     qops = quantize_valu_ops(cfg, cfg.fk, cfg.width) + (quantize_valu_ops(cfg, cfg.fv, cfg.dv) if cfg.fv is not None else 0)
     positions = int(cfg.seq_lens.sum())
+    qnames = sorted({K.kv_quantize_kernel_name(kcache[0], ksrc[0])} |
+                    ({K.kv_quantize_kernel_name(vcache[0], vsrc[0])} if vsrc[0] is not None else set()))
+    dname = K.kv_decode_attn_kernel_name(qd, kcache[0], vcache[0])
+    if tk + tvq >= td:
+        # the quantizer dominates the step: VALU-bound (lane-ops per element), HBM figure alongside
+        traffic = profiled_traffic(qnames[0], W.NAMES[args.config]) if len(qnames) == 1 else None
+        roofline = {"bound": "alu", "kernel": " / ".join(qnames),
+                    "achieved": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                    "unit": "T VALU lane-ops/s",
+                    "frac": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
+                    "traffic": traffic, "algorithmic_ops_per_launch": qops / nq,
+                    "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                    "hbm": {"achieved": round(per_launch / (avg_launch_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(per_launch / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    else:
+        # decode dominates; its timing spans the call (main kernel + split merge pass)
+        traffic = profiled_traffic(dname, W.NAMES[args.config])
+        hbm = {"achieved": round(d_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4)}
+        if dname == "decode_mla_kernel":
+            # dense f16 MFMA contraction: scores over D + R channels and values over D, per head and position
+            flops = 2.0 * positions * cfg.num_q_heads * (cfg.width + cfg.dv)
+            tf = flops / (td * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "kernel": dname + " + decode_reduce_kernel", "achieved": round(tf, 2),
+                        "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                        "traffic": traffic, "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": dbytes,
+                        "avg_launch_us": round(td * 1e3, 3), "hbm": hbm}
+        else:
+            roofline = dict(bound="hbm", kernel=dname + " + decode_reduce_kernel", traffic=traffic,
+                            algorithmic_bytes_per_launch=dbytes, avg_launch_us=round(td * 1e3, 3), **hbm)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -255,13 +305,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "kv_layout": "K token-major, V channel-major, fp16 side data",
                    "decode_splits": splits, "copy_ring": ring},
-        "roofline": {"bound": "alu", "kernel": "quantize_d128_kernel",
-                     "achieved": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12, 3), "peak": round(VALU_PEAK_TOPS, 2),
-                     "unit": "T VALU lane-ops/s", "frac": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
-                     "traffic": traffic, "algorithmic_ops_per_launch": qops / nq,
-                     "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-                     "hbm": {"achieved": round(per_launch / (avg_launch_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(per_launch / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}},
+        "roofline": roofline,
         "detail": {
             "quantize_GBps": round(q_gbs, 2), "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
             "quantize_input_GBps": round((kin_r + vin_r) / ((tk + tvq) * 1e-3) / 1e9, 2),
@@ -270,6 +314,7 @@ def main():
             "decode_GBps": round(d_gbs, 2), "decode_frac_hbm": round(d_gbs / HBM_PEAK_GBS, 4),
             "decode_us": round(td * 1e3, 3), "decode_positions_per_s": round(positions / (td * 1e-3), 1),
             "decode_bytes": dbytes, "quantize_bytes": qbytes,
+            "quantize_kernels": qnames, "decode_kernel": dname,
         },
     }
     if not args.no_cpu_baseline:

@@ -163,6 +163,21 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
                           float sm_scale, int32_t num_splits, void *workspace, size_t workspace_bytes,
                           float *out, hipStream_t stream);
 
+/* Name of the GPU kernel kv_quantize runs for these arguments (the same checks
+ * and dispatch; nothing is launched or dereferenced): "quantize_d128_kernel",
+ * "quantize_t16_kernel", "quantize_d512_kernel" (specialised tile shapes) or
+ * "quantize_kernel" (any supported format). NULL where kv_quantize would
+ * reject the arguments. The string is static. For profilers and benchmarks. */
+const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_dtype src_dtype,
+                                    int64_t stride_token, int64_t stride_head);
+
+/* Name of the main GPU kernel kv_decode_attn runs for this query pointer and
+ * these caches (the split-merge pass, "decode_reduce_kernel", follows it):
+ * "decode_mla_kernel", "decode_mfma_kernel" or "decode_generic_kernel". NULL
+ * for invalid arguments. The string is static. For profilers and benchmarks. */
+const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v,
+                                       int32_t num_q_heads);
+
 /* Static description of a status code. */
 const char *kvq_status_str(kvq_status s);
 

@@ -6,7 +6,8 @@ libkvq.so. PyTorch supplies device memory (tensor.data_ptr()) and the stream
 
     kvq_format_from_preset, kvq_cache_bytes, kv_quantize, kv_dequantize,
     kv_decode_attn_default_splits, kv_decode_attn_workspace_bytes,
-    kv_decode_attn, kvq_status_str
+    kv_decode_attn, kv_quantize_kernel_name, kv_decode_attn_kernel_name,
+    kvq_status_str
 
 plus ``DeviceCache``, a holder of the four device arrays of one cache.
 Importing this module fails if libkvq.so has not been built: there is no
@@ -37,7 +38,8 @@ KVQ_TOKEN_MAJOR, KVQ_CHANNEL_MAJOR = 0, 1
 KVQ_FLAG_NONFINITE, KVQ_FLAG_SIDE_OVERFLOW = 1, 2
 
 EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_dequantize",
-           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kvq_status_str")
+           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_quantize_kernel_name", "kv_decode_attn_kernel_name",
+           "kvq_status_str")
 
 
 class kvq_format(ctypes.Structure):
@@ -64,6 +66,8 @@ _sig = {
     "kv_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "kv_decode_attn": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _vp, _i32,
                               _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
+    "kv_quantize_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(kvq_cache), _vp, _i32, _i64, _i64]),
+    "kv_decode_attn_kernel_name": (ctypes.c_char_p, [_vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _i32]),
     "kvq_status_str": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -167,6 +171,19 @@ def kv_decode_attn_default_splits(k: DeviceCache, v: Optional[DeviceCache], num_
                                   max_seq_len: int) -> int:
     return int(_lib.kv_decode_attn_default_splits(ctypes.byref(k.struct), ctypes.byref(v.struct) if v is not None else None,
                                                   num_seqs, num_q_heads, max_seq_len))
+
+
+def kv_quantize_kernel_name(dst: DeviceCache, src) -> Optional[str]:
+    """Kernel kv_quantize(dst, src, ...) runs, or None where it would reject the arguments."""
+    r = _lib.kv_quantize_kernel_name(ctypes.byref(dst.struct), _ptr(src), _dtype_code(src), src.stride(0), src.stride(1))
+    return r.decode() if r is not None else None
+
+
+def kv_decode_attn_kernel_name(q, k: DeviceCache, v: Optional[DeviceCache]) -> Optional[str]:
+    """Main kernel kv_decode_attn(q, k, v, ...) runs, or None for invalid arguments."""
+    r = _lib.kv_decode_attn_kernel_name(_ptr(q), ctypes.byref(k.struct), ctypes.byref(v.struct) if v is not None else None,
+                                        q.shape[1])
+    return r.decode() if r is not None else None
 
 
 def kv_decode_attn_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim_v: int, num_splits: int) -> int:

@@ -87,6 +87,25 @@ kvq_status decode_layout(const kvq_cache *k, const kvq_cache *v, int32_t num_q_h
     return KVQ_OK;
 }
 
+// checks of kv_quantize's cache and source arguments
+kvq_status check_quantize_source(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+                                 int64_t stride_head) {
+    kvq_status st = check_cache(dst);
+    if (st != KVQ_OK) return st;
+    if (!src || !valid_dtype(src_dtype) || stride_token < 0 || stride_head < 0) return KVQ_EINVAL;
+    if (((uintptr_t)src & 15) || (stride_token % 8) || (stride_head % 8)) return KVQ_EUNSUPPORTED;
+    return KVQ_OK;
+}
+
+kvq::QuantArgs quant_args(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+                          int64_t stride_head, const int32_t *tile_src_token, const int32_t *tile_valid,
+                          const int32_t *tile_dst_page, uint32_t *status_flags) {
+    const kvq_format &f = dst->fmt;
+    return kvq::QuantArgs{src, (int)src_dtype, stride_token, stride_head, tile_src_token, tile_valid, tile_dst_page,
+                          dst->codes, dst->sz, dst->cnorm, dst->rope, dst->num_heads, f.hadamard_n, f.group, f.bits,
+                          f.iters, f.layout, f.rope_dim, dst->num_pages, status_flags};
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,19 +143,24 @@ kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtyp
                        int64_t stride_head, int32_t num_tiles, const int32_t *tile_src_token,
                        const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
                        hipStream_t stream) {
-    kvq_status st = check_cache(dst);
+    kvq_status st = check_quantize_source(dst, src, src_dtype, stride_token, stride_head);
     if (st != KVQ_OK) return st;
-    if (!src || num_tiles < 0 || !valid_dtype(src_dtype)) return KVQ_EINVAL;
+    if (num_tiles < 0) return KVQ_EINVAL;
     if (num_tiles > 0 && (!tile_src_token || !tile_valid || !tile_dst_page)) return KVQ_EINVAL;
-    if (stride_token < 0 || stride_head < 0) return KVQ_EINVAL;
-    if (((uintptr_t)src & 15) || (stride_token % 8) || (stride_head % 8)) return KVQ_EUNSUPPORTED;
     if (num_tiles == 0) return KVQ_OK;
     const kvq_format &f = dst->fmt;
-    kvq::QuantArgs a{src, (int)src_dtype, stride_token, stride_head, tile_src_token, tile_valid, tile_dst_page,
-                     dst->codes, dst->sz, dst->cnorm, dst->rope, dst->num_heads, f.hadamard_n, f.group, f.bits,
-                     f.iters, f.layout, f.rope_dim, dst->num_pages, status_flags};
+    const kvq::QuantArgs a = quant_args(dst, src, src_dtype, stride_token, stride_head, tile_src_token, tile_valid,
+                                        tile_dst_page, status_flags);
     if (!kvq::launch_quantize(f.head_dim, f.tile_tokens, num_tiles, a, stream)) return KVQ_EUNSUPPORTED;
     return launched();
+}
+
+const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+                                    int64_t stride_head) {
+    if (check_quantize_source(dst, src, src_dtype, stride_token, stride_head) != KVQ_OK) return nullptr;
+    const kvq::QuantArgs a =
+        quant_args(dst, src, src_dtype, stride_token, stride_head, nullptr, nullptr, nullptr, nullptr);
+    return kvq::quantize_kernel_name(dst->fmt.head_dim, dst->fmt.tile_tokens, a);
 }
 
 kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t *tile_page, const int32_t *tile_valid,
@@ -161,6 +185,15 @@ int32_t kv_decode_attn_default_splits(const kvq_cache *k, const kvq_cache *v, in
         return 1;
     a.B = num_seqs;
     return kvq::decode_default_splits(a, max_seq_len);
+}
+
+const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v, int32_t num_q_heads) {
+    kvq::DecodeArgs a{};
+    if (!q || check_cache(k) != KVQ_OK || (v && check_cache(v) != KVQ_OK) ||
+        decode_layout(k, v, num_q_heads, a) != KVQ_OK)
+        return nullptr;
+    a.q = q;
+    return kvq::decode_kernel_name(a);
 }
 
 size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,

@@ -253,6 +253,12 @@ int decode_default_splits(const DecodeArgs &a, int max_seq_len) {
     return (int)sp;
 }
 
+const char *decode_kernel_name(const DecodeArgs &a) {
+    if (decode_mla_supported(a)) return "decode_mla_kernel";
+    if (decode_mfma_supported(a)) return "decode_mfma_kernel";
+    return "decode_generic_kernel";
+}
+
 bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.splits > RED_MAX_SPLITS) return false;
     if (decode_mla_supported(a)) {

@@ -351,6 +351,13 @@ void launch_quantize_t16(int num_tiles, const QuantArgs &a, hipStream_t stream);
 bool quantize_d512_supported(int D, int T, const QuantArgs &a);
 void launch_quantize_d512(int num_tiles, const QuantArgs &a, hipStream_t stream);
 
+const char *quantize_kernel_name(int D, int T, const QuantArgs &a) {
+    if (quantize_d128_supported(D, T, a)) return "quantize_d128_kernel";
+    if (quantize_t16_supported(D, T, a)) return "quantize_t16_kernel";
+    if (quantize_d512_supported(D, T, a)) return "quantize_d512_kernel";
+    return "quantize_kernel";
+}
+
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream) {
     if (quantize_d128_supported(D, T, a)) {
         launch_quantize_d128(T, num_tiles, a, stream);

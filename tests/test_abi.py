@@ -48,7 +48,7 @@ def test_cache_bytes():
     assert K.kvq_cache_bytes(bad, 1, 1) == 0
 
 
-FAKE = 0x10000  # never dereferenced: every call below fails validation first
+FAKE = 0x10000  # never dereferenced: the calls below fail validation first or only look at alignment
 
 
 def cache_struct(fmt, pages=4, heads=2, codes=FAKE, rope=None):
@@ -122,3 +122,46 @@ def test_default_splits():
     # invalid arguments give 1
     assert default_splits(fk, fv, 0, 32, 8, 4096) == 1
     assert default_splits(fk, fv, 8, 30, 8, 4096) == 1
+
+
+def quantize_kernel(fmt, dtype, src=FAKE, stride_token=None, heads=2):
+    c = cache_struct(fmt, heads=heads, rope=FAKE if fmt.rope_dim else None)
+    st = stride_token if stride_token is not None else heads * (fmt.head_dim + fmt.rope_dim)
+    r = K._lib.kv_quantize_kernel_name(ctypes.byref(c), src, dtype, st, fmt.head_dim + fmt.rope_dim)
+    return r.decode() if r is not None else None
+
+
+def test_quantize_kernel_name():
+    bf = K.KVQ_BF16
+    f128 = K.make_format(128, 0, 128, 128, 128, 4, 4, K.KVQ_TOKEN_MAJOR)
+    assert quantize_kernel(f128, bf) == "quantize_d128_kernel"
+    assert quantize_kernel(f128, K.KVQ_F32) == "quantize_kernel"          # specialised kernels read bf16
+    f16 = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_CHANNEL_MAJOR)
+    assert quantize_kernel(f16, bf) == "quantize_t16_kernel"
+    fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)
+    assert quantize_kernel(fm, bf) == "quantize_d512_kernel"
+    fm3 = K.make_format(512, 64, 128, 512, 512, 3, 4, K.KVQ_TOKEN_MAJOR)
+    assert quantize_kernel(fm3, bf) == "quantize_kernel"
+    # what kv_quantize rejects: misaligned source, negative stride
+    assert quantize_kernel(f128, bf, src=FAKE + 2) is None
+    assert quantize_kernel(f128, bf, stride_token=-8) is None
+
+
+def decode_kernel(fk, fv, num_q_heads, num_kv_heads, q=FAKE):
+    kc = cache_struct(fk, heads=num_kv_heads, rope=FAKE if fk.rope_dim else None)
+    vc = cache_struct(fv, heads=num_kv_heads) if fv is not None else None
+    r = K._lib.kv_decode_attn_kernel_name(q, ctypes.byref(kc), ctypes.byref(vc) if vc is not None else None,
+                                          num_q_heads)
+    return r.decode() if r is not None else None
+
+
+def test_decode_kernel_name():
+    fk = K.make_format(128, 0, 128, 128, 128, 4, 4, K.KVQ_TOKEN_MAJOR)
+    fv = K.make_format(128, 0, 128, 128, 128, 2, 4, K.KVQ_CHANNEL_MAJOR)
+    assert decode_kernel(fk, fv, 32, 8) == "decode_mfma_kernel"
+    assert decode_kernel(fk, fv, 32, 8, q=FAKE + 4) == "decode_generic_kernel"   # q not 16-byte aligned
+    assert decode_kernel(fk, fv, 32 * 8, 8) == "decode_generic_kernel"          # 32 query heads per kv head
+    fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)
+    assert decode_kernel(fm, None, 128, 1) == "decode_mla_kernel"
+    assert decode_kernel(fk, fv, 30, 8) is None
+    assert decode_kernel(fk, fv, 32, 8, q=None) is None
