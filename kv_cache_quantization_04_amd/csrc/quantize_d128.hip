@@ -3,11 +3,11 @@
 // cross-lane traffic stays in the VALU (DPP, permlane swaps) or the LDS
 // crossbar without memory (ds_swizzle), and the codes are packed in registers.
 //
-// Workgroup = one (tile, head): 256 threads. Lane l of wave w holds the 8
-// consecutive channels 8 (l & 15) .. + 7 of the R = T/16 consecutive rows
-// starting at 16-row-group rg = 4 w + (l >> 4). The 16 lanes of a DPP row
-// therefore cover one token's 128 channels: the Hadamard butterflies on channel
-// bits 3..6 and every per-token reduction are DPP row operations.
+// Workgroup = one (tile, head) at a time, T / (16 R) waves. Lane l of wave w
+// holds the 8 consecutive channels 8 (l & 15) .. + 7 of the R consecutive rows
+// of row group rg = 4 w + (l >> 4). The 16 lanes of a DPP row therefore cover
+// one token's 128 channels: the Hadamard butterflies on channel bits 3..6 and
+// every per-token reduction are DPP row operations.
 //
 // Method: "KVarN" project review, Key Features ("Variance-Normalized
 // Quantization Pipeline"): rotate, run row/column RMS normalization rounds,
@@ -21,17 +21,8 @@ namespace kvq {
 namespace {
 
 constexpr int QD = 128;
-constexpr int QNT = 256;
-#ifndef KVQ_QUANT_KEEP_SQUARES
-#define KVQ_QUANT_KEEP_SQUARES 1
-#endif
-#ifndef KVQ_QUANT_MIN_BLOCKS
-#define KVQ_QUANT_MIN_BLOCKS 2
-#endif
-#ifndef KVQ_QUANT_FWHT_DPP
-#define KVQ_QUANT_FWHT_DPP 0
-#endif
-constexpr bool KEEP_SQ = KVQ_QUANT_KEEP_SQUARES != 0;
+// rows per lane: 4 (8 waves per 128-token tile, 4 per 64-token tile)
+constexpr int QR = 4;
 
 __device__ __forceinline__ void load8_bf16(const uint16_t *p, float (&v)[8]) {
     const uint4 a = *reinterpret_cast<const uint4 *>(p);
@@ -75,9 +66,8 @@ __device__ __forceinline__ uint32_t pack8(const float (&u)[8]) {
 //   token-major: the four row groups of a wave (rg & 3) spread over the slots of a
 //     row, rg = row / R, row = U / BITS;
 //   channel-major: the 16 channel groups (cc) spread over the 16 low slot bits.
-template <int T, int BITS, int LAYOUT>
+template <int T, int R, int BITS, int LAYOUT>
 __device__ __forceinline__ int code_slot(int U) {
-    constexpr int R = T / 16;
     if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
         constexpr int L = BITS == 4 ? 2 : 1;   // log2 of slots per token row
         constexpr int S = L + (R == 8 ? 3 : 2);  // log2 of slots per row group
@@ -89,9 +79,9 @@ __device__ __forceinline__ int code_slot(int U) {
         return U ^ ((U >> S) & M);
     }
 }
-template <int T, int BITS, int LAYOUT>
+template <int T, int R, int BITS, int LAYOUT>
 __device__ __forceinline__ int code_byte(int b) {
-    return (code_slot<T, BITS, LAYOUT>(b >> 4) << 4) | (b & 15);
+    return (code_slot<T, R, BITS, LAYOUT>(b >> 4) << 4) | (b & 15);
 }
 
 }  // namespace
@@ -100,18 +90,19 @@ __device__ __forceinline__ int code_byte(int b) {
 // knows that the direct-to-LDS prefetch into `stage` touches none of the others
 // and lets the prefetch stay in flight across their accesses.
 //   stage  [T * 128 * 2 / 16] source rows of the next item (bf16, swizzled chunks)
-//   colsum0/1 [4][128]  per-channel column partial sums, [wave][channel]; even/odd rounds
+//   colsum0/1 [waves][128] per-channel column partial sums, [wave][channel]; even/odd rounds
 //   wsh0/1    [128]     1 / c^2 per channel; even/odd rounds
 //   multsh [128]        per-channel output multiplier
 //   outbuf [T * 128 * BITS / 32] LDS image of the code block
 //   szbuf  [T]          (S, Z) fp16 pairs per token
-template <int T, int BITS, int LAYOUT, int NIT>
+template <int T, int R, int BITS, int LAYOUT, int NIT>
 __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_items, uint4 *__restrict__ stage,
                                                    float (*__restrict__ colsum0)[QD], float (*__restrict__ colsum1)[QD],
                                                    float *__restrict__ wsh0, float *__restrict__ wsh1,
                                                    float *__restrict__ multsh, uint32_t *__restrict__ outbuf,
                                                    uint32_t *__restrict__ szbuf) {
-    constexpr int R = T / 16;  // rows per thread
+    constexpr int NWV = T / (4 * R);  // waves (4 row groups of R rows each)
+    constexpr int NT = 64 * NWV;
     constexpr float LEVELS = (float)((1 << BITS) - 1);
     // rounds: a compile-time count (fully unrolled) or, with NIT < 0, the runtime one
     const int iters = NIT >= 0 ? NIT : a.iters;
@@ -193,34 +184,21 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float v = y[k][j];
-#if KVQ_QUANT_FWHT_DPP
-            v = __builtin_fmaf(dpp<DPP_QUAD_XOR1>(v), s1, v);
-            v = __builtin_fmaf(dpp<DPP_QUAD_XOR2>(v), s2, v);
-            v = __builtin_fmaf(swz_xor<4>(v), s4, v);
-            v = __builtin_fmaf(dpp<DPP_ROR8>(v), s8, v);
-#else
             v = __builtin_fmaf(swz_xor<1>(v), s1, v);
             v = __builtin_fmaf(swz_xor<2>(v), s2, v);
             v = __builtin_fmaf(swz_xor<4>(v), s4, v);
             v = __builtin_fmaf(swz_xor<8>(v), s8, v);
-#endif
             y[k][j] = v;
         }
     const float sigma = s1 * s2 * s4 * s8;
 
     // ---- normalization rounds on A = Y^2: u = 1/r^2 per row, w = 1/c^2 per channel
-    // A = Y^2, kept in registers (KEEP_SQ) or recomputed where used
-    float A[KEEP_SQ ? R : 1][8];
-    if constexpr (KEEP_SQ) {
+    // A = Y^2, kept in registers
+    float A[R][8];
 #pragma unroll
-        for (int k = 0; k < R; ++k)
+    for (int k = 0; k < R; ++k)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) A[k][j] = y[k][j] * y[k][j];
-    }
-    auto sq = [&](int k, int j) -> float {
-        if constexpr (KEEP_SQ) return A[k][j];
-        else return y[k][j] * y[k][j];
-    };
+        for (int j = 0; j < 8; ++j) A[k][j] = y[k][j] * y[k][j];
     // non-finite detector: a row's sum of squares is finite iff the row is
     // (first round below; computed here when there is no round)
     uint32_t bad = 0;
@@ -250,7 +228,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         for (int k = 0; k < R; ++k) {
             float s = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s = __builtin_fmaf(sq(k, j), w[j], s);
+            for (int j = 0; j < 8; ++j) s = __builtin_fmaf(A[k][j], w[j], s);
             s = row_sum16(s);
             if (it == 0 && !isfinite(s)) bad |= KVQ_FLAG_NONFINITE;
             u[k] = fD * __builtin_amdgcn_rcpf(fmaxf(s, TINY));
@@ -261,7 +239,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         for (int j = 0; j < 8; ++j) {
             float acc = 0.f;
 #pragma unroll
-            for (int k = 0; k < R; ++k) acc = __builtin_fmaf(sq(k, j), u[k], acc);
+            for (int k = 0; k < R; ++k) acc = __builtin_fmaf(A[k][j], u[k], acc);
             t[j] = acc;
         }
         // across the four row groups of the wave: permlane swaps pair up halves
@@ -283,7 +261,11 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         colsum[wave][cc * 8 + 2 * rr + 1] = h2[1];
         lds_barrier();
         if (tid < QD) {
-            t_own = (colsum[0][tid] + colsum[1][tid]) + (colsum[2][tid] + colsum[3][tid]);
+            float acc[NWV / 4];
+#pragma unroll
+            for (int v = 0; v < NWV / 4; ++v)
+                acc[v] = (colsum[4 * v][tid] + colsum[4 * v + 1][tid]) + (colsum[4 * v + 2][tid] + colsum[4 * v + 3][tid]);
+            t_own = NWV == 8 ? acc[0] + acc[NWV / 8] : acc[0];
             // a zero column keeps a large finite w (its A entries are all zero)
             wsh[tid] = fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
         }
@@ -352,9 +334,9 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
             const uint32_t word = pack8<BITS>(q);
             if constexpr (BITS == 4)
-                *reinterpret_cast<uint32_t *>(cbase + code_byte<T, BITS, LAYOUT>(4 * (row * (QD / 8) + cc))) = word;
+                *reinterpret_cast<uint32_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(4 * (row * (QD / 8) + cc))) = word;
             else
-                *reinterpret_cast<uint16_t *>(cbase + code_byte<T, BITS, LAYOUT>(2 * (row * (QD / 8) + cc))) = (uint16_t)word;
+                *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(2 * (row * (QD / 8) + cc))) = (uint16_t)word;
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -375,16 +357,16 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
             const int pos = (cc * 8 + j) * T + rg * R;
             if constexpr (BITS == 4) {
                 const uint32_t word = cma[j] | (cmb[j] << 4);
-                if constexpr (R == 8) *reinterpret_cast<uint32_t *>(cbase + code_byte<T, BITS, LAYOUT>(pos / 2)) = word;
-                else *reinterpret_cast<uint16_t *>(cbase + code_byte<T, BITS, LAYOUT>(pos / 2)) = (uint16_t)word;
+                if constexpr (R == 8) *reinterpret_cast<uint32_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 2)) = word;
+                else *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 2)) = (uint16_t)word;
             } else {
                 auto squeeze = [](uint32_t x) {  // four byte codes (< 4) -> one byte, LE 2-bit fields
                     return (x & 0x03u) | ((x >> 6) & 0x0Cu) | ((x >> 12) & 0x30u) | ((x >> 18) & 0xC0u);
                 };
                 if constexpr (R == 8)
-                    *reinterpret_cast<uint16_t *>(cbase + code_byte<T, BITS, LAYOUT>(pos / 4)) =
+                    *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 4)) =
                         (uint16_t)(squeeze(cma[j]) | (squeeze(cmb[j]) << 8));
-                else cbase[code_byte<T, BITS, LAYOUT>(pos / 4)] = (uint8_t)squeeze(cma[j]);
+                else cbase[code_byte<T, R, BITS, LAYOUT>(pos / 4)] = (uint8_t)squeeze(cma[j]);
             }
         }
     }
@@ -395,7 +377,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         uint4 *gcodes = reinterpret_cast<uint4 *>(a.codes + blk * (T * QD * BITS / 8));
         const uint4 *lcodes = reinterpret_cast<const uint4 *>(outbuf);
 #pragma unroll
-        for (int i = tid; i < NW / 4; i += QNT) gcodes[i] = lcodes[code_slot<T, BITS, LAYOUT>(i)];
+        for (int i = tid; i < NW / 4; i += NT) gcodes[i] = lcodes[code_slot<T, R, BITS, LAYOUT>(i)];
         if (tid < T / 4)
             reinterpret_cast<uint4 *>(a.sz + blk * T * 2)[tid] = reinterpret_cast<const uint4 *>(szbuf)[tid];
     }
@@ -408,15 +390,20 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
     }
 }
 
-template <int T, int BITS, int LAYOUT, int NIT>
-__global__ void __launch_bounds__(QNT, KVQ_QUANT_MIN_BLOCKS) quantize_d128_kernel(QuantArgs a, int num_items) {
+// Four waves per SIMD (the second bound: HIP passes it on as the minimum waves per
+// execution unit), so at most 128 registers per lane: two 8-wave workgroups per
+// compute unit for 128-token tiles. Four rows per lane need a few more than that;
+// the compiler spills a handful of addresses, reloaded once per item.
+template <int T, int R, int BITS, int LAYOUT, int NIT>
+__global__ void __launch_bounds__(16 * T / R, 4) quantize_d128_kernel(QuantArgs a, int num_items) {
+    constexpr int NWV = T / (4 * R);
     __shared__ uint4 stage[T * QD * 2 / 16];
-    __shared__ float colsum0[4][QD], colsum1[4][QD];
+    __shared__ float colsum0[NWV][QD], colsum1[NWV][QD];
     __shared__ float wsh0[QD], wsh1[QD];
     __shared__ float multsh[QD];
     __shared__ uint32_t outbuf[T * QD * BITS / 32];
     __shared__ uint32_t szbuf[T];
-    quantize_d128_body<T, BITS, LAYOUT, NIT>(a, num_items, stage, colsum0, colsum1, wsh0, wsh1, multsh, outbuf,
+    quantize_d128_body<T, R, BITS, LAYOUT, NIT>(a, num_items, stage, colsum0, colsum1, wsh0, wsh1, multsh, outbuf,
                                              szbuf);
 }
 
@@ -429,15 +416,17 @@ bool quantize_d128_supported(int D, int T, const QuantArgs &a) {
 
 template <int T, int BITS, int LAYOUT, int NIT>
 static void launch_one(int num_tiles, const QuantArgs &a, hipStream_t stream) {
+    constexpr int R = QR;
+    constexpr int NT = 16 * T / R;
     const int items = num_tiles * a.H;
     int dev = 0, cus = 256, per_cu = 2;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_d128_kernel<T, BITS, LAYOUT, NIT>, QNT, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_d128_kernel<T, R, BITS, LAYOUT, NIT>, NT, 0) !=
             hipSuccess || per_cu < 1)
         per_cu = 1;
     const int grid = items < cus * per_cu ? items : cus * per_cu;
-    hipLaunchKernelGGL((quantize_d128_kernel<T, BITS, LAYOUT, NIT>), dim3(grid), dim3(QNT), 0, stream, a, items);
+    hipLaunchKernelGGL((quantize_d128_kernel<T, R, BITS, LAYOUT, NIT>), dim3(grid), dim3(NT), 0, stream, a, items);
 }
 
 template <int T, int BITS, int LAYOUT>
