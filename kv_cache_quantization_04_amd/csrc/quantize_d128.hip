@@ -3,11 +3,12 @@
 // cross-lane traffic stays in the VALU (DPP, permlane swaps) or the LDS
 // crossbar without memory (ds_swizzle), and the codes are packed in registers.
 //
-// Workgroup = one (tile, head) at a time, T / (16 R) waves. Lane l of wave w
-// holds the 8 consecutive channels 8 (l & 15) .. + 7 of the R consecutive rows
+// Workgroup = one (tile, head) at a time, T / (4 R) waves. Lane l of wave w
+// loads the 8 consecutive channels 8 (l & 15) .. + 7 of the R consecutive rows
 // of row group rg = 4 w + (l >> 4). The 16 lanes of a DPP row therefore cover
 // one token's 128 channels: the Hadamard butterflies on channel bits 3..6 and
-// every per-token reduction are DPP row operations.
+// every per-token reduction are DPP row operations. After the rotation the lane
+// holds rotated channel group hperm16(l & 15) (the lane stages relabel them).
 //
 // Method: "KVarN" project review, Key Features ("Variance-Normalized
 // Quantization Pipeline"): rotate, run row/column RMS normalization rounds,
@@ -172,25 +173,14 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
                     y[k][j] = p + q;
                     y[k][j | s] = p - q;
                 }
-    // Cross-lane stages (lane bit b <-> channel bit 3 + b) in the sign-deferred
-    // form t' = t + s_b * partner(t), s_b = -1 on lanes with bit b set: one fused
-    // multiply-add per value, the partner read through ds_swizzle. After
-    // the four stages t = sigma * Y with sigma = s_1 s_2 s_4 s_8 per lane; the
-    // squares ignore sigma and it is folded into the per-channel multiplier.
-    const float s1 = (cc & 1) ? -1.f : 1.f, s2 = (cc & 2) ? -1.f : 1.f;
-    const float s4 = (cc & 4) ? -1.f : 1.f, s8 = (cc & 8) ? -1.f : 1.f;
+    // Cross-lane stages on channel bits 3..6 (the lane bits), one DPP-fused
+    // multiply-add per value and stage. Afterwards lane (cc, rr) holds
+    // sigma * Y of channel group pcc = hperm16(cc): channels 8 pcc .. 8 pcc + 7.
+    // The squares ignore sigma; it is folded into the per-channel multiplier.
 #pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float v = y[k][j];
-            v = __builtin_fmaf(swz_xor<1>(v), s1, v);
-            v = __builtin_fmaf(swz_xor<2>(v), s2, v);
-            v = __builtin_fmaf(swz_xor<4>(v), s4, v);
-            v = __builtin_fmaf(swz_xor<8>(v), s8, v);
-            y[k][j] = v;
-        }
-    const float sigma = s1 * s2 * s4 * s8;
+    for (int k = 0; k < R; ++k) hadamard16_lanes(y[k], cc);
+    const int pcc = hperm16(cc);
+    const float sigma = hsign16(cc);
 
     // ---- normalization rounds on A = Y^2: u = 1/r^2 per row, w = 1/c^2 per channel
     // A = Y^2, kept in registers
@@ -253,12 +243,12 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
-            h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 cc + 2 rr + j
+            h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 pcc + 2 rr + j
         }
         float(*colsum)[QD] = (it & 1) ? colsum1 : colsum0;
         float *wsh = (it & 1) ? wsh1 : wsh0;
-        colsum[wave][cc * 8 + 2 * rr] = h2[0];
-        colsum[wave][cc * 8 + 2 * rr + 1] = h2[1];
+        colsum[wave][pcc * 8 + 2 * rr] = h2[0];
+        colsum[wave][pcc * 8 + 2 * rr + 1] = h2[1];
         lds_barrier();
         if (tid < QD) {
             float acc[NWV / 4];
@@ -270,8 +260,8 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
             wsh[tid] = fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
         }
         lds_barrier();
-        const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[cc * 8]);
-        const float4 w1 = *reinterpret_cast<const float4 *>(&wsh[cc * 8 + 4]);
+        const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[pcc * 8]);
+        const float4 w1 = *reinterpret_cast<const float4 *>(&wsh[pcc * 8 + 4]);
         w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
         w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
     }
@@ -291,8 +281,8 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
     lds_barrier();
     float mult[8];
     {
-        const float4 m0 = *reinterpret_cast<const float4 *>(&multsh[cc * 8]);
-        const float4 m1 = *reinterpret_cast<const float4 *>(&multsh[cc * 8 + 4]);
+        const float4 m0 = *reinterpret_cast<const float4 *>(&multsh[pcc * 8]);
+        const float4 m1 = *reinterpret_cast<const float4 *>(&multsh[pcc * 8 + 4]);
         mult[0] = m0.x * sigma; mult[1] = m0.y * sigma; mult[2] = m0.z * sigma; mult[3] = m0.w * sigma;
         mult[4] = m1.x * sigma; mult[5] = m1.y * sigma; mult[6] = m1.z * sigma; mult[7] = m1.w * sigma;
     }
@@ -334,9 +324,9 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
             const uint32_t word = pack8<BITS>(q);
             if constexpr (BITS == 4)
-                *reinterpret_cast<uint32_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(4 * (row * (QD / 8) + cc))) = word;
+                *reinterpret_cast<uint32_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(4 * (row * (QD / 8) + pcc))) = word;
             else
-                *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(2 * (row * (QD / 8) + cc))) = (uint16_t)word;
+                *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(2 * (row * (QD / 8) + pcc))) = (uint16_t)word;
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -354,7 +344,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         // channel ch: rows rg*R .. rg*R + R - 1 are stream positions ch * T + rg * R + k
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int pos = (cc * 8 + j) * T + rg * R;
+            const int pos = (pcc * 8 + j) * T + rg * R;
             if constexpr (BITS == 4) {
                 const uint32_t word = cma[j] | (cmb[j] << 4);
                 if constexpr (R == 8) *reinterpret_cast<uint32_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 2)) = word;

@@ -22,6 +22,45 @@ __device__ __forceinline__ float swz_xor(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
 }
 
+// Walsh-Hadamard butterflies over the 16 lanes of a DPP row, all in DPP-fused
+// FMAs, t <- t + s partner: stage 1 pairs lane l with l ^ 15 (row mirror, s = -1
+// on lanes with bit 3 set), stage 2 with l ^ 7 (half-row mirror, bit 2), stage 3
+// with l ^ 1 (bit 0), stage 4 with l ^ 2 (bit 1). The mirror pairings are linearly
+// independent over the lane bits, so the four stages compute the 16-point Sylvester
+// transform with its outputs relabelled and signed: lane l ends with
+// hsign16(l) * (H16 x)[hperm16(l)] (checked against the plain transform on the CPU).
+// The compiler does not fold a DPP move into an FMA, hence asm: one block per
+// stage and eight independent values, led by the two wait states a DPP read needs
+// after a VALU write of its source.
+__device__ __forceinline__ int hperm16(int l) { return (int)((0x7214BED8FA9C3650ull >> (4 * l)) & 15); }
+__device__ __forceinline__ float hsign16(int l) { return ((0xF9F6u >> l) & 1) ? -1.f : 1.f; }
+
+#define KVQ_DPP_FMAC8(CTRL)                                                                                         \
+    asm volatile("s_nop 1\n\t"                                                                                      \
+                 "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                               \
+                 "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                               \
+                 "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                               \
+                 "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                               \
+                 "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                               \
+                 "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                               \
+                 "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                               \
+                 "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                                     \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])   \
+                 : "v"(s))
+
+// the four stages on eight values per lane; cc = lane & 15
+__device__ __forceinline__ void hadamard16_lanes(float *v, int cc) {
+    float s = (cc & 8) ? -1.f : 1.f;
+    KVQ_DPP_FMAC8("row_mirror");
+    s = (cc & 4) ? -1.f : 1.f;
+    KVQ_DPP_FMAC8("row_half_mirror");
+    s = (cc & 1) ? -1.f : 1.f;
+    KVQ_DPP_FMAC8("quad_perm:[1,0,3,2]");
+    s = (cc & 2) ? -1.f : 1.f;
+    KVQ_DPP_FMAC8("quad_perm:[2,3,0,1]");
+}
+#undef KVQ_DPP_FMAC8
+
 // Sum / min / max over the 16 lanes of a DPP row; every lane gets the same bits.
 __device__ __forceinline__ float row_sum16(float s) {
     s += dpp<DPP_ROR8>(s);
