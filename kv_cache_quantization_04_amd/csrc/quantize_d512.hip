@@ -3,10 +3,11 @@
 // gfx950. Same method and results as the other quantizer kernels.
 //
 // Workgroup = 8 waves, one (tile, head) item at a time, persistent. Lane l of wave
-// w holds the 32 consecutive channels 32 (l & 15) .. + 31 of the four rows
+// w loads the 32 consecutive channels 32 (l & 15) .. + 31 of the four rows
 // 4 rg .. + 3, rg = 4 w + (l >> 4). The 16 lanes of a DPP row cover one token's
-// 512 channels: five Hadamard stages run in registers, four across lanes, and
-// every per-token reduction is a row operation. Column partials are reduced over
+// 512 channels: five Hadamard stages run in registers, four across lanes (after
+// which the lane holds rotated channel group hperm16(l & 15)), and every
+// per-token reduction is a row operation. Column partials are reduced over
 // the four row groups of a wave by permlane swaps and over the 8 waves through
 // LDS. The 128 values per lane leave no room for their squares, which are
 // recomputed in every round. Codes of a row leave as one 16-byte store per lane.
@@ -101,9 +102,8 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
     constexpr float TINY = 1e-30f;
     constexpr float INV_SQRT_H = 0.04419417382415922f;  // 1 / sqrt(512)
     const int iters = NIT >= 0 ? NIT : a.iters;
-    const float s1 = (cc & 1) ? -1.f : 1.f, s2 = (cc & 2) ? -1.f : 1.f;
-    const float s4 = (cc & 4) ? -1.f : 1.f, s8 = (cc & 8) ? -1.f : 1.f;
-    const float sigma = s1 * s2 * s4 * s8;
+    const int pcc = hperm16(cc);      // rotated channel group held after the lane stages
+    const float sigma = hsign16(cc);  // and its sign
     const int W = LD + a.R;  // source channels per token
 
     // rows 16 w .. 16 w + 15 of item itm: one wave-wide copy (1 KB) per row,
@@ -164,8 +164,8 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
         if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
 
         // ---- unnormalized Walsh-Hadamard transform along the 512 channels: bits
-        // 0..4 in registers, bits 5..8 across lanes in the sign-deferred form
-        // t' = t + s_b partner(t); afterwards t = sigma Y
+        // 0..4 in registers, bits 5..8 across lanes (DPP-fused multiply-adds);
+        // afterwards the lane holds sigma * Y of channels 32 pcc .. 32 pcc + 31
 #pragma unroll
         for (int s = 1; s < 32; s <<= 1)
 #pragma unroll
@@ -180,14 +180,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                float v = y[k][e];
-                v = __builtin_fmaf(swz_xor<1>(v), s1, v);
-                v = __builtin_fmaf(swz_xor<2>(v), s2, v);
-                v = __builtin_fmaf(swz_xor<4>(v), s4, v);
-                v = __builtin_fmaf(swz_xor<8>(v), s8, v);
-                y[k][e] = v;
-            }
+            for (int e = 0; e < 32; e += 8) hadamard16_lanes(&y[k][e], cc);
 
         // ---- normalization rounds on A = Y^2 (recomputed): u = 1/r^2 per row, w = 1/c^2 per channel
         if (iters == 0) {
@@ -209,7 +202,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const f32x4 q = it == 0 ? f32x4{1.f, 1.f, 1.f, 1.f}
-                                        : *reinterpret_cast<const f32x4 *>(&wprev[pch(32 * cc) + 4 * i]);
+                                        : *reinterpret_cast<const f32x4 *>(&wprev[pch(32 * pcc) + 4 * i]);
                 const float w4[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
@@ -230,7 +223,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                 for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(y[k][e] * u[k], y[k][e], acc);
                 t[e] = acc;
             }
-            // across the four row groups of the wave: lane (cc, rr) ends with channels 32 cc + 8 rr + j
+            // across the four row groups of the wave: lane (cc, rr) ends with channels 32 pcc + 8 rr + j
             float h16[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -243,7 +236,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                 const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h16[j]), __float_as_uint(h16[j + 8]), false, false);
                 h8[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
             }
-            lds_store_8f32(&colsum[wave][pch(32 * cc + 8 * rr)], h8);
+            lds_store_8f32(&colsum[wave][pch(32 * pcc + 8 * rr)], h8);
             lds_barrier();
             float *wsh = (it & 1) ? wsh1 : wsh0;
             {
@@ -269,7 +262,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
         // y <- y * multiplier (read four at a time)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const f32x4 q = *reinterpret_cast<const f32x4 *>(&multsh[pch(32 * cc) + 4 * i]);
+            const f32x4 q = *reinterpret_cast<const f32x4 *>(&multsh[pch(32 * pcc) + 4 * i]);
             const float m4[4] = {q.x * sigma, q.y * sigma, q.z * sigma, q.w * sigma};
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -312,7 +305,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                     }
                     word[d] = ev | (od << 4);
                 }
-                *reinterpret_cast<uint4 *>(codes + row * (LD / 2) + 16 * cc) = uint4{word[0], word[1], word[2], word[3]};
+                *reinterpret_cast<uint4 *>(codes + row * (LD / 2) + 16 * pcc) = uint4{word[0], word[1], word[2], word[3]};
             } else {  // BITS == 2: 16 codes per word
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
@@ -324,7 +317,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                             q4[m] = __builtin_amdgcn_cvt_pk_u8_f32(fminf(__builtin_fmaf(y[k][16 * d + 4 * b + m], inv, zi), LEVELS), b, q4[m]);
                     word[d] = q4[0] | (q4[1] << 2) | (q4[2] << 4) | (q4[3] << 6);
                 }
-                *reinterpret_cast<uint2 *>(codes + row * (LD / 4) + 8 * cc) = uint2{word[0], word[1]};
+                *reinterpret_cast<uint2 *>(codes + row * (LD / 4) + 8 * pcc) = uint2{word[0], word[1]};
             }
             if (cc == 0) reinterpret_cast<uint32_t *>(a.sz)[blk * LT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         }

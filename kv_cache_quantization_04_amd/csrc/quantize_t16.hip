@@ -2,10 +2,11 @@
 // scale group per token), gfx950: one wave per (tile, head), no workgroup
 // barriers. Same method and results as the other quantizer kernels.
 //
-// Lane l of a wave holds the 8 consecutive channels 8 (l & 15) .. + 7 of the four
+// Lane l of a wave loads the 8 consecutive channels 8 (l & 15) .. + 7 of the four
 // rows 4 (l >> 4) .. + 3. The 16 lanes of a DPP row cover one token's 128
-// channels: Hadamard butterflies on channel bits 3..6 and all per-token
-// reductions are row operations. Column sums finish inside the wave (permlane
+// channels: Hadamard butterflies on channel bits 3..6 (after which the lane holds
+// rotated channel group hperm16(l & 15)) and all per-token reductions are row
+// operations. Column sums finish inside the wave (permlane
 // swaps across the four row groups) and come back to the lanes through a small
 // per-wave LDS array. Codes go to a per-wave LDS byte image in bitstream order
 // (token-major t * 128 + j, channel-major j * 16 + t); each lane then packs 32
@@ -60,9 +61,10 @@ __global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_
     constexpr float TINY = 1e-30f;
     constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
     const int iters = NIT >= 0 ? NIT : a.iters;
-    const float s1 = (cc & 1) ? -1.f : 1.f, s2 = (cc & 2) ? -1.f : 1.f;
-    const float s4 = (cc & 4) ? -1.f : 1.f, s8 = (cc & 8) ? -1.f : 1.f;
-    const float sigma = s1 * s2 * s4 * s8;
+    // after the lane stages of the rotation the lane holds sigma * Y of channel
+    // group pcc: channels 8 pcc .. 8 pcc + 7
+    const int pcc = hperm16(cc);
+    const float sigma = hsign16(cc);
     float *cv = chv[wave];
     uint8_t *im = img[wave];
 
@@ -89,8 +91,7 @@ __global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_
         const int64_t blk = (int64_t)dst_page * a.H + head;
 
         // ---- unnormalized Walsh-Hadamard transform along the 128 channels: bits
-        // 0..2 in registers, bits 3..6 across lanes in the sign-deferred form
-        // t' = t + s_b partner(t); afterwards t = sigma Y
+        // 0..2 in registers, bits 3..6 across lanes (DPP-fused multiply-adds)
 #pragma unroll
         for (int s = 1; s < 8; s <<= 1)
 #pragma unroll
@@ -103,16 +104,7 @@ __global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_
                         y[k][j | s] = p - q;
                     }
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v = y[k][j];
-                v = __builtin_fmaf(swz_xor<1>(v), s1, v);
-                v = __builtin_fmaf(swz_xor<2>(v), s2, v);
-                v = __builtin_fmaf(swz_xor<4>(v), s4, v);
-                v = __builtin_fmaf(swz_xor<8>(v), s8, v);
-                y[k][j] = v;
-            }
+        for (int k = 0; k < 4; ++k) hadamard16_lanes(y[k], cc);
 
         // ---- normalization rounds on A = Y^2: u = 1/r^2 per row, w = 1/c^2 per channel
         float A[4][8];
@@ -164,13 +156,13 @@ __global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
-                t_own[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 cc + 2 rr + j
+                t_own[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 pcc + 2 rr + j
             }
             // a zero column keeps a large finite w (its A entries are all zero)
-            *reinterpret_cast<float2 *>(&cv[8 * cc + 2 * rr]) =
+            *reinterpret_cast<float2 *>(&cv[8 * pcc + 2 * rr]) =
                 float2{fn * __builtin_amdgcn_rcpf(fmaxf(t_own[0], TINY)), fn * __builtin_amdgcn_rcpf(fmaxf(t_own[1], TINY))};
-            const float4 w0 = *reinterpret_cast<const float4 *>(&cv[8 * cc]);
-            const float4 w1 = *reinterpret_cast<const float4 *>(&cv[8 * cc + 4]);
+            const float4 w0 = *reinterpret_cast<const float4 *>(&cv[8 * pcc]);
+            const float4 w1 = *reinterpret_cast<const float4 *>(&cv[8 * pcc + 4]);
             w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
             w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
         }
@@ -190,13 +182,13 @@ __global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_
                 m2[j] = INV_SQRT_H / cvj;
                 c2 |= (uint32_t)c16 << (16 * j);
             }
-            *reinterpret_cast<uint32_t *>(a.cnorm + blk * ZD + 8 * cc + 2 * rr) = c2;
-            *reinterpret_cast<float2 *>(&cv[8 * cc + 2 * rr]) = float2{m2[0], m2[1]};
+            *reinterpret_cast<uint32_t *>(a.cnorm + blk * ZD + 8 * pcc + 2 * rr) = c2;
+            *reinterpret_cast<float2 *>(&cv[8 * pcc + 2 * rr]) = float2{m2[0], m2[1]};
         }
         float mult[8];
         {
-            const float4 m0 = *reinterpret_cast<const float4 *>(&cv[8 * cc]);
-            const float4 m1 = *reinterpret_cast<const float4 *>(&cv[8 * cc + 4]);
+            const float4 m0 = *reinterpret_cast<const float4 *>(&cv[8 * pcc]);
+            const float4 m1 = *reinterpret_cast<const float4 *>(&cv[8 * pcc + 4]);
             mult[0] = m0.x * sigma; mult[1] = m0.y * sigma; mult[2] = m0.z * sigma; mult[3] = m0.w * sigma;
             mult[4] = m1.x * sigma; mult[5] = m1.y * sigma; mult[6] = m1.z * sigma; mult[7] = m1.w * sigma;
         }
@@ -240,7 +232,7 @@ __global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_
                     lo = __builtin_amdgcn_cvt_pk_u8_f32(q[b], b, lo);
                     hi = __builtin_amdgcn_cvt_pk_u8_f32(q[b + 4], b, hi);
                 }
-                *reinterpret_cast<uint2 *>(&im[row * ZD + 8 * cc]) = uint2{lo, hi};
+                *reinterpret_cast<uint2 *>(&im[row * ZD + 8 * pcc]) = uint2{lo, hi};
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) cm[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k, cm[j]);
@@ -248,7 +240,7 @@ __global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_
         }
         if constexpr (LAYOUT == KVQ_CHANNEL_MAJOR) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t *>(&im[(8 * cc + j) * ZT + 4 * rr]) = cm[j];
+            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t *>(&im[(8 * pcc + j) * ZT + 4 * rr]) = cm[j];
         }
 
         // ---- pack: lane l takes stream positions 32 l .. 32 l + 31 -> BITS words
