@@ -50,7 +50,7 @@ __device__ __forceinline__ Rows load_rows(const QuantArgs &a, int item, int lane
 }  // namespace
 
 template <int BITS, int LAYOUT, int NIT>
-__global__ void __launch_bounds__(ZNT) quantize_t16_kernel(QuantArgs a, int num_items) {
+__global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int num_items) {
     __shared__ float chv[4][ZD];                                // per wave: one value per channel
     __shared__ __attribute__((aligned(16))) uint8_t img[4][ZT * ZD];  // per wave: codes in stream order
 

@@ -80,12 +80,24 @@ def half_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(key(a) - key(b))
 
 
+# A channel normalizer c16 that rounds 1 ulp away from the oracle's (an fp32 vs
+# fp64 rounding boundary) changes y = x'/c16 of that channel by up to 2^-10
+# relative. In a token whose minimum or maximum lies in that channel, Z (the
+# minimum, rounded to fp16) then moves by up to 2 ulps plus its own rounding, and
+# S by up to 2 ulps: "quantize with what you store" carries the difference on.
+SIDE_CASCADE_ULP = 3
+
+
 def compare_blocks(gpu: O.HostCache, orc: O.HostCache, pages, heads=None, stats=None):
-    """Compare codes, (S, Z) and c of the given pages; returns accumulated stats."""
+    """Compare codes, (S, Z) and c of the given pages; returns accumulated stats.
+    An (S, Z) pair more than 1 ulp off counts as a cascade (side_cascade) when its
+    group holds a channel whose c16 differs and it is within SIDE_CASCADE_ULP;
+    otherwise as side_bad."""
     f = orc.f
     heads = range(orc.num_heads) if heads is None else heads
     st = stats if stats is not None else dict(codes=0, flips=0, maxdiff=0, side=0, side_ulp1=0, side_bad=0,
-                                              bits=f.bits)
+                                              side_cascade=0, bits=f.bits)
+    ng = f.head_dim // f.group
     for p in pages:
         for h in heads:
             cg = O.unpack(gpu.codes[p, h], f).astype(np.int32)
@@ -94,11 +106,16 @@ def compare_blocks(gpu: O.HostCache, orc: O.HostCache, pages, heads=None, stats=
             st["codes"] += d.size
             st["flips"] += int((d != 0).sum())
             st["maxdiff"] = max(st["maxdiff"], int(d.max()))
-            for a, b in ((gpu.sz[p, h], orc.sz[p, h]), (gpu.cnorm[p, h], orc.cnorm[p, h])):
-                u = half_ulp_diff(a.reshape(-1), b.reshape(-1))
+            uc = half_ulp_diff(gpu.cnorm[p, h].reshape(-1), orc.cnorm[p, h].reshape(-1))
+            us = half_ulp_diff(gpu.sz[p, h].reshape(-1), orc.sz[p, h].reshape(-1))  # [token][group][S, Z]
+            flipped_group = (uc.reshape(ng, f.group) != 0).any(axis=1)
+            us_group = np.broadcast_to(np.repeat(flipped_group, 2)[None, :], (us.size // (2 * ng), 2 * ng)).reshape(-1)
+            for u, cascade in ((uc, np.zeros(uc.size, bool)), (us, us_group)):
                 st["side"] += u.size
                 st["side_ulp1"] += int((u == 1).sum())
-                st["side_bad"] += int((u > 1).sum())
+                casc = (u > 1) & cascade & (u <= SIDE_CASCADE_ULP)
+                st["side_cascade"] += int(casc.sum())
+                st["side_bad"] += int(((u > 1) & ~casc).sum())
             if orc.rope is not None:
                 assert np.array_equal(gpu.rope[p, h], orc.rope[p, h])
     return st
