@@ -149,6 +149,71 @@ def cpu_baseline(cfg, ks, vs, q, nseq):
                       f"all {cfg.num_q_heads} query heads ({td:.2f} s), {threads} threads"}
 
 
+def bench_append(args, cfg, torch, K, W, dev):
+    """Append path: every step appends one token to the K and V caches of every
+    sequence, starting from the workload's context lengths (each sequence's tail
+    holds its partial tile). Timed with HIP events on the launch stream."""
+    B, H, T = cfg.num_seqs, cfg.num_kv_heads, cfg.fk.tile_tokens
+    total = args.warmup + args.steps
+    fmts = [cfg.fk] + ([cfg.fv] if cfg.fv is not None else [])
+    widths = [cfg.width] + ([cfg.dv] if cfg.fv is not None else [])
+    dt = torch.float32 if cfg.src_dtype == "f32" else torch.bfloat16
+    es = ESIZE[cfg.src_dtype]
+    lens0 = np.asarray(cfg.seq_lens, np.int64)
+    npg = (lens0 + total + T - 1) // T
+    P = int(npg.sum())
+    bt = np.full((B, int(npg.max())), -1, np.int32)
+    k = 0
+    for s_ in range(B):
+        bt[s_, :npg[s_]] = np.arange(k, k + npg[s_])
+        k += int(npg[s_])
+    btd = torch.from_numpy(bt).to(dev)
+    caches, tails, news = [], [], []
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + args.config)
+    for f, w in zip(fmts, widths):
+        caches.append(K.DeviceCache(K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits,
+                                                  f.iters, f.layout), P, H, device=dev))
+        tails.append(torch.randn((B, T, H, w), generator=g, device=dev).to(dt))
+        news.append(torch.randn((total, B, H, w), generator=g, device=dev).to(dt))
+    lens = [torch.from_numpy((lens0 + i).astype(np.int32)).to(dev) for i in range(total)]
+    ws = torch.empty(max(K.kv_append_workspace_bytes(B), 4), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        for c, t_, n_ in zip(caches, tails, news):
+            K.kv_append(c, t_, n_[i], lens[i], btd, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.warmup, total):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # algorithmic bytes per step: the re-quantized rows read, the new rows written to
+    # the tails, and each touched page block written whole
+    rows = sum(int(((lens0 + i) % T + 1).sum()) for i in range(args.warmup, total)) / args.steps
+    byts = sum(rows * H * w * es + B * H * w * es + B * H * block_bytes(f) for f, w in zip(fmts, widths))
+    gbs = byts / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "kv_append tokens/s (one token per sequence per step, K and V re-quantized)",
+        "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + " (append)", "seqs": B, "kv_heads": H, "tile_tokens": T,
+                   "mean_rows_requantized": round(rows / B, 1)},
+        "roofline": {"bound": "hbm", "kernel": "append_prep_kernel + " + K.kv_quantize_kernel_name(caches[0], tails[0].view(B * T, H, -1)),
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None, "algorithmic_bytes_per_step": byts,
+                     "note": "B x H tiles per launch: latency-bound, far from either roofline"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +223,8 @@ def main():
     ap.add_argument("--ring-mb", type=int, default=2048, help="live bytes of the copy ring")
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append", action="store_true",
+                    help="measure the append path (one token per sequence per step, K and V) instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures a single GPU: the quantizer and decode shard by sequence and kv head with no "
@@ -172,6 +239,9 @@ def main():
     dev = torch.device("cuda:0")
     cfg = W.config(args.config)
     log(f"workload: {cfg.name}")
+    if args.append:
+        bench_append(args, cfg, torch, K, W, dev)
+        return
     ks = W.gen_k(cfg)
     vs = W.gen_v(cfg) if cfg.fv is not None else None
     q = W.gen_q(cfg)

@@ -163,6 +163,39 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
                           float sm_scale, int32_t num_splits, void *workspace, size_t workspace_bytes,
                           float *out, hipStream_t stream);
 
+/* Append one new token per sequence to a paged quantized cache, keeping every
+ * token in it: the token's row goes into the sequence's partial last tile and
+ * that tile is quantized again from its unquantized rows (the method's
+ * statistics are per tile: "KVarN" project review, Key Features,
+ * "Variance-Normalized Quantization Pipeline"). After the call, page
+ * block_table[s][L / T] (L = seq_lens[s]) holds the quantization of the
+ * sequence's tokens T*(L/T) .. L, exactly what kv_quantize gives for that tile.
+ *   tail (device, caller-owned, read and written): [num_seqs][T][H][D + R] in
+ *     dtype; row r of sequence s holds token T*(L/T) + r of s. The call writes
+ *     row L % T; rows below it must hold the sequence's earlier tokens of the
+ *     tile (they do when every token was appended through this call, or the
+ *     caller copied them in). 16-byte aligned.
+ *   new_tokens (device): element (s, h, e) at s*new_stride_seq +
+ *     h*new_stride_head + e, e < D + R, in dtype.
+ *   seq_lens (device int32): [num_seqs], the lengths BEFORE the append; not
+ *     modified (the caller increments). A negative length skips the sequence.
+ *   block_table (device int32): [num_seqs][block_table_stride]; a page index
+ *     L / T outside the row, or a page number outside [0, num_pages), leaves
+ *     the cache unchanged for that sequence (the tail row is still written).
+ *   workspace (device): at least kv_append_workspace_bytes(num_seqs) bytes,
+ *     4-byte aligned; overwritten.
+ *   status_flags: as for kv_quantize.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (as kv_quantize), KVQ_EWORKSPACE,
+ * KVQ_ELAUNCH. Calls on one stream are ordered; two appends to one sequence
+ * must not run concurrently. */
+kvq_status kv_append(const kvq_cache *dst, void *tail, kvq_dtype dtype, const void *new_tokens,
+                     int64_t new_stride_seq, int64_t new_stride_head, int32_t num_seqs,
+                     const int32_t *seq_lens, const int32_t *block_table, int32_t block_table_stride,
+                     void *workspace, size_t workspace_bytes, uint32_t *status_flags, hipStream_t stream);
+
+/* Workspace bytes kv_append needs for num_seqs sequences (0 for negative). */
+size_t kv_append_workspace_bytes(int32_t num_seqs);
+
 /* Name of the GPU kernel kv_quantize runs for these arguments (the same checks
  * and dispatch; nothing is launched or dereferenced): "quantize_d128_kernel",
  * "quantize_t16_kernel", "quantize_d512_kernel" (specialised tile shapes) or

@@ -6,8 +6,8 @@ libkvq.so. PyTorch supplies device memory (tensor.data_ptr()) and the stream
 
     kvq_format_from_preset, kvq_cache_bytes, kv_quantize, kv_dequantize,
     kv_decode_attn_default_splits, kv_decode_attn_workspace_bytes,
-    kv_decode_attn, kv_quantize_kernel_name, kv_decode_attn_kernel_name,
-    kvq_status_str
+    kv_decode_attn, kv_append, kv_append_workspace_bytes, kv_quantize_kernel_name,
+    kv_decode_attn_kernel_name, kvq_status_str
 
 plus ``DeviceCache``, a holder of the four device arrays of one cache.
 Importing this module fails if libkvq.so has not been built: there is no
@@ -38,8 +38,8 @@ KVQ_TOKEN_MAJOR, KVQ_CHANNEL_MAJOR = 0, 1
 KVQ_FLAG_NONFINITE, KVQ_FLAG_SIDE_OVERFLOW = 1, 2
 
 EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_dequantize",
-           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_quantize_kernel_name", "kv_decode_attn_kernel_name",
-           "kvq_status_str")
+           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_append", "kv_append_workspace_bytes",
+           "kv_quantize_kernel_name", "kv_decode_attn_kernel_name", "kvq_status_str")
 
 
 class kvq_format(ctypes.Structure):
@@ -66,6 +66,9 @@ _sig = {
     "kv_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "kv_decode_attn": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _vp, _i32,
                               _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
+    "kv_append": (_i32, [ctypes.POINTER(kvq_cache), _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _sz, _vp,
+                         _vp]),
+    "kv_append_workspace_bytes": (_sz, [_i32]),
     "kv_quantize_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(kvq_cache), _vp, _i32, _i64, _i64]),
     "kv_decode_attn_kernel_name": (ctypes.c_char_p, [_vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _i32]),
     "kvq_status_str": (ctypes.c_char_p, [_i32]),
@@ -171,6 +174,30 @@ def kv_decode_attn_default_splits(k: DeviceCache, v: Optional[DeviceCache], num_
                                   max_seq_len: int) -> int:
     return int(_lib.kv_decode_attn_default_splits(ctypes.byref(k.struct), ctypes.byref(v.struct) if v is not None else None,
                                                   num_seqs, num_q_heads, max_seq_len))
+
+
+def kv_append_workspace_bytes(num_seqs: int) -> int:
+    return int(_lib.kv_append_workspace_bytes(num_seqs))
+
+
+def kv_append(dst: DeviceCache, tail, new_tokens, seq_lens, block_table, workspace=None, status_flags=None,
+              stream=None):
+    """Append new_tokens[s] ([num_seqs][H][D + R], same dtype as tail) to each sequence:
+    row seq_lens[s] % T of tail[s] ([num_seqs][T][H][D + R]) and a re-quantization of
+    that partial tile into page block_table[s][seq_lens[s] // T]. seq_lens are the
+    lengths before the append and are not modified."""
+    torch = _torch()
+    B = new_tokens.shape[0]
+    if tail.dtype != new_tokens.dtype:
+        raise ValueError("tail and new_tokens must have the same dtype")
+    if new_tokens.dim() != 3 or new_tokens.stride(2) != 1 or not tail.is_contiguous():
+        raise ValueError("new_tokens must be [num_seqs][H][D + R] with unit stride in the last dimension; tail contiguous")
+    if workspace is None:
+        workspace = torch.empty(max(kv_append_workspace_bytes(B), 4), dtype=torch.uint8, device=new_tokens.device)
+    _check(_lib.kv_append(ctypes.byref(dst.struct), _ptr(tail), _dtype_code(tail), _ptr(new_tokens),
+                          new_tokens.stride(0), new_tokens.stride(1), B, _ptr(seq_lens), _ptr(block_table),
+                          block_table.shape[1], _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _ptr(status_flags), _stream(stream)), "kv_append")
 
 
 def kv_quantize_kernel_name(dst: DeviceCache, src) -> Optional[str]:

@@ -177,6 +177,41 @@ kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t 
     return launched();
 }
 
+size_t kv_append_workspace_bytes(int32_t num_seqs) {
+    if (num_seqs < 0) return 0;
+    return (size_t)3 * num_seqs * sizeof(int32_t);
+}
+
+kvq_status kv_append(const kvq_cache *dst, void *tail, kvq_dtype dtype, const void *new_tokens,
+                     int64_t new_stride_seq, int64_t new_stride_head, int32_t num_seqs, const int32_t *seq_lens,
+                     const int32_t *block_table, int32_t block_table_stride, void *workspace, size_t workspace_bytes,
+                     uint32_t *status_flags, hipStream_t stream) {
+    kvq_status st = check_cache(dst);
+    if (st != KVQ_OK) return st;
+    if (!tail || !new_tokens || !valid_dtype(dtype) || num_seqs < 0) return KVQ_EINVAL;
+    if (new_stride_seq < 0 || new_stride_head < 0) return KVQ_EINVAL;
+    if ((uintptr_t)new_tokens & (dtype == KVQ_F32 ? 3 : 1)) return KVQ_EINVAL;
+    if (num_seqs == 0) return KVQ_OK;
+    if (!seq_lens || !block_table || block_table_stride <= 0) return KVQ_EINVAL;
+    if (!workspace || workspace_bytes < kv_append_workspace_bytes(num_seqs)) return KVQ_EWORKSPACE;
+    if ((uintptr_t)workspace & 3) return KVQ_EINVAL;
+    const kvq_format &f = dst->fmt;
+    const int W = f.head_dim + f.rope_dim;
+    const int64_t row = (int64_t)dst->num_heads * W;  // tail elements per token
+    if ((int64_t)num_seqs * f.tile_tokens * row > (int64_t(1) << 40) || (int64_t)num_seqs * f.tile_tokens >= (1 << 30))
+        return KVQ_EUNSUPPORTED;
+    // the tail is the quantizer's source: same alignment rules as kv_quantize
+    if ((st = check_quantize_source(dst, tail, dtype, row, W)) != KVQ_OK) return st;
+    int32_t *ws = (int32_t *)workspace;
+    kvq::AppendArgs ap{new_tokens, new_stride_seq, new_stride_head, tail, dtype == KVQ_F32 ? 4 : 2, num_seqs,
+                       f.tile_tokens, dst->num_heads, W, seq_lens, block_table, block_table_stride, ws,
+                       ws + num_seqs, ws + 2 * num_seqs};
+    const kvq::QuantArgs q = quant_args(dst, tail, dtype, row, W, ap.tile_src_token, ap.tile_valid, ap.tile_dst_page,
+                                        status_flags);
+    if (!kvq::launch_append(ap, f.head_dim, f.tile_tokens, q, stream)) return KVQ_EUNSUPPORTED;
+    return launched();
+}
+
 int32_t kv_decode_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_seq_len) {
     kvq::DecodeArgs a{};

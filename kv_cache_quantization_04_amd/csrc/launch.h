@@ -48,7 +48,20 @@ struct DecodeArgs {
     float *out;
 };
 
+// append path: new token rows -> tail buffer, tile descriptors -> workspace
+struct AppendArgs {
+    const void *new_tokens;
+    int64_t new_stride_seq, new_stride_head;  // elements
+    void *tail;                               // [num_seqs][T][H][W]
+    int esize;                                // bytes per element
+    int num_seqs, T, H, W;                    // W = D + R
+    const int32_t *seq_lens, *block_table;
+    int bt_stride;
+    int32_t *tile_src_token, *tile_valid, *tile_dst_page;  // [num_seqs] each
+};
+
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
+bool launch_append(const AppendArgs &a, int D, int T, const QuantArgs &q, hipStream_t stream);
 bool launch_dequant(int D, int T, int num_tiles, const DequantArgs &a, hipStream_t stream);
 bool launch_decode(const DecodeArgs &a, hipStream_t stream);
 // split-K partitions for a decode call whose fields other than q, block table,

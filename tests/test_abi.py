@@ -165,3 +165,29 @@ def test_decode_kernel_name():
     assert decode_kernel(fm, None, 128, 1) == "decode_mla_kernel"
     assert decode_kernel(fk, fv, 30, 8) is None
     assert decode_kernel(fk, fv, 32, 8, q=None) is None
+
+
+def append_status(fmt, tail=FAKE, new=FAKE, num_seqs=2, ws_bytes=None, ws=FAKE, dtype=2, bt_stride=4):
+    c = cache_struct(fmt, rope=FAKE if fmt.rope_dim else None)
+    if ws_bytes is None:
+        ws_bytes = K._lib.kv_append_workspace_bytes(num_seqs)
+    return K._lib.kv_append(ctypes.byref(c), tail, dtype, new, 256, 128, num_seqs, FAKE, FAKE, bt_stride, ws,
+                            ws_bytes, None, None)
+
+
+def test_append_argument_errors():
+    f = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_TOKEN_MAJOR)
+    assert K._lib.kv_append_workspace_bytes(5) == 60
+    assert K._lib.kv_append_workspace_bytes(-1) == 0
+    assert append_status(f, num_seqs=0) == K.KVQ_OK                     # nothing to do, nothing read
+    assert append_status(f, tail=None) == K.KVQ_EINVAL
+    assert append_status(f, new=None) == K.KVQ_EINVAL
+    assert append_status(f, new=FAKE + 1) == K.KVQ_EINVAL               # bf16 elements are 2-byte aligned
+    assert append_status(f, dtype=7) == K.KVQ_EINVAL
+    assert append_status(f, num_seqs=-1) == K.KVQ_EINVAL
+    assert append_status(f, bt_stride=0) == K.KVQ_EINVAL
+    assert append_status(f, ws_bytes=8) == K.KVQ_EWORKSPACE
+    assert append_status(f, ws=None) == K.KVQ_EWORKSPACE
+    assert append_status(f, tail=FAKE + 8) == K.KVQ_EUNSUPPORTED        # the tail is a quantizer source
+    bad = K.make_format(96, 0, 16, 32, 32, 4, 2, K.KVQ_TOKEN_MAJOR)
+    assert append_status(bad) == K.KVQ_EUNSUPPORTED

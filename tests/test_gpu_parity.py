@@ -153,6 +153,90 @@ def test_flags_latent_tile_rope_nonfinite(gpu):
     assert int(flags.item()) == fl
 
 
+# ----------------------------------------------------------------------------- append path
+APPEND = [
+    # D, R, T, bits, iters, dtype, layout: one format per quantizer kernel
+    (128, 0, 16, 3, 2, "bf16", 0),     # 16-token tiles
+    (128, 0, 16, 3, 2, "bf16", 1),
+    (128, 0, 128, 4, 4, "bf16", 0),    # 128-channel tiles
+    (128, 0, 128, 2, 4, "bf16", 1),
+    (512, 64, 128, 4, 4, "bf16", 0),   # latent tiles with rope
+    (64, 0, 64, 4, 4, "f32", 0),       # generic kernel
+]
+
+
+@pytest.mark.parametrize("case", APPEND, ids=lambda c: "D{}R{}T{}b{}N{}{}L{}".format(*c))
+def test_append_matches_quantize_of_the_tile(gpu, case):
+    """Token-by-token appends: after each one, the sequence's last page equals the
+    quantization of the tokens of that tile so far (kv_quantize semantics), for
+    sequences that start empty, one token short of a page boundary, and mid-page."""
+    D, R, T, bits, iters, dtype, layout = case
+    log("append case", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    H, W_ = 2, D + R
+    f = W.Fmt(D, R, T, D, D, bits, iters, layout)
+    start = [0, T - 2, 2 * T + 5]
+    steps = 4
+    B = len(start)
+    hist = [np.concatenate([heavy(rng, L + steps, H, D), rng.standard_normal((L + steps, H, R))], axis=2) if R
+            else heavy(rng, L + steps, H, D) for L in start]
+    srcs = [make_src(x, dtype) for x in hist]
+    npg = [(L + steps + T - 1) // T for L in start]
+    P = sum(npg) + 2
+    perm = rng.permutation(P)
+    bt = np.full((B, max(npg) + 1), -1, np.int64)
+    k = 0
+    for s_ in range(B):
+        bt[s_, :npg[s_]] = perm[k:k + npg[s_]]
+        k += npg[s_]
+    dc = K.DeviceCache(kfmt(f), P, H)
+    # the tail starts with each sequence's partial tile
+    tail_h = np.zeros((B, T, H, W_), srcs[0].dtype)
+    for s_, L in enumerate(start):
+        r = L % T
+        tail_h[s_, :r] = srcs[s_][L - r:L]
+    tail = to_dev(tail_h, dtype)
+    btd = i32(bt)
+    flags = torch.zeros(1, dtype=torch.int32, device=gpu)
+    for step in range(steps):
+        lens = [L + step for L in start]
+        new = to_dev(np.stack([srcs[s_][lens[s_]] for s_ in range(B)]), dtype)
+        K.kv_append(dc, tail, new, i32(lens), btd, status_flags=flags)
+        torch.cuda.synchronize()
+        got = host_copy(dc, f)
+        # expected: the tile of token lens[s] from its first token through it
+        allsrc = np.concatenate(srcs, axis=0)
+        off = np.cumsum([0] + [len(x) for x in srcs])[:-1]
+        t0 = [off[s_] + T * (lens[s_] // T) for s_ in range(B)]
+        pages = [int(bt[s_, lens[s_] // T]) for s_ in range(B)]
+        hc, fl = orc_quantize(f, allsrc, dtype, np.array(t0), np.array([L % T + 1 for L in lens]), np.array(pages), P)
+        st = compare_blocks(got, hc, pages)
+        log("  step", step, "lens", lens, "stats", st)
+        assert_block_parity(st, f"{case} step {step}")
+        assert fl == 0
+    assert int(flags.item()) == 0
+
+
+def test_append_skips_invalid_destinations(gpu):
+    """A page index past the block table row, or a negative page number, leaves
+    the cache as it was; the tail row is still written."""
+    f = W.Fmt(128, 0, 16, 128, 128, 4, 2, 0)
+    rng = np.random.default_rng(21)
+    dc = K.DeviceCache(kfmt(f), 4, 1)
+    for t_ in (dc.codes, dc.sz, dc.cnorm):
+        t_.fill_(7)
+    before = [t_.clone() for t_ in (dc.codes, dc.sz, dc.cnorm)]
+    tail = torch.zeros((2, 16, 1, 128), dtype=torch.bfloat16, device=gpu)
+    new = to_dev(make_src(rng.standard_normal((2, 1, 128)), "bf16"), "bf16")
+    bt = i32(np.array([[0, -1], [1, 2]]))
+    K.kv_append(dc, tail, new, i32([20, 40]), bt)   # seq 0 -> page slot 1 = -1; seq 1 -> slot 2: past its row
+    torch.cuda.synchronize()
+    for t_, b_ in zip((dc.codes, dc.sz, dc.cnorm), before):
+        assert torch.equal(t_, b_)
+    assert torch.equal(tail[0, 4].view(torch.int16), new[0].view(torch.int16))
+    assert torch.equal(tail[1, 8].view(torch.int16), new[1].view(torch.int16))
+
+
 # ----------------------------------------------------------------------------- dequantize and decode, small
 def small_paged(seed, D=128, T=16, Hq=8, Hkv=2, lens=(300, 1, 77, 16), kbits=4, vbits=3, iters=2, G=None, mla=False,
                 R=0, dtype="bf16", qscale=1.0):
