@@ -214,6 +214,76 @@ def bench_append(args, cfg, torch, K, W, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_prefill(args, cfg, torch, K, W, dev):
+    """Chunked prefill attention: the last LQ tokens of every sequence of the workload
+    are the chunk (their K and V quantized into the cache with the rest); each step
+    is one kv_prefill_attn call. Timed with HIP events on the launch stream."""
+    Lq = args.prefill
+    B, H, Hq = cfg.num_seqs, cfg.num_kv_heads, cfg.num_q_heads
+
+    def to_dev(a):
+        if cfg.src_dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+    def kfmt(f):
+        return K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
+
+    tst, tv, tp = i32(cfg.tile_src_token), i32(cfg.tile_valid), i32(cfg.tile_page)
+    kc = K.DeviceCache(kfmt(cfg.fk), cfg.num_pages, H, device=dev)
+    K.kv_quantize(kc, to_dev(W.gen_k(cfg)), tst, tv, tp)
+    vc = None
+    if cfg.fv is not None:
+        vc = K.DeviceCache(kfmt(cfg.fv), cfg.num_pages, H, device=dev)
+        K.kv_quantize(vc, to_dev(W.gen_v(cfg)), tst, tv, tp)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + args.config)
+    dt = torch.float32 if cfg.src_dtype == "f32" else torch.bfloat16
+    q = torch.randn((B, Lq, Hq, cfg.width), generator=g, device=dev).to(dt)
+    bt, sl = i32(cfg.block_table), i32(cfg.seq_lens)
+    max_len = int(cfg.seq_lens.max())
+    splits = K.kv_prefill_attn_default_splits(kc, vc, B, Lq, Hq, max_len)
+    ws = torch.empty(K.kv_prefill_attn_workspace_bytes(B, Lq, Hq, cfg.dv, splits, bt.shape[1]), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, Lq, Hq, cfg.dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        K.kv_prefill_attn(q, kc, vc, bt, sl, max_len, cfg.sm_scale, num_splits=splits, workspace=ws, out=out,
+                          stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # algorithmic: scores over D + R and values over Dv per (query position, head, attended token)
+    attended = float(sum(int(L) - Lq + i + 1 for L in cfg.seq_lens for i in range(Lq)))
+    flops = 2.0 * attended * Hq * (cfg.width + cfg.dv)
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "prefill query tokens/s (causal chunk over the quantized cache)",
+        "value": round(B * Lq / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + f" (prefill chunk {Lq})", "chunk": Lq, "decode_splits": splits},
+        "roofline": {"bound": "mfma", "kernel": "prefill_prep_kernel + " +
+                     K.kv_decode_attn_kernel_name(q.view(B * Lq, Hq, -1), kc, vc) + " + decode_reduce_kernel",
+                     "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 5), "traffic": None, "algorithmic_flops_per_step": flops,
+                     "note": "each chunk position runs as its own decode sequence: the pages are re-read per position"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +295,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", action="store_true",
                     help="measure the append path (one token per sequence per step, K and V) instead")
+    ap.add_argument("--prefill", type=int, default=0, metavar="LQ",
+                    help="measure chunked prefill attention with LQ query positions per sequence instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures a single GPU: the quantizer and decode shard by sequence and kv head with no "
@@ -241,6 +313,9 @@ def main():
     log(f"workload: {cfg.name}")
     if args.append:
         bench_append(args, cfg, torch, K, W, dev)
+        return
+    if args.prefill > 0:
+        bench_prefill(args, cfg, torch, K, W, dev)
         return
     ks = W.gen_k(cfg)
     vs = W.gen_v(cfg) if cfg.fv is not None else None

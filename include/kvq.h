@@ -211,6 +211,37 @@ const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_d
 const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v,
                                        int32_t num_q_heads);
 
+/* Chunked prefill attention over the paged quantized cache. Each sequence b
+ * ends with a chunk of chunk_len query positions whose keys and values are
+ * already in the cache (its last chunk_len tokens); position i of the chunk
+ * attends causally to tokens 0 .. seq_lens[b] - chunk_len + i (a position with
+ * no token left gives the result of an empty decode). The result per (b, i) is
+ * exactly kv_decode_attn's for that query over that prefix (same fold, same
+ * kernels: the chunk positions run as chunk_len virtual sequences sharing b's
+ * block-table row).
+ *   q (device): [num_seqs][chunk_len][num_q_heads][D + R] in q_dtype.
+ *   seq_lens (device int32): [num_seqs], total lengths including the chunk.
+ *   out (device fp32): [num_seqs][chunk_len][num_q_heads][Dv].
+ *   workspace (device): at least kv_prefill_attn_workspace_bytes(...) bytes,
+ *     256-byte aligned; holds the split partials, the virtual block table and
+ *     the virtual lengths.
+ *   num_splits: 0 = kv_prefill_attn_default_splits(...).
+ * Other arguments and errors as kv_decode_attn; KVQ_EUNSUPPORTED when
+ * num_seqs * chunk_len exceeds 2^24. */
+kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t chunk_len,
+                           int32_t num_q_heads, const kvq_cache *k, const kvq_cache *v,
+                           const int32_t *block_table, int32_t block_table_stride, const int32_t *seq_lens,
+                           int32_t max_seq_len, float sm_scale, int32_t num_splits, void *workspace,
+                           size_t workspace_bytes, float *out, hipStream_t stream);
+
+/* Workspace bytes of kv_prefill_attn (num_splits >= 1); 0 for invalid sizes. */
+size_t kv_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t chunk_len, int32_t num_q_heads,
+                                       int32_t head_dim_v, int32_t num_splits, int32_t block_table_stride);
+
+/* Split count kv_prefill_attn uses for num_splits = 0 (1 for invalid arguments). */
+int32_t kv_prefill_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs,
+                                       int32_t chunk_len, int32_t num_q_heads, int32_t max_seq_len);
+
 /* Static description of a status code. */
 const char *kvq_status_str(kvq_status s);
 

@@ -6,8 +6,9 @@ libkvq.so. PyTorch supplies device memory (tensor.data_ptr()) and the stream
 
     kvq_format_from_preset, kvq_cache_bytes, kv_quantize, kv_dequantize,
     kv_decode_attn_default_splits, kv_decode_attn_workspace_bytes,
-    kv_decode_attn, kv_append, kv_append_workspace_bytes, kv_quantize_kernel_name,
-    kv_decode_attn_kernel_name, kvq_status_str
+    kv_decode_attn, kv_append, kv_append_workspace_bytes, kv_prefill_attn,
+    kv_prefill_attn_workspace_bytes, kv_prefill_attn_default_splits,
+    kv_quantize_kernel_name, kv_decode_attn_kernel_name, kvq_status_str
 
 plus ``DeviceCache``, a holder of the four device arrays of one cache.
 Importing this module fails if libkvq.so has not been built: there is no
@@ -38,7 +39,8 @@ KVQ_TOKEN_MAJOR, KVQ_CHANNEL_MAJOR = 0, 1
 KVQ_FLAG_NONFINITE, KVQ_FLAG_SIDE_OVERFLOW = 1, 2
 
 EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_dequantize",
-           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_append", "kv_append_workspace_bytes",
+           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_append", "kv_append_workspace_bytes", "kv_prefill_attn",
+           "kv_prefill_attn_workspace_bytes", "kv_prefill_attn_default_splits",
            "kv_quantize_kernel_name", "kv_decode_attn_kernel_name", "kvq_status_str")
 
 
@@ -69,6 +71,10 @@ _sig = {
     "kv_append": (_i32, [ctypes.POINTER(kvq_cache), _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _sz, _vp,
                          _vp]),
     "kv_append_workspace_bytes": (_sz, [_i32]),
+    "kv_prefill_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _vp,
+                               _i32, _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
+    "kv_prefill_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "kv_prefill_attn_default_splits": (_i32, [ctypes.c_void_p, ctypes.c_void_p, _i32, _i32, _i32, _i32]),
     "kv_quantize_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(kvq_cache), _vp, _i32, _i64, _i64]),
     "kv_decode_attn_kernel_name": (ctypes.c_char_p, [_vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _i32]),
     "kvq_status_str": (ctypes.c_char_p, [_i32]),
@@ -198,6 +204,43 @@ def kv_append(dst: DeviceCache, tail, new_tokens, seq_lens, block_table, workspa
                           new_tokens.stride(0), new_tokens.stride(1), B, _ptr(seq_lens), _ptr(block_table),
                           block_table.shape[1], _ptr(workspace), workspace.numel() * workspace.element_size(),
                           _ptr(status_flags), _stream(stream)), "kv_append")
+
+
+def kv_prefill_attn_workspace_bytes(num_seqs: int, chunk_len: int, num_q_heads: int, head_dim_v: int,
+                                    num_splits: int, block_table_stride: int) -> int:
+    return int(_lib.kv_prefill_attn_workspace_bytes(num_seqs, chunk_len, num_q_heads, head_dim_v, num_splits,
+                                                    block_table_stride))
+
+
+def kv_prefill_attn_default_splits(k: DeviceCache, v: Optional[DeviceCache], num_seqs: int, chunk_len: int,
+                                   num_q_heads: int, max_seq_len: int) -> int:
+    return int(_lib.kv_prefill_attn_default_splits(ctypes.byref(k.struct),
+                                                   ctypes.byref(v.struct) if v is not None else None,
+                                                   num_seqs, chunk_len, num_q_heads, max_seq_len))
+
+
+def kv_prefill_attn(q, k: DeviceCache, v: Optional[DeviceCache], block_table, seq_lens, max_seq_len: int,
+                    sm_scale: float, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """q: [num_seqs][chunk_len][num_q_heads][D + R]; seq_lens include the chunk.
+    Returns out [num_seqs][chunk_len][num_q_heads][Dv] (fp32)."""
+    torch = _torch()
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [num_seqs][chunk_len][num_q_heads][D + R] tensor")
+    B, Lq, Hq = q.shape[0], q.shape[1], q.shape[2]
+    dv = (v or k).fmt.head_dim
+    if num_splits <= 0:
+        num_splits = kv_prefill_attn_default_splits(k, v, B, Lq, Hq, max_seq_len)
+    need = kv_prefill_attn_workspace_bytes(B, Lq, Hq, dv, num_splits, block_table.shape[1])
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Lq, Hq, dv), dtype=torch.float32, device=q.device)
+    _check(_lib.kv_prefill_attn(_ptr(q), _dtype_code(q), B, Lq, Hq, ctypes.byref(k.struct),
+                                ctypes.byref(v.struct) if v is not None else None, _ptr(block_table),
+                                block_table.shape[1], _ptr(seq_lens), max_seq_len, sm_scale, num_splits,
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                                _stream(stream)), "kv_prefill_attn")
+    return out
 
 
 def kv_quantize_kernel_name(dst: DeviceCache, src) -> Optional[str]:

@@ -267,4 +267,60 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
     return launched();
 }
 
+size_t kv_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t chunk_len, int32_t num_q_heads, int32_t head_dim_v,
+                                       int32_t num_splits, int32_t block_table_stride) {
+    if (num_seqs < 0 || chunk_len <= 0 || num_q_heads <= 0 || head_dim_v <= 0 || num_splits <= 0 ||
+        block_table_stride <= 0 || (int64_t)num_seqs * chunk_len > (1 << 24))
+        return 0;
+    const int32_t nv = num_seqs * chunk_len;
+    const size_t dec = (kv_decode_attn_workspace_bytes(nv, num_q_heads, head_dim_v, num_splits) + 255) & ~(size_t)255;
+    return dec + (size_t)nv * block_table_stride * sizeof(int32_t) + (size_t)nv * sizeof(int32_t);
+}
+
+int32_t kv_prefill_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs, int32_t chunk_len,
+                                       int32_t num_q_heads, int32_t max_seq_len) {
+    if (chunk_len <= 0 || (int64_t)num_seqs * chunk_len > (1 << 24)) return 1;
+    return kv_decode_attn_default_splits(k, v, num_seqs * chunk_len, num_q_heads, max_seq_len);
+}
+
+kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t chunk_len, int32_t num_q_heads,
+                           const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
+                           int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                           int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                           hipStream_t stream) {
+    kvq_status st = check_cache(k);
+    if (st != KVQ_OK) return st;
+    if (v && (st = check_cache(v)) != KVQ_OK) return st;
+    if (!q || !valid_dtype(q_dtype) || num_seqs < 0 || chunk_len <= 0 || num_q_heads <= 0 || !out || max_seq_len < 0)
+        return KVQ_EINVAL;
+    if ((int64_t)num_seqs * chunk_len > (1 << 24)) return KVQ_EUNSUPPORTED;
+    if (num_seqs == 0) return KVQ_OK;
+    if (!block_table || !seq_lens || block_table_stride <= 0 || num_splits < 0) return KVQ_EINVAL;
+    kvq::DecodeArgs a{};
+    if ((st = decode_layout(k, v, num_q_heads, a)) != KVQ_OK) return st;
+    if ((int64_t)block_table_stride * a.T < max_seq_len) return KVQ_EINVAL;
+    const int32_t nv = num_seqs * chunk_len;
+    a.B = nv;
+    const int splits = num_splits > 0 ? num_splits : kvq::decode_default_splits(a, max_seq_len);
+    if (!workspace || ((uintptr_t)workspace & 255) ||
+        workspace_bytes < kv_prefill_attn_workspace_bytes(num_seqs, chunk_len, num_q_heads, a.Dv, splits,
+                                                          block_table_stride))
+        return KVQ_EWORKSPACE;
+    const size_t dec = (kv_decode_attn_workspace_bytes(nv, num_q_heads, a.Dv, splits) + 255) & ~(size_t)255;
+    int32_t *vbt = (int32_t *)((char *)workspace + dec);
+    int32_t *vlens = vbt + (size_t)nv * block_table_stride;
+    kvq::PrefillArgs p{num_seqs, chunk_len, seq_lens, block_table, block_table_stride, vbt, vlens};
+    a.q = q;
+    a.q_dtype = (int)q_dtype;
+    a.bt = vbt;
+    a.bt_stride = block_table_stride;
+    a.seq_lens = vlens;
+    a.sm = sm_scale;
+    a.splits = splits;
+    a.ws = (float *)workspace;
+    a.out = out;
+    if (!kvq::launch_prefill(p, a, stream)) return KVQ_EUNSUPPORTED;
+    return launched();
+}
+
 }  // extern "C"

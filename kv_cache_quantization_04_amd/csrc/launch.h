@@ -60,8 +60,17 @@ struct AppendArgs {
     int32_t *tile_src_token, *tile_valid, *tile_dst_page;  // [num_seqs] each
 };
 
+// chunked prefill: virtual block table and lengths for B * Lq virtual sequences
+struct PrefillArgs {
+    int num_seqs, Lq;
+    const int32_t *seq_lens, *block_table;
+    int bt_stride;
+    int32_t *vbt, *vlens;  // workspace: [num_seqs * Lq][bt_stride], [num_seqs * Lq]
+};
+
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
 bool launch_append(const AppendArgs &a, int D, int T, const QuantArgs &q, hipStream_t stream);
+bool launch_prefill(const PrefillArgs &p, const DecodeArgs &d, hipStream_t stream);
 bool launch_dequant(int D, int T, int num_tiles, const DequantArgs &a, hipStream_t stream);
 bool launch_decode(const DecodeArgs &a, hipStream_t stream);
 // split-K partitions for a decode call whose fields other than q, block table,

@@ -191,3 +191,28 @@ def test_append_argument_errors():
     assert append_status(f, tail=FAKE + 8) == K.KVQ_EUNSUPPORTED        # the tail is a quantizer source
     bad = K.make_format(96, 0, 16, 32, 32, 4, 2, K.KVQ_TOKEN_MAJOR)
     assert append_status(bad) == K.KVQ_EUNSUPPORTED
+
+
+def prefill_status(fk, fv, num_seqs=2, chunk=4, hq=8, ws_bytes=1 << 20, ws=FAKE * 16, q=FAKE, max_len=64,
+                   bt_stride=4):
+    kc = cache_struct(fk, heads=2)
+    vc = cache_struct(fv, heads=2)
+    return K._lib.kv_prefill_attn(q, 2, num_seqs, chunk, hq, ctypes.byref(kc), ctypes.byref(vc), FAKE, bt_stride,
+                                  FAKE, max_len, 0.1, 1, ws, ws_bytes, FAKE, None)
+
+
+def test_prefill_argument_errors():
+    fk = K.make_format(128, 0, 16, 128, 128, 4, 2, K.KVQ_TOKEN_MAJOR)
+    fv = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_CHANNEL_MAJOR)
+    need = K._lib.kv_prefill_attn_workspace_bytes(2, 4, 8, 128, 1, 4)
+    # decode partials for 8 virtual sequences (256-byte rounded) + virtual table and lengths
+    assert need == ((8 * 8 * 1 * 130 * 4 + 255) // 256) * 256 + 8 * 4 * 4 + 8 * 4
+    assert K._lib.kv_prefill_attn_workspace_bytes(2, 0, 8, 128, 1, 4) == 0
+    assert prefill_status(fk, fv, num_seqs=0) == K.KVQ_OK
+    assert prefill_status(fk, fv, chunk=0) == K.KVQ_EINVAL
+    assert prefill_status(fk, fv, q=None) == K.KVQ_EINVAL
+    assert prefill_status(fk, fv, hq=5) == K.KVQ_EINVAL                 # not a multiple of the kv heads
+    assert prefill_status(fk, fv, bt_stride=2) == K.KVQ_EINVAL          # 2 pages of 16 < max_len 64
+    assert prefill_status(fk, fv, ws_bytes=need - 1) == K.KVQ_EWORKSPACE
+    assert prefill_status(fk, fv, ws=FAKE * 16 + 16) == K.KVQ_EWORKSPACE  # not 256-byte aligned
+    assert prefill_status(fk, fv, num_seqs=1 << 20, chunk=32) == K.KVQ_EUNSUPPORTED

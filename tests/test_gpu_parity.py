@@ -297,6 +297,46 @@ DEC_SMALL = [
 ]
 
 
+PREFILL = [
+    dict(T=16, lens=(300, 40, 77), kbits=3, vbits=3),                                # decode_mfma_kernel, staged pages
+    dict(T=128, lens=(600, 131), kbits=4, vbits=4, iters=4),                         # decode_mfma_kernel
+    dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(700, 140), iters=4),     # decode_mla_kernel
+    dict(T=64, D=64, lens=(256, 70), kbits=4, vbits=4, iters=4, Hq=2, Hkv=2, dtype="f32"),  # generic
+]
+
+
+@pytest.mark.parametrize("kw", PREFILL, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+@pytest.mark.parametrize("splits", [0, 3])
+def test_prefill_chunk_is_causal_decode(gpu, kw, splits):
+    """Chunk position i of sequence b equals the oracle's attention of that query over
+    the sequence's tokens 0 .. L_b - Lq + i (dequantize, then softmax attention)."""
+    log("prefill case", kw, "splits", splits)
+    w = small_paged(31 + len(kw), **kw)
+    rng = np.random.default_rng(zlib.crc32(repr(sorted(kw.items())).encode()))
+    B, Hq, Wd, Lq = len(w["lens"]), w["Hq"], w["fk"].head_dim + w["fk"].rope_dim, 9
+    q = make_src(rng.standard_normal((B, Lq, Hq, Wd)), w["dtype"])
+    sm = 1.0 / math.sqrt(Wd)
+    kc, _ = orc_quantize(w["fk"], w["ks"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
+    vc = None
+    if w["fv"] is not None:
+        vc, _ = orc_quantize(w["fv"], w["vs"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
+    vl = np.array([L - Lq + i + 1 for L in w["lens"] for i in range(Lq)])
+    ref = O.decode_attn(q.reshape(B * Lq, Hq, Wd), ORC_DT[w["dtype"]], kc, vc, np.repeat(w["bt"], Lq, axis=0), vl, sm,
+                        folded=False, nthreads=16)
+    dk = K.DeviceCache(kfmt(w["fk"]), w["P"], w["Hkv"])
+    upload(kc, dk)
+    dv = None
+    if vc is not None:
+        dv = K.DeviceCache(kfmt(w["fv"]), w["P"], w["Hkv"])
+        upload(vc, dv)
+    out = K.kv_prefill_attn(to_dev(q, w["dtype"]), dk, dv, i32(w["bt"]), i32(w["lens"]), int(w["lens"].max()), sm,
+                            num_splits=splits)
+    torch.cuda.synchronize()
+    err = rel_rowwise(out.cpu().numpy().astype(np.float64).reshape(B * Lq, Hq, -1), ref)
+    log("  prefill rel err", err)
+    assert err <= DECODE_RTOL
+
+
 @pytest.mark.parametrize("kw", DEC_SMALL, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) or "default")
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_decode_small(gpu, kw, splits):
