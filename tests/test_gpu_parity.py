@@ -153,6 +153,47 @@ def test_flags_latent_tile_rope_nonfinite(gpu):
     assert int(flags.item()) == fl
 
 
+# ----------------------------------------------------------------------------- the shipped preset, end to end
+def test_preset_k4v2_g128_end_to_end(gpu):
+    """The pages' preset string, parsed by the library: 4-bit keys, 2-bit values,
+    128-token tiles. GPU quantize of K and V against the oracle, then decode on
+    the GPU caches against the oracle's dequantize-then-attention on them."""
+    kf, vf = K.kvq_format_from_preset("kvarn_k4v2_g128", 128)
+    fk, fv = (W.Fmt(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
+              for f in (kf, vf))
+    assert (fk.bits, fv.bits, fk.tile_tokens, fk.layout, fv.layout) == (4, 2, 128, 0, 1)
+    rng = np.random.default_rng(zlib.crc32(b"kvarn_k4v2_g128"))
+    lens, Hq, Hkv = [700, 128, 5], 16, 4
+    tst, tv, tp, tok = tiles_for(lens, 128, rng)
+    P = len(tp)
+    ks = make_src(heavy(rng, tok, Hkv, 128), "bf16")
+    vs = make_src(rng.standard_normal((tok, Hkv, 128)), "bf16")
+    dk = gpu_quantize(fk, ks, "bf16", tst, tv, tp, P)
+    dv = gpu_quantize(fv, vs, "bf16", tst, tv, tp, P)
+    torch.cuda.synchronize()
+    for f, src, dc in ((fk, ks, dk), (fv, vs, dv)):
+        hc, fl = orc_quantize(f, src, "bf16", tst, tv, tp, P)
+        st = compare_blocks(host_copy(dc, f), hc, range(P))
+        log("  preset quantize", f.bits, st)
+        assert_block_parity(st, "preset")
+        assert fl == 0
+    npg = [(L + 127) // 128 for L in lens]
+    bt = np.zeros((len(lens), max(npg)), np.int32)
+    k = 0
+    for s_, n in enumerate(npg):
+        bt[s_, :n] = tp[k:k + n]
+        k += n
+    q = make_src(rng.standard_normal((len(lens), Hq, 128)), "bf16")
+    sm = 1.0 / math.sqrt(128)
+    out = K.kv_decode_attn(to_dev(q, "bf16"), dk, dv, i32(bt), i32(lens), max(lens), sm)
+    torch.cuda.synchronize()
+    ref = O.decode_attn(q, O.BF16, host_copy(dk, fk), host_copy(dv, fv), bt, np.array(lens), sm, folded=False,
+                        nthreads=16)
+    err = rel_rowwise(out.cpu().numpy().astype(np.float64), ref)
+    log("  preset decode rel err", err)
+    assert err <= DECODE_RTOL
+
+
 # ----------------------------------------------------------------------------- append path
 APPEND = [
     # D, R, T, bits, iters, dtype, layout: one format per quantizer kernel
