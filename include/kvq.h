@@ -70,6 +70,11 @@ typedef struct {
     int32_t bits;        /* code width: 2, 3, 4 or 8                                     */
     int32_t iters;       /* normalization rounds (row step then column step), >= 0       */
     int32_t layout;      /* KVQ_TOKEN_MAJOR (keys) or KVQ_CHANNEL_MAJOR (values)          */
+    int32_t center;      /* 0: each round scales rows, then columns, to unit RMS about
+                            zero (the default reading of the pages' "variance");
+                            1: to unit standard deviation about their mean. Only the
+                            quantizer reads it; the stored data mean the same either
+                            way. 1 runs on the general quantizer kernel only.         */
 } kvq_format;
 
 /* One paged quantized cache (K, V, or the MLA latent). Byte layout, per
@@ -95,7 +100,7 @@ typedef struct {
  * kvarn_k4v2_g128: 4-bit keys, 2-bit values, 128-token tiles; "KVarN"
  * project review, Key Features, "4-bit Keys, 2-bit Values Preset"). Sets
  * head_dim, tile_tokens and bits; hadamard_n = group = head_dim, iters = 4,
- * rope_dim = 0; keys token-major, values channel-major.
+ * rope_dim = 0, center = 0; keys token-major, values channel-major.
  * Returns KVQ_EINVAL for a malformed string or null pointers. */
 kvq_status kvq_format_from_preset(const char *preset, int32_t head_dim, kvq_format *k, kvq_format *v);
 

@@ -46,7 +46,7 @@ EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_dequa
 
 class kvq_format(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("head_dim", "rope_dim", "tile_tokens", "hadamard_n", "group", "bits", "iters", "layout")]
+                ("head_dim", "rope_dim", "tile_tokens", "hadamard_n", "group", "bits", "iters", "layout", "center")]
 
     def __repr__(self):
         return "kvq_format(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -122,8 +122,8 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def make_format(head_dim, rope_dim, tile_tokens, hadamard_n, group, bits, iters, layout) -> kvq_format:
-    return kvq_format(head_dim, rope_dim, tile_tokens, hadamard_n, group, bits, iters, layout)
+def make_format(head_dim, rope_dim, tile_tokens, hadamard_n, group, bits, iters, layout, center=0) -> kvq_format:
+    return kvq_format(head_dim, rope_dim, tile_tokens, hadamard_n, group, bits, iters, layout, center)
 
 
 def kvq_format_from_preset(preset: str, head_dim: int):

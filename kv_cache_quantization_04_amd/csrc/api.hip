@@ -24,6 +24,7 @@ kvq_status check_format(const kvq_format *f) {
     if (f->group % 8 != 0) return KVQ_EUNSUPPORTED;
     if (f->rope_dim % 8 != 0) return KVQ_EUNSUPPORTED;
     if (f->iters > 64) return KVQ_EUNSUPPORTED;
+    if (f->center != 0 && f->center != 1) return KVQ_EINVAL;
     return KVQ_OK;
 }
 
@@ -103,7 +104,7 @@ kvq::QuantArgs quant_args(const kvq_cache *dst, const void *src, kvq_dtype src_d
     const kvq_format &f = dst->fmt;
     return kvq::QuantArgs{src, (int)src_dtype, stride_token, stride_head, tile_src_token, tile_valid, tile_dst_page,
                           dst->codes, dst->sz, dst->cnorm, dst->rope, dst->num_heads, f.hadamard_n, f.group, f.bits,
-                          f.iters, f.layout, f.rope_dim, dst->num_pages, status_flags};
+                          f.iters, f.layout, f.rope_dim, dst->num_pages, status_flags, f.center};
 }
 
 }  // namespace
@@ -127,8 +128,8 @@ kvq_status kvq_format_from_preset(const char *preset, int32_t head_dim, kvq_form
     if (std::sscanf(preset, "kvarn_k%dv%d_g%d%n", &bk, &bv, &T, &used) != 3 || preset[used] != '\0')
         return KVQ_EINVAL;
     if (bk <= 0 || bv <= 0 || T <= 0) return KVQ_EINVAL;
-    *k = kvq_format{head_dim, 0, T, head_dim, head_dim, bk, 4, KVQ_TOKEN_MAJOR};
-    *v = kvq_format{head_dim, 0, T, head_dim, head_dim, bv, 4, KVQ_CHANNEL_MAJOR};
+    *k = kvq_format{head_dim, 0, T, head_dim, head_dim, bk, 4, KVQ_TOKEN_MAJOR, 0};
+    *v = kvq_format{head_dim, 0, T, head_dim, head_dim, bv, 4, KVQ_CHANNEL_MAJOR, 0};
     return KVQ_OK;
 }
 

@@ -15,6 +15,7 @@ struct QuantArgs {
     uint16_t *sz, *cnorm, *rope;
     int H, h, G, bits, iters, layout, R, num_pages;
     uint32_t *flags;
+    int center;  // 1: rounds use the standard deviation about the mean
 };
 
 struct DequantArgs {

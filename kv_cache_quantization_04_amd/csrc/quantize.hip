@@ -138,7 +138,82 @@ __global__ void __launch_bounds__(2 * D) quantize_kernel(QuantArgs a) {
     for (int k = 0; k < RR; ++k) u[k] = 1.f;
     float csq = 1.f;  // c^2 of channel tid (tid < D)
 
-    for (int it = 0; it < a.iters; ++it) {
+    if (a.center) {
+        // Centered rounds: each step divides by the standard deviation about the
+        // row's (column's) mean. With sr = 1/r and vc = 1/c, Z = Y sr vc; a row step
+        // sets sr_i = 1 / std_j(Y_ij vc_j), a column step vc_j = 1 / std_i(Y_ij sr_i)
+        // over the n valid rows (two passes each: mean, then squared deviations).
+        float sr[RR], vc[8];
+#pragma unroll
+        for (int k = 0; k < RR; ++k) sr[k] = 1.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vc[j] = 1.f;
+        for (int it = 0; it < a.iters; ++it) {
+#pragma unroll
+            for (int k = 0; k < RR; ++k) {
+                float m = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m += y[k][j] * vc[j];
+#pragma unroll
+                for (int mm = 1; mm < LPR; mm <<= 1) m += xor_shfl(m, mm);
+                m *= 1.0f / (float)D;
+                float v = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float d = y[k][j] * vc[j] - m;  // z - mean, as rounded z: exact 0 for a constant row
+                    v = __builtin_fmaf(d, d, v);
+                }
+#pragma unroll
+                for (int mm = 1; mm < LPR; mm <<= 1) v += xor_shfl(v, mm);
+                v *= 1.0f / (float)D;
+                if (v > 0.f && isfinite(v)) sr[k] = 1.0f / sqrtf(v);
+            }
+            // column mean over the valid rows
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float t = 0.f;
+#pragma unroll
+                for (int k = 0; k < RR; ++k)
+                    if (rg * RR + k < n) t += y[k][j] * sr[k];
+                colpart[rg][cc * 8 + j] = t;
+            }
+            __syncthreads();
+            if (tid < D) {
+                float t = 0.f;
+#pragma unroll
+                for (int g = 0; g < NRG; ++g) t += colpart[g][tid];
+                wsh[tid] = n > 0 ? t / (float)n : 0.f;
+            }
+            __syncthreads();
+            float cm[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cm[j] = wsh[cc * 8 + j];
+            // column variance about that mean
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float t = 0.f;
+#pragma unroll
+                for (int k = 0; k < RR; ++k)
+                    if (rg * RR + k < n) {
+                        const float d = y[k][j] * sr[k] - cm[j];  // exact 0 for a single valid row
+                        t = __builtin_fmaf(d, d, t);
+                    }
+                colpart[rg][cc * 8 + j] = t;
+            }
+            __syncthreads();
+            if (tid < D) {
+                float t = 0.f;
+#pragma unroll
+                for (int g = 0; g < NRG; ++g) t += colpart[g][tid];
+                if (n > 0 && t > 0.f && isfinite(t)) csq = t / (float)n;  // c_j = std (new)
+                wsh[tid] = 1.0f / sqrtf(csq);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vc[j] = wsh[cc * 8 + j];
+        }
+    }
+    for (int it = 0; it < (a.center ? 0 : a.iters); ++it) {
         // row step: r_i^2 = mean_j A_ij / c_j^2
 #pragma unroll
         for (int k = 0; k < RR; ++k) {

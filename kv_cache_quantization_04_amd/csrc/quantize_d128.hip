@@ -400,6 +400,7 @@ __global__ void __launch_bounds__(16 * T / R, 4) quantize_d128_kernel(QuantArgs 
 bool quantize_d128_supported(int D, int T, const QuantArgs &a) {
     // the per-lane source offset (up to 3 token strides) is kept in 32 bits
     return D == QD && (T == 64 || T == 128) && a.h == QD && a.G == QD && a.R == 0 && a.dtype == KVQ_BF16 &&
+           a.center == 0 &&
            a.stride_token < (int64_t(1) << 28) &&
            (a.bits == 2 || a.bits == 4) && (a.layout == KVQ_TOKEN_MAJOR || a.layout == KVQ_CHANNEL_MAJOR);
 }

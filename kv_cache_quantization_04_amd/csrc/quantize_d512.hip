@@ -354,6 +354,7 @@ __global__ void __launch_bounds__(LNT) quantize_d512_kernel(QuantArgs a, int num
 bool quantize_d512_supported(int D, int T, const QuantArgs &a) {
     auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
     return D == LD && T == LT && a.h == LD && a.G == LD && (a.R == 0 || a.R == 64) && a.dtype == KVQ_BF16 &&
+           a.center == 0 &&
            (a.bits == 2 || a.bits == 4) && a.layout == KVQ_TOKEN_MAJOR && a.stride_token < (int64_t(1) << 40) &&
            al16(a.codes) && (a.R == 0 || al16(a.rope));
 }

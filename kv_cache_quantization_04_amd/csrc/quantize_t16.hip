@@ -276,7 +276,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
 }
 
 bool quantize_t16_supported(int D, int T, const QuantArgs &a) {
-    return D == ZD && T == ZT && a.h == ZD && a.G == ZD && a.R == 0 && a.dtype == KVQ_BF16 &&
+    return D == ZD && T == ZT && a.h == ZD && a.G == ZD && a.R == 0 && a.dtype == KVQ_BF16 && a.center == 0 &&
            (a.bits == 2 || a.bits == 3 || a.bits == 4) &&
            (a.layout == KVQ_TOKEN_MAJOR || a.layout == KVQ_CHANNEL_MAJOR) && a.stride_token < (int64_t(1) << 40) &&
            ((uintptr_t)a.codes & 15) == 0 && ((uintptr_t)a.cnorm & 3) == 0;

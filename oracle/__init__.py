@@ -22,7 +22,7 @@ FLAG_NONFINITE, FLAG_SIDE_OVERFLOW = 1, 2
 
 class OrcFormat(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("head_dim", "rope_dim", "tile_tokens", "hadamard_n", "group", "bits", "iters", "layout")]
+                ("head_dim", "rope_dim", "tile_tokens", "hadamard_n", "group", "bits", "iters", "layout", "center")]
 
 
 class OrcCache(ctypes.Structure):
@@ -46,7 +46,7 @@ def lib():
             "orc_double_to_bf16": (ctypes.c_uint16, [f64]),
             "orc_hadamard_matrix": (None, [i32, vp]),
             "orc_rotate": (None, [vp, i32, i32, i32, vp]),
-            "orc_normalizers": (None, [vp, i32, i32, i32, vp, vp]),
+            "orc_normalizers": (None, [vp, i32, i32, i32, i32, vp, vp]),
             "orc_quantize_tile": (ctypes.c_uint32, [vp, i32, vp, vp, vp, vp, vp]),
             "orc_pack": (None, [vp, vp, vp]),
             "orc_unpack": (None, [vp, vp, vp]),
@@ -68,7 +68,8 @@ def _p(a: Optional[np.ndarray]):
 
 
 def fmt_struct(f) -> OrcFormat:
-    return OrcFormat(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
+    return OrcFormat(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout,
+                     getattr(f, "center", 0))
 
 
 def half_to_double(h: int) -> float:
@@ -108,12 +109,12 @@ def rotate(x: np.ndarray, h: int) -> np.ndarray:
     return out
 
 
-def normalizers(xr: np.ndarray, iters: int):
+def normalizers(xr: np.ndarray, iters: int, center: int = 0):
     xr = np.ascontiguousarray(xr, dtype=np.float64)
     n, D = xr.shape
     c = np.empty(D, np.float64)
     r = np.empty(max(n, 1), np.float64)
-    lib().orc_normalizers(xr.ctypes.data, n, D, iters, c.ctypes.data, r.ctypes.data)
+    lib().orc_normalizers(xr.ctypes.data, n, D, iters, center, c.ctypes.data, r.ctypes.data)
     return c, r[:n]
 
 

@@ -111,16 +111,23 @@ void rotate_rows(const double *x, int n, int D, int h, double *out) {
 /* iterative, equalizes variance across the tile; [TAG] KVarN item: dual-axis).*/
 /* Reading: "variance" is the second moment about zero (RMS); one round is a  */
 /* row step then a column step; a factor that is zero or not finite is        */
-/* replaced by one. Only the valid n rows take part.                          */
+/* replaced by one. Only the valid n rows take part. With center = 1 (the     */
+/* other reading of "variance") each step uses the standard deviation about   */
+/* the row's / column's mean instead; the means are not removed from the data.*/
 /* ------------------------------------------------------------------------ */
-void normalizers(const double *xr, int n, int D, int iters, double *c, double *r) {
+void normalizers(const double *xr, int n, int D, int iters, int center, double *c, double *r) {
     std::vector<double> rr(std::max(n, 1), 1.0);
     for (int j = 0; j < D; ++j) c[j] = 1.0;
     for (int it = 0; it < iters; ++it) {
-        for (int i = 0; i < n; ++i) { /* row step: each row of X'/(r c) to unit RMS */
+        for (int i = 0; i < n; ++i) { /* row step: each row of Z = X'/(r c) to unit RMS (or std) */
+            double mu = 0.0;
+            if (center) {
+                for (int j = 0; j < D; ++j) mu += xr[(size_t)i * D + j] / (rr[i] * c[j]);
+                mu /= D;
+            }
             double s = 0.0;
             for (int j = 0; j < D; ++j) {
-                const double z = xr[(size_t)i * D + j] / (rr[i] * c[j]);
+                const double z = xr[(size_t)i * D + j] / (rr[i] * c[j]) - mu;
                 s += z * z;
             }
             double rho = std::sqrt(s / D);
@@ -128,10 +135,15 @@ void normalizers(const double *xr, int n, int D, int iters, double *c, double *r
             rr[i] *= rho;
         }
         if (n == 0) continue;
-        for (int j = 0; j < D; ++j) { /* column step: each column of X'/(r c) to unit RMS */
+        for (int j = 0; j < D; ++j) { /* column step: each column of Z to unit RMS (or std) */
+            double mu = 0.0;
+            if (center) {
+                for (int i = 0; i < n; ++i) mu += xr[(size_t)i * D + j] / (rr[i] * c[j]);
+                mu /= n;
+            }
             double s = 0.0;
             for (int i = 0; i < n; ++i) {
-                const double z = xr[(size_t)i * D + j] / (rr[i] * c[j]);
+                const double z = xr[(size_t)i * D + j] / (rr[i] * c[j]) - mu;
                 s += z * z;
             }
             double gam = std::sqrt(s / n);
@@ -211,8 +223,8 @@ void orc_hadamard_matrix(int32_t h, double *out) {
 
 void orc_rotate(const double *x, int32_t n, int32_t D, int32_t h, double *out) { rotate_rows(x, n, D, h, out); }
 
-void orc_normalizers(const double *xr, int32_t n, int32_t D, int32_t iters, double *c, double *r) {
-    normalizers(xr, n, D, iters, c, r);
+void orc_normalizers(const double *xr, int32_t n, int32_t D, int32_t iters, int32_t center, double *c, double *r) {
+    normalizers(xr, n, D, iters, center, c, r);
 }
 
 uint32_t orc_quantize_tile(const double *x, int32_t n, const orc_format *f, uint16_t *codes, uint16_t *sz,
@@ -229,7 +241,7 @@ uint32_t orc_quantize_tile(const double *x, int32_t n, const orc_format *f, uint
     /* 2. per-channel normalizer c (the row factors only re-scale each token,
      *    which the per-token scale and zero absorb, so they are not stored) */
     std::vector<double> c(D);
-    normalizers(xr.data(), n, D, f->iters, c.data(), nullptr);
+    normalizers(xr.data(), n, D, f->iters, f->center, c.data(), nullptr);
     std::vector<double> cval(D);
     for (int j = 0; j < D; ++j) {
         c16[j] = to_half(c[j]);

@@ -49,6 +49,8 @@ typedef struct {
     int32_t bits;        /* b: code width                                       */
     int32_t iters;       /* N: row/column normalization rounds                  */
     int32_t layout;      /* ORC_TOKEN_MAJOR or ORC_CHANNEL_MAJOR                */
+    int32_t center;      /* 0: rounds scale rows/columns to unit RMS about zero;
+                            1: to unit standard deviation about their mean      */
 } orc_format;
 
 /* Host-memory paged quantized cache. Per (page p, head h):
@@ -76,7 +78,7 @@ uint16_t orc_double_to_bf16(double x);
 /* ---- tile-level steps ---- */
 void orc_hadamard_matrix(int32_t h, double *out /* h*h, row-major */);
 void orc_rotate(const double *x, int32_t n, int32_t D, int32_t h, double *out);
-void orc_normalizers(const double *xr, int32_t n, int32_t D, int32_t iters,
+void orc_normalizers(const double *xr, int32_t n, int32_t D, int32_t iters, int32_t center,
                      double *c /* [D] */, double *r /* [n] or NULL */);
 /* Quantize one tile of n valid rows (n <= T) of D channels (rope excluded).
  * codes: [T][D] unpacked integer codes (rows >= n zero); sz: [T][D/G][2];

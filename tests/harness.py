@@ -33,7 +33,8 @@ ORC_DT = {"f32": O.F32, "bf16": O.BF16, "f16": O.F16}
 
 
 def kfmt(f: W.Fmt) -> K.kvq_format:
-    return K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
+    return K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout,
+                         f.center)
 
 
 def to_dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:

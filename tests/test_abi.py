@@ -216,3 +216,13 @@ def test_prefill_argument_errors():
     assert prefill_status(fk, fv, ws_bytes=need - 1) == K.KVQ_EWORKSPACE
     assert prefill_status(fk, fv, ws=FAKE * 16 + 16) == K.KVQ_EWORKSPACE  # not 256-byte aligned
     assert prefill_status(fk, fv, num_seqs=1 << 20, chunk=32) == K.KVQ_EUNSUPPORTED
+
+
+def test_center_field():
+    ok = K.make_format(128, 0, 128, 128, 128, 4, 4, 0, 1)
+    assert ctypes.sizeof(K.kvq_format) == 36
+    assert quantize_kernel(ok, K.KVQ_BF16) == "quantize_kernel"          # the centered rounds: general kernel
+    bad = K.make_format(128, 0, 128, 128, 128, 4, 4, 0, 2)
+    assert quantize_status(bad) == K.KVQ_EINVAL
+    k, v = K.kvq_format_from_preset("kvarn_k4v2_g128", 128)
+    assert k.center == 0 and v.center == 0

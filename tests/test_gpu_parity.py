@@ -89,14 +89,35 @@ SMALL = [
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "D{}T{}b{}G{}h{}N{}{}L{}R{}".format(*c))
 def test_quantize_every_element(gpu, case):
+    check_quantize_case(gpu, case)
+
+
+# the other reading of "variance": rounds on the standard deviation about the mean
+CENTERED = [
+    (128, 128, 4, 128, 128, 4, "bf16", 0, 0),
+    (128, 16, 3, 128, 128, 2, "bf16", 1, 0),
+    (64, 64, 4, 32, 64, 4, "f32", 0, 0),
+    (512, 128, 4, 512, 512, 4, "bf16", 0, 64),
+]
+
+
+@pytest.mark.parametrize("case", CENTERED, ids=lambda c: "D{}T{}b{}G{}h{}N{}{}L{}R{}".format(*c))
+def test_quantize_centered_every_element(gpu, case):
+    check_quantize_case(gpu, case, center=1)
+
+
+def check_quantize_case(gpu, case, center=0):
     D, T, bits, G, h, iters, dtype, layout, R = case
-    log("quantize case", case)
-    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
-    f = W.Fmt(D, R, T, h, G, bits, iters, layout)
+    log("quantize case", case, "center", center)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + center)
+    f = W.Fmt(D, R, T, h, G, bits, iters, layout, center)
     H = 2
     lens = [3 * T + T // 2 + 1, 1, T, 0] if T <= 64 else [2 * T + 37, 1, T]
     tst, tv, tp, tok = tiles_for(lens, T, rng)
-    x = np.concatenate([heavy(rng, tok, H, D), rng.standard_normal((tok, H, R))], axis=2) if R else heavy(rng, tok, H, D)
+    xl = heavy(rng, tok, H, D)
+    if center:  # per-channel offsets, so that column and row means are far from zero
+        xl = xl + 3.0 * rng.standard_normal((1, H, D))
+    x = np.concatenate([xl, rng.standard_normal((tok, H, R))], axis=2) if R else xl
     src = make_src(x, dtype)
     P = len(tp)
     flags = torch.zeros(1, dtype=torch.int32, device=gpu)

@@ -457,3 +457,53 @@ def test_full_chain_against_independent_recomputation(bits, iters, G):
         assert np.array_equal(sz[:, g, 0], S) and np.array_equal(sz[:, g, 1], Z)
         d = codes[:, g * G:(g + 1) * G].astype(int) - q
         assert np.abs(d).max() <= 1 and (d != 0).mean() < 1e-3
+
+
+# ---------------------------------------------------------------- centered variant (rounds use std about the mean)
+def test_centered_normalizers_hand_example():
+    # X' = [[1, 3], [0, 4]], one round. Rows: (1, 3) has mean 2 and std 1 -> r0 = 1;
+    # (0, 4) has mean 2 and std 2 -> r1 = 2. Columns of X'/r: (1, 0) -> std 0.5;
+    # (3, 2) -> std 0.5. So c = (0.5, 0.5), r = (1, 2).
+    c, r = O.normalizers(np.array([[1.0, 3.0], [0.0, 4.0]]), 1, center=1)
+    assert np.allclose(c, [0.5, 0.5], rtol=0, atol=1e-15)
+    assert np.allclose(r, [1.0, 2.0], rtol=0, atol=1e-15)
+
+
+def test_centered_normalizers_steady_state():
+    """Z = X'/(r c) after many rounds is left unchanged by a further round. A row step
+    (rows / rho_i) followed by a column step (columns / gamma_j) maps Z to itself only if
+    rho_i gamma_j = 1 for all i, j: every row has the same std rho and every column std 1
+    (after the column step). With offsets in the tile rho != 1, and then r grows and c
+    shrinks by rho per round (their product, and Z, stay fixed)."""
+    rng = np.random.default_rng(3)
+    n, D = 24, 32
+    xr = rng.standard_normal((n, D)) * np.exp(rng.standard_normal(D))[None] + 3.0 * rng.standard_normal(D)[None]
+    xr += 2.0 * rng.standard_normal(n)[:, None]            # row and column offsets: means far from zero
+    c, r = O.normalizers(xr, 300, center=1)                # the shape converges geometrically
+    z = xr / (r[:, None] * c[None, :])
+    rs = z.std(axis=1)
+    assert np.allclose(z.std(axis=0), 1.0, atol=1e-9)     # the last step was the column step
+    assert rs.max() - rs.min() < 1e-9                      # one common row std
+    assert abs(rs[0] - 1.0) > 0.1                          # ... which is not 1 for this tile
+    c1, r1 = O.normalizers(xr, 301, center=1)
+    assert np.allclose(c / c1, rs[0], rtol=1e-9) and np.allclose(r1 / r, rs[0], rtol=1e-9)
+    # the uncentered rounds on the same tile reach unit RMS columns (a fixed point)
+    cu, ru = O.normalizers(xr, 60, center=0)
+    zu = xr / (ru[:, None] * cu[None, :])
+    assert np.allclose(np.sqrt((zu ** 2).mean(axis=0)), 1.0, atol=1e-12)
+
+
+def test_centered_normalizers_scale_equivariant():
+    rng = np.random.default_rng(4)
+    xr = rng.standard_normal((16, 64)) + 1.5
+    c1, _ = O.normalizers(xr, 4, center=1)
+    c2, _ = O.normalizers(xr * 2.0 ** 7, 4, center=1)     # the row step absorbs a common factor
+    assert np.allclose(c1, c2, rtol=1e-13, atol=0)
+
+
+def test_centered_equals_uncentered_on_zero_mean_tiles():
+    # a +-1 checkerboard: every row and column has mean 0 and RMS 1 at every round
+    xr = np.fromfunction(lambda i, j: (-1.0) ** (i + j), (8, 16))
+    c1, r1 = O.normalizers(xr, 3, center=1)
+    c0, r0 = O.normalizers(xr, 3, center=0)
+    assert np.array_equal(c1, c0) and np.array_equal(r1, r0) and np.array_equal(c1, np.ones(16))

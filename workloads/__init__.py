@@ -107,6 +107,7 @@ class Fmt:
     bits: int
     iters: int
     layout: int
+    center: int = 0   # 1: rounds normalize to unit std about the mean (else RMS about zero)
 
     def code_bytes(self) -> int:          # per (page, head)
         return self.tile_tokens * self.head_dim * self.bits // 8
