@@ -178,49 +178,101 @@ __global__ void __launch_bounds__(DEC_NT) decode_generic_kernel(DecodeArgs a) {
 }
 
 // Merge the split partials of one (sequence, query head), normalize, rotate back.
-// The split weights exp(m_i - M) / l are formed once in LDS, then every output
-// channel is one pass of fused multiply-adds over the splits.
+// One wave per (sequence, query head), no workgroup barriers: lane l owns the
+// E = Dv / 64 consecutive channels E l .. E l + E - 1. The lanes load the split
+// maxima and sums in parallel (split i on lane i mod 64), reduce them across the
+// wave, and leave the weights exp(m_i - M) in a wave-private LDS array; the
+// output pass then streams the partial outputs with independent loads. The
+// inverse rotation runs in registers (channel bits below E) and across lanes.
 constexpr int RED_MAX_SPLITS = 1024;
+constexpr int RED_WAVES = 4;
 
-__global__ void __launch_bounds__(DEC_NT) decode_reduce_kernel(DecodeArgs a) {
-    extern __shared__ float buf[];  // [Dv] outputs, then [splits] weights
-    __shared__ float red[DEC_NT / 64];
-    const int hq = blockIdx.x, s = blockIdx.y;
-    const int Dv = a.Dv, tid = threadIdx.x;
-    float *wgt = buf + Dv;
+__device__ __forceinline__ float wave_max(float v) {
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <int E>
+__device__ __forceinline__ void reduce_one(const DecodeArgs &a, int s, int hq, int lane, float *wgt) {
+    constexpr int Dv = 64 * E;
     const float *w = a.ws + ((int64_t)s * a.Hq + hq) * a.splits * (Dv + 2);
-    // M = max_i m_i
     float M = -INFINITY;
-    for (int i = tid; i < a.splits; i += DEC_NT) M = fmaxf(M, w[(int64_t)i * (Dv + 2) + Dv]);
-    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = M;
-    __syncthreads();
-    M = red[0];
-    for (int i = 1; i < DEC_NT / 64; ++i) M = fmaxf(M, red[i]);
-    __syncthreads();
-    // weights e_i = exp(m_i - M) and l = sum_i e_i l_i
+    for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, w[(int64_t)i * (Dv + 2) + Dv]);
+    M = wave_max(M);
     float l = 0.f;
-    for (int i = tid; i < a.splits; i += DEC_NT) {
+    for (int i = lane; i < a.splits; i += 64) {
         const float mi = w[(int64_t)i * (Dv + 2) + Dv];
         const float e = mi == -INFINITY ? 0.f : __expf(mi - M);
         wgt[i] = e;
         l = __builtin_fmaf(e, w[(int64_t)i * (Dv + 2) + Dv + 1], l);
     }
-    for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m, 64);
-    if ((tid & 63) == 0) red[tid >> 6] = l;
-    __syncthreads();
-    l = 0.f;
-    for (int i = 0; i < DEC_NT / 64; ++i) l += red[i];
-    const float invl = l > 0.f ? 1.0f / l : 0.f;
-    for (int j = tid; j < Dv; j += DEC_NT) {
-        float acc = 0.f;
-        for (int i = 0; i < a.splits; ++i) acc = __builtin_fmaf(wgt[i], w[(int64_t)i * (Dv + 2) + j], acc);
-        buf[j] = acc * invl;
+    l = wave_sum(l);  // the weights' LDS writes are ordered before the reads below (one wave)
+    float acc[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < a.splits; ++i) {
+        const float *wi = w + (int64_t)i * (Dv + 2) + E * lane;
+        const float e = wgt[i];
+#pragma unroll
+        for (int k = 0; k < E; k += (E > 1 ? 2 : 1)) {
+            if constexpr (E == 1) acc[0] = __builtin_fmaf(e, wi[0], acc[0]);
+            else {
+                const float2 v = *reinterpret_cast<const float2 *>(wi + k);
+                acc[k] = __builtin_fmaf(e, v.x, acc[k]);
+                acc[k + 1] = __builtin_fmaf(e, v.y, acc[k + 1]);
+            }
+        }
     }
-    __syncthreads();
-    lds_fwht(buf, 1, Dv, a.vh);
-    const float sc = 1.0f / sqrtf((float)a.vh);
-    for (int j = tid; j < Dv; j += DEC_NT) a.out[((int64_t)s * a.Hq + hq) * Dv + j] = buf[j] * sc;
+    const float invl = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] *= invl;
+    // Walsh-Hadamard over blocks of vh channels: channel c = E lane + k
+    for (int len = 1; len < a.vh; len <<= 1) {
+        if (len < E) {
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                if (!(k & len) && (k | len) < E) {
+                    const float x = acc[k], y = acc[k | len];
+                    acc[k] = x + y;
+                    acc[k | len] = x - y;
+                }
+        } else {
+            const int m = len / E;  // partner lane
+            const bool upper = (lane & m) != 0;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const float pv = __shfl_xor(acc[k], m, 64);
+                acc[k] = upper ? pv - acc[k] : acc[k] + pv;
+            }
+        }
+    }
+    const float scl = 1.0f / sqrtf((float)a.vh);
+    float *out = a.out + ((int64_t)s * a.Hq + hq) * Dv + E * lane;
+#pragma unroll
+    for (int k = 0; k < E; ++k) out[k] = acc[k] * scl;
+}
+
+__global__ void __launch_bounds__(64 * RED_WAVES) decode_reduce_kernel(DecodeArgs a) {
+    __shared__ float wgt[RED_WAVES][RED_MAX_SPLITS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int hq = blockIdx.x * RED_WAVES + wave, s = blockIdx.y;
+    if (hq >= a.Hq) return;  // whole wave
+    switch (a.Dv) {
+    case 64: reduce_one<1>(a, s, hq, lane, wgt[wave]); break;
+    case 128: reduce_one<2>(a, s, hq, lane, wgt[wave]); break;
+    case 256: reduce_one<4>(a, s, hq, lane, wgt[wave]); break;
+    default: reduce_one<8>(a, s, hq, lane, wgt[wave]); break;  // 512
+    }
+}
+
+static void launch_reduce(const DecodeArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3((a.Hq + RED_WAVES - 1) / RED_WAVES, a.B), dim3(64 * RED_WAVES), 0,
+                       stream, a);
 }
 
 bool decode_mfma_supported(const DecodeArgs &a);
@@ -263,14 +315,12 @@ bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.splits > RED_MAX_SPLITS) return false;
     if (decode_mla_supported(a)) {
         if (!launch_decode_mla(a, stream)) return false;
-        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * (a.Dv + a.splits),
-                           stream, a);
+        launch_reduce(a, stream);
         return true;
     }
     if (decode_mfma_supported(a)) {
         if (!launch_decode_mfma(a, stream)) return false;
-        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * (a.Dv + a.splits),
-                           stream, a);
+        launch_reduce(a, stream);
         return true;
     }
     const size_t smem = sizeof(float) * (2 * a.hc * a.D + a.hc * (a.D / a.kG) + a.hc * a.R + a.hc * a.T + 3 * a.hc);
@@ -280,8 +330,7 @@ bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
             hipSuccess)
         return false;
     hipLaunchKernelGGL(decode_generic_kernel, dim3(a.splits, a.Hkv * a.nhc, a.B), dim3(DEC_NT), smem, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.Hq, a.B), dim3(DEC_NT), sizeof(float) * (a.Dv + a.splits), stream,
-                       a);
+    launch_reduce(a, stream);
     return true;
 }
 
