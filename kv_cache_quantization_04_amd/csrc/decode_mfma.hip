@@ -271,6 +271,19 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
         const int rows = min(T, L - cur * T);
         const int64_t kblk = (int64_t)page * a.Hkv + hk;
+        // the page's K code words of every M-tile, issued now so that they travel
+        // while the query is folded (a page in HBM, not staged)
+        const uint8_t *kbase = STAGED ? &stg[wave][PI::O_KC] : a.kcodes + kblk * (T * MD * KB / 8);
+        uint32_t kpre[MT][KB];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            int tok;
+            if constexpr (T >= 32) tok = 32 * (j >> 1) + 8 * (l16 >> 2) + 4 * (j & 1) + (l16 & 3);
+            else tok = 8 * ((l16 >> 2) & 1) + 4 * (l16 >> 3) + (l16 & 3);
+            const uint8_t *row = kbase + tok * (MD * KB / 8) + lq * KCB;
+#pragma unroll
+            for (int i = 0; i < KB; ++i) kpre[j][i] = reinterpret_cast<const uint32_t *>(row)[i];
+        }
 
         // c_K of the lane's 32 channels (lq*32 ..)
         const uint4 *cp = STAGED ? reinterpret_cast<const uint4 *>(&stg[wave][PI::O_KCN + 64 * lq])
@@ -310,17 +323,10 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
 
         // ---- scores: one MFMA chain per 16-token M-tile
-        const uint8_t *kbase = STAGED ? &stg[wave][PI::O_KC] : a.kcodes + kblk * (T * MD * KB / 8);
         f32x4 sc[MT];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
-            int tok;
-            if constexpr (T >= 32) tok = 32 * (j >> 1) + 8 * (l16 >> 2) + 4 * (j & 1) + (l16 & 3);
-            else tok = 8 * ((l16 >> 2) & 1) + 4 * (l16 >> 3) + (l16 & 3);
-            const uint8_t *row = kbase + tok * (MD * KB / 8) + lq * KCB;
-            uint32_t kw[KB];
-#pragma unroll
-            for (int i = 0; i < KB; ++i) kw[i] = reinterpret_cast<const uint32_t *>(row)[i];
+            const uint32_t *kw = kpre[j];
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
@@ -417,6 +423,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
 
         // ---- values: channel tiles mc; lane (channel 16 mc + l16, tokens 32 sv + 8 lq ..)
+        // (their code words are loaded where used: loading them with the K words
+        // halves the waves per SIMD and loses more than it hides)
         const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &stg[wave][PI::O_VC]) : a.vcodes + kblk * (T * MD * VB / 8);
         const uint16_t *vcn = STAGED ? reinterpret_cast<const uint16_t *>(&stg[wave][PI::O_VCN]) : a.vcn + kblk * MD;
 #pragma unroll
