@@ -423,13 +423,31 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
 
         // ---- values: channel tiles mc; lane (channel 16 mc + l16, tokens 32 sv + 8 lq ..)
-        // (their code words are loaded where used: loading them with the K words
-        // halves the waves per SIMD and loses more than it hides)
+        // (their code words are loaded two tiles ahead of use: loading all of them
+        // with the K words halves the waves per SIMD and loses more than it hides)
         const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &stg[wave][PI::O_VC]) : a.vcodes + kblk * (T * MD * VB / 8);
+        constexpr bool VRING = !STAGED && T >= 32 && VB != 3;
+        uint32_t vw[VRING ? 8 : 1][VRING ? KSV : 1];
+        auto vword = [&](int mc, int sv) -> uint32_t {
+            const int64_t bit0 = ((int64_t)(16 * mc + l16) * T + 32 * sv + 8 * lq) * VB;
+            if constexpr (VB == 4) return reinterpret_cast<const uint32_t *>(vbase)[bit0 >> 5];
+            else return reinterpret_cast<const uint16_t *>(vbase)[bit0 >> 4];
+        };
+        if constexpr (VRING) {
+#pragma unroll
+            for (int sv = 0; sv < KSV; ++sv) {
+                vw[0][sv] = vword(0, sv);
+                vw[1][sv] = vword(1, sv);
+            }
+        }
         const uint16_t *vcn = STAGED ? reinterpret_cast<const uint16_t *>(&stg[wave][PI::O_VCN]) : a.vcn + kblk * MD;
 #pragma unroll
         for (int mc = 0; mc < 8; ++mc) {
             const int ch = 16 * mc + l16;
+            if constexpr (VRING)
+                if (mc + 2 < 8)
+#pragma unroll
+                    for (int sv = 0; sv < KSV; ++sv) vw[mc + 2][sv] = vword(mc + 2, sv);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sv = 0; sv < KSV; ++sv) {
@@ -437,7 +455,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                 if (T >= 32 || lq < 2) {
                     const int64_t bit0 = ((int64_t)ch * T + 32 * sv + 8 * lq) * VB;
                     uint32_t bitsv;
-                    if constexpr (VB == 4) bitsv = reinterpret_cast<const uint32_t *>(vbase)[bit0 >> 5];
+                    if constexpr (VRING) bitsv = vw[mc][sv];
+                    else if constexpr (VB == 4) bitsv = reinterpret_cast<const uint32_t *>(vbase)[bit0 >> 5];
                     else if constexpr (VB == 2) bitsv = reinterpret_cast<const uint16_t *>(vbase)[bit0 >> 4];
                     else if constexpr (STAGED) bitsv = reinterpret_cast<const uint32_t *>(vbase)[bit0 / 24];  // re-aligned
                     else bitsv = load_bits3(vbase, bit0);
