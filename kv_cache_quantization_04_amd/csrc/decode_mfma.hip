@@ -108,6 +108,24 @@ struct PageImage {
     static constexpr int VCW = VB == 3 ? MD * (T / 8) * 4 : 16;  // re-aligned V codes
 };
 
+// Copy N bytes from global memory into LDS with the wave's direct-to-LDS loads,
+// every lane active in every instruction: 16-byte loads (1 KB per instruction)
+// when N is a multiple of 1 KB, else 4-byte loads (256 B per instruction). No lane
+// guard: the compiler has merged guarded direct-to-LDS loads of different regions
+// across divergent branches into one instruction with one LDS base.
+template <int N>
+__device__ __forceinline__ void copy_region(const uint8_t *src, uint8_t *dst, int lane) {
+    constexpr int W = N % 1024 == 0 ? 16 : 4;
+    static_assert(N % (64 * W) == 0, "region size");
+#pragma unroll
+    for (int k = 0; k < N / (64 * W); ++k) {
+        const void *g = (const void *)(src + 64 * W * k + W * lane);
+        auto *l = (__attribute__((address_space(3))) void *)(dst + 64 * W * k);
+        if constexpr (W == 16) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+        else __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+    }
+}
+
 template <int N>
 struct Chunks {
     uint4 v[N];
@@ -147,14 +165,24 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     // registers while the current page is processed from the wave's LDS image (`stg`,
     // plus `wrk` for re-aligned 3-bit V codes).
     constexpr bool STAGED = T == 16;
+    // Pages of 64 and 128 tokens are copied whole (codes, side data, normalizers) into
+    // the wave's LDS image by direct-to-LDS loads at the top of the page: one HBM round
+    // trip per page instead of one per tile of codes and side data.
+    constexpr bool IMG = T >= 64;
+    constexpr bool LDSPAGE = STAGED || IMG;
     using PI = PageImage<T, KB, VB>;
-    __shared__ __attribute__((aligned(16))) uint8_t stg[4][STAGED ? PI::BYTES : 16];
+    // One pool: the four waves' page images during the page walk, the split merge after
+    // it (a barrier separates the two uses).
+    constexpr int RED_O = 4 * 16 * (MD + 1) * 4, RED_BYTES = RED_O + 4 * 16 * 2 * 4;
+    constexpr int IMG_BYTES = LDSPAGE ? 4 * PI::BYTES : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t pool[IMG_BYTES > RED_BYTES ? IMG_BYTES : RED_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t wrk[4][STAGED ? PI::VCW : 16];
-    __shared__ float red_o[4][16][MD + 1];
-    __shared__ float red_ml[4][16][2];
+    float(*red_o)[16][MD + 1] = reinterpret_cast<float(*)[16][MD + 1]>(pool);
+    float(*red_ml)[16][2] = reinterpret_cast<float(*)[16][2]>(pool + RED_O);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint8_t *stg = pool + wave * (LDSPAGE ? PI::BYTES : 0);  // this wave's page image
     const int l16 = lane & 15, lq = lane >> 4;
     const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
     const int g = a.grp;
@@ -162,6 +190,33 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     const int npages = min((L + T - 1) / T, a.bt_stride);
     const int pps = (npages + a.splits - 1) / a.splits;
     const int p0 = split * pps, p1 = min(npages, p0 + pps);
+
+    auto page_of = [&](int q) { return load_const(a.bt, (int64_t)s * a.bt_stride + q); };
+    auto valid = [&](int q) {
+        const int page = page_of(q);
+        return page >= 0 && page < a.num_pages;
+    };
+    // staged path: the next page's image chunks, in registers
+    Chunks<STAGED ? PI::NPRE : 1> pre{};
+    int pi = p0 + wave;
+    while (pi < p1 && !valid(pi)) pi += 4;
+    if constexpr (STAGED)
+        if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);
+    // whole-page images: the copies of the wave's first page travel while the query
+    // is loaded and rotated
+    auto copy_page = [&](int64_t kblk) {
+        if constexpr (IMG) {
+        copy_region<PI::KC>(a.kcodes + kblk * PI::KC, stg + PI::O_KC, lane);
+        copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.ksz) + kblk * PI::SZ, stg + PI::O_KSZ, lane);
+        copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.kcn) + kblk * PI::CN, stg + PI::O_KCN, lane);
+        copy_region<PI::VC>(a.vcodes + kblk * PI::VC, stg + PI::O_VC, lane);
+        copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.vsz) + kblk * PI::SZ, stg + PI::O_VSZ, lane);
+        copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.vcn) + kblk * PI::CN, stg + PI::O_VCN, lane);
+        }
+    };
+    const int first = pi;
+    if constexpr (IMG)
+        if (pi < p1) copy_page((int64_t)page_of(pi) * a.Hkv + hk);
 
     // ---- rotated query qbar = q Q of head l16 (< g; other lanes hold zeros) in the
     // B-operand layout: lane (head l16, chunk lq), K-step st covers channels
@@ -234,17 +289,6 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mc = 0; mc < 8; ++mc) o[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto page_of = [&](int q) { return load_const(a.bt, (int64_t)s * a.bt_stride + q); };
-    auto valid = [&](int q) {
-        const int page = page_of(q);
-        return page >= 0 && page < a.num_pages;
-    };
-    // staged path: the next page's image chunks, in registers
-    Chunks<STAGED ? PI::NPRE : 1> pre{};
-    int pi = p0 + wave;
-    while (pi < p1 && !valid(pi)) pi += 4;
-    if constexpr (STAGED)
-        if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);
     while (pi < p1) {
         const int cur = pi;
         const int page = page_of(cur);
@@ -255,12 +299,12 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < PI::NPRE; ++k) {
                 const int off = 1024 * k + 16 * lane;
-                if (off < PI::BYTES) *reinterpret_cast<uint4 *>(&stg[wave][off]) = pre.v[k];
+                if (off < PI::BYTES) *reinterpret_cast<uint4 *>(&stg[off]) = pre.v[k];
             }
             if constexpr (VB == 3) {  // four 3-byte chunks per lane -> four words
 #pragma unroll
                 for (int c4 = lane; c4 < MD * (T / 8) / 4; c4 += 64) {
-                    const uint32_t *sw = reinterpret_cast<const uint32_t *>(&stg[wave][PI::O_VC + 12 * c4]);
+                    const uint32_t *sw = reinterpret_cast<const uint32_t *>(&stg[PI::O_VC + 12 * c4]);
                     const uint32_t w0 = sw[0], w1 = sw[1], w2 = sw[2];
                     const uint4 r = {w0 & 0xFFFFFFu, (w0 >> 24) | ((w1 & 0xFFFFu) << 8), (w1 >> 16) | ((w2 & 0xFFu) << 16),
                                      w2 >> 8};
@@ -271,9 +315,18 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
         const int rows = min(T, L - cur * T);
         const int64_t kblk = (int64_t)page * a.Hkv + hk;
+        if constexpr (IMG) {
+            if (cur != first) {
+                // the previous page's LDS reads have returned (their values were consumed);
+                // make sure before the copies overwrite the image
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                copy_page(kblk);
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // the wave's copies have landed (it alone reads its image)
+        }
         // the page's K code words of every M-tile, issued now so that they travel
         // while the query is folded (a page in HBM, not staged)
-        const uint8_t *kbase = STAGED ? &stg[wave][PI::O_KC] : a.kcodes + kblk * (T * MD * KB / 8);
+        const uint8_t *kbase = LDSPAGE ? &stg[PI::O_KC] : a.kcodes + kblk * (T * MD * KB / 8);
         uint32_t kpre[MT][KB];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
@@ -286,7 +339,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
 
         // c_K of the lane's 32 channels (lq*32 ..)
-        const uint4 *cp = STAGED ? reinterpret_cast<const uint4 *>(&stg[wave][PI::O_KCN + 64 * lq])
+        const uint4 *cp = LDSPAGE ? reinterpret_cast<const uint4 *>(&stg[PI::O_KCN + 64 * lq])
                                  : reinterpret_cast<const uint4 *>(a.kcn + kblk * MD + lq * 32);
         uint32_t cw[16];
 #pragma unroll
@@ -350,9 +403,9 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             int tok0;
             if constexpr (T >= 32) tok0 = 32 * (j >> 1) + 8 * lq + 4 * (j & 1);
             else tok0 = 8 * (lq & 1) + 4 * (lq >> 1);
-            const uint4 kz = STAGED ? *reinterpret_cast<const uint4 *>(&stg[wave][PI::O_KSZ + 4 * tok0])
+            const uint4 kz = LDSPAGE ? *reinterpret_cast<const uint4 *>(&stg[PI::O_KSZ + 4 * tok0])
                                     : *reinterpret_cast<const uint4 *>(a.ksz + (kblk * T + tok0) * 2);
-            vzq[j] = STAGED ? *reinterpret_cast<const uint4 *>(&stg[wave][PI::O_VSZ + 4 * tok0])
+            vzq[j] = LDSPAGE ? *reinterpret_cast<const uint4 *>(&stg[PI::O_VSZ + 4 * tok0])
                             : *reinterpret_cast<const uint4 *>(a.vsz + (kblk * T + tok0) * 2);
             const uint32_t kzw[4] = {kz.x, kz.y, kz.z, kz.w};
 #pragma unroll
@@ -425,8 +478,9 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         // ---- values: channel tiles mc; lane (channel 16 mc + l16, tokens 32 sv + 8 lq ..)
         // (their code words are loaded two tiles ahead of use: loading all of them
         // with the K words halves the waves per SIMD and loses more than it hides)
-        const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &stg[wave][PI::O_VC]) : a.vcodes + kblk * (T * MD * VB / 8);
-        constexpr bool VRING = !STAGED && T >= 32 && VB != 3;
+        const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &stg[PI::O_VC])
+                                      : IMG ? &stg[PI::O_VC] : a.vcodes + kblk * (T * MD * VB / 8);
+        constexpr bool VRING = !LDSPAGE && T >= 32 && VB != 3;
         uint32_t vw[VRING ? 8 : 1][VRING ? KSV : 1];
         auto vword = [&](int mc, int sv) -> uint32_t {
             const int64_t bit0 = ((int64_t)(16 * mc + l16) * T + 32 * sv + 8 * lq) * VB;
@@ -440,7 +494,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                 vw[1][sv] = vword(1, sv);
             }
         }
-        const uint16_t *vcn = STAGED ? reinterpret_cast<const uint16_t *>(&stg[wave][PI::O_VCN]) : a.vcn + kblk * MD;
+        const uint16_t *vcn = LDSPAGE ? reinterpret_cast<const uint16_t *>(&stg[PI::O_VCN]) : a.vcn + kblk * MD;
 #pragma unroll
         for (int mc = 0; mc < 8; ++mc) {
             const int ch = 16 * mc + l16;
@@ -479,6 +533,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 
     // ---- merge the four waves, write the split partial (m, l in log2 units -> natural)
     l_run = xlane_sum_q(l_run);
+    if constexpr (LDSPAGE) __syncthreads();  // the merge buffers overlay the page images
     if (lq == 0) {
         red_ml[wave][l16][0] = m_run;
         red_ml[wave][l16][1] = l_run;
