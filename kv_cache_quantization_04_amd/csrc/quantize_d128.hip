@@ -121,19 +121,24 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
     // chunk l & 15. LDS slot (l & 15) of a row holds chunk slot ^ ((row / R) & 3),
     // so the four row groups of a wave read different banks; for a fixed b that
     // swizzle is the constant ((4 i) / R) & 3.
-    const uint32_t lane_row_bytes = (uint32_t)rr * (uint32_t)a.stride_token * 2u;
     auto fetch = [&](int itm) {
         const int tl = itm / a.H, hd = itm % a.H;
         const int nv = load_const(a.tile_valid, tl);
         const char *src = reinterpret_cast<const char *>(a.src) +
                           2 * (hd * a.stride_head + (int64_t)load_const(a.tile_src_token, tl) * a.stride_token);
+        if (nv <= 0) return;
+        // every lane takes part in every copy (rows past the valid ones repeat the last
+        // valid row, never read): no guarded direct-to-LDS loads for the compiler to merge
+        const int last = nv - 1;
+        const uint32_t row_bytes = (uint32_t)a.stride_token * 2u;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const int b = wave * R + i;
-            const uint32_t off = lane_row_bytes + 16u * (uint32_t)(cc ^ (((4 * i) / R) & 3));
-            if (4 * b + rr < nv)
-                __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)(4 * b) * a.stride_token * 2 + off),
-                                                 (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
+            const int rb = min(4 * b, last);                // wave-uniform first row of the copy
+            const int dr = min(4 * b + rr, last) - rb;      // this lane's row, 0..3 rows further
+            const uint32_t off = (uint32_t)dr * row_bytes + 16u * (uint32_t)(cc ^ (((4 * i) / R) & 3));
+            __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)rb * a.stride_token * 2 + off),
+                                             (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
         }
     };
     int item = blockIdx.x;
@@ -289,7 +294,8 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 
     // ---- per token: asymmetric RTN with fp16 (S, Z), codes packed in registers
     // channel-major: two byte-accumulators per channel (4-bit: even / odd rows,
-    // 2-bit: rows 0..3 / 4..7) assembled into the channel's bitstream at the end
+    // 2-bit: rows 0..3 in the first), assembled into the channel's bitstream at the end
+    static_assert(R == 4, "four rows per lane");
     uint32_t cma[8], cmb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) cma[j] = cmb[j] = 0;
@@ -331,11 +337,10 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if constexpr (BITS == 4) {
-                    if (k & 1) cmb[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], (k >> 1) & 3, cmb[j]);
-                    else cma[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], (k >> 1) & 3, cma[j]);
+                    if (k & 1) cmb[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k >> 1, cmb[j]);
+                    else cma[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k >> 1, cma[j]);
                 } else {
-                    if (k < 4) cma[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k, cma[j]);
-                    else cmb[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k - 4, cmb[j]);
+                    cma[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k, cma[j]);
                 }
             }
         }
@@ -346,17 +351,12 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         for (int j = 0; j < 8; ++j) {
             const int pos = (pcc * 8 + j) * T + rg * R;
             if constexpr (BITS == 4) {
-                const uint32_t word = cma[j] | (cmb[j] << 4);
-                if constexpr (R == 8) *reinterpret_cast<uint32_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 2)) = word;
-                else *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 2)) = (uint16_t)word;
-            } else {
-                auto squeeze = [](uint32_t x) {  // four byte codes (< 4) -> one byte, LE 2-bit fields
-                    return (x & 0x03u) | ((x >> 6) & 0x0Cu) | ((x >> 12) & 0x30u) | ((x >> 18) & 0xC0u);
-                };
-                if constexpr (R == 8)
-                    *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 4)) =
-                        (uint16_t)(squeeze(cma[j]) | (squeeze(cmb[j]) << 8));
-                else cbase[code_byte<T, R, BITS, LAYOUT>(pos / 4)] = (uint8_t)squeeze(cma[j]);
+                *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 2)) =
+                    (uint16_t)(cma[j] | (cmb[j] << 4));
+            } else {  // four byte codes (< 4) -> one byte, LE 2-bit fields
+                const uint32_t x = cma[j];
+                cbase[code_byte<T, R, BITS, LAYOUT>(pos / 4)] =
+                    (uint8_t)((x & 0x03u) | ((x >> 6) & 0x0Cu) | ((x >> 12) & 0x30u) | ((x >> 18) & 0xC0u));
             }
         }
     }
