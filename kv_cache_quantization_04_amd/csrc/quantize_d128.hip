@@ -131,12 +131,17 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         // valid row, never read): no guarded direct-to-LDS loads for the compiler to merge
         const int last = nv - 1;
         const uint32_t row_bytes = (uint32_t)a.stride_token * 2u;
+        // lane id made opaque here: its few derived offsets are recomputed per copy
+        // instead of being kept (or spilled) across the item
+        int fl = tid & 63;
+        asm volatile("" : "+v"(fl));
+        const int fcc = fl & 15, frr = fl >> 4;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const int b = wave * R + i;
             const int rb = min(4 * b, last);                // wave-uniform first row of the copy
-            const int dr = min(4 * b + rr, last) - rb;      // this lane's row, 0..3 rows further
-            const uint32_t off = (uint32_t)dr * row_bytes + 16u * (uint32_t)(cc ^ (((4 * i) / R) & 3));
+            const int dr = min(4 * b + frr, last) - rb;     // this lane's row, 0..3 rows further
+            const uint32_t off = (uint32_t)dr * row_bytes + 16u * (uint32_t)(fcc ^ (((4 * i) / R) & 3));
             __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)rb * a.stride_token * 2 + off),
                                              (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
         }
