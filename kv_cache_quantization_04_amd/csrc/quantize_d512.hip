@@ -152,9 +152,11 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
         uint4 rp[2] = {uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}};
         uint32_t bad = 0;
         if (a.R == 64 && n > 0) {
+            int ot = tid;  // opaque: the addresses are formed here, not kept across the item
+            asm volatile("" : "+v"(ot));
 #pragma unroll
             for (int m = 0; m < 2; ++m) {  // branch-free: padding rows read the last valid row, zeroed below
-                const int q = tid + LNT * m, row = min(q >> 3, n - 1), part = q & 7;
+                const int q = ot + LNT * m, row = min(q >> 3, n - 1), part = q & 7;
                 rp[m] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.src) + head * a.stride_head +
                                                          (tok0 + row) * a.stride_token + LD + 8 * part);
             }
