@@ -265,6 +265,14 @@ def bench_prefill(args, cfg, torch, K, W, dev):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    kname = K.kv_prefill_attn_kernel_name(q, kc, vc)
+    chunk_mode = kname == "decode_mfma_kernel"
+    kernel_label = ("" if chunk_mode else "prefill_prep_kernel + ") + kname + " + decode_reduce_kernel"
+    if chunk_mode:
+        ppb = 16 // (Hq // H)
+        note = f"chunk mode: (position, head) MFMA columns, {ppb} positions per page read"
+    else:
+        note = "each chunk position runs as its own decode sequence: the pages are re-read per position"
     # algorithmic: scores over D + R and values over Dv per (query position, head, attended token)
     attended = float(sum(int(L) - Lq + i + 1 for L in cfg.seq_lens for i in range(Lq)))
     flops = 2.0 * attended * Hq * (cfg.width + cfg.dv)
@@ -275,11 +283,10 @@ def bench_prefill(args, cfg, torch, K, W, dev):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name + f" (prefill chunk {Lq})", "chunk": Lq, "decode_splits": splits},
-        "roofline": {"bound": "mfma", "kernel": "prefill_prep_kernel + " +
-                     K.kv_decode_attn_kernel_name(q.view(B * Lq, Hq, -1), kc, vc) + " + decode_reduce_kernel",
+        "roofline": {"bound": "mfma", "kernel": kernel_label,
                      "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 5), "traffic": None, "algorithmic_flops_per_step": flops,
-                     "note": "each chunk position runs as its own decode sequence: the pages are re-read per position"},
+                     "note": note},
     }
     print(json.dumps(res), flush=True)
 

@@ -161,7 +161,8 @@ size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  * The score rotation and normalizer fold is exact in real arithmetic; in fp32
  * the result differs from fp64 dequantize-then-attention by rounding only.
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (layouts: K token-major, V channel-major,
- * MLA latent token-major; T in {16, 32, 64, 128}), KVQ_EWORKSPACE, KVQ_ELAUNCH. */
+ * MLA latent token-major; T in {16, 32, 64, 128}; num_seqs above 65535 except
+ * for MLA), KVQ_EWORKSPACE, KVQ_ELAUNCH. */
 kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
                           const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
                           int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
@@ -220,10 +221,13 @@ const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const 
  * ends with a chunk of chunk_len query positions whose keys and values are
  * already in the cache (its last chunk_len tokens); position i of the chunk
  * attends causally to tokens 0 .. seq_lens[b] - chunk_len + i (a position with
- * no token left gives the result of an empty decode). The result per (b, i) is
- * exactly kv_decode_attn's for that query over that prefix (same fold, same
- * kernels: the chunk positions run as chunk_len virtual sequences sharing b's
- * block-table row).
+ * no token left gives zeros, the result of an empty decode). The result per
+ * (b, i) is kv_decode_attn's for that query over that prefix, with the same fold
+ * (scores and values from the codes, normalizers folded into the query and the
+ * output). Formats that kv_decode_attn runs on "decode_mfma_kernel" run that
+ * kernel in its chunk mode (the MFMA columns hold (position, head) pairs, so one
+ * page read serves 16 / (num_q_heads / H) positions); other formats run the
+ * chunk positions as chunk_len virtual sequences sharing b's block-table row.
  *   q (device): [num_seqs][chunk_len][num_q_heads][D + R] in q_dtype.
  *   seq_lens (device int32): [num_seqs], total lengths including the chunk.
  *   out (device fp32): [num_seqs][chunk_len][num_q_heads][Dv].
@@ -246,6 +250,13 @@ size_t kv_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t chunk_len, int3
 /* Split count kv_prefill_attn uses for num_splits = 0 (1 for invalid arguments). */
 int32_t kv_prefill_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs,
                                        int32_t chunk_len, int32_t num_q_heads, int32_t max_seq_len);
+
+/* Name of the main GPU kernel kv_prefill_attn runs for this query pointer and
+ * these caches ("decode_mfma_kernel" in its chunk mode, else the decode kernel
+ * the virtual sequences run on); the split merge, "decode_reduce_kernel",
+ * follows it. NULL for invalid arguments. The string is static. */
+const char *kv_prefill_attn_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v,
+                                        int32_t num_q_heads);
 
 /* Static description of a status code. */
 const char *kvq_status_str(kvq_status s);

@@ -280,8 +280,23 @@ size_t kv_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t chunk_len, int3
 
 int32_t kv_prefill_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs, int32_t chunk_len,
                                        int32_t num_q_heads, int32_t max_seq_len) {
-    if (chunk_len <= 0 || (int64_t)num_seqs * chunk_len > (1 << 24)) return 1;
-    return kv_decode_attn_default_splits(k, v, num_seqs * chunk_len, num_q_heads, max_seq_len);
+    if (chunk_len <= 0 || num_seqs < 0 || (int64_t)num_seqs * chunk_len > (1 << 24) || max_seq_len < 0) return 1;
+    kvq::DecodeArgs a{};
+    if (check_cache(k) != KVQ_OK || (v && check_cache(v) != KVQ_OK) || decode_layout(k, v, num_q_heads, a) != KVQ_OK)
+        return 1;
+    alignas(16) static const uint8_t aligned_probe[16] = {};
+    a.q = aligned_probe;  // the split count assumes a 16-byte aligned query
+    a.B = num_seqs;
+    return kvq::prefill_default_splits(a, chunk_len, max_seq_len);
+}
+
+const char *kv_prefill_attn_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v, int32_t num_q_heads) {
+    kvq::DecodeArgs a{};
+    if (!q || check_cache(k) != KVQ_OK || (v && check_cache(v) != KVQ_OK) ||
+        decode_layout(k, v, num_q_heads, a) != KVQ_OK)
+        return nullptr;
+    a.q = q;
+    return kvq::prefill_kernel_name(a);
 }
 
 kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t chunk_len, int32_t num_q_heads,
@@ -301,8 +316,10 @@ kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, i
     if ((st = decode_layout(k, v, num_q_heads, a)) != KVQ_OK) return st;
     if ((int64_t)block_table_stride * a.T < max_seq_len) return KVQ_EINVAL;
     const int32_t nv = num_seqs * chunk_len;
+    a.q = q;
+    a.B = num_seqs;
+    const int splits = num_splits > 0 ? num_splits : kvq::prefill_default_splits(a, chunk_len, max_seq_len);
     a.B = nv;
-    const int splits = num_splits > 0 ? num_splits : kvq::decode_default_splits(a, max_seq_len);
     if (!workspace || ((uintptr_t)workspace & 255) ||
         workspace_bytes < kv_prefill_attn_workspace_bytes(num_seqs, chunk_len, num_q_heads, a.Dv, splits,
                                                           block_table_stride))

@@ -260,7 +260,8 @@ __device__ __forceinline__ void reduce_one(const DecodeArgs &a, int s, int hq, i
 __global__ void __launch_bounds__(64 * RED_WAVES) decode_reduce_kernel(DecodeArgs a) {
     __shared__ float wgt[RED_WAVES][RED_MAX_SPLITS];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int hq = blockIdx.x * RED_WAVES + wave, s = blockIdx.y;
+    const int nhg = (a.Hq + RED_WAVES - 1) / RED_WAVES;  // head groups per row
+    const int s = blockIdx.x / nhg, hq = (blockIdx.x - s * nhg) * RED_WAVES + wave;
     if (hq >= a.Hq) return;  // whole wave
     switch (a.Dv) {
     case 64: reduce_one<1>(a, s, hq, lane, wgt[wave]); break;
@@ -271,8 +272,9 @@ __global__ void __launch_bounds__(64 * RED_WAVES) decode_reduce_kernel(DecodeArg
 }
 
 static void launch_reduce(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3((a.Hq + RED_WAVES - 1) / RED_WAVES, a.B), dim3(64 * RED_WAVES), 0,
-                       stream, a);
+    // one workgroup per (row, group of RED_WAVES query heads), rows = a.B
+    const int64_t nwg = (int64_t)((a.Hq + RED_WAVES - 1) / RED_WAVES) * a.B;
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)nwg), dim3(64 * RED_WAVES), 0, stream, a);
 }
 
 bool decode_mfma_supported(const DecodeArgs &a);
@@ -311,6 +313,18 @@ const char *decode_kernel_name(const DecodeArgs &a) {
     return "decode_generic_kernel";
 }
 
+// chunked prefill on the MFMA kernel: a.B real sequences of a.Lq positions; the
+// split partials, the reduce and the output cover a.B * a.Lq rows
+bool launch_decode_chunk(const DecodeArgs &a, hipStream_t stream) {
+    if (a.splits > RED_MAX_SPLITS || a.Lq <= 0 || !decode_mfma_supported(a)) return false;
+    if (!launch_decode_mfma(a, stream)) return false;
+    DecodeArgs r = a;
+    r.B = a.B * a.Lq;
+    r.Lq = 0;
+    launch_reduce(r, stream);
+    return true;
+}
+
 bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.splits > RED_MAX_SPLITS) return false;
     if (decode_mla_supported(a)) {
@@ -318,6 +332,7 @@ bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
         launch_reduce(a, stream);
         return true;
     }
+    if (a.B > 65535) return false;  // the grids below put sequences on z
     if (decode_mfma_supported(a)) {
         if (!launch_decode_mfma(a, stream)) return false;
         launch_reduce(a, stream);

@@ -18,6 +18,13 @@
 // workgroup merge before writing the split partial. Token order inside a page
 // is permuted so that the score tile of two 16-token M-tiles lands, lane for
 // lane, in the layout of the 32-token operand of the value product.
+//
+// Chunked prefill (PF) runs the same kernel with the 16 MFMA columns holding
+// (query position, head) pairs, 16 / g consecutive positions of one kv head's g
+// query heads, each column with its own causal length: one page read serves
+// 16 / g positions and no column is padding. Workgroups that share pages (the
+// column blocks of one sequence, kv head and split) are given consecutive ids
+// on one XCD, so the repeated page reads hit that XCD's L2.
 #include "common.h"
 #include "launch.h"
 
@@ -156,7 +163,7 @@ __device__ __forceinline__ Chunks<PageImage<T, KB, VB>::NPRE> fetch_page(const D
     return r;
 }
 
-template <int T, int KB, int VB>
+template <int T, int KB, int VB, bool PF>
 __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = T / 16;                 // 16-token M-tiles of the score product
     constexpr int KSV = T >= 32 ? T / 32 : 1;  // 32-token K-steps of the value product
@@ -184,9 +191,36 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint8_t *stg = pool + wave * (LDSPAGE ? PI::BYTES : 0);  // this wave's page image
     const int l16 = lane & 15, lq = lane >> 4;
-    const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
     const int g = a.grp;
-    const int L = load_const(a.seq_lens, s);
+    int split, hk, s, cb = 0;
+    if constexpr (PF) {
+        // work item n = ((s * Hkv + hk) * splits + split) * ncb + cb; XCD x (= id mod 8
+        // under round-robin dispatch) takes items x * chunk .. in id order
+        const int ncb = (a.Lq * g + 15) / 16;
+        const int64_t W = (int64_t)a.B * a.Hkv * a.splits * ncb, chunk = (W + 7) / 8;
+        const int64_t n = (int64_t)(blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
+        if (n >= W) return;  // whole workgroup, before any barrier
+        cb = (int)(n % ncb);
+        int64_t t = n / ncb;
+        split = (int)(t % a.splits);
+        t /= a.splits;
+        hk = (int)(t % a.Hkv);
+        s = (int)(t / a.Hkv);
+    } else {
+        split = blockIdx.x;
+        hk = blockIdx.y;
+        s = blockIdx.z;
+    }
+    // column l16: decode, query head hk g + l16 (l16 < g); prefill, position
+    // pos = cb (16 / g) + l16 / g of the chunk and query head hk g + l16 mod g
+    const int ppb = PF ? 16 / g : 1;
+    const int pos = PF ? cb * ppb + l16 / g : 0;
+    const int hh = PF ? l16 - (l16 / g) * g : l16;
+    const bool hv = PF ? pos < a.Lq : l16 < g;
+    const int Ls = load_const(a.seq_lens, s);
+    // tokens the workgroup attends (the longest column) and this lane's column
+    const int L = PF ? max(0, Ls - a.Lq + min(a.Lq, (cb + 1) * ppb)) : Ls;
+    const int Lc = PF ? (hv ? Ls - a.Lq + pos + 1 : 0) : Ls;
     const int npages = min((L + T - 1) / T, a.bt_stride);
     const int pps = (npages + a.splits - 1) / a.splits;
     const int p0 = split * pps, p1 = min(npages, p0 + pps);
@@ -225,8 +259,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     // across lanes 16 and 32 apart; blocks of h channels rotate separately.
     float qv[32];
     {
-        const bool hv = l16 < g;
-        const int64_t qb = ((int64_t)s * a.Hq + hk * g + (hv ? l16 : 0)) * MD + lq * 32;
+        const int64_t qrow = PF ? (int64_t)s * a.Lq + (hv ? pos : 0) : s;
+        const int64_t qb = (qrow * a.Hq + hk * g + (hv ? hh : 0)) * MD + lq * 32;
         // 32 consecutive channels: 16-byte loads under one (uniform) dtype branch
         if (a.q_dtype == KVQ_F32) {
             const float4 *p4 = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qb);
@@ -313,7 +347,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
             if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);  // travels meanwhile
         }
-        const int rows = min(T, L - cur * T);
+        const int rows = min(T, Lc - cur * T);  // valid tokens of this column (may be <= 0 in PF)
         const int64_t kblk = (int64_t)page * a.Hkv + hk;
         if constexpr (IMG) {
             if (cur != first) {
@@ -418,9 +452,12 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
         }
         pmax = xlane_max_q(pmax);
-        const float m_new = fmaxf(m_run, pmax);
+        float m_new = fmaxf(m_run, pmax);
+        // a prefill column may have seen no valid token yet: exponents against 0 then
+        // give alpha = 0 and p = 0 (decode pages always hold a valid token)
+        if constexpr (PF) m_new = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
+        m_run = PF ? fmaxf(m_run, pmax) : m_new;
         // P~ = p S_V scaled by 2^sp with max_t S_V,t near 2^14 (p <= 1)
         float smax = 0.f;
 #pragma unroll
@@ -543,22 +580,30 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) red_o[wave][l16][16 * mc + 4 * lq + i] = o[mc][i];
     __syncthreads();
-    for (int e = tid; e < g * MD; e += MNT) {
-        const int hh = e / MD, j = e % MD;
+    for (int e = tid; e < (PF ? 16 : g) * MD; e += MNT) {
+        const int cc = e / MD, j = e % MD;
+        int64_t wrow;  // workspace row: (sequence or chunk position, query head)
+        if constexpr (PF) {
+            const int cpos = cb * ppb + cc / g;
+            if (cpos >= a.Lq) continue;
+            wrow = ((int64_t)s * a.Lq + cpos) * a.Hq + hk * g + cc % g;
+        } else {
+            wrow = (int64_t)s * a.Hq + hk * g + cc;
+        }
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[w][hh][0]);
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[w][cc][0]);
         float acc = 0.f, lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float mw = red_ml[w][hh][0];
+            const float mw = red_ml[w][cc][0];
             if (mw != -INFINITY) {
                 const float f = exp2f(mw - M);
-                acc = __builtin_fmaf(f, red_o[w][hh][j], acc);
-                lsum = __builtin_fmaf(f, red_ml[w][hh][1], lsum);
+                acc = __builtin_fmaf(f, red_o[w][cc][j], acc);
+                lsum = __builtin_fmaf(f, red_ml[w][cc][1], lsum);
             }
         }
-        float *wsr = a.ws + (((int64_t)s * a.Hq + hk * g + hh) * a.splits + split) * (MD + 2);
+        float *wsr = a.ws + (wrow * a.splits + split) * (MD + 2);
         wsr[j] = acc;
         if (j == 0) {
             // partial max stored in natural-log units for the merge kernel
@@ -580,35 +625,46 @@ bool decode_mfma_supported(const DecodeArgs &a) {
     return a.T == 16 || a.T == 32 || a.T == 64 || a.T == 128;
 }
 
-template <int T, int KB>
+template <int T, int KB, bool PF>
 static bool launch_vb(const DecodeArgs &a, hipStream_t stream) {
-    const dim3 grid(a.splits, a.Hkv, a.B);
+    dim3 grid(a.splits, a.Hkv, a.B);
+    if constexpr (PF) {
+        const int64_t W = (int64_t)a.B * a.Hkv * a.splits * ((a.Lq * a.grp + 15) / 16);
+        if (W > ((int64_t)1 << 30)) return false;
+        grid = dim3((unsigned)(8 * ((W + 7) / 8)));
+    }
     switch (a.vbits) {
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 2>), grid, dim3(MNT), 0, stream, a); return true;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 3>), grid, dim3(MNT), 0, stream, a); return true;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 4>), grid, dim3(MNT), 0, stream, a); return true;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 2, PF>), grid, dim3(MNT), 0, stream, a); return true;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 3, PF>), grid, dim3(MNT), 0, stream, a); return true;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 4, PF>), grid, dim3(MNT), 0, stream, a); return true;
     }
     return false;
 }
 
-template <int T>
+template <int T, bool PF>
 static bool launch_kb(const DecodeArgs &a, hipStream_t stream) {
     switch (a.kbits) {
-    case 2: return launch_vb<T, 2>(a, stream);
-    case 3: return launch_vb<T, 3>(a, stream);
-    case 4: return launch_vb<T, 4>(a, stream);
+    case 2: return launch_vb<T, 2, PF>(a, stream);
+    case 3: return launch_vb<T, 3, PF>(a, stream);
+    case 4: return launch_vb<T, 4, PF>(a, stream);
     }
     return false;
 }
 
-bool launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+template <bool PF>
+static bool launch_t(const DecodeArgs &a, hipStream_t stream) {
     switch (a.T) {
-    case 16: return launch_kb<16>(a, stream);
-    case 32: return launch_kb<32>(a, stream);
-    case 64: return launch_kb<64>(a, stream);
-    case 128: return launch_kb<128>(a, stream);
+    case 16: return launch_kb<16, PF>(a, stream);
+    case 32: return launch_kb<32, PF>(a, stream);
+    case 64: return launch_kb<64, PF>(a, stream);
+    case 128: return launch_kb<128, PF>(a, stream);
     }
     return false;
+}
+
+// decode (a.Lq == 0) or chunked prefill (a.Lq > 0, a.B real sequences)
+bool launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+    return a.Lq > 0 ? launch_t<true>(a, stream) : launch_t<false>(a, stream);
 }
 
 }  // namespace kvq

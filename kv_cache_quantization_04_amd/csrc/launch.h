@@ -47,6 +47,10 @@ struct DecodeArgs {
     int splits;
     float *ws;
     float *out;
+    // chunked prefill on the MFMA kernel: Lq > 0 query positions per sequence (q rows
+    // [B][Lq][Hq]), position i attending to tokens 0 .. seq_lens[b] - Lq + i; the
+    // workspace and the reduce run over B * Lq rows. 0 for decode.
+    int Lq;
 };
 
 // append path: new token rows -> tail buffer, tile descriptors -> workspace
@@ -72,6 +76,9 @@ struct PrefillArgs {
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
 bool launch_append(const AppendArgs &a, int D, int T, const QuantArgs &q, hipStream_t stream);
 bool launch_prefill(const PrefillArgs &p, const DecodeArgs &d, hipStream_t stream);
+// split-K partitions and main kernel of a prefill call (d.B = real sequences)
+int prefill_default_splits(const DecodeArgs &d, int Lq, int max_seq_len);
+const char *prefill_kernel_name(const DecodeArgs &d);
 bool launch_dequant(int D, int T, int num_tiles, const DequantArgs &a, hipStream_t stream);
 bool launch_decode(const DecodeArgs &a, hipStream_t stream);
 // split-K partitions for a decode call whose fields other than q, block table,

@@ -218,6 +218,27 @@ def test_prefill_argument_errors():
     assert prefill_status(fk, fv, num_seqs=1 << 20, chunk=32) == K.KVQ_EUNSUPPORTED
 
 
+def test_prefill_kernel_name_and_splits():
+    fk = K.make_format(128, 0, 128, 128, 128, 4, 4, K.KVQ_TOKEN_MAJOR)
+    fv = K.make_format(128, 0, 128, 128, 128, 4, 4, K.KVQ_CHANNEL_MAJOR)
+    kc, vc = cache_struct(fk, heads=8), cache_struct(fv, heads=8)
+
+    def name(q=FAKE, hq=32, v=vc, k=kc):
+        r = K._lib.kv_prefill_attn_kernel_name(q, ctypes.byref(k), ctypes.byref(v) if v is not None else None, hq)
+        return r.decode() if r is not None else None
+
+    assert name() == "decode_mfma_kernel"                  # chunk mode: (position, head) columns
+    assert name(q=FAKE + 4) == "decode_generic_kernel"     # q not 16-byte aligned: virtual sequences
+    assert name(hq=30) is None
+    fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)
+    assert name(k=cache_struct(fm, heads=1, rope=FAKE), v=None, hq=128) == "decode_mla_kernel"
+    # chunk mode counts 16 / g positions per workgroup: 8 sequences x 16 positions x 4 heads
+    # = 8 x 4 column blocks x 8 kv heads = 256 units -> 4 splits (32 pages allow 8)
+    assert K._lib.kv_prefill_attn_default_splits(ctypes.byref(kc), ctypes.byref(vc), 8, 16, 32, 4096) == 4
+    assert K._lib.kv_prefill_attn_default_splits(ctypes.byref(kc), ctypes.byref(vc), 8, 128, 32, 4096) == 1
+    assert K._lib.kv_prefill_attn_default_splits(ctypes.byref(kc), ctypes.byref(vc), 8, 0, 32, 4096) == 1
+
+
 def test_center_field():
     ok = K.make_format(128, 0, 128, 128, 128, 4, 4, 0, 1)
     assert ctypes.sizeof(K.kvq_format) == 36

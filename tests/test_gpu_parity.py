@@ -360,8 +360,16 @@ DEC_SMALL = [
 
 
 PREFILL = [
-    dict(T=16, lens=(300, 40, 77), kbits=3, vbits=3),                                # decode_mfma_kernel, staged pages
-    dict(T=128, lens=(600, 131), kbits=4, vbits=4, iters=4),                         # decode_mfma_kernel
+    # decode_mfma_kernel in chunk mode (16 / g positions per column block); chunk of 9
+    # positions unless Lq is given, so the last column block is ragged
+    dict(T=16, lens=(300, 40, 77), kbits=3, vbits=3),                                # g 4, staged pages
+    dict(T=128, lens=(600, 131), kbits=4, vbits=4, iters=4),                         # g 4
+    dict(T=128, lens=(700, 5, 130), kbits=4, vbits=2, iters=4, Hq=16, Hkv=2),        # g 8; a sequence shorter than the chunk
+    dict(T=64, lens=(400, 64), kbits=2, vbits=4, Hq=32, Hkv=2),                      # g 16: one position per block
+    dict(T=32, lens=(200, 33), kbits=3, vbits=2, Hq=2, Hkv=2),                       # g 1: 16 positions per block
+    dict(T=16, lens=(500, 8), kbits=4, vbits=4, Hq=8, Hkv=1, Lq=40),                 # g 8, staged pages, chunk 40
+    dict(T=128, lens=(1500, 300), kbits=4, vbits=4, iters=4, Lq=200),                # chunk over several pages
+    # other kernels: the positions run as virtual decode sequences
     dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(700, 140), iters=4),     # decode_mla_kernel
     dict(T=64, D=64, lens=(256, 70), kbits=4, vbits=4, iters=4, Hq=2, Hkv=2, dtype="f32"),  # generic
 ]
@@ -373,9 +381,11 @@ def test_prefill_chunk_is_causal_decode(gpu, kw, splits):
     """Chunk position i of sequence b equals the oracle's attention of that query over
     the sequence's tokens 0 .. L_b - Lq + i (dequantize, then softmax attention)."""
     log("prefill case", kw, "splits", splits)
+    kw = dict(kw)
+    Lq = kw.pop("Lq", 9)
     w = small_paged(31 + len(kw), **kw)
     rng = np.random.default_rng(zlib.crc32(repr(sorted(kw.items())).encode()))
-    B, Hq, Wd, Lq = len(w["lens"]), w["Hq"], w["fk"].head_dim + w["fk"].rope_dim, 9
+    B, Hq, Wd = len(w["lens"]), w["Hq"], w["fk"].head_dim + w["fk"].rope_dim
     q = make_src(rng.standard_normal((B, Lq, Hq, Wd)), w["dtype"])
     sm = 1.0 / math.sqrt(Wd)
     kc, _ = orc_quantize(w["fk"], w["ks"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
@@ -383,20 +393,26 @@ def test_prefill_chunk_is_causal_decode(gpu, kw, splits):
     if w["fv"] is not None:
         vc, _ = orc_quantize(w["fv"], w["vs"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
     vl = np.array([L - Lq + i + 1 for L in w["lens"] for i in range(Lq)])
-    ref = O.decode_attn(q.reshape(B * Lq, Hq, Wd), ORC_DT[w["dtype"]], kc, vc, np.repeat(w["bt"], Lq, axis=0), vl, sm,
-                        folded=False, nthreads=16)
+    live = vl > 0  # positions with no token left give zeros
+    ref = O.decode_attn(q.reshape(B * Lq, Hq, Wd)[live], ORC_DT[w["dtype"]], kc, vc,
+                        np.repeat(w["bt"], Lq, axis=0)[live], vl[live], sm, folded=False, nthreads=16)
     dk = K.DeviceCache(kfmt(w["fk"]), w["P"], w["Hkv"])
     upload(kc, dk)
     dv = None
     if vc is not None:
         dv = K.DeviceCache(kfmt(w["fv"]), w["P"], w["Hkv"])
         upload(vc, dv)
-    out = K.kv_prefill_attn(to_dev(q, w["dtype"]), dk, dv, i32(w["bt"]), i32(w["lens"]), int(w["lens"].max()), sm,
-                            num_splits=splits)
+    qd = to_dev(q, w["dtype"])
+    # chunk mode exactly where decode runs the GQA MFMA kernel
+    kname = K.kv_prefill_attn_kernel_name(qd, dk, dv)
+    assert kname == K.kv_decode_attn_kernel_name(qd.view(B * Lq, Hq, Wd), dk, dv)
+    out = K.kv_prefill_attn(qd, dk, dv, i32(w["bt"]), i32(w["lens"]), int(w["lens"].max()), sm, num_splits=splits)
     torch.cuda.synchronize()
-    err = rel_rowwise(out.cpu().numpy().astype(np.float64).reshape(B * Lq, Hq, -1), ref)
-    log("  prefill rel err", err)
+    got = out.cpu().numpy().astype(np.float64).reshape(B * Lq, Hq, -1)
+    err = rel_rowwise(got[live], ref)
+    log("  prefill", kname, "rel err", err, "empty positions", int((~live).sum()))
     assert err <= DECODE_RTOL
+    assert np.all(got[~live] == 0)
 
 
 @pytest.mark.parametrize("kw", DEC_SMALL, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) or "default")
@@ -540,3 +556,23 @@ def test_full_workload_sampled(gpu, ci):
     err = rel_rowwise(got, ref[0])
     log("  decode seq", s, "kv head", hk, "rel err", err)
     assert err <= DECODE_RTOL
+    del out
+
+    # ---- chunked prefill as bench.py --prefill 128 launches it: the sampled sequence's
+    # chunk gets seeded queries (the other sequences zeros); sampled positions of it
+    # are compared with the oracle's attention over their prefixes
+    Lq, Hq, Wd = 128, cfg.num_q_heads, cfg.width
+    qs = make_src(np.random.default_rng(200 + ci).standard_normal((Lq, Hq, Wd)), cfg.src_dtype)
+    qd = torch.zeros((cfg.num_seqs, Lq, Hq, Wd), dtype=torch.float32 if cfg.src_dtype == "f32" else torch.bfloat16,
+                     device=gpu)
+    qd[s] = to_dev(qs, cfg.src_dtype, gpu)
+    out = K.kv_prefill_attn(qd, dk, dv, i32(cfg.block_table), i32(cfg.seq_lens), int(cfg.seq_lens.max()),
+                            cfg.sm_scale)
+    torch.cuda.synchronize()
+    for i in sorted({0, 1, Lq // 2, Lq - 1, int(rng.integers(Lq))}):
+        ref = O.decode_attn(np.ascontiguousarray(qs[i:i + 1, hk * grp: hk * grp + nq]), ORC_DT[cfg.src_dtype], kc, vc,
+                            loc_page[None, :], np.array([L - Lq + i + 1]), cfg.sm_scale, folded=False, nthreads=16)
+        got = out[s, i, hk * grp: hk * grp + nq].cpu().numpy().astype(np.float64)
+        err = rel_rowwise(got, ref[0])
+        log("  prefill", K.kv_prefill_attn_kernel_name(qd, dk, dv), "seq", s, "position", i, "rel err", err)
+        assert err <= DECODE_RTOL
