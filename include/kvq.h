@@ -30,7 +30,8 @@
  *    enqueues its kernels on `stream` and returns KVQ_OK without synchronizing.
  *  - Data conditions found on the device (non-finite input, fp16 overflow of a
  *    scale, zero point or normalizer) set bits in *status_flags; they never
- *    abort a launch.
+ *    abort a launch. The codes of a block with such a condition are
+ *    unspecified but stay in 0 .. 2^bits - 1.
  *  - The library allocates no device memory and keeps no mutable global state;
  *    calls on different streams may run concurrently.
  */

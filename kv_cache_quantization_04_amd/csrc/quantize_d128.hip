@@ -210,28 +210,39 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
             for (int j = 0; j < 8; ++j) ssq += y[k][j] * y[k][j];
         if (!isfinite(ssq)) bad |= KVQ_FLAG_NONFINITE;
     }
+    // w holds 1 / c^2 in the first round and 1 / (128 c^2) after it (the mean over
+    // the 128 channels folded in: powers of two, so the row sums and u = 1 / r^2 are
+    // the same bits as with the plain mean)
     float w[8], u[R];
 #pragma unroll
     for (int j = 0; j < 8; ++j) w[j] = 1.f;
 #pragma unroll
     for (int k = 0; k < R; ++k) u[k] = 1.f;
-    const float fD = (float)QD, fn = (float)n;
+    const float fn = (float)n, fn_d = fn * (1.0f / QD);
     // owner of channel tid (tid < 128): column sum of the last round
     float t_own = 0.f;
-    constexpr float TINY = 1e-30f;
+    constexpr float TINY = 1e-30f, HUGE_F = 3.4028234663852886e38f;
 
 #pragma unroll
     for (int it = 0; it < iters; ++it) {
-        // row step: r^2 = mean_j A_ij w_j over the 128 channels. A zero row keeps a
-        // large finite u and contributes 0 * u = 0 below, as with an unchanged factor.
+        // row step: r^2 = mean_j A_ij / c_j^2 over the 128 channels. A zero row keeps
+        // a large finite u and contributes 0 * u = 0 below, as with an unchanged factor.
+        float rs[R];
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             float s = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) s = __builtin_fmaf(A[k][j], w[j], s);
-            s = row_sum16(s);
-            if (it == 0 && !isfinite(s)) bad |= KVQ_FLAG_NONFINITE;
-            u[k] = fD * __builtin_amdgcn_rcpf(fmaxf(s, TINY));
+            rs[k] = s;
+        }
+        row_sum16_x4(rs);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            if (it == 0 && !isfinite(rs[k])) bad |= KVQ_FLAG_NONFINITE;
+            // max(s, tiny) as a median with the largest float: one instruction (fmaxf would first
+            // quiet the value the DPP asm produced); a NaN sum is flagged above
+            u[k] = it == 0 ? (float)QD * __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY, HUGE_F))
+                           : __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY * (1.0f / QD), HUGE_F));
         }
         // column step: c^2 = mean_i A_ij u_i over the n valid rows
         float t[8];
@@ -267,7 +278,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
                 acc[v] = (colsum[4 * v][tid] + colsum[4 * v + 1][tid]) + (colsum[4 * v + 2][tid] + colsum[4 * v + 3][tid]);
             t_own = NWV == 8 ? acc[0] + acc[NWV / 8] : acc[0];
             // a zero column keeps a large finite w (its A entries are all zero)
-            wsh[tid] = fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
+            wsh[tid] = fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
         }
         lds_barrier();
         const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[pcc * 8]);
@@ -305,20 +316,26 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 #pragma unroll
     for (int j = 0; j < 8; ++j) cma[j] = cmb[j] = 0;
     uint8_t *cbase = reinterpret_cast<uint8_t *>(outbuf);  // LDS image of the code block
+    // y -> y / c16 (scaled, signed), in place; row minima and maxima over the 128 channels
+    float mnr[R], mxr[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[k][j] *= mult[j];
+        float mn = y[k][0], mx = y[k][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+            mn = fminf(mn, y[k][j]);
+            mx = fmaxf(mx, y[k][j]);
+        }
+        mnr[k] = mn;
+        mxr[k] = mx;
+    }
+    row_minmax16_x4(mnr, mxr);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
         const int row = rg * R + k;
-        float yy[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) yy[j] = y[k][j] * mult[j];
-        float mn = yy[0], mx = yy[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) {
-            mn = fminf(mn, yy[j]);
-            mx = fmaxf(mx, yy[j]);
-        }
-        mn = row_min16(mn);
-        mx = row_max16(mx);
+        const float mn = mnr[k], mx = mxr[k];
         uint16_t S16 = 0, Z16 = 0;
         if (row < n) {
             S16 = float_to_half_bits((mx - mn) * (1.0f / LEVELS));
@@ -328,9 +345,17 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
         const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
         const float zi = -Zv * inv;
-        float q[8];  // (y - Z) / S, clamped above; rounding and the lower clamp in cvt_pk_u8
+        // (y - Z) / S; cvt_pk_u8 rounds to nearest even and clamps below at 0. The upper
+        // clamp changes a code only for a value at or above LEVELS + 1/2 (below it the
+        // rounding gives at most LEVELS), and the map is monotone (inv >= 0), so only when
+        // the row's largest value gets there: fp16 rounding of S and Z far larger than
+        // usual (an offset much larger than the range), or a non-finite value
+        float q[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) q[j] = fminf(__builtin_fmaf(yy[j], inv, zi), LEVELS);
+        for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[k][j], inv, zi);
+        if (bad || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = fminf(q[j], LEVELS);
         if (cc == 0) szbuf[row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
             const uint32_t word = pack8<BITS>(q);

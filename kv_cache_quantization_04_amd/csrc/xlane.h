@@ -61,6 +61,39 @@ __device__ __forceinline__ void hadamard16_lanes(float *v, int cc) {
 }
 #undef KVQ_DPP_FMAC8
 
+// Sum over the 16 lanes of a DPP row of four independent values, and min and max
+// of four more, in DPP-fused instructions (t <- op(partner, t)): the stages rotate
+// by 8 and by 4 inside the row, then swap lanes 2 and 1 apart inside each quad.
+// Each instruction's DPP source was written one stage (four or eight instructions)
+// earlier, so only the first stage needs the two wait states after the caller's
+// writes.
+#define KVQ_DPP_OP4(OP, CTRL)                                                                     \
+    OP "_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t" OP "_dpp %1, %1, %1 " CTRL \
+       " row_mask:0xf bank_mask:0xf\n\t" OP "_dpp %2, %2, %2 " CTRL                           \
+       " row_mask:0xf bank_mask:0xf\n\t" OP "_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void row_sum16_x4(float (&v)[4]) {
+    asm volatile("s_nop 1\n\t" KVQ_DPP_OP4("v_add_f32", "row_ror:8") KVQ_DPP_OP4("v_add_f32", "row_ror:4")
+                     KVQ_DPP_OP4("v_add_f32", "quad_perm:[2,3,0,1]") KVQ_DPP_OP4("v_add_f32", "quad_perm:[1,0,3,2]")
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+#define KVQ_DPP_MINMAX(CTRL)                                                                              \
+    "v_min_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                                 \
+    "v_min_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                                 \
+    "v_min_f32_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                                 \
+    "v_min_f32_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                                 \
+    "v_max_f32_dpp %4, %4, %4 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                                 \
+    "v_max_f32_dpp %5, %5, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                                 \
+    "v_max_f32_dpp %6, %6, %6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                                 \
+    "v_max_f32_dpp %7, %7, %7 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void row_minmax16_x4(float (&mn)[4], float (&mx)[4]) {
+    asm volatile("s_nop 1\n\t" KVQ_DPP_MINMAX("row_ror:8") KVQ_DPP_MINMAX("row_ror:4")
+                     KVQ_DPP_MINMAX("quad_perm:[2,3,0,1]") KVQ_DPP_MINMAX("quad_perm:[1,0,3,2]")
+                 : "+v"(mn[0]), "+v"(mn[1]), "+v"(mn[2]), "+v"(mn[3]), "+v"(mx[0]), "+v"(mx[1]), "+v"(mx[2]),
+                   "+v"(mx[3]));
+}
+#undef KVQ_DPP_OP4
+#undef KVQ_DPP_MINMAX
+
 // Sum / min / max over the 16 lanes of a DPP row; every lane gets the same bits.
 __device__ __forceinline__ float row_sum16(float s) {
     s += dpp<DPP_ROR8>(s);
