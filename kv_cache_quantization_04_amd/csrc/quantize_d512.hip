@@ -193,12 +193,16 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                 for (int e = 0; e < 32; ++e) ssq = __builtin_fmaf(y[k][e], y[k][e], ssq);
             if (!isfinite(ssq)) bad |= KVQ_FLAG_NONFINITE;
         }
+        // w holds 1 / c^2 before the first round and 1 / (512 c^2) after it (the mean over
+        // the 512 channels folded in: powers of two, so the row sums and u = 1 / r^2 are
+        // the same bits as with the plain mean)
         float u[4];
-        const float fD = (float)LD, fn = (float)n;
+        const float fn = (float)n, fn_d = fn * (1.0f / LD);
+        constexpr float HUGE_F = 3.4028234663852886e38f;
         float t_own = 0.f;  // column sum of channel tid (last round)
 #pragma unroll
         for (int it = 0; it < iters; ++it) {
-            // row step: r^2 = mean_j A_ij w_j, the lane's w read four at a time (w = 1 before the first round)
+            // row step: r^2 = mean_j A_ij / c_j^2, the lane's w read four at a time (w = 1 before the first round)
             float sk[4] = {0.f, 0.f, 0.f, 0.f};
             const float *wprev = (it & 1) ? wsh0 : wsh1;  // written by the previous round
 #pragma unroll
@@ -211,11 +215,14 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
 #pragma unroll
                     for (int h = 0; h < 4; ++h) sk[k] = __builtin_fmaf(y[k][4 * i + h] * w4[h], y[k][4 * i + h], sk[k]);
             }
+            row_sum16_x4(sk);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float s = row_sum16(sk[k]);
-                if (it == 0 && !isfinite(s)) bad |= KVQ_FLAG_NONFINITE;
-                u[k] = fD * __builtin_amdgcn_rcpf(fmaxf(s, TINY));
+                if (it == 0 && !isfinite(sk[k])) bad |= KVQ_FLAG_NONFINITE;
+                // max(s, tiny) as a median with the largest float: one instruction (fmaxf
+                // would first quiet the value the DPP asm produced); a NaN sum is flagged
+                u[k] = it == 0 ? (float)LD * __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(sk[k], TINY, HUGE_F))
+                               : __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(sk[k], TINY * (1.0f / LD), HUGE_F));
             }
             float t[32];
 #pragma unroll
@@ -245,7 +252,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                 const int pc = pch(tid);
                 t_own = lds_sum8_stride(&colsum[0][pc]);
                 // a zero column keeps a large finite w (its A entries are all zero)
-                lds_store_f32(&wsh[pc], fn * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY)));
+                lds_store_f32(&wsh[pc], fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY)));
             }
             lds_barrier();  // w of this round visible to every lane
         }
@@ -274,17 +281,23 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
 
         // ---- per token: asymmetric RTN with fp16 (S, Z); 32 codes per lane and row
         uint8_t *codes = a.codes + blk * (LT * LD * BITS / 8);
+        float mnr[4], mxr[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int row = 4 * rg + k;
             float mn = y[k][0], mx = y[k][0];
 #pragma unroll
             for (int e = 1; e < 32; ++e) {
                 mn = fminf(mn, y[k][e]);
                 mx = fmaxf(mx, y[k][e]);
             }
-            mn = row_min16(mn);
-            mx = row_max16(mx);
+            mnr[k] = mn;
+            mxr[k] = mx;
+        }
+        row_minmax16_x4(mnr, mxr);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = 4 * rg + k;
+            const float mn = mnr[k], mx = mxr[k];
             uint16_t S16 = 0, Z16 = 0;
             if (row < n) {
                 S16 = float_to_half_bits((mx - mn) * (1.0f / LEVELS));
@@ -294,33 +307,45 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
             if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
             const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
             const float zi = -Zv * inv;
-            // (y - Z) / S, clamped above; rounding and the lower clamp in v_cvt_pk_u8_f32
-            uint32_t word[BITS];
-            if constexpr (BITS == 4) {
+            // (y - Z) / S; v_cvt_pk_u8_f32 rounds to nearest even and clamps below at 0.
+            // The upper clamp changes a code only for a value at or above LEVELS + 1/2, and
+            // the map is monotone (inv >= 0), so only when the row's largest value gets there
+            // (fp16 rounding of S and Z far larger than usual, or a non-finite value): the
+            // packing runs in one of two copies, with and without it
+            auto pack_row = [&](auto clamp) {
+                auto code = [&](float v) {
+                    const float q = __builtin_fmaf(v, inv, zi);
+                    return decltype(clamp)::value ? fminf(q, LEVELS) : q;
+                };
+                uint32_t word[BITS];
+                if constexpr (BITS == 4) {
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint32_t ev = 0, od = 0;
+                    for (int d = 0; d < 4; ++d) {
+                        uint32_t ev = 0, od = 0;
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        ev = __builtin_amdgcn_cvt_pk_u8_f32(fminf(__builtin_fmaf(y[k][8 * d + 2 * b], inv, zi), LEVELS), b, ev);
-                        od = __builtin_amdgcn_cvt_pk_u8_f32(fminf(__builtin_fmaf(y[k][8 * d + 2 * b + 1], inv, zi), LEVELS), b, od);
+                        for (int b = 0; b < 4; ++b) {
+                            ev = __builtin_amdgcn_cvt_pk_u8_f32(code(y[k][8 * d + 2 * b]), b, ev);
+                            od = __builtin_amdgcn_cvt_pk_u8_f32(code(y[k][8 * d + 2 * b + 1]), b, od);
+                        }
+                        word[d] = ev | (od << 4);
                     }
-                    word[d] = ev | (od << 4);
+                    *reinterpret_cast<uint4 *>(codes + row * (LD / 2) + 16 * pcc) = uint4{word[0], word[1], word[2], word[3]};
+                } else {  // BITS == 2: 16 codes per word
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        uint32_t q4[4] = {0, 0, 0, 0};
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+#pragma unroll
+                            for (int m = 0; m < 4; ++m)
+                                q4[m] = __builtin_amdgcn_cvt_pk_u8_f32(code(y[k][16 * d + 4 * b + m]), b, q4[m]);
+                        word[d] = q4[0] | (q4[1] << 2) | (q4[2] << 4) | (q4[3] << 6);
+                    }
+                    *reinterpret_cast<uint2 *>(codes + row * (LD / 4) + 8 * pcc) = uint2{word[0], word[1]};
                 }
-                *reinterpret_cast<uint4 *>(codes + row * (LD / 2) + 16 * pcc) = uint4{word[0], word[1], word[2], word[3]};
-            } else {  // BITS == 2: 16 codes per word
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    uint32_t q4[4] = {0, 0, 0, 0};
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            q4[m] = __builtin_amdgcn_cvt_pk_u8_f32(fminf(__builtin_fmaf(y[k][16 * d + 4 * b + m], inv, zi), LEVELS), b, q4[m]);
-                    word[d] = q4[0] | (q4[1] << 2) | (q4[2] << 4) | (q4[3] << 6);
-                }
-                *reinterpret_cast<uint2 *>(codes + row * (LD / 4) + 8 * pcc) = uint2{word[0], word[1]};
-            }
+            };
+            if (bad || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f)) pack_row(std::true_type{});
+            else pack_row(std::false_type{});
             if (cc == 0) reinterpret_cast<uint32_t *>(a.sz)[blk * LT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         }
         if (a.R == 64) {

@@ -121,22 +121,34 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
                 for (int j = 0; j < 8; ++j) ssq += A[k][j];
             if (!isfinite(ssq)) bad |= KVQ_FLAG_NONFINITE;
         }
+        // w holds 1 / c^2 in the first round and 1 / (128 c^2) after it (the mean over
+        // the 128 channels folded in: powers of two, so the row sums and u = 1 / r^2 are
+        // the same bits as with the plain mean)
         float w[8], u[4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) w[j] = 1.f;
-        const float fD = (float)ZD, fn = (float)n;
+        const float fn = (float)n, fn_d = fn * (1.0f / ZD);
+        constexpr float HUGE_F = 3.4028234663852886e38f;
         float t_own[2] = {0.f, 0.f};  // column sums of channels 8 cc + 2 rr + {0, 1} (last round)
 #pragma unroll
         for (int it = 0; it < iters; ++it) {
-            // row step: r^2 = mean_j A_ij w_j over the 128 channels
+            // row step: r^2 = mean_j A_ij / c_j^2 over the 128 channels
+            float rs[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float s = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) s = __builtin_fmaf(A[k][j], w[j], s);
-                s = row_sum16(s);
-                if (it == 0 && !isfinite(s)) bad |= KVQ_FLAG_NONFINITE;
-                u[k] = fD * __builtin_amdgcn_rcpf(fmaxf(s, TINY));
+                rs[k] = s;
+            }
+            row_sum16_x4(rs);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (it == 0 && !isfinite(rs[k])) bad |= KVQ_FLAG_NONFINITE;
+                // max(s, tiny) as a median with the largest float: one instruction (fmaxf
+                // would first quiet the value the DPP asm produced); a NaN sum is flagged
+                u[k] = it == 0 ? (float)ZD * __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY, HUGE_F))
+                               : __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY * (1.0f / ZD), HUGE_F));
             }
             // column step: c^2 = mean_i A_ij u_i over the n valid rows (padding rows are zero)
             float t[8];
@@ -160,7 +172,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
             }
             // a zero column keeps a large finite w (its A entries are all zero)
             *reinterpret_cast<float2 *>(&cv[8 * pcc + 2 * rr]) =
-                float2{fn * __builtin_amdgcn_rcpf(fmaxf(t_own[0], TINY)), fn * __builtin_amdgcn_rcpf(fmaxf(t_own[1], TINY))};
+                float2{fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[0], TINY)), fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[1], TINY))};
             const float4 w0 = *reinterpret_cast<const float4 *>(&cv[8 * pcc]);
             const float4 w1 = *reinterpret_cast<const float4 *>(&cv[8 * pcc + 4]);
             w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
@@ -197,20 +209,26 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
         uint32_t cm[8];  // channel-major: bytes of rows 4 rr .. + 3 of channel 8 cc + j
 #pragma unroll
         for (int j = 0; j < 8; ++j) cm[j] = 0;
+        // y -> y / c16 (scaled, signed), in place; row minima and maxima over the 128 channels
+        float mnr[4], mxr[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[k][j] *= mult[j];
+            float mn = y[k][0], mx = y[k][0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) {
+                mn = fminf(mn, y[k][j]);
+                mx = fmaxf(mx, y[k][j]);
+            }
+            mnr[k] = mn;
+            mxr[k] = mx;
+        }
+        row_minmax16_x4(mnr, mxr);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int row = 4 * rr + k;
-            float yy[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) yy[j] = y[k][j] * mult[j];
-            float mn = yy[0], mx = yy[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) {
-                mn = fminf(mn, yy[j]);
-                mx = fmaxf(mx, yy[j]);
-            }
-            mn = row_min16(mn);
-            mx = row_max16(mx);
+            const float mn = mnr[k], mx = mxr[k];
             uint16_t S16 = 0, Z16 = 0;
             if (row < n) {
                 S16 = float_to_half_bits((mx - mn) * (1.0f / LEVELS));
@@ -220,9 +238,15 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
             if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
             const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
             const float zi = -Zv * inv;
-            float q[8];  // (y - Z) / S, clamped above; rounding and the lower clamp in cvt_pk_u8
+            // (y - Z) / S; cvt_pk_u8 rounds to nearest even and clamps below at 0. The upper
+            // clamp changes a code only for a value at or above LEVELS + 1/2, and the map
+            // is monotone (inv >= 0), so only when the row's largest value gets there
+            float q[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = fminf(__builtin_fmaf(yy[j], inv, zi), LEVELS);
+            for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[k][j], inv, zi);
+            if (bad || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = fminf(q[j], LEVELS);
             if (cc == 0)
                 reinterpret_cast<uint32_t *>(a.sz)[blk * ZT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
             if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
