@@ -155,11 +155,20 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
     const int64_t blk = (int64_t)dst_page * a.H + head;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into LDS have landed
     lds_barrier();                  // and every other wave's
+    // rows past the valid ones hold copies of the last valid row (see fetch): read
+    // unconditionally, zeroed below only when the tile is partial (a uniform branch)
+    uint4 v4[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) v4[k] = stage[(rg * R + k) * 16 + (cc ^ rr)];
+    if (n < T) {
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (rg * R + k >= n) v4[k] = uint4{0, 0, 0, 0};
+    }
     float y[R][8];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-        const int row = rg * R + k;
-        const uint4 v = row < n ? stage[row * 16 + (cc ^ rr)] : uint4{0, 0, 0, 0};
+        const uint4 v = v4[k];
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -201,14 +210,15 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         for (int j = 0; j < 8; ++j) A[k][j] = y[k][j] * y[k][j];
     // non-finite detector: a row's sum of squares is finite iff the row is
     // (first round below; computed here when there is no round)
-    uint32_t bad = 0;
+    // data conditions of this lane (lane masks: no vector registers)
+    bool nonfinite = false, sideov = false;
     if (iters == 0) {
         float ssq = 0.f;
 #pragma unroll
         for (int k = 0; k < R; ++k)
 #pragma unroll
             for (int j = 0; j < 8; ++j) ssq += y[k][j] * y[k][j];
-        if (!isfinite(ssq)) bad |= KVQ_FLAG_NONFINITE;
+        if (!isfinite(ssq)) nonfinite = true;
     }
     // w holds 1 / c^2 in the first round and 1 / (128 c^2) after it (the mean over
     // the 128 channels folded in: powers of two, so the row sums and u = 1 / r^2 are
@@ -238,7 +248,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         row_sum16_x4(rs);
 #pragma unroll
         for (int k = 0; k < R; ++k) {
-            if (it == 0 && !isfinite(rs[k])) bad |= KVQ_FLAG_NONFINITE;
+            if (it == 0 && !isfinite(rs[k])) nonfinite = true;
             // max(s, tiny) as a median with the largest float: one instruction (fmaxf would first
             // quiet the value the DPP asm produced); a NaN sum is flagged above
             u[k] = it == 0 ? (float)QD * __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY, HUGE_F))
@@ -295,7 +305,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         const float csq = (iters > 0 && n > 0 && t_own > 0.f && t_own < INFINITY) ? t_own / fn : 1.f;
         const uint16_t c16 = float_to_half_bits(sqrtf(csq));
         const float cv = half_bits_to_float(c16);
-        if (!(cv > 0.f && cv < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
+        if (!(cv > 0.f && cv < INFINITY)) sideov = true;
         multsh[tid] = INV_SQRT_H / cv;
         a.cnorm[blk * QD + tid] = c16;
     }
@@ -342,7 +352,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
             Z16 = float_to_half_bits(mn);
         }
         const float Sv = half_bits_to_float(S16), Zv = half_bits_to_float(Z16);
-        if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
+        if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) sideov = true;
         const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
         const float zi = -Zv * inv;
         // (y - Z) / S; cvt_pk_u8 rounds to nearest even and clamps below at 0. The upper
@@ -353,7 +363,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         float q[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[k][j], inv, zi);
-        if (bad || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))
+        if (nonfinite || sideov || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))
 #pragma unroll
             for (int j = 0; j < 8; ++j) q[j] = fminf(q[j], LEVELS);
         if (cc == 0) szbuf[row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
@@ -402,8 +412,8 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
             reinterpret_cast<uint4 *>(a.sz + blk * T * 2)[tid] = reinterpret_cast<const uint4 *>(szbuf)[tid];
     }
     if (a.flags) {  // one atomic per wave that saw a condition; no barrier
-        const bool nf = __ballot((bad & KVQ_FLAG_NONFINITE) != 0) != 0;
-        const bool so = __ballot((bad & KVQ_FLAG_SIDE_OVERFLOW) != 0) != 0;
+        const bool nf = __ballot(nonfinite) != 0;
+        const bool so = __ballot(sideov) != 0;
         if (lane == 0 && (nf || so))
             atomicOr(a.flags, (nf ? (uint32_t)KVQ_FLAG_NONFINITE : 0u) | (so ? (uint32_t)KVQ_FLAG_SIDE_OVERFLOW : 0u));
     }
