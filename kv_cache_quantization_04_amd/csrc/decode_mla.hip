@@ -28,6 +28,7 @@
 // registers while the current page is processed from LDS.
 #include "common.h"
 #include "launch.h"
+#include "xlane.h"
 
 namespace kvq {
 
@@ -96,16 +97,8 @@ __device__ __forceinline__ float code_over(float x) {
     return __uint_as_float((uint32_t)min(254, 254 + CODE_EXP - (int)(__float_as_uint(x) >> 23)) << 23);
 }
 
-__device__ __forceinline__ float lq_sum(float v) {  // over the 4 lanes sharing lane & 15
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-__device__ __forceinline__ float lq_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
-}
+__device__ __forceinline__ float lq_sum(float v) { return sum_x4rows(v); }  // the 4 lanes sharing lane & 15
+__device__ __forceinline__ float lq_max(float v) { return max_x4rows(v); }
 
 __device__ __forceinline__ uint16_t bf16_rn(float f) {  // fp32 -> bf16 bits, nearest even (finite inputs)
     uint32_t u = __float_as_uint(f);
@@ -239,9 +232,11 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         for (int st = 0; st < 16; ++st)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float v = q[st][e];
-                v = __builtin_fmaf(s16, v, __shfl_xor(v, 16, 64));
-                v = __builtin_fmaf(s32, v, __shfl_xor(v, 32, 64));
+                float v = q[st][e], lo, hi;
+                pair16(v, lo, hi);
+                v = __builtin_fmaf(s16, hi, lo);
+                pair32(v, lo, hi);
+                v = __builtin_fmaf(s32, hi, lo);
                 v *= INV_SQRT;
                 qmax = fmaxf(qmax, fabsf(v));
                 q[st][e] = v;
@@ -312,8 +307,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 cmax = fmaxf(cmax, fmaxf(fabsf(half_bits_to_float(w4[i] & 0xffffu)), fabsf(half_bits_to_float(w4[i] >> 16))));
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, m, 64));
+            cmax = max_x4rows(row_max16(cmax));  // all 64 lanes
         }
         const float qsc = pow2_scale(qmax * cmax);
         const float qinv = code_over(qsc);  // undoes the query scaling and the code unit

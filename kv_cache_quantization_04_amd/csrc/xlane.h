@@ -94,6 +94,37 @@ __device__ __forceinline__ void row_minmax16_x4(float (&mn)[4], float (&mx)[4]) 
 #undef KVQ_DPP_OP4
 #undef KVQ_DPP_MINMAX
 
+// Lanes 16 and 32 apart, through the gfx950 permlane swaps (VALU, no LDS round trip).
+// Swapping x with itself leaves in `lo` the value of the even 16-lane row (pair16) or
+// of the lower 32 lanes (pair32) of the lane's pair, and in `hi` the odd / upper one:
+// lo + hi is the pair's sum in both lanes (same bits), and lo + s hi with s = -1 on the
+// odd / upper member is the Walsh-Hadamard butterfly (even: x + partner, odd: partner - x).
+__device__ __forceinline__ void pair16(float x, float &lo, float &hi) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float &lo, float &hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+// sum / max over the four lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float sum_x4rows(float v) {
+    float lo, hi;
+    pair16(v, lo, hi);
+    v = lo + hi;
+    pair32(v, lo, hi);
+    return lo + hi;
+}
+__device__ __forceinline__ float max_x4rows(float v) {
+    float lo, hi;
+    pair16(v, lo, hi);
+    v = fmaxf(lo, hi);
+    pair32(v, lo, hi);
+    return fmaxf(lo, hi);
+}
+
 // Sum / min / max over the 16 lanes of a DPP row; every lane gets the same bits.
 __device__ __forceinline__ float row_sum16(float s) {
     s += dpp<DPP_ROR8>(s);
