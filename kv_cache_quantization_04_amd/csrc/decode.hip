@@ -9,6 +9,7 @@
 // range through the block table and writes (m, l, o') to the workspace.
 #include "common.h"
 #include "launch.h"
+#include "xlane.h"
 
 namespace kvq {
 
@@ -196,14 +197,63 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Up to RED_FAST splits with at most two channels per lane: every load in one round
+// (split i's maximum and sum on lane i, all partial outputs on every lane), the
+// maxima and sums reduced over the first 16 lanes with DPP row operations and read
+// back as wave-uniform values; the outputs accumulate in split order, as below.
+constexpr int RED_FAST = 16;
+
+template <int E>
+__device__ __forceinline__ void reduce_weights_fast(const float *w, int S, int lane, float (&part)[RED_FAST][E],
+                                                    float (&e)[RED_FAST], float &l) {
+    constexpr int Dv = 64 * E;
+    float mi = -INFINITY, li = 0.f;
+    if (lane < S) {
+        mi = w[(int64_t)lane * (Dv + 2) + Dv];
+        li = w[(int64_t)lane * (Dv + 2) + Dv + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < RED_FAST; ++i) {
+        if (i < S) {  // uniform
+            const float *wi = w + (int64_t)i * (Dv + 2) + E * lane;
+            if constexpr (E == 1) part[i][0] = wi[0];
+            else {
+                const float2 v = *reinterpret_cast<const float2 *>(wi);
+                part[i][0] = v.x;
+                part[i][1] = v.y;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < E; ++k) part[i][k] = 0.f;
+        }
+    }
+    const float Mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_max16(mi))));
+    const float ei = mi == -INFINITY ? 0.f : __expf(mi - Mx);
+    l = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_sum16(ei * li))));
+#pragma unroll
+    for (int i = 0; i < RED_FAST; ++i) e[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ei), i));
+}
+
 template <int E>
 __device__ __forceinline__ void reduce_one(const DecodeArgs &a, int s, int hq, int lane, float *wgt) {
     constexpr int Dv = 64 * E;
     const float *w = a.ws + ((int64_t)s * a.Hq + hq) * a.splits * (Dv + 2);
+    float acc[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.f;
+    float l = 0.f;
+    if (E <= 2 && a.splits <= RED_FAST) {
+        float part[RED_FAST][E], e[RED_FAST];
+        reduce_weights_fast<E>(w, a.splits, lane, part, e, l);
+#pragma unroll
+        for (int i = 0; i < RED_FAST; ++i)
+            if (i < a.splits)
+#pragma unroll
+                for (int k = 0; k < E; ++k) acc[k] = __builtin_fmaf(e[i], part[i][k], acc[k]);
+    } else {
     float M = -INFINITY;
     for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, w[(int64_t)i * (Dv + 2) + Dv]);
     M = wave_max(M);
-    float l = 0.f;
     for (int i = lane; i < a.splits; i += 64) {
         const float mi = w[(int64_t)i * (Dv + 2) + Dv];
         const float e = mi == -INFINITY ? 0.f : __expf(mi - M);
@@ -211,9 +261,6 @@ __device__ __forceinline__ void reduce_one(const DecodeArgs &a, int s, int hq, i
         l = __builtin_fmaf(e, w[(int64_t)i * (Dv + 2) + Dv + 1], l);
     }
     l = wave_sum(l);  // the weights' LDS writes are ordered before the reads below (one wave)
-    float acc[E];
-#pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] = 0.f;
 #pragma unroll 4
     for (int i = 0; i < a.splits; ++i) {
         const float *wi = w + (int64_t)i * (Dv + 2) + E * lane;
@@ -228,10 +275,40 @@ __device__ __forceinline__ void reduce_one(const DecodeArgs &a, int s, int hq, i
             }
         }
     }
+    }
     const float invl = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
     for (int k = 0; k < E; ++k) acc[k] *= invl;
-    // Walsh-Hadamard over blocks of vh channels: channel c = E lane + k
+    // Walsh-Hadamard over blocks of vh channels: channel c = E lane + k. Two channels
+    // per lane and one block of 128 (head_dim 128): the lane stages by DPP, the LDS
+    // crossbar (ds_swizzle, no memory) and permlane swaps instead of LDS permutes
+    if (E == 2 && a.vh == 128) {
+        {
+            const float x = acc[0], y = acc[E - 1];
+            acc[0] = x + y;
+            acc[E - 1] = x - y;
+        }
+        auto stage = [&](auto pv_of, int m) {
+            const bool upper = (lane & m) != 0;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const float pv = pv_of(acc[k]);
+                acc[k] = upper ? pv - acc[k] : acc[k] + pv;
+            }
+        };
+        stage([](float v) { return dpp<DPP_QUAD_XOR1>(v); }, 1);
+        stage([](float v) { return dpp<DPP_QUAD_XOR2>(v); }, 2);
+        stage([](float v) { return swz_xor<4>(v); }, 4);
+        stage([](float v) { return swz_xor<8>(v); }, 8);
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            float lo, hi;
+            pair16(acc[k], lo, hi);
+            acc[k] = (lane & 16) ? lo - hi : lo + hi;
+            pair32(acc[k], lo, hi);
+            acc[k] = (lane & 32) ? lo - hi : lo + hi;
+        }
+    } else
     for (int len = 1; len < a.vh; len <<= 1) {
         if (len < E) {
 #pragma unroll
