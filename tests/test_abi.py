@@ -96,6 +96,10 @@ def test_decode_argument_errors():
     need = K.kv_decode_attn_workspace_bytes(2, 8, 128, 3)
     assert need == 2 * 8 * 3 * 130 * 4
     assert st(splits=3, ws_bytes=need - 1) == K.KVQ_EWORKSPACE
+    assert st(splits=1025) == K.KVQ_EUNSUPPORTED     # more split partials than the merge takes
+    # no sequences: nothing to do, nothing launched (block table and workspace not needed)
+    assert K._lib.kv_decode_attn(FAKE, 2, 0, 8, ctypes.byref(kc), ctypes.byref(vc), None, 0, None, 0, 0.1, 0, None, 0,
+                                 FAKE, None) == K.KVQ_OK
 
 
 def default_splits(fk, fv, num_seqs, num_q_heads, num_kv_heads, max_len, pages=1 << 16):

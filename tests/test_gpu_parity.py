@@ -112,7 +112,8 @@ def check_quantize_case(gpu, case, center=0):
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + center)
     f = W.Fmt(D, R, T, h, G, bits, iters, layout, center)
     H = 2
-    lens = [3 * T + T // 2 + 1, 1, T, 0] if T <= 64 else [2 * T + 37, 1, T]
+    # a full tile, a one-token tile, an empty tile (no valid row) and partial tiles
+    lens = [3 * T + T // 2 + 1, 1, T, 0] if T <= 64 else [2 * T + 37, 1, T, 0]
     tst, tv, tp, tok = tiles_for(lens, T, rng)
     xl = heavy(rng, tok, H, D)
     if center:  # per-channel offsets, so that column and row means are far from zero
@@ -416,8 +417,10 @@ def test_prefill_chunk_is_causal_decode(gpu, kw, splits):
 
 
 @pytest.mark.parametrize("kw", DEC_SMALL, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) or "default")
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("splits", [0, 1, 3, 40, 100])
 def test_decode_small(gpu, kw, splits):
+    """More splits than pages leave empty partials; above 16 splits the merge takes its
+    general path (above 64, each lane weighs several splits)."""
     log("decode case", kw, "splits", splits)
     w = small_paged(11 + len(kw), **kw)
     out, ref, *_ = run_decode_case(gpu, w, 1.0 / math.sqrt(w["fk"].head_dim + w["fk"].rope_dim), splits)
