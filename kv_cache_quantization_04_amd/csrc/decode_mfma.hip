@@ -30,6 +30,11 @@
 
 namespace kvq {
 
+// 2^x as the bare v_exp_f32: exp2f adds a range split (two selects, an add and a
+// ldexp) to return denormal results, and the weights here are at most 1, so one
+// below 2^-126 flushing to zero changes nothing; exp2_fast(-inf) = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -456,7 +461,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         // a prefill column may have seen no valid token yet: exponents against 0 then
         // give alpha = 0 and p = 0 (decode pages always hold a valid token)
         if constexpr (PF) m_new = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = exp2_fast(m_run - m_new);
         m_run = PF ? fmaxf(m_run, pmax) : m_new;
         // P~ = p S_V scaled by 2^sp with max_t S_V,t near 2^14 (p <= 1)
         float smax = 0.f;
@@ -475,7 +480,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float SV = half_bits_to_float(vzw[i] & 0xffffu), ZV = half_bits_to_float(vzw[i] >> 16);
-                const float p = exp2f(sc[j][i] - m_new);
+                const float p = exp2_fast(sc[j][i] - m_new);
                 psum += p;
                 zs = __builtin_fmaf(p, ZV, zs);
                 split_h(p * SV * psc, phi[j][i], plo[j][i]);
@@ -598,7 +603,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         for (int w = 0; w < 4; ++w) {
             const float mw = red_ml[w][cc][0];
             if (mw != -INFINITY) {
-                const float f = exp2f(mw - M);
+                const float f = exp2_fast(mw - M);
                 acc = __builtin_fmaf(f, red_o[w][cc][j], acc);
                 lsum = __builtin_fmaf(f, red_ml[w][cc][1], lsum);
             }

@@ -32,6 +32,11 @@
 
 namespace kvq {
 
+// 2^x as the bare v_exp_f32: exp2f adds a range split (two selects, an add and a
+// ldexp) to return denormal results, and the weights here are at most 1, so one
+// below 2^-126 flushing to zero changes nothing; exp2_fast(-inf) = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -420,7 +425,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         pmax = lq_max(pmax);
         smax = lq_max(smax);
         const float m_new = fmaxf(m_run, pmax);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
         const float psc = pow2_scale(smax), pinv = code_over(psc);
         float psum = 0.f, zs = 0.f;
@@ -437,7 +442,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float S = half_bits_to_float(z4[i] & 0xffffu), Z = half_bits_to_float(z4[i] >> 16);
-                const float p = exp2f(sc[j][i] - m_new);
+                const float p = exp2_fast(sc[j][i] - m_new);
                 psum += p;
                 zs = __builtin_fmaf(p, Z, zs);
                 const float xs = p * S * psc;
