@@ -38,11 +38,15 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MD = 128;      // head_dim of this kernel
 constexpr int MNT = 256;     // threads per workgroup (4 waves)
 
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+// a * b with a an fp16 value: one mixed-precision FMA (v_fma_mix_f32) instead of a
+// conversion and a multiply
+__device__ __forceinline__ float mul_h(_Float16 a, float b) { return __builtin_fmaf((float)a, b, 0.f); }
 __device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
 // Eight codes of one lane chunk -> half8 in MFMA element order kk, where element
@@ -393,8 +397,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         for (int st = 0; st < 4; ++st)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t w = cw[st * 4 + (e >> 1)];
-                const float x = qv[st * 8 + e] * half_bits_to_float((e & 1) ? (w >> 16) : (w & 0xffffu));
+                const half2v c2 = as_h2(cw[st * 4 + (e >> 1)]);
+                const float x = mul_h((e & 1) ? c2.y : c2.x, qv[st * 8 + e]);
                 qt[st * 8 + e] = x;
                 qc += x;
                 qmax = fmaxf(qmax, fabsf(x));
@@ -435,6 +439,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
 
         // ---- online softmax over this page (per head l16; lanes hold tokens)
+        // score in log2 units: sm log2(e) (S qinv acc + Z sum_j q'_j)
+        const float a_s = sml2 * qinv, a_z = sml2 * qc;
         float pmax = -INFINITY;
         uint4 vzq[MT];
 #pragma unroll
@@ -449,8 +455,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             const uint32_t kzw[4] = {kz.x, kz.y, kz.z, kz.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float S = half_bits_to_float(kzw[i] & 0xffffu), Z = half_bits_to_float(kzw[i] >> 16);
-                float x = sml2 * __builtin_fmaf(S * qinv, sc[j][i], Z * qc);
+                const half2v sz = as_h2(kzw[i]);  // (S, Z)
+                float x = __builtin_fmaf((float)sz.x, a_s * sc[j][i], mul_h(sz.y, a_z));
                 if (tok0 + i >= rows) x = -INFINITY;
                 sc[j][i] = x;
                 pmax = fmaxf(pmax, x);
@@ -463,14 +469,18 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         if constexpr (PF) m_new = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2_fast(m_run - m_new);
         m_run = PF ? fmaxf(m_run, pmax) : m_new;
-        // P~ = p S_V scaled by 2^sp with max_t S_V,t near 2^14 (p <= 1)
-        float smax = 0.f;
+        // P~ = p S_V scaled by 2^sp with max_t S_V,t near 2^14 (p <= 1). The scales are
+        // >= 0, so the largest is the largest fp16 bit pattern (packed u16 maxima; the
+        // zero points in the upper halves are ignored)
+        uint32_t smaxw = 0;
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
             const uint32_t vzw[4] = {vzq[j].x, vzq[j].y, vzq[j].z, vzq[j].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) smax = fmaxf(smax, fabsf(half_bits_to_float(vzw[i] & 0xffffu)));
+            for (int i = 0; i < 4; ++i) smaxw = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                                                   __builtin_bit_cast(u16x2, smaxw), __builtin_bit_cast(u16x2, vzw[i])));
         }
+        const float smax = half_bits_to_float(smaxw & 0x7fffu);
         const float psc = pow2_scale_for(xlane_max_q(smax));
         float psum = 0.f, zs = 0.f;
         _Float16 phi[MT][4], plo[MT][4];
@@ -479,11 +489,11 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             const uint32_t vzw[4] = {vzq[j].x, vzq[j].y, vzq[j].z, vzq[j].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float SV = half_bits_to_float(vzw[i] & 0xffffu), ZV = half_bits_to_float(vzw[i] >> 16);
+                const half2v sz = as_h2(vzw[i]);  // (S_V, Z_V)
                 const float p = exp2_fast(sc[j][i] - m_new);
                 psum += p;
-                zs = __builtin_fmaf(p, ZV, zs);
-                split_h(p * SV * psc, phi[j][i], plo[j][i]);
+                zs = __builtin_fmaf((float)sz.y, p, zs);
+                split_h(mul_h(sz.x, p * psc), phi[j][i], plo[j][i]);
             }
         }
         const float pinv = pow2_over<CODE_EXP<VB>>(psc);
@@ -566,10 +576,10 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
             // fold: o' = alpha o' + c_V (acc + zs); rows 4 lq + i of tile mc are channels
             const uint2 cv2 = *reinterpret_cast<const uint2 *>(vcn + 16 * mc + 4 * lq);
-            const float cvv[4] = {half_bits_to_float(cv2.x & 0xffffu), half_bits_to_float(cv2.x >> 16),
-                                  half_bits_to_float(cv2.y & 0xffffu), half_bits_to_float(cv2.y >> 16)};
+            const half2v c01 = as_h2(cv2.x), c23 = as_h2(cv2.y);
+            const _Float16 cvv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf(o[mc][i], alpha, cvv[i] * __builtin_fmaf(acc[i], pinv, zs));
+            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf(o[mc][i], alpha, mul_h(cvv[i], __builtin_fmaf(acc[i], pinv, zs)));
         }
     }
 
