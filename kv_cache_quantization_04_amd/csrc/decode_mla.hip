@@ -44,6 +44,19 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// a * b with a an fp16 value: one mixed-precision FMA (v_fma_mix_f32) instead of a
+// conversion and a multiply
+__device__ __forceinline__ float mul_h(_Float16 a, float b) { return __builtin_fmaf((float)a, b, 0.f); }
+// largest of the fp16 values (all >= 0) in the low and high halves of four words,
+// taken on the bit patterns (the order of non-negative fp16 values)
+__device__ __forceinline__ float max_h8(const uint32_t (&w)[4]) {
+    u16x2 m = __builtin_bit_cast(u16x2, w[0]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i]));
+    return half_bits_to_float(m.x > m.y ? m.x : m.y);
+}
 
 constexpr int XD = 512;    // latent channels
 constexpr int XR = 64;     // rope channels
@@ -309,10 +322,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         {
             const uint4 cw = *reinterpret_cast<const uint4 *>(work + L_CN + 16 * lane);
             const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                cmax = fmaxf(cmax, fmaxf(fabsf(half_bits_to_float(w4[i] & 0xffffu)), fabsf(half_bits_to_float(w4[i] >> 16))));
-            cmax = max_x4rows(row_max16(cmax));  // all 64 lanes
+            cmax = max_x4rows(row_max16(max_h8(w4)));  // all 64 lanes (normalizers are > 0)
         }
         const float qsc = pow2_scale(qmax * cmax);
         const float qinv = code_over(qsc);  // undoes the query scaling and the code unit
@@ -337,8 +347,8 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
                     const int e = (kk >> 1) + 4 * (kk & 1);
-                    const uint32_t w = c4[e >> 1];
-                    const float x = qv[st][e] * half_bits_to_float((e & 1) ? (w >> 16) : (w & 0xffffu));
+                    const half2v c2 = as_h2(c4[e >> 1]);
+                    const float x = mul_h((e & 1) ? c2.y : c2.x, qv[st][e]);
                     qc += x;
                     const float xs = x * qsc;
                     const _Float16 hi = (_Float16)xs;
@@ -371,7 +381,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                 const uint4 zw = *reinterpret_cast<const uint4 *>(work + L_SZ + 4 * t0);
                 const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[j][i] = __builtin_fmaf(half_bits_to_float(z4[i] & 0xffffu) * qinv, sc[j][i], rp[i]);
+                for (int i = 0; i < 4; ++i) sc[j][i] = __builtin_fmaf((float)as_h2(z4[i]).x, qinv * sc[j][i], rp[i]);  // qinv: a power of two
             }
             // the low half publishes its partial sums
             if (half == 0) {
@@ -406,7 +416,11 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         qc = lq_sum(qc);
 
         // ---- online softmax; lane (head l16, lq) holds tokens 64 pi2 + 16 lq + 4 b + i of tile (pi2, b)
-        float smax = 0.f, pmax = -INFINITY;
+        // scales are >= 0: their largest is the largest fp16 bit pattern (packed u16
+        // maxima; the zero points in the upper halves are ignored)
+        uint32_t smaxw = 0;
+        float pmax = -INFINITY;
+        const float a_z = sml2 * qc;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int t0 = 64 * (j >> 2) + 16 * olq + 4 * (j & 3);
@@ -414,16 +428,16 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float S = half_bits_to_float(z4[i] & 0xffffu), Z = half_bits_to_float(z4[i] >> 16);
-                smax = fmaxf(smax, fabsf(S));
-                float x = sml2 * __builtin_fmaf(Z, qc, sc[j][i]);
+                smaxw = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, smaxw),
+                                                                               __builtin_bit_cast(u16x2, z4[i])));
+                float x = __builtin_fmaf((float)as_h2(z4[i]).y, a_z, sml2 * sc[j][i]);
                 if (t0 + i >= rows) x = -INFINITY;
                 sc[j][i] = x;
                 pmax = fmaxf(pmax, x);
             }
         }
         pmax = lq_max(pmax);
-        smax = lq_max(smax);
+        const float smax = lq_max(half_bits_to_float(smaxw & 0x7fffu));
         const float m_new = fmaxf(m_run, pmax);
         const float alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
@@ -441,11 +455,11 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float S = half_bits_to_float(z4[i] & 0xffffu), Z = half_bits_to_float(z4[i] >> 16);
+                const half2v sz = as_h2(z4[i]);  // (S, Z)
                 const float p = exp2_fast(sc[j][i] - m_new);
                 psum += p;
-                zs = __builtin_fmaf(p, Z, zs);
-                const float xs = p * S * psc;
+                zs = __builtin_fmaf((float)sz.y, p, zs);
+                const float xs = mul_h(sz.x, p * psc);
                 const _Float16 hi = (_Float16)xs;
                 pbh[kap][2 * i + (j & 1)] = hi;
                 pbl[kap][2 * i + (j & 1)] = (_Float16)(xs - (float)hi);
@@ -473,10 +487,10 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             }
             // fold: rows 4 lq + i of tile mc are channels 16 mc + 4 lq + i
             const uint2 cv2 = *reinterpret_cast<const uint2 *>(cn + 16 * mc + 4 * lq);
-            const float cvv[4] = {half_bits_to_float(cv2.x & 0xffffu), half_bits_to_float(cv2.x >> 16),
-                                  half_bits_to_float(cv2.y & 0xffffu), half_bits_to_float(cv2.y >> 16)};
+            const half2v c01 = as_h2(cv2.x), c23 = as_h2(cv2.y);
+            const _Float16 cvv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[m2][i] = __builtin_fmaf(o[m2][i], alpha, cvv[i] * __builtin_fmaf(acc[i], pinv, zs));
+            for (int i = 0; i < 4; ++i) o[m2][i] = __builtin_fmaf(o[m2][i], alpha, mul_h(cvv[i], __builtin_fmaf(acc[i], pinv, zs)));
             if (m2 & 1) __builtin_amdgcn_sched_barrier(0);  // at most two tiles' operands in flight
         }
     }
