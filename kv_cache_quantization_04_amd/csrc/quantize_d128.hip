@@ -422,8 +422,8 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 
 // Four waves per SIMD (the second bound: HIP passes it on as the minimum waves per
 // execution unit), so at most 128 registers per lane: two 8-wave workgroups per
-// compute unit for 128-token tiles. Four rows per lane need a few more than that;
-// the compiler spills a handful of addresses, reloaded once per item.
+// compute unit for 128-token tiles. Every variant fits without spilling (the few
+// addresses that would not are recomputed from an opaque lane id where used).
 template <int T, int R, int BITS, int LAYOUT, int NIT>
 __global__ void __launch_bounds__(16 * T / R, 4) quantize_d128_kernel(QuantArgs a, int num_items) {
     constexpr int NWV = T / (4 * R);
