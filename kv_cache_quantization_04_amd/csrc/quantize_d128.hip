@@ -165,24 +165,30 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         for (int k = 0; k < R; ++k)
             if (rg * R + k >= n) v4[k] = uint4{0, 0, 0, 0};
     }
-    float y[R][8];
+    // channels 2i and 2i + 1 share word i: the first butterfly stage (channel bit 0)
+    // comes out of the packed pair directly, and so does each row's sum of squares of
+    // the source (by Parseval the rotated row's is 128 times it: the first row step)
+    float y[R][8], ssq[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
         const uint4 v = v4[k];
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            y[k][2 * i] = __uint_as_float(w4[i] << 16);
-            y[k][2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+            bf16_pair_butterfly(w4[i], y[k][2 * i], y[k][2 * i + 1]);
+            acc = bf16_pair_sumsq(w4[i], acc);
         }
+        ssq[k] = acc;
     }
     lds_barrier();  // the staging buffer is free again
     if (item + (int)gridDim.x < num_items) fetch(item + gridDim.x);
     if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
 
     // ---- unnormalized Walsh-Hadamard transform along the 128 channels -------
+    // (channel bit 0 done above)
 #pragma unroll
-    for (int s = 1; s < 8; s <<= 1)
+    for (int s = 2; s < 8; s <<= 1)
 #pragma unroll
         for (int k = 0; k < R; ++k)
 #pragma unroll
@@ -213,12 +219,10 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
     // data conditions of this lane (lane masks: no vector registers)
     bool nonfinite = false, sideov = false;
     if (iters == 0) {
-        float ssq = 0.f;
+        float t = 0.f;
 #pragma unroll
-        for (int k = 0; k < R; ++k)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ssq += y[k][j] * y[k][j];
-        if (!isfinite(ssq)) nonfinite = true;
+        for (int k = 0; k < R; ++k) t += ssq[k];
+        if (!isfinite(t)) nonfinite = true;
     }
     // w holds 1 / c^2 in the first round and 1 / (128 c^2) after it (the mean over
     // the 128 channels folded in: powers of two, so the row sums and u = 1 / r^2 are
@@ -237,12 +241,15 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
     for (int it = 0; it < iters; ++it) {
         // row step: r^2 = mean_j A_ij / c_j^2 over the 128 channels. A zero row keeps
         // a large finite u and contributes 0 * u = 0 below, as with an unchanged factor.
+        // (first round: c = 1, and the row's sum of squares is 128 times the source's)
         float rs[R];
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             float s = 0.f;
+            if (it == 0) s = ssq[k];
+            else
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s = __builtin_fmaf(A[k][j], w[j], s);
+                for (int j = 0; j < 8; ++j) s = __builtin_fmaf(A[k][j], w[j], s);
             rs[k] = s;
         }
         row_sum16_x4(rs);
@@ -250,8 +257,9 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         for (int k = 0; k < R; ++k) {
             if (it == 0 && !isfinite(rs[k])) nonfinite = true;
             // max(s, tiny) as a median with the largest float: one instruction (fmaxf would first
-            // quiet the value the DPP asm produced); a NaN sum is flagged above
-            u[k] = it == 0 ? (float)QD * __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY, HUGE_F))
+            // quiet the value the DPP asm produced); a NaN sum is flagged above. First round:
+            // u = 128 / (128 sum x^2) = 1 / sum x^2
+            u[k] = it == 0 ? __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY * (1.0f / QD), HUGE_F * (1.0f / QD)))
                            : __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY * (1.0f / QD), HUGE_F));
         }
         // column step: c^2 = mean_i A_ij u_i over the n valid rows

@@ -142,10 +142,7 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                                         : uint4{0, 0, 0, 0};
                 const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    y[k][8 * i + 2 * h] = __uint_as_float(w4[h] << 16);
-                    y[k][8 * i + 2 * h + 1] = __uint_as_float(w4[h] & 0xffff0000u);
-                }
+                for (int h = 0; h < 4; ++h) bf16_pair_butterfly(w4[h], y[k][8 * i + 2 * h], y[k][8 * i + 2 * h + 1]);
             }
         }
         // rope part (bf16, copied unrotated): two 16-byte chunks per thread, loaded now, stored at the end
@@ -165,11 +162,12 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
         if (item + (int)gridDim.x < num_items) fetch(item + gridDim.x);
         if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
 
-        // ---- unnormalized Walsh-Hadamard transform along the 512 channels: bits
-        // 0..4 in registers, bits 5..8 across lanes (DPP-fused multiply-adds);
-        // afterwards the lane holds sigma * Y of channels 32 pcc .. 32 pcc + 31
+        // ---- unnormalized Walsh-Hadamard transform along the 512 channels: bit 0
+        // straight from the packed source pairs (above), bits 1..4 in registers, bits
+        // 5..8 across lanes (DPP-fused multiply-adds); afterwards the lane holds
+        // sigma * Y of channels 32 pcc .. 32 pcc + 31
 #pragma unroll
-        for (int s = 1; s < 32; s <<= 1)
+        for (int s = 2; s < 32; s <<= 1)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
 #pragma unroll

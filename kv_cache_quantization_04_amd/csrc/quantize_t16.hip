@@ -81,19 +81,17 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
         for (int k = 0; k < 4; ++k) {
             const uint32_t w4[4] = {nxt.v[k].x, nxt.v[k].y, nxt.v[k].z, nxt.v[k].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                y[k][2 * i] = __uint_as_float(w4[i] << 16);
-                y[k][2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
-            }
+            for (int i = 0; i < 4; ++i) bf16_pair_butterfly(w4[i], y[k][2 * i], y[k][2 * i + 1]);
         }
         if (item + stride < num_items) nxt = load_rows(a, item + stride, lane);  // travels meanwhile
         if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
         const int64_t blk = (int64_t)dst_page * a.H + head;
 
-        // ---- unnormalized Walsh-Hadamard transform along the 128 channels: bits
-        // 0..2 in registers, bits 3..6 across lanes (DPP-fused multiply-adds)
+        // ---- unnormalized Walsh-Hadamard transform along the 128 channels: bit 0
+        // straight from the packed source pairs (above), bits 1..2 in registers, bits
+        // 3..6 across lanes (DPP-fused multiply-adds)
 #pragma unroll
-        for (int s = 1; s < 8; s <<= 1)
+        for (int s = 2; s < 8; s <<= 1)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
 #pragma unroll

@@ -94,6 +94,22 @@ __device__ __forceinline__ void row_minmax16_x4(float (&mn)[4], float (&mx)[4]) 
 #undef KVQ_DPP_OP4
 #undef KVQ_DPP_MINMAX
 
+// One packed bf16 pair (x0 in the low half, x1 in the high half) -> x0 + x1 and
+// x0 - x1 in fp32, the first Walsh-Hadamard butterfly straight from the loaded word:
+// v_dot2_f32_bf16 against the pair (1, 1), the second with the upper product negated.
+// A sum whose exact value needs more than 24 bits (exponents more than 14 apart) is
+// truncated rather than rounded to nearest (checked on the box): at most 1 ulp.
+__device__ __forceinline__ void bf16_pair_butterfly(uint32_t w, float &sum, float &dif) {
+    const uint32_t one2 = 0x3F803F80u;  // bf16 (1, 1)
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(sum) : "v"(w), "s"(one2));
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(dif) : "v"(w), "s"(one2));
+}
+// acc + x0^2 + x1^2 of a packed bf16 pair (the products are exact in fp32)
+__device__ __forceinline__ float bf16_pair_sumsq(uint32_t w, float acc) {
+    asm("v_dot2_f32_bf16 %0, %1, %1, %0" : "+v"(acc) : "v"(w));
+    return acc;
+}
+
 // Lanes 16 and 32 apart, through the gfx950 permlane swaps (VALU, no LDS round trip).
 // Swapping x with itself leaves in `lo` the value of the even 16-lane row (pair16) or
 // of the lower 32 lanes (pair32) of the lane's pair, and in `hi` the odd / upper one:
