@@ -360,28 +360,44 @@ bool decode_mla_supported(const DecodeArgs &a);
 int decode_mla_head_groups(const DecodeArgs &a);
 bool launch_decode_mla(const DecodeArgs &a, hipStream_t stream);
 
-int decode_default_splits(const DecodeArgs &a, int max_seq_len) {
-    const int64_t pages = (max_seq_len + a.T - 1) / a.T;
-    int64_t units, target, min_pages;
-    if (decode_mla_supported(a)) {
-        // one 256-thread workgroup per compute unit (its registers fill the SIMDs),
-        // per (sequence, kv head, 64 query heads, split); at least 2 pages per split
-        units = (int64_t)a.B * a.Hkv * decode_mla_head_groups(a);
-        target = 256;
-        min_pages = 2;
-    } else {
-        // about 4 workgroups per compute unit, and at least 4 pages per split (the
-        // four waves of a workgroup walk pages independently)
-        units = (int64_t)a.B * a.Hkv;
-        target = 1024;
-        min_pages = 4;
-    }
+// Split count for `units` independent (sequence, kv head[, head group]) items: about
+// `target` workgroups in all, at least `min_pages` pages per split.
+static int splits_for(int64_t units, int64_t target, int64_t pages, int64_t min_pages) {
+    if (units < 1) return 1;
     int64_t sp = (target + units - 1) / units;
     const int64_t cap = (pages + min_pages - 1) / min_pages;
     if (sp > cap) sp = cap;
     if (sp > RED_MAX_SPLITS) sp = RED_MAX_SPLITS;
     if (sp < 1) sp = 1;
     return (int)sp;
+}
+
+int decode_default_splits(const DecodeArgs &a, int max_seq_len) {
+    const int64_t pages = (max_seq_len + a.T - 1) / a.T;
+    if (decode_mla_supported(a)) {
+        // one 256-thread workgroup per compute unit (its registers fill the SIMDs),
+        // per (sequence, kv head, 64 query heads, split); at least 2 pages per split
+        return splits_for((int64_t)a.B * a.Hkv * decode_mla_head_groups(a), 256, pages, 2);
+    }
+    // Four waves per workgroup walk the split's pages independently. Two bounds, the
+    // larger wins: at least 512 workgroups (two per compute unit), and at most 2048
+    // tokens of the longest sequence per split (512 per wave), so that with unequal
+    // lengths the longest sequences do not trail; each wave keeps at least one page.
+    // (Measured on the GQA workloads against 2..256 splits: best or within 2% of it.)
+    const int64_t units = (int64_t)a.B * a.Hkv;
+    if (units < 1) return 1;
+    int64_t sp = (512 + units - 1) / units;
+    const int64_t by_len = ((int64_t)max_seq_len + 2047) / 2048;
+    if (sp < by_len) sp = by_len;
+    return splits_for(1, sp, pages, 4);
+}
+
+int decode_chunk_splits(const DecodeArgs &a, int max_seq_len) {
+    // chunked prefill (the column blocks counted as sequences): about 4 workgroups per
+    // compute unit, at least 4 pages per split
+    const int64_t pages = (max_seq_len + a.T - 1) / a.T;
+    if (decode_mla_supported(a)) return splits_for((int64_t)a.B * a.Hkv * decode_mla_head_groups(a), 256, pages, 2);
+    return splits_for((int64_t)a.B * a.Hkv, 1024, pages, 4);
 }
 
 const char *decode_kernel_name(const DecodeArgs &a) {

@@ -84,6 +84,7 @@ bool launch_decode(const DecodeArgs &a, hipStream_t stream);
 // split-K partitions for a decode call whose fields other than q, block table,
 // lengths, splits and buffers are filled in
 int decode_default_splits(const DecodeArgs &a, int max_seq_len);
+int decode_chunk_splits(const DecodeArgs &a, int max_seq_len);
 // name of the main kernel launch_quantize / launch_decode would run for these arguments
 const char *quantize_kernel_name(int D, int T, const QuantArgs &a);
 const char *decode_kernel_name(const DecodeArgs &a);

@@ -70,10 +70,10 @@ int prefill_default_splits(const DecodeArgs &d, int Lq, int max_seq_len) {
     if (decode_mfma_supported(a)) {
         // as decode, counting the chunk's column blocks as sequences
         a.B = d.B * ((Lq * d.grp + 15) / 16);
-        return decode_default_splits(a, max_seq_len);
+        return decode_chunk_splits(a, max_seq_len);
     }
     a.B = d.B * Lq;
-    return decode_default_splits(a, max_seq_len);
+    return decode_chunk_splits(a, max_seq_len);
 }
 
 const char *prefill_kernel_name(const DecodeArgs &d) { return decode_kernel_name(d); }

@@ -114,10 +114,14 @@ def test_default_splits():
     fv = K.make_format(128, 0, 128, 128, 128, 2, 4, K.KVQ_CHANNEL_MAJOR)
     # long context, one sequence: at least 256 partitions over the 8 kv heads
     assert 8 * default_splits(fk, fv, 1, 32, 8, 131072) >= 256
-    assert default_splits(fk, fv, 8, 32, 8, 4096) <= 32
+    assert default_splits(fk, fv, 1, 32, 8, 131072) == 64     # at most 2048 tokens per split
+    assert default_splits(fk, fv, 8, 32, 8, 4096) == 8        # at least 512 workgroups
+    assert default_splits(fk, fv, 1, 32, 1, 256) == 1         # 2 pages: every wave keeps a page
     f16k = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_TOKEN_MAJOR)
     f16v = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_CHANNEL_MAJOR)
     assert default_splits(f16k, f16v, 1, 8, 1, 5) == 1
+    # 64 sequences up to 16384 tokens in 16-token pages: the length bound
+    assert default_splits(f16k, f16v, 64, 64, 8, 16384) == 8
     # MLA latent (512 + 64 rope, 4-bit): one workgroup per compute unit over
     # (sequence, 64 query heads, split): 32 sequences x 2 head groups x 4 splits
     fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)
