@@ -87,10 +87,12 @@ __device__ __forceinline__ float pow2_over(float x) {
     return __uint_as_float((uint32_t)min(254, 254 + E - (int)(__float_as_uint(x) >> 23)) << 23);
 }
 
-// fp32 -> fp16 hi + lo split of one value.
-__device__ __forceinline__ void split_h(float x, _Float16 &hi, _Float16 &lo) {
-    hi = (_Float16)x;
-    lo = (_Float16)(x - (float)hi);
+// fp16 hi + lo parts of the product a b: hi = f16(a b), lo = f16(a b - hi). Each is
+// one mixed-precision FMA (v_fma_mixlo/mixhi_f16: b may be an fp16 value, the product
+// is formed exactly inside the FMA), so lo carries the exact residual of hi.
+__device__ __forceinline__ void split_prod(float a, float b, _Float16 &hi, _Float16 &lo) {
+    hi = (_Float16)__builtin_fmaf(a, b, 0.f);
+    lo = (_Float16)__builtin_fmaf(a, b, -(float)hi);
 }
 
 __device__ __forceinline__ float xlane_sum_q(float v) {  // sum over the 4 lanes sharing lane & 15
@@ -413,7 +415,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             for (int kk = 0; kk < 8; ++kk) {
                 const int e = (kk >> 1) + 4 * (kk & 1);
                 _Float16 hi, lo;
-                split_h(qt[st * 8 + e] * qsc, hi, lo);
+                split_prod(qt[st * 8 + e], qsc, hi, lo);
                 qhi[st][kk] = hi;
                 qlo[st][kk] = lo;
             }
@@ -482,6 +484,10 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
         const float smax = half_bits_to_float(smaxw & 0x7fffu);
         const float psc = pow2_scale_for(xlane_max_q(smax));
+        // the scaling enters the exponent: ps = p psc = 2^(score - m + log2 psc), and the
+        // sums over ps are scaled back once (powers of two: the same values as unscaled)
+        const float m_ps = m_new - (float)((int)(__float_as_uint(psc) >> 23) - 127);
+        const float pscinv = pow2_over<0>(psc);
         float psum = 0.f, zs = 0.f;
         _Float16 phi[MT][4], plo[MT][4];
 #pragma unroll
@@ -490,15 +496,15 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const half2v sz = as_h2(vzw[i]);  // (S_V, Z_V)
-                const float p = exp2_fast(sc[j][i] - m_new);
-                psum += p;
-                zs = __builtin_fmaf((float)sz.y, p, zs);
-                split_h(mul_h(sz.x, p * psc), phi[j][i], plo[j][i]);
+                const float ps = exp2_fast(sc[j][i] - m_ps);
+                psum += ps;
+                zs = __builtin_fmaf((float)sz.y, ps, zs);
+                split_prod(ps, (float)sz.x, phi[j][i], plo[j][i]);
             }
         }
         const float pinv = pow2_over<CODE_EXP<VB>>(psc);
-        l_run = __builtin_fmaf(l_run, alpha, psum);
-        zs = xlane_sum_q(zs);
+        l_run = __builtin_fmaf(l_run, alpha, psum * pscinv);
+        zs = xlane_sum_q(zs) * pscinv;
 
         // ---- P~ as the B operand of the value product: K-step sv, lane (head, lq)
         // element kk <-> token 32 sv + 8 lq + e(kk), e < 4 from M-tile 2sv, e >= 4 from 2sv+1

@@ -49,6 +49,13 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // a * b with a an fp16 value: one mixed-precision FMA (v_fma_mix_f32) instead of a
 // conversion and a multiply
 __device__ __forceinline__ float mul_h(_Float16 a, float b) { return __builtin_fmaf((float)a, b, 0.f); }
+// fp16 hi + lo parts of the product a b: hi = f16(a b), lo = f16(a b - hi). Each is
+// one mixed-precision FMA (v_fma_mixlo/mixhi_f16: b may be an fp16 value, the product
+// is formed exactly inside the FMA), so lo carries the exact residual of hi.
+__device__ __forceinline__ void split_prod(float a, float b, _Float16 &hi, _Float16 &lo) {
+    hi = (_Float16)__builtin_fmaf(a, b, 0.f);
+    lo = (_Float16)__builtin_fmaf(a, b, -(float)hi);
+}
 // largest of the fp16 values (all >= 0) in the low and high halves of four words,
 // taken on the bit patterns (the order of non-negative fp16 values)
 __device__ __forceinline__ float max_h8(const uint32_t (&w)[4]) {
@@ -350,10 +357,10 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                     const half2v c2 = as_h2(c4[e >> 1]);
                     const float x = mul_h((e & 1) ? c2.y : c2.x, qv[st][e]);
                     qc += x;
-                    const float xs = x * qsc;
-                    const _Float16 hi = (_Float16)xs;
+                    _Float16 hi, lo;
+                    split_prod(x, qsc, hi, lo);
                     bh[kk] = hi;
-                    bl[kk] = (_Float16)(xs - (float)hi);
+                    bl[kk] = lo;
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -442,6 +449,10 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         const float alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
         const float psc = pow2_scale(smax), pinv = code_over(psc);
+        // the scaling enters the exponent: ps = p psc = 2^(score - m + log2 psc), and the
+        // sums over ps are scaled back once (powers of two: the same values as unscaled)
+        const float m_ps = m_new - (float)((int)(__float_as_uint(psc) >> 23) - 127);
+        const float pscinv = __uint_as_float((uint32_t)(254 - (int)(__float_as_uint(psc) >> 23)) << 23);
         float psum = 0.f, zs = 0.f;
         // P~ = p S psc straight into the B operand of the value product: K-step
         // kap = 2 pi2 + beta covers tokens 64 pi2 + 16 lq + 8 beta + e(kk); element
@@ -456,17 +467,17 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const half2v sz = as_h2(z4[i]);  // (S, Z)
-                const float p = exp2_fast(sc[j][i] - m_new);
-                psum += p;
-                zs = __builtin_fmaf((float)sz.y, p, zs);
-                const float xs = mul_h(sz.x, p * psc);
-                const _Float16 hi = (_Float16)xs;
+                const float ps = exp2_fast(sc[j][i] - m_ps);
+                psum += ps;
+                zs = __builtin_fmaf((float)sz.y, ps, zs);
+                _Float16 hi, lo;
+                split_prod(ps, (float)sz.x, hi, lo);
                 pbh[kap][2 * i + (j & 1)] = hi;
-                pbl[kap][2 * i + (j & 1)] = (_Float16)(xs - (float)hi);
+                pbl[kap][2 * i + (j & 1)] = lo;
             }
         }
-        l_run = __builtin_fmaf(l_run, alpha, psum);
-        zs = lq_sum(zs);
+        l_run = __builtin_fmaf(l_run, alpha, psum * pscinv);
+        zs = lq_sum(zs) * pscinv;
 
         // ---- values^T over this wave's latent half: tile mc (channels 16 mc + l16 as A rows);
         // the transposed read gives lane (l16, lq) channel 16 mc + l16 of tokens 64 pi2 + 16 lq + 0..15
