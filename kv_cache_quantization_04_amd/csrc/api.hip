@@ -264,6 +264,7 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
     a.splits = splits;
     a.ws = (float *)workspace;
     a.out = out;
+    a.max_len = max_seq_len;
     if (!kvq::launch_decode(a, stream)) return KVQ_EUNSUPPORTED;
     return launched();
 }

@@ -389,7 +389,15 @@ int decode_default_splits(const DecodeArgs &a, int max_seq_len) {
     int64_t sp = (512 + units - 1) / units;
     const int64_t by_len = ((int64_t)max_seq_len + 2047) / 2048;
     if (sp < by_len) sp = by_len;
-    return splits_for(1, sp, pages, 4);
+    sp = splits_for(1, sp, pages, 4);
+    // Long splits of 64- and 128-token pages (4 or more pages per wave): one workgroup
+    // per compute unit with double-buffered page images, when each wave then walks at
+    // least 8 pages (the kernel picks that variant from the split length).
+    if (a.T >= 64 && (pages + sp - 1) / sp >= 16) {
+        const int64_t db = splits_for(units, 256, pages, 32);
+        if ((pages + db - 1) / db >= 32) return (int)db;
+    }
+    return (int)sp;
 }
 
 int decode_chunk_splits(const DecodeArgs &a, int max_seq_len) {

@@ -174,7 +174,7 @@ __device__ __forceinline__ Chunks<PageImage<T, KB, VB>::NPRE> fetch_page(const D
     return r;
 }
 
-template <int T, int KB, int VB, bool PF>
+template <int T, int KB, int VB, bool PF, bool DB>
 __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = T / 16;                 // 16-token M-tiles of the score product
     constexpr int KSV = T >= 32 ? T / 32 : 1;  // 32-token K-steps of the value product
@@ -188,12 +188,18 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     // trip per page instead of one per tile of codes and side data.
     constexpr bool IMG = T >= 64;
     constexpr bool LDSPAGE = STAGED || IMG;
+    // DB (whole-page images, several pages per wave): two images per wave; the copies of
+    // the wave's next page travel while the current page is computed. The two images
+    // are separate LDS arrays and the page loop is unrolled by two, so each LDS read
+    // provably misses the copies in flight (no wait for them is inserted).
+    static_assert(!DB || (IMG && !PF), "double-buffered images: decode, pages of 64 or 128 tokens");
     using PI = PageImage<T, KB, VB>;
     // One pool: the four waves' page images during the page walk, the split merge after
     // it (a barrier separates the two uses).
     constexpr int RED_O = 4 * 16 * (MD + 1) * 4, RED_BYTES = RED_O + 4 * 16 * 2 * 4;
     constexpr int IMG_BYTES = LDSPAGE ? 4 * PI::BYTES : 0;
     __shared__ __attribute__((aligned(16))) uint8_t pool[IMG_BYTES > RED_BYTES ? IMG_BYTES : RED_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t pool2[DB ? 4 * PI::BYTES : 16];
     __shared__ __attribute__((aligned(16))) uint8_t wrk[4][STAGED ? PI::VCW : 16];
     float(*red_o)[16][MD + 1] = reinterpret_cast<float(*)[16][MD + 1]>(pool);
     float(*red_ml)[16][2] = reinterpret_cast<float(*)[16][2]>(pool + RED_O);
@@ -201,6 +207,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint8_t *stg = pool + wave * (LDSPAGE ? PI::BYTES : 0);  // this wave's page image
+    uint8_t *stg2 = pool2 + wave * (DB ? PI::BYTES : 0);     // its second image (DB)
     const int l16 = lane & 15, lq = lane >> 4;
     const int g = a.grp;
     int split, hk, s, cb = 0;
@@ -249,19 +256,19 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);
     // whole-page images: the copies of the wave's first page travel while the query
     // is loaded and rotated
-    auto copy_page = [&](int64_t kblk) {
+    auto copy_page = [&](int64_t kblk, uint8_t *__restrict__ dst) {
         if constexpr (IMG) {
-        copy_region<PI::KC>(a.kcodes + kblk * PI::KC, stg + PI::O_KC, lane);
-        copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.ksz) + kblk * PI::SZ, stg + PI::O_KSZ, lane);
-        copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.kcn) + kblk * PI::CN, stg + PI::O_KCN, lane);
-        copy_region<PI::VC>(a.vcodes + kblk * PI::VC, stg + PI::O_VC, lane);
-        copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.vsz) + kblk * PI::SZ, stg + PI::O_VSZ, lane);
-        copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.vcn) + kblk * PI::CN, stg + PI::O_VCN, lane);
+        copy_region<PI::KC>(a.kcodes + kblk * PI::KC, dst + PI::O_KC, lane);
+        copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.ksz) + kblk * PI::SZ, dst + PI::O_KSZ, lane);
+        copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.kcn) + kblk * PI::CN, dst + PI::O_KCN, lane);
+        copy_region<PI::VC>(a.vcodes + kblk * PI::VC, dst + PI::O_VC, lane);
+        copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.vsz) + kblk * PI::SZ, dst + PI::O_VSZ, lane);
+        copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.vcn) + kblk * PI::CN, dst + PI::O_VCN, lane);
         }
     };
     const int first = pi;
     if constexpr (IMG)
-        if (pi < p1) copy_page((int64_t)page_of(pi) * a.Hkv + hk);
+        if (pi < p1) copy_page((int64_t)page_of(pi) * a.Hkv + hk, stg);
 
     // ---- rotated query qbar = q Q of head l16 (< g; other lanes hold zeros) in the
     // B-operand layout: lane (head l16, chunk lq), K-step st covers channels
@@ -334,7 +341,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mc = 0; mc < 8; ++mc) o[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    while (pi < p1) {
+    // one page: `img` holds it (whole-page images), `nimg` receives the next (DB)
+    auto page_step = [&](uint8_t *__restrict__ img, uint8_t *__restrict__ nimg) {
         const int cur = pi;
         const int page = page_of(cur);
         pi += 4;
@@ -344,12 +352,12 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < PI::NPRE; ++k) {
                 const int off = 1024 * k + 16 * lane;
-                if (off < PI::BYTES) *reinterpret_cast<uint4 *>(&stg[off]) = pre.v[k];
+                if (off < PI::BYTES) *reinterpret_cast<uint4 *>(&img[off]) = pre.v[k];
             }
             if constexpr (VB == 3) {  // four 3-byte chunks per lane -> four words
 #pragma unroll
                 for (int c4 = lane; c4 < MD * (T / 8) / 4; c4 += 64) {
-                    const uint32_t *sw = reinterpret_cast<const uint32_t *>(&stg[PI::O_VC + 12 * c4]);
+                    const uint32_t *sw = reinterpret_cast<const uint32_t *>(&img[PI::O_VC + 12 * c4]);
                     const uint32_t w0 = sw[0], w1 = sw[1], w2 = sw[2];
                     const uint4 r = {w0 & 0xFFFFFFu, (w0 >> 24) | ((w1 & 0xFFFFu) << 8), (w1 >> 16) | ((w2 & 0xFFu) << 16),
                                      w2 >> 8};
@@ -360,18 +368,26 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
         const int rows = min(T, Lc - cur * T);  // valid tokens of this column (may be <= 0 in PF)
         const int64_t kblk = (int64_t)page * a.Hkv + hk;
-        if constexpr (IMG) {
+        if constexpr (DB) {
+            __builtin_amdgcn_s_waitcnt(0);  // this page's copies, issued one page earlier, have landed
+            if (pi < p1) {
+                // the other image's LDS reads (the previous page) have returned; make sure
+                // before the copies overwrite it
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                copy_page((int64_t)page_of(pi) * a.Hkv + hk, nimg);
+            }
+        } else if constexpr (IMG) {
             if (cur != first) {
                 // the previous page's LDS reads have returned (their values were consumed);
                 // make sure before the copies overwrite the image
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                copy_page(kblk);
+                copy_page(kblk, img);
             }
             __builtin_amdgcn_s_waitcnt(0);  // the wave's copies have landed (it alone reads its image)
         }
         // the page's K code words of every M-tile, issued now so that they travel
         // while the query is folded (a page in HBM, not staged)
-        const uint8_t *kbase = LDSPAGE ? &stg[PI::O_KC] : a.kcodes + kblk * (T * MD * KB / 8);
+        const uint8_t *kbase = LDSPAGE ? &img[PI::O_KC] : a.kcodes + kblk * (T * MD * KB / 8);
         uint32_t kpre[MT][KB];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
@@ -384,7 +400,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
 
         // c_K of the lane's 32 channels (lq*32 ..)
-        const uint4 *cp = LDSPAGE ? reinterpret_cast<const uint4 *>(&stg[PI::O_KCN + 64 * lq])
+        const uint4 *cp = LDSPAGE ? reinterpret_cast<const uint4 *>(&img[PI::O_KCN + 64 * lq])
                                  : reinterpret_cast<const uint4 *>(a.kcn + kblk * MD + lq * 32);
         uint32_t cw[16];
 #pragma unroll
@@ -450,9 +466,9 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             int tok0;
             if constexpr (T >= 32) tok0 = 32 * (j >> 1) + 8 * lq + 4 * (j & 1);
             else tok0 = 8 * (lq & 1) + 4 * (lq >> 1);
-            const uint4 kz = LDSPAGE ? *reinterpret_cast<const uint4 *>(&stg[PI::O_KSZ + 4 * tok0])
+            const uint4 kz = LDSPAGE ? *reinterpret_cast<const uint4 *>(&img[PI::O_KSZ + 4 * tok0])
                                     : *reinterpret_cast<const uint4 *>(a.ksz + (kblk * T + tok0) * 2);
-            vzq[j] = LDSPAGE ? *reinterpret_cast<const uint4 *>(&stg[PI::O_VSZ + 4 * tok0])
+            vzq[j] = LDSPAGE ? *reinterpret_cast<const uint4 *>(&img[PI::O_VSZ + 4 * tok0])
                             : *reinterpret_cast<const uint4 *>(a.vsz + (kblk * T + tok0) * 2);
             const uint32_t kzw[4] = {kz.x, kz.y, kz.z, kz.w};
 #pragma unroll
@@ -536,8 +552,8 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         // ---- values: channel tiles mc; lane (channel 16 mc + l16, tokens 32 sv + 8 lq ..)
         // (their code words are loaded two tiles ahead of use: loading all of them
         // with the K words halves the waves per SIMD and loses more than it hides)
-        const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &stg[PI::O_VC])
-                                      : IMG ? &stg[PI::O_VC] : a.vcodes + kblk * (T * MD * VB / 8);
+        const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &img[PI::O_VC])
+                                      : IMG ? &img[PI::O_VC] : a.vcodes + kblk * (T * MD * VB / 8);
         constexpr bool VRING = !LDSPAGE && T >= 32 && VB != 3;
         uint32_t vw[VRING ? 8 : 1][VRING ? KSV : 1];
         auto vword = [&](int mc, int sv) -> uint32_t {
@@ -552,7 +568,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                 vw[1][sv] = vword(1, sv);
             }
         }
-        const uint16_t *vcn = LDSPAGE ? reinterpret_cast<const uint16_t *>(&stg[PI::O_VCN]) : a.vcn + kblk * MD;
+        const uint16_t *vcn = LDSPAGE ? reinterpret_cast<const uint16_t *>(&img[PI::O_VCN]) : a.vcn + kblk * MD;
 #pragma unroll
         for (int mc = 0; mc < 8; ++mc) {
             const int ch = 16 * mc + l16;
@@ -587,6 +603,15 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf(o[mc][i], alpha, mul_h(cvv[i], __builtin_fmaf(acc[i], pinv, zs)));
         }
+    };
+    if constexpr (DB) {
+        while (pi < p1) {
+            page_step(stg, stg2);
+            if (!(pi < p1)) break;
+            page_step(stg2, stg);
+        }
+    } else {
+        while (pi < p1) page_step(stg, stg);
     }
 
     // ---- merge the four waves, write the split partial (m, l in log2 units -> natural)
@@ -646,6 +671,26 @@ bool decode_mfma_supported(const DecodeArgs &a) {
     return a.T == 16 || a.T == 32 || a.T == 64 || a.T == 128;
 }
 
+// Double-buffered page images (one workgroup per compute unit: the two images fill
+// its LDS) for decode with pages of 64 or 128 tokens when every wave of a split walks
+// at least 8 pages; below that, two single-image workgroups per compute unit hide the
+// page latency better (measured on the long-context workload).
+bool decode_use_db(const DecodeArgs &a, int max_seq_len) {
+    if (a.Lq > 0 || a.T < 64) return false;
+    const int64_t pages = (max_seq_len + a.T - 1) / a.T;
+    return (pages + a.splits - 1) / a.splits >= 32;
+}
+
+template <int T, int KB, bool PF, bool DB>
+static bool launch_vb2(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+    switch (a.vbits) {
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 2, PF, DB>), grid, dim3(MNT), 0, stream, a); return true;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 3, PF, DB>), grid, dim3(MNT), 0, stream, a); return true;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 4, PF, DB>), grid, dim3(MNT), 0, stream, a); return true;
+    }
+    return false;
+}
+
 template <int T, int KB, bool PF>
 static bool launch_vb(const DecodeArgs &a, hipStream_t stream) {
     dim3 grid(a.splits, a.Hkv, a.B);
@@ -653,13 +698,12 @@ static bool launch_vb(const DecodeArgs &a, hipStream_t stream) {
         const int64_t W = (int64_t)a.B * a.Hkv * a.splits * ((a.Lq * a.grp + 15) / 16);
         if (W > ((int64_t)1 << 30)) return false;
         grid = dim3((unsigned)(8 * ((W + 7) / 8)));
+        return launch_vb2<T, KB, PF, false>(a, grid, stream);
+    } else {
+        if constexpr (T >= 64)
+            if (decode_use_db(a, a.max_len)) return launch_vb2<T, KB, false, true>(a, grid, stream);
+        return launch_vb2<T, KB, false, false>(a, grid, stream);
     }
-    switch (a.vbits) {
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 2, PF>), grid, dim3(MNT), 0, stream, a); return true;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 3, PF>), grid, dim3(MNT), 0, stream, a); return true;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<T, KB, 4, PF>), grid, dim3(MNT), 0, stream, a); return true;
-    }
-    return false;
 }
 
 template <int T, bool PF>

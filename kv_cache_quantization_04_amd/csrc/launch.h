@@ -51,6 +51,8 @@ struct DecodeArgs {
     // [B][Lq][Hq]), position i attending to tokens 0 .. seq_lens[b] - Lq + i; the
     // workspace and the reduce run over B * Lq rows. 0 for decode.
     int Lq;
+    // longest sequence the caller names (host-side launch choices only)
+    int max_len;
 };
 
 // append path: new token rows -> tail buffer, tile descriptors -> workspace

@@ -114,7 +114,10 @@ def test_default_splits():
     fv = K.make_format(128, 0, 128, 128, 128, 2, 4, K.KVQ_CHANNEL_MAJOR)
     # long context, one sequence: at least 256 partitions over the 8 kv heads
     assert 8 * default_splits(fk, fv, 1, 32, 8, 131072) >= 256
-    assert default_splits(fk, fv, 1, 32, 8, 131072) == 64     # at most 2048 tokens per split
+    # one sequence of 1024 pages: one double-buffered workgroup per compute unit
+    assert default_splits(fk, fv, 1, 32, 8, 131072) == 32
+    # 512 pages: 64 splits of 8 (2 pages per wave), two single-image workgroups per CU
+    assert default_splits(fk, fv, 1, 32, 8, 65536) == 64
     assert default_splits(fk, fv, 8, 32, 8, 4096) == 8        # at least 512 workgroups
     assert default_splits(fk, fv, 1, 32, 1, 256) == 1         # 2 pages: every wave keeps a page
     f16k = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_TOKEN_MAJOR)
