@@ -2,10 +2,11 @@
 """Benchmark of the KV-cache quantization hot path on one MI355X.
 
 One step = quantize the K and V of one batch (every tile and kv head of the
-workload) and run quantized decode attention over the cache just written.
+workload) and run quantized decode attention over one batch's quantized cache.
 Inputs are seeded synthetic data already resident in device memory; a ring of
 independent copies (inputs and caches) larger than the 256 MB last-level cache
-makes every step read from and write to HBM.
+makes every step read from and write to HBM: the decode reads the cache that the
+quantizer wrote half a ring of steps earlier, not the one it has just written.
 
 Prints one JSON line: whole-step throughput in GB/s of algorithmic bytes
 (inputs read + codes and side data written by the quantizer; codes and side data
@@ -366,9 +367,19 @@ def main():
     torch.empty_like(calib).copy_(calib)
 
     stream = torch.cuda.current_stream()
+    # Every ring slot holds a quantized cache before the first step. A step quantizes
+    # slot j and decodes the cache of slot j - ring/2, written half a ring of steps
+    # earlier: neither the quantizer's source nor the decoder's cache is still in the
+    # 256 MB last-level cache (at least 1 GB of other traffic in between).
+    for j in range(ring):
+        K.kv_quantize(kcache[j], ksrc[j], tst, tv, tp, stream=stream)
+        if vsrc[j] is not None:
+            K.kv_quantize(vcache[j], vsrc[j], tst, tv, tp, stream=stream)
+    lag = ring // 2
 
     def step(i, evs=None):
         j = i % ring
+        jd = (i - lag) % ring
         if evs:
             evs[0].record(stream)
         K.kv_quantize(kcache[j], ksrc[j], tst, tv, tp, stream=stream)
@@ -378,7 +389,7 @@ def main():
             K.kv_quantize(vcache[j], vsrc[j], tst, tv, tp, stream=stream)
         if evs:
             evs[2].record(stream)
-        K.kv_decode_attn(qd, kcache[j], vcache[j], bt, sl, max_len, cfg.sm_scale, num_splits=splits, workspace=ws,
+        K.kv_decode_attn(qd, kcache[jd], vcache[jd], bt, sl, max_len, cfg.sm_scale, num_splits=splits, workspace=ws,
                          out=out, stream=stream)
         if evs:
             evs[3].record(stream)
