@@ -144,6 +144,18 @@ __device__ __forceinline__ void copy_region(const uint8_t *src, uint8_t *dst, in
     }
 }
 
+// Direct-to-LDS load instructions that copy_region<N> issues.
+template <int N>
+constexpr int copy_instrs() { return N / (64 * (N % 1024 == 0 ? 16 : 4)); }
+
+// s_waitcnt for at most N vector-memory operations outstanding (the other counters
+// left alone)
+template <int N>
+__device__ __forceinline__ void wait_vm_upto() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int N>
 struct Chunks {
     uint4 v[N];
@@ -248,12 +260,41 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         const int page = page_of(q);
         return page >= 0 && page < a.num_pages;
     };
+    // The query's raw words are loaded before the first page is requested: the vector-
+    // memory counter is in order, so waiting for the query then leaves the page's loads
+    // in flight while the query is converted and rotated.
+    uint4 qraw[8];
+    {
+        const int64_t qrow = PF ? (int64_t)s * a.Lq + (hv ? pos : 0) : s;
+        const int64_t qb = (qrow * a.Hq + hk * g + (hv ? hh : 0)) * MD + lq * 32;
+        // 32 consecutive channels: 16-byte loads under one (uniform) dtype branch
+        if (a.q_dtype == KVQ_F32) {
+            const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.q) + qb);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qraw[i] = p4[i];
+        } else {
+            const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qraw[i] = p4[i];
+#pragma unroll
+            for (int i = 4; i < 8; ++i) qraw[i] = uint4{0, 0, 0, 0};
+        }
+    }
+    asm volatile("" ::: "memory");  // keep the query loads ahead of the page requests
     // staged path: the next page's image chunks, in registers
     Chunks<STAGED ? PI::NPRE : 1> pre{};
     int pi = p0 + wave;
     while (pi < p1 && !valid(pi)) pi += 4;
-    if constexpr (STAGED)
-        if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);
+    // (each path waits for the query loads itself, leaving the page's loads in flight:
+    // the compiler cannot count the outstanding loads past a conditional request)
+    if constexpr (STAGED) {
+        if (pi < p1) {
+            pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);
+            wait_vm_upto<PI::NPRE>();
+        } else {
+            wait_vm_upto<0>();
+        }
+    }
     // whole-page images: the copies of the wave's first page travel while the query
     // is loaded and rotated
     auto copy_page = [&](int64_t kblk, uint8_t *__restrict__ dst) {
@@ -261,14 +302,22 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         copy_region<PI::KC>(a.kcodes + kblk * PI::KC, dst + PI::O_KC, lane);
         copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.ksz) + kblk * PI::SZ, dst + PI::O_KSZ, lane);
         copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.kcn) + kblk * PI::CN, dst + PI::O_KCN, lane);
-        copy_region<PI::VC>(a.vcodes + kblk * PI::VC, dst + PI::O_VC, lane);
+        // V codes last: the scores need everything else, the value product these
         copy_region<PI::SZ>(reinterpret_cast<const uint8_t *>(a.vsz) + kblk * PI::SZ, dst + PI::O_VSZ, lane);
         copy_region<PI::CN>(reinterpret_cast<const uint8_t *>(a.vcn) + kblk * PI::CN, dst + PI::O_VCN, lane);
+        copy_region<PI::VC>(a.vcodes + kblk * PI::VC, dst + PI::O_VC, lane);
         }
     };
     const int first = pi;
-    if constexpr (IMG)
-        if (pi < p1) copy_page((int64_t)page_of(pi) * a.Hkv + hk, stg);
+    if constexpr (IMG) {
+        if (pi < p1) {
+            copy_page((int64_t)page_of(pi) * a.Hkv + hk, stg);
+            wait_vm_upto<2 * copy_instrs<PI::SZ>() + 2 * copy_instrs<PI::CN>() + copy_instrs<PI::KC>() +
+                         copy_instrs<PI::VC>()>();
+        } else {
+            wait_vm_upto<0>();
+        }
+    }
 
     // ---- rotated query qbar = q Q of head l16 (< g; other lanes hold zeros) in the
     // B-operand layout: lane (head l16, chunk lq), K-step st covers channels
@@ -277,22 +326,18 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     // across lanes 16 and 32 apart; blocks of h channels rotate separately.
     float qv[32];
     {
-        const int64_t qrow = PF ? (int64_t)s * a.Lq + (hv ? pos : 0) : s;
-        const int64_t qb = (qrow * a.Hq + hk * g + (hv ? hh : 0)) * MD + lq * 32;
-        // 32 consecutive channels: 16-byte loads under one (uniform) dtype branch
         if (a.q_dtype == KVQ_F32) {
-            const float4 *p4 = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qb);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float4 v = p4[i];
-                qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+                const uint4 v = qraw[i];
+                qv[4 * i] = __uint_as_float(v.x); qv[4 * i + 1] = __uint_as_float(v.y);
+                qv[4 * i + 2] = __uint_as_float(v.z); qv[4 * i + 3] = __uint_as_float(v.w);
             }
         } else {
-            const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
             uint32_t w[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint4 v = p4[i];
+                const uint4 v = qraw[i];
                 w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
             }
             if (a.q_dtype == KVQ_BF16) {
@@ -383,7 +428,9 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 copy_page(kblk, img);
             }
-            __builtin_amdgcn_s_waitcnt(0);  // the wave's copies have landed (it alone reads its image)
+            // all but the V code copies have landed (in order; the wave alone reads its
+            // image): the scores run while the V codes travel
+            wait_vm_upto<copy_instrs<PI::VC>()>();
         }
         // the page's K code words of every M-tile, issued now so that they travel
         // while the query is folded (a page in HBM, not staged)
@@ -552,6 +599,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         // ---- values: channel tiles mc; lane (channel 16 mc + l16, tokens 32 sv + 8 lq ..)
         // (their code words are loaded two tiles ahead of use: loading all of them
         // with the K words halves the waves per SIMD and loses more than it hides)
+        if constexpr (IMG && !DB) wait_vm_upto<0>();  // the V codes have landed
         const uint8_t *vbase = STAGED ? (VB == 3 ? &wrk[wave][0] : &img[PI::O_VC])
                                       : IMG ? &img[PI::O_VC] : a.vcodes + kblk * (T * MD * VB / 8);
         constexpr bool VRING = !LDSPAGE && T >= 32 && VB != 3;
