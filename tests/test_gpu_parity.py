@@ -429,6 +429,28 @@ def test_decode_small(gpu, kw, splits):
     assert err <= DECODE_RTOL
 
 
+DEC_DB = [
+    dict(T=128, lens=(9000, 4100, 130), kbits=4, vbits=2, iters=4),   # 71, 33 and 2 pages, ragged last pages
+    dict(T=64, lens=(5000, 70), kbits=3, vbits=4, Hq=16, Hkv=2),      # 79 and 2 pages, g = 8
+]
+
+
+@pytest.mark.parametrize("kw", DEC_DB, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+@pytest.mark.parametrize("splits", [1, 2])
+def test_decode_double_buffered_pages(gpu, kw, splits):
+    """Splits of at least 32 pages of 64 or 128 tokens run the double-buffered variant
+    (two page images per wave, the next page's copies in flight); sequences shorter than
+    the longest walk fewer pages, odd counts end on either image."""
+    log("decode double-buffered case", kw, "splits", splits)
+    w = small_paged(97 + len(kw), **kw)
+    T = w["fk"].tile_tokens
+    assert -(-(-(-int(w["lens"].max()) // T)) // splits) >= 32
+    out, ref, *_ = run_decode_case(gpu, w, 1.0 / math.sqrt(w["fk"].head_dim), splits)
+    err = rel_rowwise(out, ref)
+    log("  decode rel err", err)
+    assert err <= DECODE_RTOL
+
+
 def test_decode_closed_forms(gpu):
     """q = 0 averages the values; sequence length 0 gives zeros."""
     w = small_paged(3, lens=(50, 0, 17))
