@@ -533,6 +533,12 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         // give alpha = 0 and p = 0 (decode pages always hold a valid token)
         if constexpr (PF) m_new = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2_fast(m_run - m_new);
+        // 16-token pages: the rescaling of o' runs only when some column's running maximum
+        // moved (most pages once the first few are seen leave every alpha at exactly 1);
+        // larger pages keep it fused into the fold (a separate pass costs them registers,
+        // and at 256 the kernel would drop to one wave per SIMD)
+        constexpr bool LAZY = STAGED;
+        const bool rescale = LAZY && __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
         m_run = PF ? fmaxf(m_run, pmax) : m_new;
         // P~ = p S_V scaled by 2^sp with max_t S_V,t near 2^14 (p <= 1). The scales are
         // >= 0, so the largest is the largest fp16 bit pattern (packed u16 maxima; the
@@ -617,6 +623,11 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
         }
         const uint16_t *vcn = LDSPAGE ? reinterpret_cast<const uint16_t *>(&img[PI::O_VCN]) : a.vcn + kblk * MD;
+        if (rescale)
+#pragma unroll
+            for (int mc = 0; mc < 8; ++mc)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[mc][i] *= alpha;
 #pragma unroll
         for (int mc = 0; mc < 8; ++mc) {
             const int ch = 16 * mc + l16;
@@ -644,12 +655,16 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbh[sv], acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbl[sv], acc, 0, 0, 0);
             }
-            // fold: o' = alpha o' + c_V (acc + zs); rows 4 lq + i of tile mc are channels
+            // fold: o' = alpha o' + c_V (acc + zs), or with o' rescaled above (LAZY) one mixed
+            // FMA with c_V an fp16 operand; rows 4 lq + i of tile mc are channels
             const uint2 cv2 = *reinterpret_cast<const uint2 *>(vcn + 16 * mc + 4 * lq);
             const half2v c01 = as_h2(cv2.x), c23 = as_h2(cv2.y);
             const _Float16 cvv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf(o[mc][i], alpha, mul_h(cvv[i], __builtin_fmaf(acc[i], pinv, zs)));
+            for (int i = 0; i < 4; ++i) {
+                const float t = __builtin_fmaf(acc[i], pinv, zs);
+                o[mc][i] = LAZY ? __builtin_fmaf((float)cvv[i], t, o[mc][i]) : __builtin_fmaf(o[mc][i], alpha, mul_h(cvv[i], t));
+            }
         }
     };
     if constexpr (DB) {

@@ -447,6 +447,9 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         const float smax = lq_max(half_bits_to_float(smaxw & 0x7fffu));
         const float m_new = fmaxf(m_run, pmax);
         const float alpha = exp2_fast(m_run - m_new);
+        // the rescaling of o' runs only when some head's running maximum moved (most
+        // pages once the first few are seen leave every alpha at exactly 1)
+        const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
         m_run = m_new;
         const float psc = pow2_scale(smax), pinv = code_over(psc);
         // the scaling enters the exponent: ps = p psc = 2^(score - m + log2 psc), and the
@@ -479,6 +482,11 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         l_run = __builtin_fmaf(l_run, alpha, psum * pscinv);
         zs = lq_sum(zs) * pscinv;
 
+        if (rescale)
+#pragma unroll
+            for (int m2 = 0; m2 < 16; ++m2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[m2][i] *= alpha;
         // ---- values^T over this wave's latent half: tile mc (channels 16 mc + l16 as A rows);
         // the transposed read gives lane (l16, lq) channel 16 mc + l16 of tokens 64 pi2 + 16 lq + 0..15
 #pragma unroll
@@ -496,12 +504,12 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbl[2 * p2 + beta], acc, 0, 0, 0);
                 }
             }
-            // fold: rows 4 lq + i of tile mc are channels 16 mc + 4 lq + i
+            // fold (o' rescaled above): rows 4 lq + i of tile mc are channels 16 mc + 4 lq + i
             const uint2 cv2 = *reinterpret_cast<const uint2 *>(cn + 16 * mc + 4 * lq);
             const half2v c01 = as_h2(cv2.x), c23 = as_h2(cv2.y);
             const _Float16 cvv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[m2][i] = __builtin_fmaf(o[m2][i], alpha, mul_h(cvv[i], __builtin_fmaf(acc[i], pinv, zs)));
+            for (int i = 0; i < 4; ++i) o[m2][i] = __builtin_fmaf((float)cvv[i], __builtin_fmaf(acc[i], pinv, zs), o[m2][i]);
             if (m2 & 1) __builtin_amdgcn_sched_barrier(0);  // at most two tiles' operands in flight
         }
     }
