@@ -128,6 +128,22 @@ kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtyp
                        const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
                        hipStream_t stream);
 
+/* The K and V caches of one batch quantized by one launch: the same result as
+ * kv_quantize(k_dst, k_src, ...) followed by kv_quantize(v_dst, v_src, ...) with
+ * the shared tile arrays and status_flags ("KVarN" project review, Key Features,
+ * "Variance-Normalized Quantization Pipeline", applied to keys and values alike).
+ * Arguments per cache as for kv_quantize. Taken when both formats fit the
+ * 128-channel quantizer: head_dim 128, hadamard_n = group = 128, rope_dim 0,
+ * center 0, bf16 sources, 2- or 4-bit codes, 64- or 128-token tiles, keys
+ * token-major and values channel-major, both caches with the same tile_tokens,
+ * iters and number of heads. Otherwise KVQ_EUNSUPPORTED and nothing is launched
+ * (two kv_quantize calls do the work). Errors as for kv_quantize. */
+kvq_status kv_quantize_kv(const kvq_cache *k_dst, const kvq_cache *v_dst, const void *k_src, const void *v_src,
+                          kvq_dtype src_dtype, int64_t k_stride_token, int64_t k_stride_head, int64_t v_stride_token,
+                          int64_t v_stride_head, int32_t num_tiles, const int32_t *tile_src_token,
+                          const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
+                          hipStream_t stream);
+
 /* Rebuilds tiles from the cache: x_hat = ((S code + Z) o c) Q, rope copied.
  * dst (device): [num_tiles][H][T][D + R] in dst_dtype (f32, f16 or bf16); rows
  * t >= tile_valid[i] are written as zero. tile_page, tile_valid: device int32. */

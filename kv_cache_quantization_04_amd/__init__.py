@@ -39,7 +39,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_ELAUNCH = 0, -1, -2, -
 KVQ_TOKEN_MAJOR, KVQ_CHANNEL_MAJOR = 0, 1
 KVQ_FLAG_NONFINITE, KVQ_FLAG_SIDE_OVERFLOW = 1, 2
 
-EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_dequantize",
+EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_quantize_kv", "kv_dequantize",
            "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_append", "kv_append_workspace_bytes", "kv_prefill_attn",
            "kv_prefill_attn_workspace_bytes", "kv_prefill_attn_default_splits",
            "kv_quantize_kernel_name", "kv_decode_attn_kernel_name", "kv_prefill_attn_kernel_name", "kvq_status_str")
@@ -64,6 +64,8 @@ _sig = {
     "kvq_format_from_preset": (_i32, [ctypes.c_char_p, _i32, ctypes.POINTER(kvq_format), ctypes.POINTER(kvq_format)]),
     "kvq_cache_bytes": (_sz, [ctypes.POINTER(kvq_format), _i32, _i32]),
     "kv_quantize": (_i32, [ctypes.POINTER(kvq_cache), _vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "kv_quantize_kv": (_i32, [ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _vp, _vp, _i32, _i64, _i64, _i64,
+                              _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
     "kv_dequantize": (_i32, [ctypes.POINTER(kvq_cache), _i32, _vp, _vp, _vp, _i32, _vp]),
     "kv_decode_attn_default_splits": (_i32, [ctypes.c_void_p, ctypes.c_void_p, _i32, _i32, _i32]),
     "kv_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
@@ -165,6 +167,18 @@ def kv_quantize(dst: DeviceCache, src, tile_src_token, tile_valid, tile_dst_page
     _check(_lib.kv_quantize(ctypes.byref(dst.struct), _ptr(src), _dtype_code(src), src.stride(0), src.stride(1),
                             tile_src_token.numel(), _ptr(tile_src_token), _ptr(tile_valid), _ptr(tile_dst_page),
                             _ptr(status_flags), _stream(stream)), "kv_quantize")
+
+
+def kv_quantize_kv(k_dst: DeviceCache, v_dst: DeviceCache, k_src, v_src, tile_src_token, tile_valid, tile_dst_page,
+                   status_flags=None, stream=None):
+    """K and V caches of one batch in one launch (same result as kv_quantize on each).
+    Raises KvqError (KVQ_EUNSUPPORTED) for formats the one-launch kernel does not take."""
+    assert k_src.dim() == 3 and k_src.stride(2) == 1 and v_src.dim() == 3 and v_src.stride(2) == 1
+    assert k_src.dtype == v_src.dtype
+    _check(_lib.kv_quantize_kv(ctypes.byref(k_dst.struct), ctypes.byref(v_dst.struct), _ptr(k_src), _ptr(v_src),
+                               _dtype_code(k_src), k_src.stride(0), k_src.stride(1), v_src.stride(0), v_src.stride(1),
+                               tile_src_token.numel(), _ptr(tile_src_token), _ptr(tile_valid), _ptr(tile_dst_page),
+                               _ptr(status_flags), _stream(stream)), "kv_quantize_kv")
 
 
 def kv_dequantize(src: DeviceCache, tile_page, tile_valid, out=None, dtype=None, stream=None):

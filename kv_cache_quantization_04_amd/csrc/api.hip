@@ -156,6 +156,29 @@ kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtyp
     return launched();
 }
 
+kvq_status kv_quantize_kv(const kvq_cache *k_dst, const kvq_cache *v_dst, const void *k_src, const void *v_src,
+                          kvq_dtype src_dtype, int64_t k_stride_token, int64_t k_stride_head, int64_t v_stride_token,
+                          int64_t v_stride_head, int32_t num_tiles, const int32_t *tile_src_token,
+                          const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
+                          hipStream_t stream) {
+    kvq_status st = check_quantize_source(k_dst, k_src, src_dtype, k_stride_token, k_stride_head);
+    if (st != KVQ_OK) return st;
+    if ((st = check_quantize_source(v_dst, v_src, src_dtype, v_stride_token, v_stride_head)) != KVQ_OK) return st;
+    if (num_tiles < 0) return KVQ_EINVAL;
+    if (num_tiles > 0 && (!tile_src_token || !tile_valid || !tile_dst_page)) return KVQ_EINVAL;
+    const kvq_format &fk = k_dst->fmt, &fv = v_dst->fmt;
+    if (fk.head_dim != fv.head_dim || fk.tile_tokens != fv.tile_tokens || k_dst->num_pages != v_dst->num_pages)
+        return KVQ_EUNSUPPORTED;
+    const kvq::QuantArgs ak = quant_args(k_dst, k_src, src_dtype, k_stride_token, k_stride_head, tile_src_token,
+                                         tile_valid, tile_dst_page, status_flags);
+    const kvq::QuantArgs av = quant_args(v_dst, v_src, src_dtype, v_stride_token, v_stride_head, tile_src_token,
+                                         tile_valid, tile_dst_page, status_flags);
+    if (!kvq::quantize_pair_supported(fk.head_dim, fk.tile_tokens, ak, av)) return KVQ_EUNSUPPORTED;
+    if (num_tiles == 0) return KVQ_OK;
+    if (!kvq::launch_quantize_pair(fk.head_dim, fk.tile_tokens, num_tiles, ak, av, stream)) return KVQ_EUNSUPPORTED;
+    return launched();
+}
+
 const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
                                     int64_t stride_head) {
     if (check_quantize_source(dst, src, src_dtype, stride_token, stride_head) != KVQ_OK) return nullptr;

@@ -76,6 +76,9 @@ struct PrefillArgs {
 };
 
 bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
+// K and V of one batch in one launch; false (nothing launched) outside the formats it takes
+bool quantize_pair_supported(int D, int T, const QuantArgs &k, const QuantArgs &v);
+bool launch_quantize_pair(int D, int T, int num_tiles, const QuantArgs &k, const QuantArgs &v, hipStream_t stream);
 bool launch_append(const AppendArgs &a, int D, int T, const QuantArgs &q, hipStream_t stream);
 bool launch_prefill(const PrefillArgs &p, const DecodeArgs &d, hipStream_t stream);
 // split-K partitions and main kernel of a prefill call (d.B = real sequences)

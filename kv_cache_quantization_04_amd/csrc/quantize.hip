@@ -421,6 +421,8 @@ __global__ void __launch_bounds__(2 * D) dequant_kernel(DequantArgs a) {
 
 bool quantize_d128_supported(int D, int T, const QuantArgs &a);
 void launch_quantize_d128(int T, int num_tiles, const QuantArgs &a, hipStream_t stream);
+bool quantize_d128_pair_supported(int T, const QuantArgs &k, const QuantArgs &v);
+void launch_quantize_d128_pair(int T, int num_tiles, const QuantArgs &k, const QuantArgs &v, hipStream_t stream);
 bool quantize_t16_supported(int D, int T, const QuantArgs &a);
 void launch_quantize_t16(int num_tiles, const QuantArgs &a, hipStream_t stream);
 bool quantize_d512_supported(int D, int T, const QuantArgs &a);
@@ -450,6 +452,16 @@ bool launch_quantize(int D, int T, int num_tiles, const QuantArgs &a, hipStream_
     hipLaunchKernelGGL((quantize_kernel<D_, T_>), dim3(num_tiles, a.H), dim3(2 * D_), 0, stream, a)
     KVQ_DISPATCH(KVQ_LQ)
 #undef KVQ_LQ
+    return true;
+}
+
+bool quantize_pair_supported(int D, int T, const QuantArgs &k, const QuantArgs &v) {
+    return D == 128 && k.H == v.H && quantize_d128_pair_supported(T, k, v);
+}
+
+bool launch_quantize_pair(int D, int T, int num_tiles, const QuantArgs &k, const QuantArgs &v, hipStream_t stream) {
+    if (!quantize_pair_supported(D, T, k, v)) return false;
+    launch_quantize_d128_pair(T, num_tiles, k, v, stream);
     return true;
 }
 

@@ -96,17 +96,23 @@ __device__ __forceinline__ int code_byte(int b) {
 //   multsh [128]        per-channel output multiplier
 //   outbuf [T * 128 * BITS / 32] LDS image of the code block
 //   szbuf  [T]          (S, Z) fp16 pairs per token
-template <int T, int R, int BITS, int LAYOUT, int NIT>
-__device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_items, uint4 *__restrict__ stage,
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+// Items 0 .. nk - 1 belong to cache `ak` (format BK, LK); with PAIR, items nk ..
+// num_items - 1 are item - nk of cache `av` (BV, LV): the K and V caches of one batch
+// in one launch, the prefetch running on from the last K item into the first V items.
+template <int T, int R, int BK, int LK, int BV, int LV, int NIT, bool PAIR>
+__device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const QuantArgs &av, int nk, int num_items,
+                                                   uint4 *__restrict__ stage,
                                                    float (*__restrict__ colsum0)[QD], float (*__restrict__ colsum1)[QD],
                                                    float *__restrict__ wsh0, float *__restrict__ wsh1,
                                                    float *__restrict__ multsh, uint32_t *__restrict__ outbuf,
                                                    uint32_t *__restrict__ szbuf) {
     constexpr int NWV = T / (4 * R);  // waves (4 row groups of R rows each)
     constexpr int NT = 64 * NWV;
-    constexpr float LEVELS = (float)((1 << BITS) - 1);
-    // rounds: a compile-time count (fully unrolled) or, with NIT < 0, the runtime one
-    const int iters = NIT >= 0 ? NIT : a.iters;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,7 +127,10 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
     // chunk l & 15. LDS slot (l & 15) of a row holds chunk slot ^ ((row / R) & 3),
     // so the four row groups of a wave read different banks; for a fixed b that
     // swizzle is the constant ((4 i) / R) & 3.
-    auto fetch = [&](int itm) {
+    auto fetch = [&](int gitm) {
+        const bool isk = !PAIR || gitm < nk;  // uniform
+        const QuantArgs &a = isk ? ak : av;
+        const int itm = isk ? gitm : gitm - nk;
         const int tl = itm / a.H, hd = itm % a.H;
         const int nv = load_const(a.tile_valid, tl);
         const char *src = reinterpret_cast<const char *>(a.src) +
@@ -146,9 +155,12 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
                                              (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
         }
     };
-    int item = blockIdx.x;
-    if (item < num_items) fetch(item);
-    for (; item < num_items; item += gridDim.x) {
+    // one item of cache `a` (local index `item`, global index `gitem`)
+    auto process = [&](auto bits_c, auto layout_c, const QuantArgs &a, int item, int gitem) {
+    constexpr int BITS = decltype(bits_c)::value, LAYOUT = decltype(layout_c)::value;
+    constexpr float LEVELS = (float)((1 << BITS) - 1);
+    // rounds: a compile-time count (fully unrolled) or, with NIT < 0, the runtime one
+    const int iters = NIT >= 0 ? NIT : a.iters;
     const int tile = item / a.H, head = item % a.H;
     const int dst_page = load_const(a.tile_dst_page, tile);
     const int n = load_const(a.tile_valid, tile);
@@ -182,8 +194,8 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         ssq[k] = acc;
     }
     lds_barrier();  // the staging buffer is free again
-    if (item + (int)gridDim.x < num_items) fetch(item + gridDim.x);
-    if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
+    if (gitem + (int)gridDim.x < num_items) fetch(gitem + gridDim.x);
+    if (dst_page < 0 || dst_page >= a.num_pages) return;  // invalid destination: tile skipped (uniform)
 
     // ---- unnormalized Walsh-Hadamard transform along the 128 channels -------
     // (channel bit 0 done above)
@@ -315,7 +327,12 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         const float cv = half_bits_to_float(c16);
         if (!(cv > 0.f && cv < INFINITY)) sideov = true;
         multsh[tid] = INV_SQRT_H / cv;
-        a.cnorm[blk * QD + tid] = c16;
+        // thread id made opaque: the store address is formed here, not hoisted out of
+        // the item loop (with two caches' addresses held, they would spill, and a spill
+        // reload waits for the prefetch in flight)
+        int otid = tid;
+        asm volatile("" : "+v"(otid));
+        a.cnorm[blk * QD + otid] = c16;
     }
     lds_barrier();
     float mult[8];
@@ -414,10 +431,15 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         constexpr int NW = T * QD * BITS / 32;  // 32-bit words of the code block
         uint4 *gcodes = reinterpret_cast<uint4 *>(a.codes + blk * (T * QD * BITS / 8));
         const uint4 *lcodes = reinterpret_cast<const uint4 *>(outbuf);
+        int otid = tid;  // opaque, as for the normalizer store
+        asm volatile("" : "+v"(otid));
 #pragma unroll
-        for (int i = tid; i < NW / 4; i += NT) gcodes[i] = lcodes[code_slot<T, R, BITS, LAYOUT>(i)];
-        if (tid < T / 4)
-            reinterpret_cast<uint4 *>(a.sz + blk * T * 2)[tid] = reinterpret_cast<const uint4 *>(szbuf)[tid];
+        for (int k = 0; k < (NW / 4 + NT - 1) / NT; ++k) {
+            const int i = otid + k * NT;
+            if ((NW / 4) % NT == 0 || i < NW / 4) gcodes[i] = lcodes[code_slot<T, R, BITS, LAYOUT>(i)];
+        }
+        if (otid < T / 4)
+            reinterpret_cast<uint4 *>(a.sz + blk * T * 2)[otid] = reinterpret_cast<const uint4 *>(szbuf)[otid];
     }
     if (a.flags) {  // one atomic per wave that saw a condition; no barrier
         const bool nf = __ballot(nonfinite) != 0;
@@ -425,6 +447,12 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
         if (lane == 0 && (nf || so))
             atomicOr(a.flags, (nf ? (uint32_t)KVQ_FLAG_NONFINITE : 0u) | (so ? (uint32_t)KVQ_FLAG_SIDE_OVERFLOW : 0u));
     }
+    };
+    int item = blockIdx.x;
+    if (item < num_items) fetch(item);
+    for (; item < num_items; item += gridDim.x) {
+        if (!PAIR || item < nk) process(IntC<BK>{}, IntC<LK>{}, ak, item, item);
+        else process(IntC<BV>{}, IntC<LV>{}, av, item - nk, item);
     }
 }
 
@@ -432,17 +460,18 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &a, int num_i
 // execution unit), so at most 128 registers per lane: two 8-wave workgroups per
 // compute unit for 128-token tiles. Every variant fits without spilling (the few
 // addresses that would not are recomputed from an opaque lane id where used).
-template <int T, int R, int BITS, int LAYOUT, int NIT>
-__global__ void __launch_bounds__(16 * T / R, 4) quantize_d128_kernel(QuantArgs a, int num_items) {
+template <int T, int R, int BK, int LK, int BV, int LV, int NIT, bool PAIR>
+__global__ void __launch_bounds__(16 * T / R, 4) quantize_d128_kernel(QuantArgs ak, QuantArgs av, int nk, int num_items) {
     constexpr int NWV = T / (4 * R);
+    constexpr int MB = BK > BV ? BK : BV;
     __shared__ uint4 stage[T * QD * 2 / 16];
     __shared__ float colsum0[NWV][QD], colsum1[NWV][QD];
     __shared__ float wsh0[QD], wsh1[QD];
     __shared__ float multsh[QD];
-    __shared__ uint32_t outbuf[T * QD * BITS / 32];
+    __shared__ uint32_t outbuf[T * QD * MB / 32];
     __shared__ uint32_t szbuf[T];
-    quantize_d128_body<T, R, BITS, LAYOUT, NIT>(a, num_items, stage, colsum0, colsum1, wsh0, wsh1, multsh, outbuf,
-                                             szbuf);
+    quantize_d128_body<T, R, BK, LK, BV, LV, NIT, PAIR>(ak, av, nk, num_items, stage, colsum0, colsum1, wsh0, wsh1,
+                                                        multsh, outbuf, szbuf);
 }
 
 bool quantize_d128_supported(int D, int T, const QuantArgs &a) {
@@ -453,19 +482,21 @@ bool quantize_d128_supported(int D, int T, const QuantArgs &a) {
            (a.bits == 2 || a.bits == 4) && (a.layout == KVQ_TOKEN_MAJOR || a.layout == KVQ_CHANNEL_MAJOR);
 }
 
+static int d128_grid(int items, const void *kernel, int threads) {
+    int dev = 0, cus = 256, per_cu = 2;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    return items < cus * per_cu ? items : cus * per_cu;
+}
+
 template <int T, int BITS, int LAYOUT, int NIT>
 static void launch_one(int num_tiles, const QuantArgs &a, hipStream_t stream) {
     constexpr int R = QR;
     constexpr int NT = 16 * T / R;
     const int items = num_tiles * a.H;
-    int dev = 0, cus = 256, per_cu = 2;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_d128_kernel<T, R, BITS, LAYOUT, NIT>, NT, 0) !=
-            hipSuccess || per_cu < 1)
-        per_cu = 1;
-    const int grid = items < cus * per_cu ? items : cus * per_cu;
-    hipLaunchKernelGGL((quantize_d128_kernel<T, R, BITS, LAYOUT, NIT>), dim3(grid), dim3(NT), 0, stream, a, items);
+    auto kern = quantize_d128_kernel<T, R, BITS, LAYOUT, BITS, LAYOUT, NIT, false>;
+    hipLaunchKernelGGL(kern, dim3(d128_grid(items, (const void *)kern, NT)), dim3(NT), 0, stream, a, a, items, items);
 }
 
 template <int T, int BITS, int LAYOUT>
@@ -489,6 +520,45 @@ void launch_quantize_d128(int T, int num_tiles, const QuantArgs &a, hipStream_t 
         if (a.bits == 4) launch_l<64, 4>(num_tiles, a, stream);
         else launch_l<64, 2>(num_tiles, a, stream);
     }
+}
+
+// K (token-major) and V (channel-major) caches of one batch in one launch: same
+// tiles, tile size and round count; each cache's own bits
+bool quantize_d128_pair_supported(int T, const QuantArgs &k, const QuantArgs &v) {
+    return quantize_d128_supported(QD, T, k) && quantize_d128_supported(QD, T, v) && k.layout == KVQ_TOKEN_MAJOR &&
+           v.layout == KVQ_CHANNEL_MAJOR && k.iters == v.iters;
+}
+
+template <int T, int BK, int BV, int NIT>
+static void launch_pair_n(int num_tiles, const QuantArgs &k, const QuantArgs &v, hipStream_t stream) {
+    constexpr int R = QR;
+    constexpr int NT = 16 * T / R;
+    const int nk = num_tiles * k.H, items = nk + num_tiles * v.H;
+    auto kern = quantize_d128_kernel<T, R, BK, KVQ_TOKEN_MAJOR, BV, KVQ_CHANNEL_MAJOR, NIT, true>;
+    hipLaunchKernelGGL(kern, dim3(d128_grid(items, (const void *)kern, NT)), dim3(NT), 0, stream, k, v, nk, items);
+}
+
+template <int T, int BK, int BV>
+static void launch_pair_i(int num_tiles, const QuantArgs &k, const QuantArgs &v, hipStream_t stream) {
+    if (k.iters == 4) launch_pair_n<T, BK, BV, 4>(num_tiles, k, v, stream);
+    else if (k.iters == 2) launch_pair_n<T, BK, BV, 2>(num_tiles, k, v, stream);
+    else launch_pair_n<T, BK, BV, -1>(num_tiles, k, v, stream);
+}
+
+template <int T>
+static void launch_pair_t(int num_tiles, const QuantArgs &k, const QuantArgs &v, hipStream_t stream) {
+    if (k.bits == 4) {
+        if (v.bits == 4) launch_pair_i<T, 4, 4>(num_tiles, k, v, stream);
+        else launch_pair_i<T, 4, 2>(num_tiles, k, v, stream);
+    } else {
+        if (v.bits == 4) launch_pair_i<T, 2, 4>(num_tiles, k, v, stream);
+        else launch_pair_i<T, 2, 2>(num_tiles, k, v, stream);
+    }
+}
+
+void launch_quantize_d128_pair(int T, int num_tiles, const QuantArgs &k, const QuantArgs &v, hipStream_t stream) {
+    if (T == 128) launch_pair_t<128>(num_tiles, k, v, stream);
+    else launch_pair_t<64>(num_tiles, k, v, stream);
 }
 
 }  // namespace kvq

@@ -60,6 +60,32 @@ def quantize_status(fmt, src=FAKE, stride_token=256, stride_head=128, tiles=1, c
     return K._lib.kv_quantize(ctypes.byref(c), src, 2, stride_token, stride_head, tiles, FAKE, FAKE, FAKE, None, None)
 
 
+def quantize_kv_status(fk, fv, k_src=FAKE, v_src=FAKE, tiles=1, heads=(2, 2), pages=(4, 4)):
+    k = K.kvq_cache(fk, pages[0], heads[0], FAKE, FAKE, FAKE, None)
+    v = K.kvq_cache(fv, pages[1], heads[1], FAKE, FAKE, FAKE, None)
+    return K._lib.kv_quantize_kv(ctypes.byref(k), ctypes.byref(v), k_src, v_src, 2, 256, 128, 256, 128, tiles, FAKE,
+                                 FAKE, FAKE, None, None)
+
+
+def test_quantize_kv_argument_errors():
+    """kv_quantize_kv: per-cache checks as kv_quantize, then KVQ_EUNSUPPORTED (nothing
+    launched) for any pair the one-launch kernel does not take; zero tiles launch nothing."""
+    fk = K.make_format(128, 0, 128, 128, 128, 4, 4, K.KVQ_TOKEN_MAJOR)
+    fv = K.make_format(128, 0, 128, 128, 128, 2, 4, K.KVQ_CHANNEL_MAJOR)
+    assert quantize_kv_status(fk, fv, tiles=0) == K.KVQ_OK
+    assert quantize_kv_status(fk, fv, k_src=None) == K.KVQ_EINVAL
+    assert quantize_kv_status(fk, fv, v_src=None) == K.KVQ_EINVAL
+    assert quantize_kv_status(fk, fv, tiles=-1) == K.KVQ_EINVAL
+    assert quantize_kv_status(fk, fv, v_src=FAKE + 2) == K.KVQ_EUNSUPPORTED           # not 16-byte aligned
+    assert quantize_kv_status(fk, fk, tiles=0) == K.KVQ_EUNSUPPORTED                  # V token-major
+    assert quantize_kv_status(fv, fv, tiles=0) == K.KVQ_EUNSUPPORTED                  # K channel-major
+    assert quantize_kv_status(fk, K.make_format(128, 0, 64, 128, 128, 2, 4, 1), tiles=0) == K.KVQ_EUNSUPPORTED  # tiles
+    assert quantize_kv_status(fk, K.make_format(128, 0, 128, 128, 128, 2, 2, 1), tiles=0) == K.KVQ_EUNSUPPORTED  # rounds
+    assert quantize_kv_status(fk, K.make_format(128, 0, 128, 128, 128, 3, 4, 1), tiles=0) == K.KVQ_EUNSUPPORTED  # 3-bit
+    assert quantize_kv_status(fk, fv, heads=(2, 1), tiles=0) == K.KVQ_EUNSUPPORTED
+    assert quantize_kv_status(fk, fv, pages=(4, 5), tiles=0) == K.KVQ_EUNSUPPORTED
+
+
 def test_quantize_argument_errors():
     ok = K.make_format(128, 0, 128, 128, 128, 4, 4, 0)
     assert quantize_status(ok, src=None) == K.KVQ_EINVAL

@@ -131,6 +131,65 @@ def check_quantize_case(gpu, case, center=0):
     assert int(flags.item()) == fl == 0
 
 
+PAIR = [
+    # T, K bits, V bits, iters, sequence lengths (partial last tiles), heads
+    (128, 4, 4, 4, (300, 128, 1), 2),
+    (128, 4, 2, 4, (700, 60), 3),
+    (64, 2, 4, 2, (200, 64, 5), 2),
+    (64, 4, 4, 3, (130,), 1),          # round count not specialised
+]
+
+
+@pytest.mark.parametrize("case", PAIR, ids=lambda c: "T{}k{}v{}N{}".format(*c[:4]))
+def test_quantize_kv_one_launch_equals_two(gpu, case):
+    """kv_quantize_kv (K and V in one launch) writes exactly the caches and flags of
+    two kv_quantize calls; the pages of invalid destinations stay untouched."""
+    T, kb, vb, iters, lens, H = case
+    log("pair case", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    tst, tv, tp, tok = tiles_for(list(lens), T, rng)
+    P = len(tp)
+    tp = tp.copy()
+    skipped_page = int(tp[len(tp) // 2])
+    tp[len(tp) // 2] = -1  # one tile skipped: its page is written by no tile
+    fk, fv = W.Fmt(128, 0, T, 128, 128, kb, iters, 0), W.Fmt(128, 0, T, 128, 128, vb, iters, 1)
+    kx = to_dev(make_src(heavy(rng, tok, H, 128), "bf16"), "bf16")
+    vx = to_dev(make_src(rng.standard_normal((tok, H, 128)), "bf16"), "bf16")
+    ts, tvd, tpd = i32(tst), i32(tv), i32(tp)
+    caches = []
+    for pair in (False, True):
+        dk, dv = K.DeviceCache(kfmt(fk), P, H), K.DeviceCache(kfmt(fv), P, H)
+        for c in (dk, dv):
+            c.codes.fill_(0x5A)
+            c.sz.fill_(0x1234)
+            c.cnorm.fill_(0x4321)
+        fl = torch.zeros(1, dtype=torch.int32, device=gpu)
+        if pair:
+            K.kv_quantize_kv(dk, dv, kx, vx, ts, tvd, tpd, status_flags=fl)
+        else:
+            K.kv_quantize(dk, kx, ts, tvd, tpd, status_flags=fl)
+            K.kv_quantize(dv, vx, ts, tvd, tpd, status_flags=fl)
+        torch.cuda.synchronize()
+        caches.append((dk, dv, int(fl.item())))
+    (a, b, fa), (c, d, fb) = caches
+    assert fa == fb
+    for x, y in ((a, c), (b, d)):
+        assert torch.equal(x.codes, y.codes) and torch.equal(x.sz, y.sz) and torch.equal(x.cnorm, y.cnorm)
+    for x in (c, d):
+        assert bool((x.codes[skipped_page] == 0x5A).all()) and bool((x.cnorm[skipped_page] == 0x4321).all())
+
+
+def test_quantize_kv_unsupported_formats(gpu):
+    """Formats outside the one-launch kernel: KVQ_EUNSUPPORTED, nothing written."""
+    fk, fv = W.Fmt(128, 0, 16, 128, 128, 3, 2, 0), W.Fmt(128, 0, 16, 128, 128, 3, 2, 1)
+    dk, dv = K.DeviceCache(kfmt(fk), 4, 1), K.DeviceCache(kfmt(fv), 4, 1)
+    x = torch.zeros((64, 1, 128), dtype=torch.bfloat16, device=gpu)
+    t = i32(np.arange(4) * 16)
+    with pytest.raises(K.KvqError) as e:
+        K.kv_quantize_kv(dk, dv, x, x, t, i32(np.full(4, 16)), i32(np.arange(4)))
+    assert e.value.status == K.KVQ_EUNSUPPORTED
+
+
 def test_quantize_is_deterministic(gpu):
     cfg = W.config(1)
     rng = np.random.default_rng(5)
