@@ -179,6 +179,37 @@ def test_quantize_kv_one_launch_equals_two(gpu, case):
         assert bool((x.codes[skipped_page] == 0x5A).all()) and bool((x.cnorm[skipped_page] == 0x4321).all())
 
 
+@pytest.mark.parametrize("vbits", [4, 2])
+def test_quantize_kv_one_launch_full_size(gpu, vbits):
+    """At the GQA workload's size (8 x 4096 tokens, 8 kv heads: 4096 items over a grid
+    of at most two workgroups per compute unit) each workgroup walks several items and
+    its prefetch crosses from K items into V items; the caches still equal those of
+    two kv_quantize calls bit for bit."""
+    T, H, tiles = 128, 8, 8 * 32
+    g = torch.Generator(device=gpu)
+    g.manual_seed(4321 + vbits)
+    kx = (torch.randn((tiles * T, H, 128), generator=g, device=gpu) *
+          torch.exp(torch.randn((1, H, 128), generator=g, device=gpu))).to(torch.bfloat16)
+    vx = torch.randn((tiles * T, H, 128), generator=g, device=gpu).to(torch.bfloat16)
+    tst = i32(np.arange(tiles) * T)
+    tv = i32(np.full(tiles, T))
+    perm = np.random.default_rng(vbits).permutation(tiles)
+    tp = i32(perm)
+    fk, fv = W.Fmt(128, 0, T, 128, 128, 4, 4, 0), W.Fmt(128, 0, T, 128, 128, vbits, 4, 1)
+    out = []
+    for pair in (False, True):
+        dk, dv = K.DeviceCache(kfmt(fk), tiles, H), K.DeviceCache(kfmt(fv), tiles, H)
+        if pair:
+            K.kv_quantize_kv(dk, dv, kx, vx, tst, tv, tp)
+        else:
+            K.kv_quantize(dk, kx, tst, tv, tp)
+            K.kv_quantize(dv, vx, tst, tv, tp)
+        torch.cuda.synchronize()
+        out.append((dk, dv))
+    for x, y in zip(out[0], out[1]):
+        assert torch.equal(x.codes, y.codes) and torch.equal(x.sz, y.sz) and torch.equal(x.cnorm, y.cnorm)
+
+
 def test_quantize_kv_unsupported_formats(gpu):
     """Formats outside the one-launch kernel: KVQ_EUNSUPPORTED, nothing written."""
     fk, fv = W.Fmt(128, 0, 16, 128, 128, 3, 2, 0), W.Fmt(128, 0, 16, 128, 128, 3, 2, 1)
