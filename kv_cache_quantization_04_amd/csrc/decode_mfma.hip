@@ -25,6 +25,12 @@
 // 16 / g positions and no column is padding. Workgroups that share pages (the
 // column blocks of one sequence, kv head and split) are given consecutive ids
 // on one XCD, so the repeated page reads hit that XCD's L2.
+//
+// Page staging by page size: 16-token pages are prefetched into registers one page
+// ahead; 64- and 128-token pages are copied whole into a per-wave LDS image by
+// direct-to-LDS loads (V codes last, waited for only before the value product),
+// and with long splits (DB) into two alternating images, the next page's copies
+// travelling while the current page is computed.
 #include "common.h"
 #include "launch.h"
 

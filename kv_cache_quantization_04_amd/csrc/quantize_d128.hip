@@ -10,6 +10,11 @@
 // every per-token reduction are DPP row operations. After the rotation the lane
 // holds rotated channel group hperm16(l & 15) (the lane stages relabel them).
 //
+// Persistent workgroups walk items (tile, head); the next item's rows are copied
+// HBM -> LDS while the current one is computed. One launch can cover the K and V
+// caches of a batch (PAIR): K items first, then V items, each with its own layout
+// and bit width.
+//
 // Method: "KVarN" project review, Key Features ("Variance-Normalized
 // Quantization Pipeline"): rotate, run row/column RMS normalization rounds,
 // asymmetric round-to-nearest with fp16 scale, zero point and normalizer.
