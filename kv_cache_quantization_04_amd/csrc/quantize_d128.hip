@@ -313,8 +313,10 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
                 acc[v] = (colsum[4 * v][tid] + colsum[4 * v + 1][tid]) + (colsum[4 * v + 2][tid] + colsum[4 * v + 3][tid]);
             t_own = NWV == 8 ? acc[0] + acc[NWV / 8] : acc[0];
             // a zero column keeps a large finite w (its A entries are all zero)
-            wsh[tid] = fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
+            if (it + 1 < iters) wsh[tid] = fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY));
         }
+        // the last round's column sums go straight to the normalizer below (no w)
+        if (it + 1 == iters) break;
         lds_barrier();
         const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[pcc * 8]);
         const float4 w1 = *reinterpret_cast<const float4 *>(&wsh[pcc * 8 + 4]);

@@ -249,10 +249,11 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
             {
                 const int pc = pch(tid);
                 t_own = lds_sum8_stride(&colsum[0][pc]);
-                // a zero column keeps a large finite w (its A entries are all zero)
-                lds_store_f32(&wsh[pc], fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY)));
+                // a zero column keeps a large finite w (its A entries are all zero); the
+                // last round's sums go straight to the normalizer below (no w)
+                if (it + 1 < iters) lds_store_f32(&wsh[pc], fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own, TINY)));
             }
-            lds_barrier();  // w of this round visible to every lane
+            if (it + 1 < iters) lds_barrier();  // w of this round visible to every lane
         }
 
         // ---- fp16 normalizer c16 (thread tid owns channel tid) and the multiplier
