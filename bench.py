@@ -3,15 +3,20 @@
 
 One step = quantize the K and V of one batch (every tile and kv head of the
 workload) and run quantized decode attention over one batch's quantized cache.
-Inputs are seeded synthetic data already resident in device memory; a ring of
-independent copies (inputs and caches) larger than the 256 MB last-level cache
-makes every step read from and write to HBM: the decode reads the cache that the
-quantizer wrote half a ring of steps earlier, not the one it has just written.
+The default run times the four workloads (GQA decode, long context, paged
+serving, MLA latent) one after the other and quotes the headline on paged
+serving, the largest. Inputs are seeded synthetic data already resident in
+device memory; a ring of independent copies (inputs and caches) larger than the
+256 MB last-level cache makes every step read from and write to HBM: the decode
+reads the cache that the quantizer wrote half a ring of steps earlier, not the
+one it has just written.
 
 Prints one JSON line: whole-step throughput in GB/s of algorithmic bytes
 (inputs read + codes and side data written by the quantizer; codes and side data
-of every attended page + queries + outputs for decode), the quantizer's roofline
-position, and the CPU oracle timed on a bounded sample of the same workload.
+of every attended page + queries + outputs for decode) on the headline workload,
+the HBM roofline position of its dominant kernel (algorithmic bytes per launch
+over the average duration of back-to-back launches), per-workload figures under
+"detail", and the CPU oracle timed on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -117,37 +122,47 @@ def profiled_traffic(kernel, workload_key):
     return float(t.group(1))
 
 
-def cpu_baseline(cfg, ks, vs, q, nseq):
+def cpu_baseline(cfg, nseq):
+    """The CPU oracle, as it stands, on the first nseq sequences of the workload: fp64
+    quantization of their K and V tiles and dequantize-then-softmax decode for every
+    query head, on all host threads. GB/s of the same algorithmic bytes as the GPU
+    figures, over the sample."""
     import oracle as O
+    import workloads as W
 
     threads = os.cpu_count() or 1
     seqs = list(range(min(nseq, cfg.num_seqs)))
     sel = np.nonzero(np.isin(cfg.tile_seq, seqs))[0]
+    t_end = int(cfg.seq_start[seqs[-1]] + cfg.seq_lens[seqs[-1]])
+    ks = W.gen_k(cfg, 0, t_end)
+    vs = W.gen_v(cfg, 0, t_end) if cfg.fv is not None else None
+    q = W.gen_q(cfg)
     Hkv = cfg.num_kv_heads
+    dt = O.F32 if cfg.src_dtype == "f32" else O.BF16
     t0 = time.perf_counter()
     kc = O.HostCache(cfg.fk, cfg.num_pages, Hkv)
-    O.quantize_cache(kc, ks, O.F32 if cfg.src_dtype == "f32" else O.BF16, cfg.tile_src_token[sel],
-                     cfg.tile_valid[sel], cfg.tile_page[sel], nthreads=threads)
+    O.quantize_cache(kc, ks, dt, cfg.tile_src_token[sel], cfg.tile_valid[sel], cfg.tile_page[sel], nthreads=threads)
     vc = None
     if cfg.fv is not None:
         vc = O.HostCache(cfg.fv, cfg.num_pages, Hkv)
-        O.quantize_cache(vc, vs, O.F32 if cfg.src_dtype == "f32" else O.BF16, cfg.tile_src_token[sel],
-                         cfg.tile_valid[sel], cfg.tile_page[sel], nthreads=threads)
+        O.quantize_cache(vc, vs, dt, cfg.tile_src_token[sel], cfg.tile_valid[sel], cfg.tile_page[sel],
+                         nthreads=threads)
     tq = time.perf_counter() - t0
     t1 = time.perf_counter()
-    O.decode_attn(q[seqs], O.F32 if cfg.src_dtype == "f32" else O.BF16, kc, vc, cfg.block_table[seqs],
-                  cfg.seq_lens[seqs], cfg.sm_scale, folded=False, nthreads=threads)
+    O.decode_attn(q[seqs], dt, kc, vc, cfg.block_table[seqs], cfg.seq_lens[seqs], cfg.sm_scale, folded=False,
+                  nthreads=threads)
     td = time.perf_counter() - t1
     tokens = int(cfg.seq_lens[seqs].sum())
-    W = cfg.width
-    qb = tokens * Hkv * W * ESIZE[cfg.src_dtype] + sel.size * Hkv * block_bytes(cfg.fk)
+    W_ = cfg.width
+    qb = tokens * Hkv * W_ * ESIZE[cfg.src_dtype] + sel.size * Hkv * block_bytes(cfg.fk)
     if cfg.fv is not None:
         qb += tokens * Hkv * cfg.dv * ESIZE[cfg.src_dtype] + sel.size * Hkv * block_bytes(cfg.fv)
     db = decode_bytes(cfg, seqs)
     return {"value": round((qb + db) / (tq + td) / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {len(seqs)} of {cfg.num_seqs} sequences ({tokens} tokens x {Hkv} kv heads): fp64 "
-                      f"oracle quantize of their K and V tiles ({tq:.2f} s) and dequantize-then-softmax decode for "
-                      f"all {cfg.num_q_heads} query heads ({td:.2f} s), {threads} threads"}
+            "sample": f"{cfg.name.split(':')[0]}: first {len(seqs)} of {cfg.num_seqs} sequences ({tokens} tokens x "
+                      f"{Hkv} kv heads): fp64 oracle quantize of their K and V tiles ({tq:.2f} s) and "
+                      f"dequantize-then-softmax decode for all {cfg.num_q_heads} query heads ({td:.2f} s), "
+                      f"{threads} threads"}
 
 
 def bench_append(args, cfg, torch, K, W, dev):
@@ -292,14 +307,173 @@ def bench_prefill(args, cfg, torch, K, W, dev):
     print(json.dumps(res), flush=True)
 
 
+def loop_ms(torch, stream, n, fn):
+    """Average duration of fn(i), i < n, launched back to back on `stream`: two HIP
+    events bracket the whole loop (none between launches)."""
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def run_config(ci, args, torch, K, W, dev):
+    """One workload: quantize K and V + decode per step, on a ring of input copies and
+    caches. Returns the step time and, from separate back-to-back loops of each part,
+    the quantizer's and the decode call's average durations."""
+    cfg = W.config(ci)
+    log(f"workload {ci}: {cfg.name}")
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a):
+        if cfg.src_dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def kfmt(f):
+        return K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+    tst, tv, tp = i32(cfg.tile_src_token), i32(cfg.tile_valid), i32(cfg.tile_page)
+    bt, sl = i32(cfg.block_table), i32(cfg.seq_lens)
+    qd = to_dev(W.gen_q(cfg))
+    kin_r, kout_w = quantize_bytes(cfg, cfg.fk, cfg.width)
+    vin_r, vout_w = quantize_bytes(cfg, cfg.fv, cfg.dv) if cfg.fv is not None else (0, 0)
+    qbytes = kin_r + kout_w + vin_r + vout_w
+    dbytes = decode_bytes(cfg)
+    ring = max(2, math.ceil(args.ring_mb * 1e6 / qbytes))
+    t0 = time.perf_counter()
+    ksrc0 = to_dev(W.gen_k(cfg))
+    vsrc0 = to_dev(W.gen_v(cfg)) if cfg.fv is not None else None
+    log(f"  inputs generated and uploaded in {time.perf_counter() - t0:.1f} s; ring of {ring} copies "
+        f"({ring * qbytes / 1e6:.0f} MB live)")
+    ksrc = [ksrc0] + [ksrc0.clone() for _ in range(ring - 1)]
+    vsrc = ([vsrc0] + [vsrc0.clone() for _ in range(ring - 1)]) if vsrc0 is not None else [None] * ring
+    kcache = [K.DeviceCache(kfmt(cfg.fk), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
+    vcache = ([K.DeviceCache(kfmt(cfg.fv), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
+              if cfg.fv is not None else [None] * ring)
+    max_len = int(cfg.seq_lens.max())
+    splits = K.kv_decode_attn_default_splits(kcache[0], vcache[0], cfg.num_seqs, cfg.num_q_heads, max_len)
+    ws = torch.empty(K.kv_decode_attn_workspace_bytes(cfg.num_seqs, cfg.num_q_heads, cfg.dv, splits),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.num_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device=dev)
+    # K and V in one launch (kv_quantize_kv) where the library takes the pair of formats
+    pair = False
+    if vsrc[0] is not None:
+        try:
+            K.kv_quantize_kv(kcache[0], vcache[0], ksrc[0], vsrc[0], tst, tv, tp, stream=stream)
+            pair = True
+        except K.KvqError as e:
+            if e.status != K.KVQ_EUNSUPPORTED:
+                raise
+
+    def quantize(j):
+        if pair:
+            K.kv_quantize_kv(kcache[j], vcache[j], ksrc[j], vsrc[j], tst, tv, tp, stream=stream)
+        else:
+            K.kv_quantize(kcache[j], ksrc[j], tst, tv, tp, stream=stream)
+            if vsrc[j] is not None:
+                K.kv_quantize(vcache[j], vsrc[j], tst, tv, tp, stream=stream)
+
+    def decode(j):
+        K.kv_decode_attn(qd, kcache[j], vcache[j], bt, sl, max_len, cfg.sm_scale, num_splits=splits, workspace=ws,
+                         out=out, stream=stream)
+
+    # Every ring slot holds a quantized cache before the first step. Step i quantizes
+    # slot i mod ring and decodes the cache of slot i - ring/2, written half a ring of
+    # steps earlier: neither the quantizer's source nor the decoder's cache is still in
+    # the 256 MB last-level cache (at least one copy's traffic in between).
+    for j in range(ring):
+        quantize(j)
+    lag = ring // 2
+
+    def step(i):
+        quantize(i % ring)
+        decode((i - lag) % ring)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ms = loop_ms(torch, stream, args.steps, step)
+    wall = time.perf_counter() - t0
+    log(f"  timed {args.steps} steps: {step_ms * args.steps:.3f} ms on device, {wall * 1e3:.3f} ms wall")
+    # each part alone, back to back over the ring (no event between launches)
+    n = max(args.steps, 2 * ring)
+    tq = loop_ms(torch, stream, n, lambda i: quantize(i % ring))
+    td = loop_ms(torch, stream, n, lambda i: decode(i % ring))
+    log(f"  quantize {tq * 1e3:.1f} us per step, decode {td * 1e3:.1f} us per call ({n} back to back)")
+
+    nq = 2 if cfg.fv is not None and not pair else 1  # quantizer launches per step
+    qnames = sorted({K.kv_quantize_kernel_name(kcache[0], ksrc[0])} |
+                    ({K.kv_quantize_kernel_name(vcache[0], vsrc[0])} if vsrc[0] is not None else set()))
+    dname = K.kv_decode_attn_kernel_name(qd, kcache[0], vcache[0])
+    qops = quantize_valu_ops(cfg, cfg.fk, cfg.width) + (quantize_valu_ops(cfg, cfg.fv, cfg.dv)
+                                                        if cfg.fv is not None else 0)
+    positions = int(cfg.seq_lens.sum())
+    q_gbs = qbytes / (tq * 1e-3) / 1e9
+    d_gbs = dbytes / (td * 1e-3) / 1e9
+    r = {
+        "workload": cfg.name, "key": W.NAMES[ci], "step_ms": round(step_ms, 5),
+        "step_GBps": round((qbytes + dbytes) / (step_ms * 1e-3) / 1e9, 2),
+        "quantize_kernels": qnames, "quantize_launches": nq, "quantize_us": round(tq * 1e3, 2),
+        "quantize_GBps": round(q_gbs, 2), "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+        "quantize_input_GBps": round((kin_r + vin_r) / (tq * 1e-3) / 1e9, 2),
+        "quantize_tokens_per_s": round((2 if cfg.fv is not None else 1) * cfg.total_tokens * cfg.num_kv_heads /
+                                       (tq * 1e-3), 1),
+        "quantize_valu_frac": round(qops / (tq * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
+        "decode_kernel": dname + " + decode_reduce_kernel", "decode_splits": splits, "decode_us": round(td * 1e3, 2),
+        "decode_GBps": round(d_gbs, 2), "decode_frac_hbm": round(d_gbs / HBM_PEAK_GBS, 4),
+        "decode_positions_per_s": round(positions / (td * 1e-3), 1),
+        "decode_tokens_per_s": round(cfg.num_seqs / (td * 1e-3), 1),
+        "quantize_bytes": qbytes, "decode_bytes": dbytes, "copy_ring": ring,
+    }
+    if dname == "decode_mla_kernel":
+        # dense f16 MFMA contraction: scores over D + R channels and values over D, per head and position
+        flops = 2.0 * positions * cfg.num_q_heads * (cfg.width + cfg.dv)
+        r["decode_TFLOPs"] = round(flops / (td * 1e-3) / 1e12, 2)
+        r["decode_frac_mfma_f16"] = round(flops / (td * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+    # the dominant kernel of the step and its HBM roofline position: algorithmic bytes
+    # per launch over the average launch duration
+    if tq >= td:
+        kern = qnames[0] if len(qnames) == 1 else " / ".join(qnames)
+        per_launch, launch_ms = qbytes / nq, tq / nq
+        other = {"valu": {"achieved": round(qops / nq / (launch_ms * 1e-3) / 1e12, 3),
+                          "peak": round(VALU_PEAK_TOPS, 2), "unit": "T VALU lane-ops/s",
+                          "frac": r["quantize_valu_frac"],
+                          "algorithmic_ops_per_launch": qops / nq}}
+        traffic = profiled_traffic(qnames[0], W.NAMES[ci]) if len(qnames) == 1 else None
+    else:
+        kern = dname
+        per_launch, launch_ms = dbytes, td
+        other = {}
+        if "decode_TFLOPs" in r:
+            other = {"mfma": {"achieved": r["decode_TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": r["decode_frac_mfma_f16"]}}
+        traffic = profiled_traffic(dname, W.NAMES[ci])
+    gbs = per_launch / (launch_ms * 1e-3) / 1e9
+    r["roofline"] = dict(bound="hbm", kernel=kern, achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic, algorithmic_bytes_per_launch=per_launch,
+                         avg_launch_us=round(launch_ms * 1e3, 3), **other)
+    return r, cfg
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload index (1 = GQA decode, the headline)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--configs", default="1,2,3,4", help="workload indices timed in this run")
+    ap.add_argument("--headline", type=int, default=3,
+                    help="workload the headline value is quoted on (3 = paged serving, the largest)")
+    ap.add_argument("--config", type=int, default=None, help="time one workload only (it is then the headline)")
     ap.add_argument("--ring-mb", type=int, default=2048, help="live bytes of the copy ring")
-    ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle's timed sample")
+    ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences of the headline workload the oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", action="store_true",
                     help="measure the append path (one token per sequence per step, K and V) instead")
@@ -317,193 +491,48 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
-    cfg = W.config(args.config)
-    log(f"workload: {cfg.name}")
-    if args.append:
-        bench_append(args, cfg, torch, K, W, dev)
+    if args.append or args.prefill > 0:
+        args.config = 1 if args.config is None else args.config
+        cfg = W.config(args.config)
+        log(f"workload: {cfg.name}")
+        (bench_append if args.append else bench_prefill)(args, cfg, torch, K, W, dev)
         return
-    if args.prefill > 0:
-        bench_prefill(args, cfg, torch, K, W, dev)
-        return
-    ks = W.gen_k(cfg)
-    vs = W.gen_v(cfg) if cfg.fv is not None else None
-    q = W.gen_q(cfg)
-
-    def to_dev(a):
-        if cfg.src_dtype == "f32":
-            return torch.from_numpy(a).to(dev)
-        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    def kfmt(f):
-        return K.make_format(f.head_dim, f.rope_dim, f.tile_tokens, f.hadamard_n, f.group, f.bits, f.iters, f.layout)
-
-    def i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
-
-    tst, tv, tp = i32(cfg.tile_src_token), i32(cfg.tile_valid), i32(cfg.tile_page)
-    bt, sl = i32(cfg.block_table), i32(cfg.seq_lens)
-    qd = to_dev(q)
-    kin_r, kout_w = quantize_bytes(cfg, cfg.fk, cfg.width)
-    vin_r, vout_w = quantize_bytes(cfg, cfg.fv, cfg.dv) if cfg.fv is not None else (0, 0)
-    qbytes = kin_r + kout_w + vin_r + vout_w
-    dbytes = decode_bytes(cfg)
-    per_copy = qbytes
-    ring = max(2, math.ceil(args.ring_mb * 1e6 / per_copy))
-    log(f"ring of {ring} copies ({ring * per_copy / 1e6:.0f} MB live)")
-    ksrc0 = to_dev(ks)
-    vsrc0 = to_dev(vs) if vs is not None else None
-    ksrc = [ksrc0] + [ksrc0.clone() for _ in range(ring - 1)]
-    vsrc = ([vsrc0] + [vsrc0.clone() for _ in range(ring - 1)]) if vs is not None else [None] * ring
-    kcache = [K.DeviceCache(kfmt(cfg.fk), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
-    vcache = ([K.DeviceCache(kfmt(cfg.fv), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
-              if cfg.fv is not None else [None] * ring)
-    max_len = int(cfg.seq_lens.max())
-    splits = K.kv_decode_attn_default_splits(kcache[0], vcache[0], cfg.num_seqs, cfg.num_q_heads, max_len)
-    ws = torch.empty(K.kv_decode_attn_workspace_bytes(cfg.num_seqs, cfg.num_q_heads, cfg.dv, splits),
-                     dtype=torch.uint8, device=dev)
-    out = torch.empty((cfg.num_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device=dev)
-    # a plain device copy of known size: the reference kernel for scaling HBM counters
-    calib = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-    torch.empty_like(calib).copy_(calib)
-
-    stream = torch.cuda.current_stream()
-    # Every ring slot holds a quantized cache before the first step. A step quantizes
-    # slot j and decodes the cache of slot j - ring/2, written half a ring of steps
-    # earlier: neither the quantizer's source nor the decoder's cache is still in the
-    # 256 MB last-level cache (at least 1 GB of other traffic in between).
-    # K and V in one launch (kv_quantize_kv) where the library takes the pair of formats
-    pair = False
-    if vsrc[0] is not None:
-        try:
-            K.kv_quantize_kv(kcache[0], vcache[0], ksrc[0], vsrc[0], tst, tv, tp, stream=stream)
-            pair = True
-        except K.KvqError as e:
-            if e.status != K.KVQ_EUNSUPPORTED:
-                raise
-    for j in range(ring):
-        if pair:
-            K.kv_quantize_kv(kcache[j], vcache[j], ksrc[j], vsrc[j], tst, tv, tp, stream=stream)
-        else:
-            K.kv_quantize(kcache[j], ksrc[j], tst, tv, tp, stream=stream)
-            if vsrc[j] is not None:
-                K.kv_quantize(vcache[j], vsrc[j], tst, tv, tp, stream=stream)
-    lag = ring // 2
-
-    def step(i, evs=None):
-        j = i % ring
-        jd = (i - lag) % ring
-        if evs:
-            evs[0].record(stream)
-        if pair:
-            K.kv_quantize_kv(kcache[j], vcache[j], ksrc[j], vsrc[j], tst, tv, tp, stream=stream)
-        else:
-            K.kv_quantize(kcache[j], ksrc[j], tst, tv, tp, stream=stream)
-        if evs:
-            evs[1].record(stream)
-        if vsrc[j] is not None and not pair:
-            K.kv_quantize(vcache[j], vsrc[j], tst, tv, tp, stream=stream)
-        if evs:
-            evs[2].record(stream)
-        K.kv_decode_attn(qd, kcache[jd], vcache[jd], bt, sl, max_len, cfg.sm_scale, num_splits=splits, workspace=ws,
-                         out=out, stream=stream)
-        if evs:
-            evs[3].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-
-    # Per-kernel times come from HIP events recorded around the launches of every
-    # INSTR-th timed step (at least the first): each event record holds the queue for a
-    # few microseconds, which instrumenting every step would add to the step time.
-    INSTR = 8
-    inst = list(range(0, args.steps, INSTR))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in inst}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(i, evs.get(i))
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    tk = sum(e[0].elapsed_time(e[1]) for e in evs.values()) / len(evs)
-    tvq = sum(e[1].elapsed_time(e[2]) for e in evs.values()) / len(evs)
-    td = sum(e[2].elapsed_time(e[3]) for e in evs.values()) / len(evs)
-    log(f"timed {args.steps} steps: {total_ms:.3f} ms on device, {wall * 1e3:.3f} ms wall")
-
-    value = (qbytes + dbytes) / (ms_step * 1e-3) / 1e9
-    nq = 2 if cfg.fv is not None and not pair else 1  # quantizer launches per step
-    q_gbs = qbytes / ((tk + tvq) * 1e-3) / 1e9
-    d_gbs = dbytes / (td * 1e-3) / 1e9
-    per_launch = qbytes / nq
-    avg_launch_ms = (tk + tvq) / nq
-    qops = quantize_valu_ops(cfg, cfg.fk, cfg.width) + (quantize_valu_ops(cfg, cfg.fv, cfg.dv) if cfg.fv is not None else 0)
-    positions = int(cfg.seq_lens.sum())
-    qnames = sorted({K.kv_quantize_kernel_name(kcache[0], ksrc[0])} |
-                    ({K.kv_quantize_kernel_name(vcache[0], vsrc[0])} if vsrc[0] is not None else set()))
-    dname = K.kv_decode_attn_kernel_name(qd, kcache[0], vcache[0])
-    if tk + tvq >= td:
-        # the quantizer dominates the step: VALU-bound (lane-ops per element), HBM figure alongside
-        traffic = profiled_traffic(qnames[0], W.NAMES[args.config]) if len(qnames) == 1 else None
-        roofline = {"bound": "alu", "kernel": " / ".join(qnames),
-                    "achieved": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12, 3), "peak": round(VALU_PEAK_TOPS, 2),
-                    "unit": "T VALU lane-ops/s",
-                    "frac": round(qops / nq / (avg_launch_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
-                    "traffic": traffic, "algorithmic_ops_per_launch": qops / nq,
-                    "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-                    "hbm": {"achieved": round(per_launch / (avg_launch_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(per_launch / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    if args.config is not None:
+        configs, headline = [args.config], args.config
     else:
-        # decode dominates; its timing spans the call (main kernel + split merge pass)
-        traffic = profiled_traffic(dname, W.NAMES[args.config])
-        hbm = {"achieved": round(d_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4)}
-        if dname == "decode_mla_kernel":
-            # dense f16 MFMA contraction: scores over D + R channels and values over D, per head and position
-            flops = 2.0 * positions * cfg.num_q_heads * (cfg.width + cfg.dv)
-            tf = flops / (td * 1e-3) / 1e12
-            roofline = {"bound": "mfma", "kernel": dname + " + decode_reduce_kernel", "achieved": round(tf, 2),
-                        "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                        "traffic": traffic, "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": dbytes,
-                        "avg_launch_us": round(td * 1e3, 3), "hbm": hbm}
-        else:
-            roofline = dict(bound="hbm", kernel=dname + " + decode_reduce_kernel", traffic=traffic,
-                            algorithmic_bytes_per_launch=dbytes, avg_launch_us=round(td * 1e3, 3), **hbm)
+        configs, headline = [int(c) for c in args.configs.split(",")], args.headline
+        if headline not in configs:
+            configs.append(headline)
+    per, hcfg = {}, None
+    for ci in configs:
+        r, cfg = run_config(ci, args, torch, K, W, dev)
+        per[r["key"]] = r
+        if ci == headline:
+            hcfg, h = cfg, r
+        torch.cuda.empty_cache()
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": h["step_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": h["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "kv_layout": "K token-major, V channel-major, fp16 side data",
-                   "decode_splits": splits, "copy_ring": ring,
-                   "quantize_launches": "K and V in one launch" if pair else ("K, V" if cfg.fv is not None else "K")},
-        "roofline": roofline,
-        "detail": {
-            "quantize_GBps": round(q_gbs, 2), "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
-            "quantize_input_GBps": round((kin_r + vin_r) / ((tk + tvq) * 1e-3) / 1e9, 2),
-            "quantize_tokens_per_s": round((2 if cfg.fv is not None else 1) * cfg.total_tokens * cfg.num_kv_heads /
-                                           ((tk + tvq) * 1e-3), 1),
-            "quantize_us": round((tk + tvq) * 1e3, 3),
-            "decode_GBps": round(d_gbs, 2), "decode_frac_hbm": round(d_gbs / HBM_PEAK_GBS, 4),
-            "decode_us": round(td * 1e3, 3), "decode_positions_per_s": round(positions / (td * 1e-3), 1),
-            "decode_bytes": dbytes, "quantize_bytes": qbytes,
-            "quantize_kernels": qnames, "decode_kernel": dname,
-        },
+        "config": {"workload": hcfg.name, "kv_layout": "K token-major, V channel-major, fp16 side data",
+                   "decode_splits": h["decode_splits"], "copy_ring": h["copy_ring"],
+                   "quantize_launches": h["quantize_launches"]},
+        "roofline": h["roofline"],
+        "detail": {"headline": h["key"], "step": "quantize K and V of the batch + one decode call",
+                   "configs": {k: {kk: vv for kk, vv in v.items() if kk not in ("workload", "key")}
+                               for k, v in per.items()}},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, ks, vs, q, args.cpu_seqs)
+        res["cpu_baseline"] = cpu_baseline(hcfg, args.cpu_seqs)
     print(json.dumps(res), flush=True)
 
 

@@ -28,7 +28,7 @@ class OrcFormat(ctypes.Structure):
 class OrcCache(ctypes.Structure):
     _fields_ = [("fmt", OrcFormat), ("num_pages", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("codes", ctypes.c_void_p), ("sz", ctypes.c_void_p), ("cnorm", ctypes.c_void_p),
-                ("rope", ctypes.c_void_p)]
+                ("rope", ctypes.c_void_p), ("quot", ctypes.c_void_p)]
 
 
 def lib():
@@ -47,7 +47,7 @@ def lib():
             "orc_hadamard_matrix": (None, [i32, vp]),
             "orc_rotate": (None, [vp, i32, i32, i32, vp]),
             "orc_normalizers": (None, [vp, i32, i32, i32, i32, vp, vp]),
-            "orc_quantize_tile": (ctypes.c_uint32, [vp, i32, vp, vp, vp, vp, vp]),
+            "orc_quantize_tile": (ctypes.c_uint32, [vp, i32, vp, vp, vp, vp, vp, vp]),
             "orc_pack": (None, [vp, vp, vp]),
             "orc_unpack": (None, [vp, vp, vp]),
             "orc_dequant_tile": (None, [vp, vp, vp, vp, vp]),
@@ -118,8 +118,9 @@ def normalizers(xr: np.ndarray, iters: int, center: int = 0):
     return c, r[:n]
 
 
-def quantize_tile(x: np.ndarray, f):
-    """x: [n][D] float64 (n <= T). Returns codes [T][D], sz [T][D/G][2], c16 [D], c [D], flags."""
+def quantize_tile(x: np.ndarray, f, with_quot: bool = False):
+    """x: [n][D] float64 (n <= T). Returns codes [T][D], sz [T][D/G][2], c16 [D], c [D], flags,
+    and with with_quot also quot [T][D]: the code quotient (y - Z) / S before rounding."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     n = x.shape[0]
     T, D, G = f.tile_tokens, f.head_dim, f.group
@@ -127,9 +128,12 @@ def quantize_tile(x: np.ndarray, f):
     sz = np.zeros((T, D // G, 2), np.uint16)
     c16 = np.zeros(D, np.uint16)
     c = np.zeros(D, np.float64)
+    quot = np.zeros((T, D), np.float64) if with_quot else None
     fs = fmt_struct(f)
     flags = lib().orc_quantize_tile(x.ctypes.data if n else None, n, ctypes.byref(fs), codes.ctypes.data,
-                                    sz.ctypes.data, c16.ctypes.data, c.ctypes.data)
+                                    sz.ctypes.data, c16.ctypes.data, c.ctypes.data, _p(quot))
+    if with_quot:
+        return codes, sz, c16, c, int(flags), quot
     return codes, sz, c16, c, int(flags)
 
 
@@ -160,9 +164,11 @@ def dequant_tile(codes, sz, c16, f) -> np.ndarray:
 
 
 class HostCache:
-    """Host-memory paged quantized cache in the library's byte layout."""
+    """Host-memory paged quantized cache in the library's byte layout.  With
+    with_quot, quantize_cache also records every code's quotient (y - Z) / S before
+    rounding, [P][H][T][D] float64 (NaN where S == 0 or the row is not valid)."""
 
-    def __init__(self, f, num_pages: int, num_heads: int):
+    def __init__(self, f, num_pages: int, num_heads: int, with_quot: bool = False):
         self.f = f
         self.num_pages, self.num_heads = num_pages, num_heads
         T, D, G, R = f.tile_tokens, f.head_dim, f.group, f.rope_dim
@@ -170,8 +176,9 @@ class HostCache:
         self.sz = np.zeros((num_pages, num_heads, T, D // G, 2), np.uint16)
         self.cnorm = np.zeros((num_pages, num_heads, D), np.uint16)
         self.rope = np.zeros((num_pages, num_heads, T, R), np.uint16) if R else None
+        self.quot = np.full((num_pages, num_heads, T, D), np.nan) if with_quot else None
         self.struct = OrcCache(fmt_struct(f), num_pages, num_heads, self.codes.ctypes.data, self.sz.ctypes.data,
-                               self.cnorm.ctypes.data, _p(self.rope))
+                               self.cnorm.ctypes.data, _p(self.rope), _p(self.quot))
 
 
 def quantize_cache(cache: HostCache, src: np.ndarray, src_dtype: int, tile_src_token, tile_valid, tile_page,

@@ -6,8 +6,8 @@
  * loops in IEEE double precision; see oracle.h for the sources cited below.
  *
  * Build: g++ -O2 -std=c++17 -ffp-contract=off -fPIC -shared -pthread
- * (-ffp-contract=off keeps every fp32 step of the code decision a separately
- * rounded IEEE operation).
+ * (-ffp-contract=off: every double operation is rounded on its own, as
+ * written; no fused multiply-adds).
  */
 #include "oracle.h"
 
@@ -155,19 +155,23 @@ void normalizers(const double *xr, int n, int D, int iters, int center, double *
         for (int i = 0; i < n; ++i) r[i] = rr[i];
 }
 
-/* Asymmetric round-to-nearest of one value against stored fp16 scale/zero.
- * The decision is taken in fp32, each step one IEEE operation:
- *   code = clamp(rne((f32(y) - f32(Z)) * f32(1/S)), 0, 2^b - 1);  S == 0 -> 0. */
-uint16_t rtn_code(double y, double Sv, double Zv, int levels) {
-    if (Sv == 0.0) return 0;
-    const float yf = (float)y;
-    const float zf = (float)Zv;
-    const float inv = 1.0f / (float)Sv;
-    const float d = yf - zf;
-    const float qf = std::nearbyint(d * inv); /* ties to even */
-    if (!(qf > 0.0f)) return 0;
-    if (qf > (float)levels) return (uint16_t)levels;
-    return (uint16_t)qf;
+/* Asymmetric round-to-nearest of one value against the stored fp16 scale and
+ * zero point ([REVIEW] Key Features: asymmetric round-to-nearest), the plain
+ * definition in fp64: code = clamp(rne((y - Z) / S), 0, 2^b - 1); S == 0 gives
+ * code 0 (a constant group). *quot receives (y - Z) / S before rounding (NaN
+ * for S == 0), the value whose distance from a half-integer says how close the
+ * decision was to a tie. */
+uint16_t rtn_code(double y, double Sv, double Zv, int levels, double *quot) {
+    if (Sv == 0.0) {
+        if (quot) *quot = std::nan("");
+        return 0;
+    }
+    const double qr = (y - Zv) / Sv;
+    if (quot) *quot = qr;
+    const double qn = std::nearbyint(qr); /* default rounding mode: ties to even */
+    if (!(qn > 0.0)) return 0;
+    if (qn > (double)levels) return (uint16_t)levels;
+    return (uint16_t)qn;
 }
 
 int row_bytes_of(const orc_format *f) {
@@ -228,7 +232,7 @@ void orc_normalizers(const double *xr, int32_t n, int32_t D, int32_t iters, int3
 }
 
 uint32_t orc_quantize_tile(const double *x, int32_t n, const orc_format *f, uint16_t *codes, uint16_t *sz,
-                           uint16_t *c16, double *c_exact) {
+                           uint16_t *c16, double *c_exact, double *quot) {
     const int T = f->tile_tokens, D = f->head_dim, G = f->group, ng = D / G;
     const int levels = (1 << f->bits) - 1;
     uint32_t flags = 0;
@@ -254,6 +258,8 @@ uint32_t orc_quantize_tile(const double *x, int32_t n, const orc_format *f, uint
      *    per-token asymmetric quantization) */
     std::memset(codes, 0, sizeof(uint16_t) * (size_t)T * D);
     std::memset(sz, 0, sizeof(uint16_t) * (size_t)T * ng * 2);
+    if (quot)
+        for (size_t i = 0; i < (size_t)T * D; ++i) quot[i] = std::nan("");
     std::vector<double> y(G);
     for (int t = 0; t < n; ++t) {
         for (int g = 0; g < ng; ++g) {
@@ -270,7 +276,10 @@ uint32_t orc_quantize_tile(const double *x, int32_t n, const orc_format *f, uint
             if (!std::isfinite(Sv) || !std::isfinite(Zv)) flags |= ORC_FLAG_SIDE_OVERFLOW;
             sz[((size_t)t * ng + g) * 2 + 0] = S16;
             sz[((size_t)t * ng + g) * 2 + 1] = Z16;
-            for (int k = 0; k < G; ++k) codes[(size_t)t * D + g * G + k] = rtn_code(y[k], Sv, Zv, levels);
+            for (int k = 0; k < G; ++k) {
+                const size_t e = (size_t)t * D + g * G + k;
+                codes[e] = rtn_code(y[k], Sv, Zv, levels, quot ? quot + e : nullptr);
+            }
         }
     }
     return flags;
@@ -340,8 +349,9 @@ uint32_t orc_quantize_cache(const orc_cache *dst, const void *src, int32_t src_d
                 x[(size_t)t * D + j] =
                     load_elem(src, src_dtype, (int64_t)(tile_src_token[tile] + t) * stride_token + head * stride_head + j);
         std::vector<uint16_t> codes((size_t)T * D), sz((size_t)T * (D / f->group) * 2), c16(D);
-        uint32_t fl = orc_quantize_tile(x.data(), n, f, codes.data(), sz.data(), c16.data(), nullptr);
         const size_t blk = (size_t)tile_dst_page[tile] * H + head;
+        double *qt = dst->quot ? dst->quot + blk * (size_t)T * D : nullptr;
+        uint32_t fl = orc_quantize_tile(x.data(), n, f, codes.data(), sz.data(), c16.data(), nullptr, qt);
         orc_pack(codes.data(), f, dst->codes + blk * page_head_code_bytes(f));
         std::memcpy(dst->sz + blk * page_head_sz_elems(f), sz.data(), sizeof(uint16_t) * sz.size());
         std::memcpy(dst->cnorm + blk * D, c16.data(), sizeof(uint16_t) * D);

@@ -7,8 +7,8 @@
  *
  * Everything is plain scalar code in IEEE double precision. Values are rounded
  * only where the method stores them (fp16 normalizers, scales and zero points,
- * integer codes), and the code decision itself is taken in fp32, the precision
- * in which the GPU kernels take it.
+ * integer codes); the code decision is the plain fp64 round-to-nearest-even of
+ * (y - Z) / S.
  *
  * Sources (web pages on the subject; cited by page title and section):
  *   [REVIEW]  "KVarN" project review (open-radar), sections Overview and
@@ -59,7 +59,10 @@ typedef struct {
  *                                      each row a little-endian bitstream
  *   sz     uint16 [P][H][T][D/G][2]    fp16 (scale, zero) per token and group
  *   cnorm  uint16 [P][H][D]            fp16 per-channel normalizer
- *   rope   uint16 [P][T][R]            bf16 copy of the rope channels (R > 0) */
+ *   rope   uint16 [P][H][T][R]         bf16 copy of the rope channels (R > 0)
+ *   quot   double [P][H][T][D]         nullable; written by orc_quantize_cache:
+ *                                      the code quotient (y - Z) / S before
+ *                                      rounding (NaN where S == 0 or t >= n) */
 typedef struct {
     orc_format fmt;
     int32_t num_pages, num_heads;
@@ -67,6 +70,7 @@ typedef struct {
     uint16_t *sz;
     uint16_t *cnorm;
     uint16_t *rope;
+    double *quot;
 } orc_cache;
 
 /* ---- number formats (IEEE-754 binary16, bfloat16) ---- */
@@ -82,10 +86,12 @@ void orc_normalizers(const double *xr, int32_t n, int32_t D, int32_t iters, int3
                      double *c /* [D] */, double *r /* [n] or NULL */);
 /* Quantize one tile of n valid rows (n <= T) of D channels (rope excluded).
  * codes: [T][D] unpacked integer codes (rows >= n zero); sz: [T][D/G][2];
- * c16: [D]; c_exact: [D] fp64 normalizer before rounding (nullable).
- * Returns status bits. */
+ * c16: [D]; c_exact: [D] fp64 normalizer before rounding (nullable);
+ * quot: [T][D] code quotient (y - Z) / S before rounding, NaN where S == 0 or
+ * t >= n (nullable). Returns status bits. */
 uint32_t orc_quantize_tile(const double *x, int32_t n, const orc_format *f,
-                           uint16_t *codes, uint16_t *sz, uint16_t *c16, double *c_exact);
+                           uint16_t *codes, uint16_t *sz, uint16_t *c16, double *c_exact,
+                           double *quot);
 void orc_pack(const uint16_t *codes, const orc_format *f, uint8_t *out);
 void orc_unpack(const uint8_t *in, const orc_format *f, uint16_t *codes);
 /* Dequantize one tile back to the input space: out [T][D]. */

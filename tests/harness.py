@@ -4,8 +4,14 @@ the CPU oracle on the same seeded inputs, and compare element by element.
 Parity bars (derivations in the design notes):
   codes     |gpu - oracle| <= 1 everywhere, and != on at most code_flip_max(bits) of elements:
             1e-4 for the 2/3/4-bit formats; for wider test formats the rate of
-            rounding ties grows with the number of levels, so 1e-4 (2^b - 1) / 15
-  S, Z, c   fp16 bit patterns equal, except 1-ulp differences on at most SIDE_ULP_MAX
+            rounding ties grows with the number of levels, so 1e-4 (2^b - 1) / 15.
+            Every flipped code is explained: either the oracle's fp64 quotient
+            (y - Z) / S lies within tie_margin(bits) of a half-integer and the GPU took
+            the other neighbour (a rounding tie in fp32), or the element's side data
+            (its channel's c, its token's S or Z) differ between the two
+  S, Z, c   fp16 bit patterns equal, except 1-ulp differences on at most SIDE_ULP_MAX;
+            2- or 3-ulp (S, Z) differences only in groups holding a channel whose c
+            differs (side_cascade), also at most SIDE_ULP_MAX
   dequant   per row ||x_gpu - x_orc||_inf <= 1e-3 ||x_orc||_inf  (same stored cache)
   decode    per (seq, head) ||o_gpu - o_orc||_inf <= 2e-3 ||o_orc||_inf (same stored cache)
 """
@@ -25,6 +31,16 @@ def code_flip_max(bits: int) -> float:
     return CODE_FLIP_MAX * max(1.0, (2 ** bits - 1) / 15.0)
 
 SIDE_ULP_MAX = 2e-3
+
+
+def tie_margin(bits: int) -> float:
+    """Largest distance of the oracle's quotient (y - Z) / S from a half-integer at
+    which an fp32 evaluation may still round the other way: y carries fp32 error of a
+    few units of 2^-24 relative to the row's largest value, which the quotient scales
+    by at most (2^b - 1) / (max - min) ~ levels; 2^-13 per level leaves wide margin."""
+    return (2 ** bits) * 2.0 ** -13
+
+
 DEQUANT_RTOL = 1e-3
 DECODE_RTOL = 2e-3
 
@@ -93,12 +109,17 @@ def compare_blocks(gpu: O.HostCache, orc: O.HostCache, pages, heads=None, stats=
     """Compare codes, (S, Z) and c of the given pages; returns accumulated stats.
     An (S, Z) pair more than 1 ulp off counts as a cascade (side_cascade) when its
     group holds a channel whose c16 differs and it is within SIDE_CASCADE_ULP;
-    otherwise as side_bad."""
+    otherwise as side_bad. With the oracle's quotients (orc.quot), each code flip is
+    classed as a tie (flips_tie: quotient within tie_margin of a half-integer, the
+    GPU code its other neighbour), as following a side-data difference (flips_side),
+    or as unexplained (flips_bad)."""
     f = orc.f
     heads = range(orc.num_heads) if heads is None else heads
     st = stats if stats is not None else dict(codes=0, flips=0, maxdiff=0, side=0, side_ulp1=0, side_bad=0,
-                                              side_cascade=0, bits=f.bits)
+                                              side_cascade=0, flips_tie=0, flips_side=0, flips_bad=0,
+                                              tie_dist_max=0.0, bits=f.bits)
     ng = f.head_dim // f.group
+    margin = tie_margin(f.bits)
     for p in pages:
         for h in heads:
             cg = O.unpack(gpu.codes[p, h], f).astype(np.int32)
@@ -117,6 +138,21 @@ def compare_blocks(gpu: O.HostCache, orc: O.HostCache, pages, heads=None, stats=
                 casc = (u > 1) & cascade & (u <= SIDE_CASCADE_ULP)
                 st["side_cascade"] += int(casc.sum())
                 st["side_bad"] += int(((u > 1) & ~casc).sum())
+            if orc.quot is not None and (d != 0).any():
+                # side data an element's code depends on: its channel's c, its token's (S, Z)
+                sz_diff = (us.reshape(-1, ng, 2) != 0).any(axis=2)            # [T][groups]
+                elem_side = (uc[None, :] != 0) | np.repeat(sz_diff, f.group, axis=1)
+                t, j = np.nonzero(d)
+                qv = orc.quot[p, h][t, j]
+                dist = np.abs(qv - np.floor(qv) - 0.5)
+                lo = np.floor(qv).astype(np.int64)
+                at_tie = (dist <= margin) & np.isin(cg[t, j] - lo, [0, 1]) & np.isin(co[t, j] - lo, [0, 1])
+                side = elem_side[t, j]
+                st["flips_side"] += int(side.sum())
+                st["flips_tie"] += int((~side & at_tie).sum())
+                st["flips_bad"] += int((~side & ~at_tie).sum())
+                if (~side & at_tie).any():
+                    st["tie_dist_max"] = max(st["tie_dist_max"], float(dist[~side & at_tie].max()))
             if orc.rope is not None:
                 assert np.array_equal(gpu.rope[p, h], orc.rope[p, h])
     return st
@@ -126,8 +162,10 @@ def assert_block_parity(st, where=""):
     msg = f"{where} {st}"
     assert st["maxdiff"] <= 1, msg
     assert st["flips"] <= code_flip_max(st["bits"]) * st["codes"], msg
+    assert st["flips_bad"] == 0, msg
     assert st["side_bad"] == 0, msg
     assert st["side_ulp1"] <= max(SIDE_ULP_MAX * st["side"], 0), msg
+    assert st["side_cascade"] <= max(SIDE_ULP_MAX * st["side"], 0), msg
 
 
 def gpu_quantize(f: W.Fmt, src: np.ndarray, dtype: str, tile_src_token, tile_valid, tile_page, num_pages: int,
@@ -138,8 +176,9 @@ def gpu_quantize(f: W.Fmt, src: np.ndarray, dtype: str, tile_src_token, tile_val
     return dc
 
 
-def orc_quantize(f: W.Fmt, src: np.ndarray, dtype: str, tile_src_token, tile_valid, tile_page, num_pages: int):
-    hc = O.HostCache(f, num_pages, src.shape[1])
+def orc_quantize(f: W.Fmt, src: np.ndarray, dtype: str, tile_src_token, tile_valid, tile_page, num_pages: int,
+                 with_quot: bool = True):
+    hc = O.HostCache(f, num_pages, src.shape[1], with_quot=with_quot)
     fl = O.quantize_cache(hc, src, ORC_DT[dtype], tile_src_token, tile_valid, tile_page, nthreads=16)
     return hc, fl
 

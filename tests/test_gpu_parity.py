@@ -83,7 +83,9 @@ SMALL = [
     (512, 128, 4, 512, 512, 2, "bf16", 0, 0),
     (512, 128, 2, 512, 512, 0, "bf16", 0, 64),
     (512, 16, 3, 128, 512, 2, "bf16", 0, 64),
+    (512, 64, 4, 128, 512, 4, "bf16", 0, 64),     # MLA alternative: G 128, T 64, rope 64
     (128, 128, 4, 128, 1, 4, "bf16", 0, 0),
+    (128, 64, 8, 128, 128, 4, "bf16", 1, 0),      # 8-bit codes
 ]
 
 
@@ -447,6 +449,11 @@ DEC_SMALL = [
     dict(G=32, lens=(100, 33)),
     dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(700, 128, 1), iters=4),
     dict(mla=True, D=512, R=64, T=128, Hq=128, Hkv=1, lens=(300,), iters=4),
+    # 8-bit codes (test width) on the general decode kernel
+    dict(T=32, lens=(250, 33, 31), kbits=8, vbits=8, iters=3),
+    dict(T=128, lens=(300, 5), kbits=8, vbits=4, iters=4, Hq=16, Hkv=2),
+    # the MLA alternative format: 128-channel scale groups, 64-token tiles, rope 64
+    dict(mla=True, D=512, R=64, T=64, G=128, Hq=16, Hkv=1, lens=(300, 64, 1), iters=4),
 ]
 
 
@@ -551,7 +558,9 @@ def test_decode_closed_forms(gpu):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(T=128, lens=(300, 5), kbits=4, vbits=2, iters=4),
-                                dict(mla=True, D=512, R=64, T=128, Hkv=1, Hq=4, lens=(260,), iters=4)])
+                                dict(mla=True, D=512, R=64, T=128, Hkv=1, Hq=4, lens=(260,), iters=4),
+                                dict(mla=True, D=512, R=64, T=64, G=128, Hkv=1, Hq=4, lens=(150,), iters=4),
+                                dict(T=32, lens=(100, 7), kbits=8, vbits=8, iters=3)])
 def test_dequantize_same_cache(gpu, kw):
     w = small_paged(21, **kw)
     for f, srcs in ((w["fk"], w["ks"]), (w["fv"], w["vs"])):
@@ -569,17 +578,29 @@ def test_dequantize_same_cache(gpu, kw):
 
 # ----------------------------------------------------------------------------- full-size workloads, sampled
 def full_gpu_caches(cfg, gpu):
-    """Quantize the whole workload on the GPU exactly as bench.py does."""
-    ks = W.gen_k(cfg)
-    dk = gpu_quantize(cfg.fk, ks, cfg.src_dtype, cfg.tile_src_token, cfg.tile_valid, cfg.tile_page, cfg.num_pages)
-    del ks
-    dv = None
+    """Quantize the whole workload on the GPU exactly as bench.py does: K and V in one
+    kv_quantize_kv launch where the library takes the pair of formats, else one
+    kv_quantize per cache. Returns the caches and whether the pair launch ran."""
+    ks = to_dev(W.gen_k(cfg), cfg.src_dtype)
+    dk = K.DeviceCache(kfmt(cfg.fk), cfg.num_pages, cfg.num_kv_heads)
+    tst, tv, tp = i32(cfg.tile_src_token), i32(cfg.tile_valid), i32(cfg.tile_page)
+    dv, pair = None, False
     if cfg.fv is not None:
-        vs = W.gen_v(cfg)
-        dv = gpu_quantize(cfg.fv, vs, cfg.src_dtype, cfg.tile_src_token, cfg.tile_valid, cfg.tile_page, cfg.num_pages)
+        vs = to_dev(W.gen_v(cfg), cfg.src_dtype)
+        dv = K.DeviceCache(kfmt(cfg.fv), cfg.num_pages, cfg.num_kv_heads)
+        try:
+            K.kv_quantize_kv(dk, dv, ks, vs, tst, tv, tp)
+            pair = True
+        except K.KvqError as e:
+            assert e.status == K.KVQ_EUNSUPPORTED
+            K.kv_quantize(dk, ks, tst, tv, tp)
+            K.kv_quantize(dv, vs, tst, tv, tp)
         del vs
+    else:
+        K.kv_quantize(dk, ks, tst, tv, tp)
     torch.cuda.synchronize()
-    return dk, dv
+    del ks
+    return dk, dv, pair
 
 
 def tile_sample(cfg, n, seed):
@@ -593,14 +614,21 @@ def tile_sample(cfg, n, seed):
     return tiles, heads
 
 
-def oracle_tile(cfg, f, tile, head, which):
+def oracle_tiles(cfg, f, tiles, heads, which):
+    """The oracle's blocks (with code quotients) of the sampled (tile, head) pairs,
+    page i of the returned one-head cache holding pair i."""
     T = f.tile_tokens
-    t0 = int(cfg.tile_src_token[tile])
-    n = int(cfg.tile_valid[tile])
-    x = (W.gen_k if which == "k" else W.gen_v)(cfg, t0, t0 + T if t0 + T <= cfg.total_tokens else cfg.total_tokens)
-    x = np.ascontiguousarray(x[:, head:head + 1])
-    hc = O.HostCache(f, 1, 1)
-    O.quantize_cache(hc, x, ORC_DT[cfg.src_dtype], [0], [n], [0], nthreads=1)
+    gen = W.gen_k if which == "k" else W.gen_v
+    rows, tst, tv = [], [], []
+    for tile, head in zip(tiles, heads):
+        t0, n = int(cfg.tile_src_token[tile]), int(cfg.tile_valid[tile])
+        x = gen(cfg, t0, min(t0 + T, cfg.total_tokens))[:, head:head + 1]
+        tst.append(sum(len(r) for r in rows))
+        tv.append(n)
+        rows.append(x)
+    src = np.ascontiguousarray(np.concatenate(rows, axis=0))
+    hc = O.HostCache(f, len(tiles), 1, with_quot=True)
+    O.quantize_cache(hc, src, ORC_DT[cfg.src_dtype], tst, tv, np.arange(len(tiles)), nthreads=16)
     return hc
 
 
@@ -608,23 +636,23 @@ def oracle_tile(cfg, f, tile, head, which):
 def test_full_workload_sampled(gpu, ci):
     cfg = W.config(ci)
     log("full workload", ci, cfg.name)
-    dk, dv = full_gpu_caches(cfg, gpu)
+    dk, dv, pair = full_gpu_caches(cfg, gpu)
+    log("  quantized", "K and V in one launch" if pair else "one launch per cache")
     # ---- quantizer: sampled tiles, every element of each
-    tiles, heads = tile_sample(cfg, 24, ci)
+    tiles, heads = tile_sample(cfg, 96, ci)
+    pages = torch.from_numpy(cfg.tile_page[tiles].astype(np.int64)).to(gpu)
+    hidx = torch.from_numpy(heads.astype(np.int64)).to(gpu)
     for which, f, dc in (("k", cfg.fk, dk), ("v", cfg.fv, dv)):
         if f is None:
             continue
-        st = None
-        for tile, head in zip(tiles, heads):
-            orc = oracle_tile(cfg, f, tile, head, which)
-            page = int(cfg.tile_page[tile])
-            g = O.HostCache(f, 1, 1)
-            g.codes[0, 0] = dc.codes[page, head].cpu().numpy()
-            g.sz[0, 0] = dc.sz[page, head].cpu().numpy().view(np.uint16)
-            g.cnorm[0, 0] = dc.cnorm[page, head].cpu().numpy().view(np.uint16)
-            if g.rope is not None:
-                g.rope[0, 0] = dc.rope[page, head].cpu().numpy().view(np.uint16)
-            st = compare_blocks(g, orc, [0], stats=st)
+        orc = oracle_tiles(cfg, f, tiles, heads, which)
+        g = O.HostCache(f, len(tiles), 1)
+        g.codes[:, 0] = dc.codes[pages, hidx].cpu().numpy()
+        g.sz[:, 0] = dc.sz[pages, hidx].cpu().numpy().view(np.uint16)
+        g.cnorm[:, 0] = dc.cnorm[pages, hidx].cpu().numpy().view(np.uint16)
+        if g.rope is not None:
+            g.rope[:, 0] = dc.rope[pages, hidx].cpu().numpy().view(np.uint16)
+        st = compare_blocks(g, orc, range(len(tiles)))
         log("  quantize", which, st)
         assert_block_parity(st, f"config {ci} {which}")
 

@@ -3,7 +3,7 @@ import numpy as np
 
 import oracle as O
 import workloads as W
-from harness import SIDE_CASCADE_ULP, compare_blocks
+from harness import SIDE_CASCADE_ULP, compare_blocks, tie_margin
 
 
 def pair(seed=0):
@@ -52,3 +52,46 @@ def test_normalizer_differences_are_never_cascades():
     a.cnorm[0, 0, 5] += 2
     st = compare_blocks(a, b, [0])
     assert st["side_bad"] == 1 and st["side_cascade"] == 0
+
+
+def with_quot(a, b, seed=1):
+    """b (the oracle side) gets quotients consistent with its codes: code + u, |u| < 0.4."""
+    f = b.f
+    rng = np.random.default_rng(seed)
+    b.quot = O.unpack(b.codes[0, 0], f).astype(np.float64)[None, None] + rng.uniform(-0.4, 0.4, (1, 1, 16, 64))
+    return a, b
+
+
+def set_code(c: O.HostCache, t, j, v):
+    codes = O.unpack(c.codes[0, 0], c.f)
+    codes[t, j] = v
+    c.codes[0, 0] = O.pack(codes, c.f)
+
+
+def test_flip_at_a_tie_is_explained():
+    a, b = with_quot(*pair())
+    co = int(O.unpack(b.codes[0, 0], b.f)[4, 9])
+    up = co + 1 if co < 15 else co - 1
+    b.quot[0, 0, 4, 9] = (co + up) / 2 + 0.3 * tie_margin(4) * (1 if up > co else -1)
+    set_code(a, 4, 9, up)
+    st = compare_blocks(a, b, [0])
+    assert st["flips"] == 1 and st["flips_tie"] == 1 and st["flips_bad"] == 0
+
+
+def test_flip_far_from_a_tie_is_unexplained():
+    a, b = with_quot(*pair())
+    co = int(O.unpack(b.codes[0, 0], b.f)[4, 9])
+    b.quot[0, 0, 4, 9] = co + 0.1
+    set_code(a, 4, 9, co + 1 if co < 15 else co - 1)
+    st = compare_blocks(a, b, [0])
+    assert st["flips_bad"] == 1 and st["flips_tie"] == 0
+
+
+def test_flip_after_a_side_difference_is_explained_by_it():
+    a, b = with_quot(*pair())
+    co = int(O.unpack(b.codes[0, 0], b.f)[6, 40])
+    b.quot[0, 0, 6, 40] = co + 0.1
+    set_code(a, 6, 40, co + 1 if co < 15 else co - 1)
+    a.sz[0, 0, 6, 1, 0] += 1              # S of token 6, group 1 (channels 32..63)
+    st = compare_blocks(a, b, [0])
+    assert st["flips_side"] == 1 and st["flips_bad"] == 0 and st["side_ulp1"] == 1

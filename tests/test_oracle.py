@@ -4,6 +4,7 @@ library routines, hand-computed values, brute force).  CPU only.
 Each test names the part of the oracle it pins.  The web pages print no worked
 numeric example for this method, so no test compares to printed values.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -147,17 +148,30 @@ def test_normalizers_zero_rows_and_columns_keep_factor_one():
 
 # ---------------------------------------------------------------- round-to-nearest
 def _rtn_reference(y, bits):
-    """Plain per-row asymmetric min-max RTN with fp16 scale/zero (numpy rounding)."""
+    """Plain per-row asymmetric min-max RTN with fp16 scale/zero: numpy's fp16
+    rounding of S and Z, then the code rint((y - Z) / S) in float64 (numpy's rint
+    rounds half to even), clipped to the code range."""
     levels = 2 ** bits - 1
+    y = np.asarray(y, np.float64)
     mn, mx = y.min(axis=1), y.max(axis=1)
     S = ((mx - mn) / levels).astype(np.float16)
     Z = mn.astype(np.float16)
-    Sf, Zf = S.astype(np.float32), Z.astype(np.float32)
-    with np.errstate(divide="ignore"):
-        inv = np.float32(1) / Sf
-    q = np.rint((y.astype(np.float32) - Zf[:, None]) * inv[:, None])
-    q = np.where(Sf[:, None] == 0, 0, np.clip(q, 0, levels))
+    Sd, Zd = S.astype(np.float64), Z.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint((y - Zd[:, None]) / Sd[:, None])
+    q = np.where(Sd[:, None] == 0, 0, np.clip(q, 0, levels))
     return q.astype(np.uint16), S.view(np.uint16), Z.view(np.uint16)
+
+
+def test_code_decision_ties_go_to_even():
+    """Values whose quotient (y - Z) / S lies exactly on a half-integer take the even
+    neighbour (round half to even); S = 1, Z = 0 here, so the quotient is y itself."""
+    f = fmt(D=16, T=1, h=1, bits=4, iters=0)
+    row = np.array([0.0, 15.0, 0.5, 1.5, 2.5, 3.5, 4.5, 14.5, 7.25, 7.75, 0.25, 13.5, 6.0, 8.5, 9.5, 10.5])
+    codes, sz, c16, _, _, quot = O.quantize_tile(row[None, :], f, with_quot=True)
+    assert O.halves(sz[0, 0]).tolist() == [1.0, 0.0]
+    assert np.array_equal(quot[0], row)
+    assert codes[0].tolist() == [0, 15, 0, 2, 2, 4, 4, 14, 7, 8, 0, 14, 6, 8, 10, 10]
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
@@ -289,6 +303,79 @@ def test_nonfinite_input_is_flagged():
     x = rng(7).standard_normal((8, 64))
     x[2, 3] = np.inf
     assert O.quantize_tile(x, f)[4] & O.FLAG_NONFINITE
+
+
+# ---------------------------------------------------------------- cache-level drivers
+def _bf16_round(x):
+    """float -> bf16 bit patterns through torch's conversion (round to nearest even)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+@pytest.mark.parametrize("layout,R", [(O.TOKEN_MAJOR, 0), (O.CHANNEL_MAJOR, 0), (O.TOKEN_MAJOR, 16)])
+def test_quantize_cache_gathers_strided_tiles_into_their_pages(layout, R):
+    """orc_quantize_cache over a source with padded strides (token stride > H * width,
+    head stride > width, the padding filled with huge values) and a permuted page
+    map: each (page, head) block equals the tile quantizer applied to exactly that
+    tile's rows of that head, packed; the rope channels equal bf16 of the source;
+    rows past the valid count and pages no tile names stay zero."""
+    D, T, H = 64, 16, 3
+    f = fmt(D=D, T=T, bits=3, iters=2, layout=layout, R=R)
+    g = rng(11 + layout + R)
+    lens = [T + 5, 2 * T, 1]
+    tiles = [(0, T), (T, 5), (T + 5, T), (2 * T + 5, T), (3 * T + 5, 1)]
+    tokens = sum(lens)
+    W = D + R
+    st_h, st_t = W + 8, (H + 1) * (W + 8)       # elements
+    buf = np.full(tokens * st_t, 1e30, np.float32)
+    x = k_like(tokens * H, W, 12).reshape(tokens, H, W).astype(np.float32)
+    for t in range(tokens):
+        for h in range(H):
+            buf[t * st_t + h * st_h: t * st_t + h * st_h + W] = x[t, h]
+    P = len(tiles) + 2
+    perm = g.permutation(P)[: len(tiles)].astype(np.int32)
+    tst = np.array([a for a, _ in tiles], np.int32)
+    tv = np.array([n for _, n in tiles], np.int32)
+    hc = O.HostCache(f, P, H)
+    fl = O.lib().orc_quantize_cache(ctypes.byref(hc.struct), buf.ctypes.data, O.F32, st_t, st_h, len(tiles),
+                                    tst.ctypes.data, tv.ctypes.data, perm.ctypes.data, 4)
+    assert fl == 0
+    for i, (t0, n) in enumerate(tiles):
+        for h in range(H):
+            codes, sz, c16, _, _ = O.quantize_tile(x[t0:t0 + n, h, :D].astype(np.float64), f)
+            p = perm[i]
+            assert np.array_equal(hc.codes[p, h], O.pack(codes, f))
+            assert np.array_equal(hc.sz[p, h], sz) and np.array_equal(hc.cnorm[p, h], c16)
+            if R:
+                assert np.array_equal(hc.rope[p, h, :n], _bf16_round(x[t0:t0 + n, h, D:]))
+                assert np.all(hc.rope[p, h, n:] == 0)
+    unused = sorted(set(range(P)) - set(perm.tolist()))
+    assert unused and all(not hc.codes[p].any() and not hc.sz[p].any() and not hc.cnorm[p].any() for p in unused)
+
+
+def test_dequantize_cache_matches_tile_dequantizer_and_rope():
+    """orc_dequantize_cache: each tile's rows are dequant_tile of the block it names
+    (unpacked codes, its (S, Z) and c), the rope channels are the stored bf16 values,
+    rows past the valid count are zero."""
+    D, R, T, H = 64, 8, 16, 2
+    f = fmt(D=D, T=T, bits=4, iters=1, R=R)
+    g = rng(13)
+    P = 4
+    hc = O.HostCache(f, P, H)
+    hc.codes[...] = g.integers(0, 256, hc.codes.shape, dtype=np.uint8)
+    hc.sz[...] = np.float16(g.standard_normal(hc.sz.shape) * 0.1).view(np.uint16)
+    hc.cnorm[...] = np.float16(np.exp(g.standard_normal(hc.cnorm.shape))).view(np.uint16)
+    hc.rope[...] = _bf16_round(g.standard_normal(hc.rope.shape))
+    tp = np.array([2, 0, 3], np.int32)
+    tv = np.array([T, 7, 1], np.int32)
+    out = O.dequantize_cache(hc, tp, tv)
+    for i, p in enumerate(tp):
+        for h in range(H):
+            ref = O.dequant_tile(O.unpack(hc.codes[p, h], f), hc.sz[p, h], hc.cnorm[p, h], f)
+            n = tv[i]
+            assert np.array_equal(out[i, h, :n, :D], ref[:n])
+            assert np.array_equal(out[i, h, :n, D:], bf16_to_f64(hc.rope[p, h, :n]))
+            assert np.all(out[i, h, n:] == 0)
 
 
 # ---------------------------------------------------------------- packing
