@@ -32,8 +32,10 @@
  *    scale, zero point or normalizer) set bits in *status_flags; they never
  *    abort a launch. The codes of a block with such a condition are
  *    unspecified but stay in 0 .. 2^bits - 1.
- *  - The library allocates no device memory and keeps no mutable global state;
- *    calls on different streams may run concurrently.
+ *  - The library allocates no device memory and keeps no mutable global state
+ *    (the one exception: kv_decode_attn_noalloc's per-device scratch array and its
+ *    address table); calls on different streams may run concurrently, except
+ *    kv_decode_attn_noalloc calls on one GPU.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -185,6 +187,28 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
                           int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
                           float sm_scale, int32_t num_splits, void *workspace, size_t workspace_bytes,
                           float *out, hipStream_t stream);
+
+/* Size of kv_decode_attn_noalloc's scratch array (bytes, per GPU). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kv_decode_attn for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * result, kernels and split rule, with the split-K partials in a scratch array
+ * that the library holds in every GPU's memory (KVQ_NOALLOC_SCRATCH_BYTES, held
+ * until the process ends) instead of a caller workspace. The call allocates
+ * nothing; the caller still passes q, the caches, the tables and out.
+ * The first call on a device looks up that device's copy of the array (with the
+ * device current); later calls reuse the address. The array keeps the last call's
+ * partials: calls on one GPU that overlap in time (different streams, or host
+ * threads) race on it and must be ordered by the caller.
+ * Errors: as kv_decode_attn; KVQ_EWORKSPACE when the partials,
+ * kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, Dv, splits), exceed
+ * KVQ_NOALLOC_SCRATCH_BYTES (nothing is launched); KVQ_ELAUNCH when the runtime
+ * does not give the array's device address. */
+kvq_status kv_decode_attn_noalloc(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                  const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
+                                  int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
+                                  float sm_scale, int32_t num_splits, float *out, hipStream_t stream);
 
 /* Append one new token per sequence to a paged quantized cache, keeping every
  * token in it: the token's row goes into the sequence's partial last tile and

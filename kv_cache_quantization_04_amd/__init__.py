@@ -40,7 +40,7 @@ KVQ_TOKEN_MAJOR, KVQ_CHANNEL_MAJOR = 0, 1
 KVQ_FLAG_NONFINITE, KVQ_FLAG_SIDE_OVERFLOW = 1, 2
 
 EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_quantize_kv", "kv_dequantize",
-           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_append", "kv_append_workspace_bytes", "kv_prefill_attn",
+           "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_decode_attn_noalloc", "kv_append", "kv_append_workspace_bytes", "kv_prefill_attn",
            "kv_prefill_attn_workspace_bytes", "kv_prefill_attn_default_splits",
            "kv_quantize_kernel_name", "kv_decode_attn_kernel_name", "kv_prefill_attn_kernel_name", "kvq_status_str")
 
@@ -71,6 +71,8 @@ _sig = {
     "kv_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "kv_decode_attn": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _vp, _i32,
                               _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
+    "kv_decode_attn_noalloc": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache),
+                                      _vp, _i32, _vp, _i32, ctypes.c_float, _i32, _vp, _vp]),
     "kv_append": (_i32, [ctypes.POINTER(kvq_cache), _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _sz, _vp,
                          _vp]),
     "kv_append_workspace_bytes": (_sz, [_i32]),
@@ -300,4 +302,23 @@ def kv_decode_attn(q, k: DeviceCache, v: Optional[DeviceCache], block_table, seq
                                block_table.shape[1], _ptr(seq_lens), max_seq_len, sm_scale, num_splits,
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
                                _stream(stream)), "kv_decode_attn")
+    return out
+
+
+KVQ_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def kv_decode_attn_noalloc(q, k: DeviceCache, v: Optional[DeviceCache], block_table, seq_lens, max_seq_len: int,
+                           sm_scale: float, num_splits: int = 0, out=None, stream=None):
+    """kv_decode_attn with the split partials in the library's per-GPU scratch array
+    (the C call allocates nothing; `out` is allocated here when not given)."""
+    torch = _torch()
+    B, Hq = q.shape[0], q.shape[1]
+    dv = (v or k).fmt.head_dim
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=torch.float32, device=q.device)
+    _check(_lib.kv_decode_attn_noalloc(_ptr(q), _dtype_code(q), B, Hq, ctypes.byref(k.struct),
+                                       ctypes.byref(v.struct) if v is not None else None, _ptr(block_table),
+                                       block_table.shape[1], _ptr(seq_lens), max_seq_len, sm_scale, num_splits,
+                                       _ptr(out), _stream(stream)), "kv_decode_attn_noalloc")
     return out

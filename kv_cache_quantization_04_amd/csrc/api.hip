@@ -1,6 +1,7 @@
 // C ABI of libkvq.so: host-side validation and launch.
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -106,6 +107,49 @@ kvq::QuantArgs quant_args(const kvq_cache *dst, const void *src, kvq_dtype src_d
                           dst->codes, dst->sz, dst->cnorm, dst->rope, dst->num_heads, f.hadamard_n, f.group, f.bits,
                           f.iters, f.layout, f.rope_dim, dst->num_pages, status_flags, f.center};
 }
+
+// Split-K partials of kv_decode_attn_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends. In host code `scratch`
+// names a host-side stand-in, never the device memory: the per-device address comes
+// from hipGetSymbolAddress (taken once per device, with that device current) and only
+// that address is passed to kernels. No kernel reads a partial it has not written, so
+// nothing in it needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// Device address of `scratch` on the device `stream` belongs to (the current device
+// for the null stream), or nullptr when the runtime does not give it.
+void *scratch_for(hipStream_t stream) {
+    int dev = -1, cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    dev = cur;
+    if (stream != nullptr) {
+        hipDevice_t sd;
+        if (hipStreamGetDevice(stream, &sd) != hipSuccess) return nullptr;
+        dev = (int)sd;
+    }
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev]) return scratch_ptr[dev];
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+    return ptr;
+}
+
+// kv_decode_attn after its workspace is known (nullptr with `have_ws` false: the
+// noalloc scratch, resolved after every host-side check has passed)
+kvq_status decode_attn_impl(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                            const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
+                            int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                            int32_t num_splits, void *workspace, size_t workspace_bytes, bool have_ws, float *out,
+                            hipStream_t stream);
 
 }  // namespace
 
@@ -265,31 +309,16 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
                           const kvq_cache *v, const int32_t *block_table, int32_t block_table_stride,
                           const int32_t *seq_lens, int32_t max_seq_len, float sm_scale, int32_t num_splits,
                           void *workspace, size_t workspace_bytes, float *out, hipStream_t stream) {
-    kvq_status st = check_cache(k);
-    if (st != KVQ_OK) return st;
-    if (v && (st = check_cache(v)) != KVQ_OK) return st;
-    if (!q || !valid_dtype(q_dtype) || num_seqs < 0 || num_q_heads <= 0 || !out || max_seq_len < 0) return KVQ_EINVAL;
-    if (num_seqs == 0) return KVQ_OK;
-    if (!block_table || !seq_lens || block_table_stride <= 0 || num_splits < 0) return KVQ_EINVAL;
-    kvq::DecodeArgs a{};
-    if ((st = decode_layout(k, v, num_q_heads, a)) != KVQ_OK) return st;
-    if ((int64_t)block_table_stride * a.T < max_seq_len) return KVQ_EINVAL;
-    a.B = num_seqs;
-    const int splits = num_splits > 0 ? num_splits : kvq::decode_default_splits(a, max_seq_len);
-    if (!workspace || workspace_bytes < kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, a.Dv, splits))
-        return KVQ_EWORKSPACE;
-    a.q = q;
-    a.q_dtype = (int)q_dtype;
-    a.bt = block_table;
-    a.bt_stride = block_table_stride;
-    a.seq_lens = seq_lens;
-    a.sm = sm_scale;
-    a.splits = splits;
-    a.ws = (float *)workspace;
-    a.out = out;
-    a.max_len = max_seq_len;
-    if (!kvq::launch_decode(a, stream)) return KVQ_EUNSUPPORTED;
-    return launched();
+    return decode_attn_impl(q, q_dtype, num_seqs, num_q_heads, k, v, block_table, block_table_stride, seq_lens,
+                            max_seq_len, sm_scale, num_splits, workspace, workspace_bytes, true, out, stream);
+}
+
+kvq_status kv_decode_attn_noalloc(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                  const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
+                                  int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
+                                  float sm_scale, int32_t num_splits, float *out, hipStream_t stream) {
+    return decode_attn_impl(q, q_dtype, num_seqs, num_q_heads, k, v, block_table, block_table_stride, seq_lens,
+                            max_seq_len, sm_scale, num_splits, nullptr, KVQ_NOALLOC_SCRATCH_BYTES, false, out, stream);
 }
 
 size_t kv_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t chunk_len, int32_t num_q_heads, int32_t head_dim_v,
@@ -366,3 +395,43 @@ kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, i
 }
 
 }  // extern "C"
+
+namespace {
+
+kvq_status decode_attn_impl(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                            const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
+                            int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                            int32_t num_splits, void *workspace, size_t workspace_bytes, bool have_ws, float *out,
+                            hipStream_t stream) {
+    kvq_status st = check_cache(k);
+    if (st != KVQ_OK) return st;
+    if (v && (st = check_cache(v)) != KVQ_OK) return st;
+    if (!q || !valid_dtype(q_dtype) || num_seqs < 0 || num_q_heads <= 0 || !out || max_seq_len < 0) return KVQ_EINVAL;
+    if (num_seqs == 0) return KVQ_OK;
+    if (!block_table || !seq_lens || block_table_stride <= 0 || num_splits < 0) return KVQ_EINVAL;
+    kvq::DecodeArgs a{};
+    if ((st = decode_layout(k, v, num_q_heads, a)) != KVQ_OK) return st;
+    if ((int64_t)block_table_stride * a.T < max_seq_len) return KVQ_EINVAL;
+    a.B = num_seqs;
+    const int splits = num_splits > 0 ? num_splits : kvq::decode_default_splits(a, max_seq_len);
+    if (workspace_bytes < kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, a.Dv, splits)) return KVQ_EWORKSPACE;
+    if (have_ws) {
+        if (!workspace) return KVQ_EWORKSPACE;
+    } else if (!(workspace = scratch_for(stream))) {
+        return KVQ_ELAUNCH;
+    }
+    a.q = q;
+    a.q_dtype = (int)q_dtype;
+    a.bt = block_table;
+    a.bt_stride = block_table_stride;
+    a.seq_lens = seq_lens;
+    a.sm = sm_scale;
+    a.splits = splits;
+    a.ws = (float *)workspace;
+    a.out = out;
+    a.max_len = max_seq_len;
+    if (!kvq::launch_decode(a, stream)) return KVQ_EUNSUPPORTED;
+    return launched();
+}
+
+}  // namespace
