@@ -83,7 +83,8 @@ def decode_bytes(cfg, seqs=None):
 CSRC = os.path.join(ROOT, "kv_cache_quantization_04_amd", "csrc")
 KERNEL_FILE = {"quantize_d128_kernel": "quantize_d128.hip", "quantize_t16_kernel": "quantize_t16.hip",
                "quantize_d512_kernel": "quantize_d512.hip", "quantize_kernel": "quantize.hip",
-               "decode_mfma_kernel": "decode_mfma.hip", "decode_mla_kernel": "decode_mla.hip",
+               "decode_mfma_kernel": "decode_mfma.hip", "decode_pair16_kernel": "decode_pair16.hip",
+               "decode_mla_kernel": "decode_mla.hip",
                "decode_generic_kernel": "decode.hip"}
 
 

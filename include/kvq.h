@@ -253,7 +253,9 @@ const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_d
 
 /* Name of the main GPU kernel kv_decode_attn runs for this query pointer and
  * these caches (the split-merge pass, "decode_reduce_kernel", follows it):
- * "decode_mla_kernel", "decode_mfma_kernel" or "decode_generic_kernel". NULL
+ * "decode_mla_kernel", "decode_pair16_kernel" (16-token pages, at most 8 query
+ * heads per kv head: two pages per matrix-core pass), "decode_mfma_kernel" or
+ * "decode_generic_kernel". NULL
  * for invalid arguments. The string is static. For profilers and benchmarks. */
 const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v,
                                        int32_t num_q_heads);
@@ -265,8 +267,8 @@ const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const 
  * no token left gives zeros, the result of an empty decode). The result per
  * (b, i) is kv_decode_attn's for that query over that prefix, with the same fold
  * (scores and values from the codes, normalizers folded into the query and the
- * output). Formats that kv_decode_attn runs on "decode_mfma_kernel" run that
- * kernel in its chunk mode (the MFMA columns hold (position, head) pairs, so one
+ * output). Formats that kv_decode_attn runs on "decode_mfma_kernel" or
+ * "decode_pair16_kernel" run decode_mfma_kernel in its chunk mode (the MFMA columns hold (position, head) pairs, so one
  * page read serves 16 / (num_q_heads / H) positions); other formats run the
  * chunk positions as chunk_len virtual sequences sharing b's block-table row.
  *   q (device): [num_seqs][chunk_len][num_q_heads][D + R] in q_dtype.

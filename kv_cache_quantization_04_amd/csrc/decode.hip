@@ -355,6 +355,7 @@ static void launch_reduce(const DecodeArgs &a, hipStream_t stream) {
 }
 
 bool decode_mfma_supported(const DecodeArgs &a);
+bool decode_pair16_supported(const DecodeArgs &a);
 bool launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 bool decode_mla_supported(const DecodeArgs &a);
 int decode_mla_head_groups(const DecodeArgs &a);
@@ -410,6 +411,7 @@ int decode_chunk_splits(const DecodeArgs &a, int max_seq_len) {
 
 const char *decode_kernel_name(const DecodeArgs &a) {
     if (decode_mla_supported(a)) return "decode_mla_kernel";
+    if (decode_pair16_supported(a)) return "decode_pair16_kernel";
     if (decode_mfma_supported(a)) return "decode_mfma_kernel";
     return "decode_generic_kernel";
 }

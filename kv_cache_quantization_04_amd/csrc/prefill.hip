@@ -76,6 +76,10 @@ int prefill_default_splits(const DecodeArgs &d, int Lq, int max_seq_len) {
     return decode_chunk_splits(a, max_seq_len);
 }
 
-const char *prefill_kernel_name(const DecodeArgs &d) { return decode_kernel_name(d); }
+// the chunk mode runs decode_mfma_kernel for every format it takes (also those whose
+// decode takes two pages per pass); other formats run their decode kernel
+const char *prefill_kernel_name(const DecodeArgs &d) {
+    return decode_mfma_supported(d) ? "decode_mfma_kernel" : decode_kernel_name(d);
+}
 
 }  // namespace kvq

@@ -2,22 +2,23 @@
 // scale group per token), gfx950: one wave per (tile, head), no workgroup
 // barriers. Same method and results as the other quantizer kernels.
 //
-// Lane l of a wave loads the 8 consecutive channels 8 (l & 15) .. + 7 of the four
-// rows 4 (l >> 4) .. + 3. The 16 lanes of a DPP row cover one token's 128
-// channels: Hadamard butterflies on channel bits 3..6 (after which the lane holds
-// rotated channel group hperm16(l & 15)) and all per-token reductions are row
-// operations. Column sums finish inside the wave (permlane
-// swaps across the four row groups) and come back to the lanes through a small
-// per-wave LDS array. Codes go to a per-wave LDS byte image in bitstream order
-// (token-major t * 128 + j, channel-major j * 16 + t); each lane then packs 32
-// consecutive codes into the little-endian bitstream, and the block leaves with
-// one store per lane. The next tile is loaded into registers meanwhile.
+// The 128-point rotation runs on the matrix cores (mfma_hadamard.h): lane l loads
+// the bf16 source of token l & 15, channels 32 s + 8 (l >> 4) .. + 7 for s = 0..3,
+// as the A operand, and receives the rotated rows 4 (l >> 4) .. + 3 at channels
+// 16 j + (l & 15), j = 0..7. The 16 lanes of a DPP row thus cover one token's 128
+// channels, and all per-token reductions are row operations. Column sums finish
+// inside the wave (permlane swaps across the four row groups) and come back to the
+// lanes through a small per-wave LDS array. Codes go to a per-wave LDS byte image in
+// bitstream order (token-major t * 128 + j, channel-major j * 16 + t); each lane then
+// packs 32 consecutive codes into the little-endian bitstream, and the block leaves
+// with one store per lane. The next tile is loaded into registers meanwhile.
 //
 // Method: "KVarN" project review, Key Features ("Variance-Normalized
 // Quantization Pipeline"): rotate, run row/column RMS normalization rounds,
 // asymmetric round-to-nearest with fp16 scale, zero point and normalizer.
 #include "common.h"
 #include "launch.h"
+#include "mfma_hadamard.h"
 #include "xlane.h"
 
 namespace kvq {
@@ -29,21 +30,20 @@ constexpr int ZT = 16;    // tokens per tile
 constexpr int ZNT = 256;  // 4 waves, one tile each
 
 struct Rows {
-    uint4 v[4];  // four rows x 8 bf16 channels
+    uint4 v[4];  // token lane & 15: 8 bf16 channels 32 s + 8 (lane >> 4) .. + 7 for s = 0..3
 };
 
-// The lane's 4 rows x 8 channels of an item (rows >= nv read as zero).
+// The lane's A operands of an item (a token row >= nv reads as zero).
 __device__ __forceinline__ Rows load_rows(const QuantArgs &a, int item, int lane) {
     Rows r;
     const int tl = item / a.H, hd = item % a.H;
     const int nv = load_const(a.tile_valid, tl);
+    const int row = lane & 15;
     const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src) + hd * a.stride_head +
-                          (int64_t)load_const(a.tile_src_token, tl) * a.stride_token + 8 * (lane & 15);
+                          ((int64_t)load_const(a.tile_src_token, tl) + row) * a.stride_token + 8 * (lane >> 4);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int row = 4 * (lane >> 4) + k;
-        r.v[k] = row < nv ? *reinterpret_cast<const uint4 *>(src + (int64_t)row * a.stride_token) : uint4{0, 0, 0, 0};
-    }
+    for (int s = 0; s < 4; ++s)
+        r.v[s] = row < nv ? *reinterpret_cast<const uint4 *>(src + 32 * s) : uint4{0, 0, 0, 0};
     return r;
 }
 
@@ -56,15 +56,11 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int cc = lane & 15, rr = lane >> 4;
     constexpr float LEVELS = (float)((1 << BITS) - 1);
     constexpr float TINY = 1e-30f;
     constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
     const int iters = NIT >= 0 ? NIT : a.iters;
-    // after the lane stages of the rotation the lane holds sigma * Y of channel
-    // group pcc: channels 8 pcc .. 8 pcc + 7
-    const int pcc = hperm16(cc);
-    const float sigma = hsign16(cc);
+    const Had128B hb = had128_operands(lane);
     float *cv = chv[wave];
     uint8_t *im = img[wave];
 
@@ -73,36 +69,29 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
     Rows nxt{};
     if (item < num_items) nxt = load_rows(a, item, lane);
     for (; item < num_items; item += stride) {
+        // lane id made opaque: the LDS and global addresses derived from it are formed
+        // inside the item, not hoisted out of the loop (held across it they spill, and a
+        // spill reload waits for the next item's loads in flight)
+        int ol = lane;
+        asm volatile("" : "+v"(ol));
+        // after the rotation the lane holds channels 16 j + cc, j = 0..7, of rows 4 rr + k
+        const int cc = ol & 15, rr = ol >> 4;
         const int tile = item / a.H, head = item % a.H;
         const int dst_page = load_const(a.tile_dst_page, tile);
         const int n = load_const(a.tile_valid, tile);
+        // ---- unnormalized Walsh-Hadamard transform along the 128 channels (matrix cores)
         float y[4][8];
+        {
+            f32x4 xr[8];
+            had128_rows16(nxt.v, hb, xr);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t w4[4] = {nxt.v[k].x, nxt.v[k].y, nxt.v[k].z, nxt.v[k].w};
+            for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bf16_pair_butterfly(w4[i], y[k][2 * i], y[k][2 * i + 1]);
+                for (int j = 0; j < 8; ++j) y[k][j] = xr[j][k];
         }
         if (item + stride < num_items) nxt = load_rows(a, item + stride, lane);  // travels meanwhile
         if (dst_page < 0 || dst_page >= a.num_pages) continue;  // invalid destination: tile skipped (uniform)
         const int64_t blk = (int64_t)dst_page * a.H + head;
-
-        // ---- unnormalized Walsh-Hadamard transform along the 128 channels: bit 0
-        // straight from the packed source pairs (above), bits 1..2 in registers, bits
-        // 3..6 across lanes (DPP-fused multiply-adds)
-#pragma unroll
-        for (int s = 2; s < 8; s <<= 1)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (!(j & s)) {
-                        const float p = y[k][j], q = y[k][j | s];
-                        y[k][j] = p + q;
-                        y[k][j | s] = p - q;
-                    }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) hadamard16_lanes(y[k], cc);
 
         // ---- normalization rounds on A = Y^2: u = 1/r^2 per row, w = 1/c^2 per channel
         float A[4][8];
@@ -127,7 +116,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
         for (int j = 0; j < 8; ++j) w[j] = 1.f;
         const float fn = (float)n, fn_d = fn * (1.0f / ZD);
         constexpr float HUGE_F = 3.4028234663852886e38f;
-        float t_own[2] = {0.f, 0.f};  // column sums of channels 8 cc + 2 rr + {0, 1} (last round)
+        float t_own[2] = {0.f, 0.f};  // column sums of channels 16 (2 rr + {0, 1}) + cc (last round)
 #pragma unroll
         for (int it = 0; it < iters; ++it) {
             // row step: r^2 = mean_j A_ij / c_j^2 over the 128 channels
@@ -166,22 +155,18 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
-                t_own[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 pcc + 2 rr + j
+                t_own[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 16 (2 rr + j) + cc
             }
             // a zero column keeps a large finite w (its A entries are all zero)
-            *reinterpret_cast<float2 *>(&cv[8 * pcc + 2 * rr]) =
-                float2{fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[0], TINY)), fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[1], TINY))};
-            const float4 w0 = *reinterpret_cast<const float4 *>(&cv[8 * pcc]);
-            const float4 w1 = *reinterpret_cast<const float4 *>(&cv[8 * pcc + 4]);
-            w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-            w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) cv[16 * (2 * rr + j) + cc] = fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[j], TINY));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = cv[16 * j + cc];
         }
 
         // ---- fp16 normalizer c16 of the lane's two channels and the multiplier
-        // sigma / (sqrt(128) c16); a column whose sum of squares is 0 or not finite keeps c = 1
+        // 1 / (sqrt(128) c16); a column whose sum of squares is 0 or not finite keeps c = 1
         {
-            uint32_t c2 = 0;
-            float m2[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float tj = t_own[j];
@@ -189,22 +174,17 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
                 const uint16_t c16 = float_to_half_bits(sqrtf(csq));
                 const float cvj = half_bits_to_float(c16);
                 if (!(cvj > 0.f && cvj < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
-                m2[j] = INV_SQRT_H / cvj;
-                c2 |= (uint32_t)c16 << (16 * j);
+                const int ch = 16 * (2 * rr + j) + cc;
+                a.cnorm[blk * ZD + ch] = c16;
+                cv[ch] = INV_SQRT_H / cvj;
             }
-            *reinterpret_cast<uint32_t *>(a.cnorm + blk * ZD + 8 * pcc + 2 * rr) = c2;
-            *reinterpret_cast<float2 *>(&cv[8 * pcc + 2 * rr]) = float2{m2[0], m2[1]};
         }
         float mult[8];
-        {
-            const float4 m0 = *reinterpret_cast<const float4 *>(&cv[8 * pcc]);
-            const float4 m1 = *reinterpret_cast<const float4 *>(&cv[8 * pcc + 4]);
-            mult[0] = m0.x * sigma; mult[1] = m0.y * sigma; mult[2] = m0.z * sigma; mult[3] = m0.w * sigma;
-            mult[4] = m1.x * sigma; mult[5] = m1.y * sigma; mult[6] = m1.z * sigma; mult[7] = m1.w * sigma;
-        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mult[j] = cv[16 * j + cc];
 
         // ---- per token: asymmetric RTN with fp16 (S, Z); byte codes into the image
-        uint32_t cm[8];  // channel-major: bytes of rows 4 rr .. + 3 of channel 8 cc + j
+        uint32_t cm[8];  // channel-major: bytes of rows 4 rr .. + 3 of channel 16 j + cc
 #pragma unroll
         for (int j = 0; j < 8; ++j) cm[j] = 0;
         // y -> y / c16 (scaled, signed), in place; row minima and maxima over the 128 channels
@@ -248,13 +228,8 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
             if (cc == 0)
                 reinterpret_cast<uint32_t *>(a.sz)[blk * ZT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
             if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
-                uint32_t lo = 0, hi = 0;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    lo = __builtin_amdgcn_cvt_pk_u8_f32(q[b], b, lo);
-                    hi = __builtin_amdgcn_cvt_pk_u8_f32(q[b + 4], b, hi);
-                }
-                *reinterpret_cast<uint2 *>(&im[row * ZD + 8 * pcc]) = uint2{lo, hi};
+                for (int j = 0; j < 8; ++j) im[row * ZD + 16 * j + cc] = (uint8_t)__builtin_amdgcn_cvt_pk_u8_f32(q[j], 0, 0);
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) cm[j] = __builtin_amdgcn_cvt_pk_u8_f32(q[j], k, cm[j]);
@@ -262,13 +237,13 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
         }
         if constexpr (LAYOUT == KVQ_CHANNEL_MAJOR) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t *>(&im[(8 * pcc + j) * ZT + 4 * rr]) = cm[j];
+            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t *>(&im[(16 * j + cc) * ZT + 4 * rr]) = cm[j];
         }
 
         // ---- pack: lane l takes stream positions 32 l .. 32 l + 31 -> BITS words
         {
-            const uint4 b0 = *reinterpret_cast<const uint4 *>(&im[32 * lane]);
-            const uint4 b1 = *reinterpret_cast<const uint4 *>(&im[32 * lane + 16]);
+            const uint4 b0 = *reinterpret_cast<const uint4 *>(&im[32 * ol]);
+            const uint4 b1 = *reinterpret_cast<const uint4 *>(&im[32 * ol + 16]);
             const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
             uint32_t out[BITS];
 #pragma unroll
@@ -280,7 +255,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
                 out[bit >> 5] |= c << (bit & 31);
                 if ((bit & 31) + BITS > 32) out[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
             }
-            uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + blk * (ZT * ZD * BITS / 8)) + BITS * lane;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + blk * (ZT * ZD * BITS / 8)) + BITS * ol;
             if constexpr (BITS == 4) *reinterpret_cast<uint4 *>(dst) = uint4{out[0], out[1], out[2], out[3]};
             else if constexpr (BITS == 2) *reinterpret_cast<uint2 *>(dst) = uint2{out[0], out[1]};
             else {

@@ -37,8 +37,9 @@ def tie_margin(bits: int) -> float:
     """Largest distance of the oracle's quotient (y - Z) / S from a half-integer at
     which an fp32 evaluation may still round the other way: y carries fp32 error of a
     few units of 2^-24 relative to the row's largest value, which the quotient scales
-    by at most (2^b - 1) / (max - min) ~ levels; 2^-13 per level leaves wide margin."""
-    return (2 ** bits) * 2.0 ** -13
+    by at most (2^b - 1) / (max - min) ~ levels. 2^-19 per level: measured tie flips
+    lie within 1e-6 (4-bit) and 1.4e-5 (8-bit) of the half-integer, 30x inside it."""
+    return (2 ** bits) * 2.0 ** -19
 
 
 DEQUANT_RTOL = 1e-3
