@@ -14,6 +14,13 @@
 // so B(s, t) is one of two per-lane patterns (t & 1) times a sign that depends on s
 // and t only: four operand registers of 8 bf16 cover all 32 (s, t) pairs. Lane l
 // receives X'[4 (l >> 4) + i][16 t + (l & 15)] in element i of output tile t.
+// The output channels may also be permuted by the B columns at no cost as long as
+// the pattern count stays two. The pair order used by the 128-token kernel puts
+// channel j = 32 (t >> 1) + 2 n + (t & 1) in column n of tile t, so that each lane
+// holds adjacent channel pairs: then
+//   popcount(k & j) = (e & 1)(t & 1) + popcount((e >> 1) & n & 3) + popcount(kg & (n >> 2))
+//                     + popcount(s & (t >> 1)),
+// again two per-lane patterns (t & 1) and a sign of s and t.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,6 +35,8 @@ struct Had128B {
     uint4 p0, p1;  // the two per-lane patterns (t & 1 = 0, 1), + sign; - is the sign bits flipped
 };
 
+// PAIRS = false: natural order, channel 16 t + n; true: pair order (above)
+template <bool PAIRS = false>
 __device__ __forceinline__ Had128B had128_operands(int lane) {
     const int n = lane & 15, kg = lane >> 4;
     uint32_t w[2][4];
@@ -39,7 +48,9 @@ __device__ __forceinline__ Had128B had128_operands(int lane) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 const int e = 2 * h + b;
-                const int par = (__builtin_popcount(e & n & 7) + ((kg & 1) & (n >> 3)) + ((kg >> 1) & t0)) & 1;
+                const int par = PAIRS ? ((e & 1 & t0) + __builtin_popcount((e >> 1) & n & 3) +
+                                         __builtin_popcount(kg & (n >> 2))) & 1
+                                      : (__builtin_popcount(e & n & 7) + ((kg & 1) & (n >> 3)) + ((kg >> 1) & t0)) & 1;
                 word |= (par ? 0xBF80u : 0x3F80u) << (16 * b);  // bf16 -1 / +1
             }
             w[t0][h] = word;
@@ -47,7 +58,16 @@ __device__ __forceinline__ Had128B had128_operands(int lane) {
     return Had128B{uint4{w[0][0], w[0][1], w[0][2], w[0][3]}, uint4{w[1][0], w[1][1], w[1][2], w[1][3]}};
 }
 
-// x[s]: the lane's 8 bf16 of step s (see above). out[t][i] = X'[4 (lane >> 4) + i][16 t + (lane & 15)].
+// Makes the patterns opaque to the compiler where called (inside an item loop): the
+// sign-flipped copies formed from them are then recomputed per call (8 instructions)
+// instead of being hoisted and held, 16 more registers, across the whole loop.
+__device__ __forceinline__ void opaque(Had128B &b) {
+    asm volatile("" : "+v"(b.p0.x), "+v"(b.p0.y), "+v"(b.p0.z), "+v"(b.p0.w), "+v"(b.p1.x), "+v"(b.p1.y),
+                 "+v"(b.p1.z), "+v"(b.p1.w));
+}
+
+// x[s]: the lane's 8 bf16 of step s (see above). out[t][i] = X'[4 (lane >> 4) + i][channel of
+// (lane & 15, t)] in the order the operands were built for.
 __device__ __forceinline__ void had128_rows16(const uint4 (&x)[4], const Had128B &hb, f32x4 (&out)[8]) {
     bf16x8 a[4];
 #pragma unroll

@@ -3,12 +3,13 @@
 // cross-lane traffic stays in the VALU (DPP, permlane swaps) or the LDS
 // crossbar without memory (ds_swizzle), and the codes are packed in registers.
 //
-// Workgroup = one (tile, head) at a time, T / (4 R) waves. Lane l of wave w
-// loads the 8 consecutive channels 8 (l & 15) .. + 7 of the R consecutive rows
-// of row group rg = 4 w + (l >> 4). The 16 lanes of a DPP row therefore cover
-// one token's 128 channels: the Hadamard butterflies on channel bits 3..6 and
-// every per-token reduction are DPP row operations. After the rotation the lane
-// holds rotated channel group hperm16(l & 15) (the lane stages relabel them).
+// Workgroup = one (tile, head) at a time, T / (4 R) waves, wave w owning rows
+// 16 w .. 16 w + 15. The 128-point rotation runs on the matrix cores
+// (mfma_hadamard.h, pair order): lane l supplies the bf16 source of row 16 w + (l & 15)
+// as the A operand and receives the rotated rows of row group rg = 4 w + (l >> 4)
+// (R = 4 rows) at the channel pairs 32 u + 2 (l & 15) + {0, 1}, u = 0..3. The 16 lanes
+// of a DPP row therefore cover one token's 128 channels: every per-token reduction is
+// a DPP row operation, and 4-bit token-major codes leave each lane as whole bytes.
 //
 // Persistent workgroups walk items (tile, head); the next item's rows are copied
 // HBM -> LDS while the current one is computed. One launch can cover the K and V
@@ -20,6 +21,7 @@
 // asymmetric round-to-nearest with fp16 scale, zero point and normalizer.
 #include "common.h"
 #include "launch.h"
+#include "mfma_hadamard.h"
 #include "xlane.h"
 
 namespace kvq {
@@ -29,41 +31,6 @@ namespace {
 constexpr int QD = 128;
 // rows per lane: 4 (8 waves per 128-token tile, 4 per 64-token tile)
 constexpr int QR = 4;
-
-__device__ __forceinline__ void load8_bf16(const uint16_t *p, float (&v)[8]) {
-    const uint4 a = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-
-// Pack eight byte codes c[0..7] (< 2^BITS) of consecutive stream positions into
-// the little-endian bitstream word(s): returns the low 8*BITS bits.
-template <int BITS>
-__device__ __forceinline__ uint32_t pack8(const float (&u)[8]) {
-    // u are rounded-to-be codes in fp32; v_cvt_pk_u8_f32 rounds to nearest even
-    // and clamps below at 0 (the upper clamp is applied by the caller)
-    if constexpr (BITS == 4) {
-        uint32_t x = 0, y = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            x = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * b], b, x);
-            y = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * b + 1], b, y);
-        }
-        return x | (y << 4);
-    } else {  // BITS == 2
-        uint32_t d[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            d[i] = __builtin_amdgcn_cvt_pk_u8_f32(u[i], 0, d[i]);
-            d[i] = __builtin_amdgcn_cvt_pk_u8_f32(u[i + 4], 1, d[i]);
-        }
-        return d[0] | (d[1] << 2) | (d[2] << 4) | (d[3] << 6);
-    }
-}
 
 // LDS image of a code block: 16-byte slot U of the global layout lives at slot
 // code_slot(U). The stores that run together (one row, or one channel, of every
@@ -101,6 +68,8 @@ __device__ __forceinline__ int code_byte(int b) {
 //   multsh [128]        per-channel output multiplier
 //   outbuf [T * 128 * BITS / 32] LDS image of the code block
 //   szbuf  [T]          (S, Z) fp16 pairs per token
+//   hbtab  [2][64]      the two per-lane Hadamard operand patterns (read per item:
+//                       held in registers across the item loop they spill)
 template <int V>
 struct IntC {
     static constexpr int value = V;
@@ -115,7 +84,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
                                                    float (*__restrict__ colsum0)[QD], float (*__restrict__ colsum1)[QD],
                                                    float *__restrict__ wsh0, float *__restrict__ wsh1,
                                                    float *__restrict__ multsh, uint32_t *__restrict__ outbuf,
-                                                   uint32_t *__restrict__ szbuf) {
+                                                   uint32_t *__restrict__ szbuf, uint4 *__restrict__ hbtab) {
     constexpr int NWV = T / (4 * R);  // waves (4 row groups of R rows each)
     constexpr int NT = 64 * NWV;
 
@@ -123,15 +92,20 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cc = lane & 15, rr = lane >> 4;
     const int rg = wave * 4 + rr;
+    if (wave == 0) {  // published by the first item's barrier
+        const Had128B hb = had128_operands<true>(lane);
+        hbtab[lane] = hb.p0;
+        hbtab[64 + lane] = hb.p1;
+    }
 
     // Persistent workgroups: item = tile * H + head, strided by the grid. The
     // next item's source rows are copied HBM -> LDS by direct-to-LDS loads while
     // the current item is processed in registers; only LDS-ordering barriers are
     // used until the next item starts, so the copies stay in flight. Each wave
     // load instruction moves 4 rows (1 KB): lane l -> row 4 b + (l >> 4), 16-byte
-    // chunk l & 15. LDS slot (l & 15) of a row holds chunk slot ^ ((row / R) & 3),
-    // so the four row groups of a wave read different banks; for a fixed b that
-    // swizzle is the constant ((4 i) / R) & 3.
+    // chunk l & 15. LDS slot (l & 15) of row r holds chunk slot ^ (r & 15), so the
+    // 16 rows that the lanes of a wave read as one operand step (one chunk each) sit
+    // in 16 different bank windows.
     auto fetch = [&](int gitm) {
         const bool isk = !PAIR || gitm < nk;  // uniform
         const QuantArgs &a = isk ? ak : av;
@@ -155,7 +129,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
             const int b = wave * R + i;
             const int rb = min(4 * b, last);                // wave-uniform first row of the copy
             const int dr = min(4 * b + frr, last) - rb;     // this lane's row, 0..3 rows further
-            const uint32_t off = (uint32_t)dr * row_bytes + 16u * (uint32_t)(fcc ^ (((4 * i) / R) & 3));
+            const uint32_t off = (uint32_t)dr * row_bytes + 16u * (uint32_t)(fcc ^ ((4 * i + frr) & 15));
             __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)rb * a.stride_token * 2 + off),
                                              (__attribute__((address_space(3))) void *)(stage + b * 64), 16, 0, 0);
         }
@@ -172,57 +146,37 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
     const int64_t blk = (int64_t)dst_page * a.H + head;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into LDS have landed
     lds_barrier();                  // and every other wave's
-    // rows past the valid ones hold copies of the last valid row (see fetch): read
-    // unconditionally, zeroed below only when the tile is partial (a uniform branch)
-    uint4 v4[R];
+    // the A operands: row 16 wave + (lane & 15), chunks 4 s + (lane >> 4). Rows past the
+    // valid ones hold copies of the last valid row (see fetch): read unconditionally,
+    // zeroed only when the tile is partial (a uniform branch)
+    uint4 x4[4];
+    {
+        const int arow = 16 * wave + cc;
 #pragma unroll
-    for (int k = 0; k < R; ++k) v4[k] = stage[(rg * R + k) * 16 + (cc ^ rr)];
-    if (n < T) {
+        for (int s4 = 0; s4 < 4; ++s4) x4[s4] = stage[arow * 16 + ((4 * s4 + rr) ^ cc)];
+        if (n < T && arow >= n)
 #pragma unroll
-        for (int k = 0; k < R; ++k)
-            if (rg * R + k >= n) v4[k] = uint4{0, 0, 0, 0};
-    }
-    // channels 2i and 2i + 1 share word i: the first butterfly stage (channel bit 0)
-    // comes out of the packed pair directly, and so does each row's sum of squares of
-    // the source (by Parseval the rotated row's is 128 times it: the first row step)
-    float y[R][8], ssq[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const uint4 v = v4[k];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf16_pair_butterfly(w4[i], y[k][2 * i], y[k][2 * i + 1]);
-            acc = bf16_pair_sumsq(w4[i], acc);
-        }
-        ssq[k] = acc;
+            for (int s4 = 0; s4 < 4; ++s4) x4[s4] = uint4{0, 0, 0, 0};
     }
     lds_barrier();  // the staging buffer is free again
     if (gitem + (int)gridDim.x < num_items) fetch(gitem + gridDim.x);
     if (dst_page < 0 || dst_page >= a.num_pages) return;  // invalid destination: tile skipped (uniform)
 
-    // ---- unnormalized Walsh-Hadamard transform along the 128 channels -------
-    // (channel bit 0 done above)
-#pragma unroll
-    for (int s = 2; s < 8; s <<= 1)
+    // ---- unnormalized Walsh-Hadamard transform along the 128 channels (matrix
+    // cores): lane (cc, rr) gets rows rg R + k at channels ch(t) = 32 (t >> 1) + 2 cc
+    // + (t & 1), t = 0..7
+    float y[R][8];
+    {
+        f32x4 xr[8];
+        int ol = lane;  // opaque: the pattern reads stay inside the item
+        asm volatile("" : "+v"(ol));
+        const Had128B hbi{hbtab[ol], hbtab[64 + ol]};
+        had128_rows16(x4, hbi, xr);
 #pragma unroll
         for (int k = 0; k < R; ++k)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (!(j & s)) {
-                    const float p = y[k][j], q = y[k][j | s];
-                    y[k][j] = p + q;
-                    y[k][j | s] = p - q;
-                }
-    // Cross-lane stages on channel bits 3..6 (the lane bits), one DPP-fused
-    // multiply-add per value and stage. Afterwards lane (cc, rr) holds
-    // sigma * Y of channel group pcc = hperm16(cc): channels 8 pcc .. 8 pcc + 7.
-    // The squares ignore sigma; it is folded into the per-channel multiplier.
-#pragma unroll
-    for (int k = 0; k < R; ++k) hadamard16_lanes(y[k], cc);
-    const int pcc = hperm16(cc);
-    const float sigma = hsign16(cc);
+            for (int t = 0; t < 8; ++t) y[k][t] = xr[t][k];
+    }
 
     // ---- normalization rounds on A = Y^2: u = 1/r^2 per row, w = 1/c^2 per channel
     // A = Y^2, kept in registers
@@ -238,7 +192,9 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
     if (iters == 0) {
         float t = 0.f;
 #pragma unroll
-        for (int k = 0; k < R; ++k) t += ssq[k];
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t += A[k][j];
         if (!isfinite(t)) nonfinite = true;
     }
     // w holds 1 / c^2 in the first round and 1 / (128 c^2) after it (the mean over
@@ -258,12 +214,14 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
     for (int it = 0; it < iters; ++it) {
         // row step: r^2 = mean_j A_ij / c_j^2 over the 128 channels. A zero row keeps
         // a large finite u and contributes 0 * u = 0 below, as with an unchanged factor.
-        // (first round: c = 1, and the row's sum of squares is 128 times the source's)
+        // (first round: c = 1, a plain sum)
         float rs[R];
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             float s = 0.f;
-            if (it == 0) s = ssq[k];
+            if (it == 0)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s += A[k][j];
             else
 #pragma unroll
                 for (int j = 0; j < 8; ++j) s = __builtin_fmaf(A[k][j], w[j], s);
@@ -275,8 +233,8 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
             if (it == 0 && !isfinite(rs[k])) nonfinite = true;
             // max(s, tiny) as a median with the largest float: one instruction (fmaxf would first
             // quiet the value the DPP asm produced); a NaN sum is flagged above. First round:
-            // u = 128 / (128 sum x^2) = 1 / sum x^2
-            u[k] = it == 0 ? __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY * (1.0f / QD), HUGE_F * (1.0f / QD)))
+            // u = 128 / sum_j Y_j^2
+            u[k] = it == 0 ? (float)QD * __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY, HUGE_F))
                            : __builtin_amdgcn_rcpf(__builtin_amdgcn_fmed3f(rs[k], TINY * (1.0f / QD), HUGE_F));
         }
         // column step: c^2 = mean_i A_ij u_i over the n valid rows
@@ -299,12 +257,11 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[j]), __float_as_uint(h4[j + 2]), false, false);
-            h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 8 pcc + 2 rr + j
+            h2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // local t = 2 rr + j: channel 32 rr + 2 cc + j
         }
         float(*colsum)[QD] = (it & 1) ? colsum1 : colsum0;
         float *wsh = (it & 1) ? wsh1 : wsh0;
-        colsum[wave][pcc * 8 + 2 * rr] = h2[0];
-        colsum[wave][pcc * 8 + 2 * rr + 1] = h2[1];
+        *reinterpret_cast<float2 *>(&colsum[wave][32 * rr + 2 * cc]) = float2{h2[0], h2[1]};
         lds_barrier();
         if (tid < QD) {
             float acc[NWV / 4];
@@ -318,15 +275,16 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
         // the last round's column sums go straight to the normalizer below (no w)
         if (it + 1 == iters) break;
         lds_barrier();
-        const float4 w0 = *reinterpret_cast<const float4 *>(&wsh[pcc * 8]);
-        const float4 w1 = *reinterpret_cast<const float4 *>(&wsh[pcc * 8 + 4]);
-        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+            const float2 wv = *reinterpret_cast<const float2 *>(&wsh[32 * u2 + 2 * cc]);
+            w[2 * u2] = wv.x;
+            w[2 * u2 + 1] = wv.y;
+        }
     }
 
     // ---- fp16 normalizer c16 (owner threads) and the per-channel multiplier
-    // sigma / (sqrt(128) c16); a column whose sum of squares is 0 or not finite
-    // keeps c = 1
+    // 1 / (sqrt(128) c16); a column whose sum of squares is 0 or not finite keeps c = 1
     constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
     if (tid < QD) {
         const float csq = (iters > 0 && n > 0 && t_own > 0.f && t_own < INFINITY) ? t_own / fn : 1.f;
@@ -343,11 +301,11 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
     }
     lds_barrier();
     float mult[8];
-    {
-        const float4 m0 = *reinterpret_cast<const float4 *>(&multsh[pcc * 8]);
-        const float4 m1 = *reinterpret_cast<const float4 *>(&multsh[pcc * 8 + 4]);
-        mult[0] = m0.x * sigma; mult[1] = m0.y * sigma; mult[2] = m0.z * sigma; mult[3] = m0.w * sigma;
-        mult[4] = m1.x * sigma; mult[5] = m1.y * sigma; mult[6] = m1.z * sigma; mult[7] = m1.w * sigma;
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2) {
+        const float2 mv = *reinterpret_cast<const float2 *>(&multsh[32 * u2 + 2 * cc]);
+        mult[2 * u2] = mv.x;
+        mult[2 * u2 + 1] = mv.y;
     }
 
     // ---- per token: asymmetric RTN with fp16 (S, Z), codes packed in registers
@@ -358,7 +316,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
 #pragma unroll
     for (int j = 0; j < 8; ++j) cma[j] = cmb[j] = 0;
     uint8_t *cbase = reinterpret_cast<uint8_t *>(outbuf);  // LDS image of the code block
-    // y -> y / c16 (scaled, signed), in place; row minima and maxima over the 128 channels
+    // y -> y / c16 (scaled), in place; row minima and maxima over the 128 channels
     float mnr[R], mxr[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
@@ -400,11 +358,22 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
             for (int j = 0; j < 8; ++j) q[j] = fminf(q[j], LEVELS);
         if (cc == 0) szbuf[row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
-            const uint32_t word = pack8<BITS>(q);
-            if constexpr (BITS == 4)
-                *reinterpret_cast<uint32_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(4 * (row * (QD / 8) + pcc))) = word;
-            else
-                *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(2 * (row * (QD / 8) + pcc))) = (uint16_t)word;
+            // the lane's channel pairs 32 u + 2 cc + {0, 1}: one byte each (4-bit, the
+            // even channel in the low nibble); 2-bit: the pair's nibble, joined with the
+            // neighbouring lane's pair (channels 32 u + 2 (cc ^ 1) + {0, 1}) into a byte
+#pragma unroll
+            for (int u2 = 0; u2 < 4; ++u2) {
+                const uint32_t lo = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * u2], 0, 0);
+                const uint32_t hi = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * u2 + 1], 0, 0);
+                if constexpr (BITS == 4) {
+                    cbase[code_byte<T, R, BITS, LAYOUT>(row * (QD / 2) + 16 * u2 + cc)] = (uint8_t)(lo | (hi << 4));
+                } else {
+                    const uint32_t nib = lo | (hi << 2);
+                    const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)nib, DPP_QUAD_XOR1, 0xF, 0xF, true);
+                    if (!(cc & 1))
+                        cbase[code_byte<T, R, BITS, LAYOUT>(row * (QD / 4) + 8 * u2 + (cc >> 1))] = (uint8_t)(nib | (nb << 4));
+                }
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -421,7 +390,7 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
         // channel ch: rows rg*R .. rg*R + R - 1 are stream positions ch * T + rg * R + k
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int pos = (pcc * 8 + j) * T + rg * R;
+            const int pos = (32 * (j >> 1) + 2 * cc + (j & 1)) * T + rg * R;
             if constexpr (BITS == 4) {
                 *reinterpret_cast<uint16_t *>(cbase + code_byte<T, R, BITS, LAYOUT>(pos / 2)) =
                     (uint16_t)(cma[j] | (cmb[j] << 4));
@@ -477,8 +446,9 @@ __global__ void __launch_bounds__(16 * T / R, 4) quantize_d128_kernel(QuantArgs 
     __shared__ float multsh[QD];
     __shared__ uint32_t outbuf[T * QD * MB / 32];
     __shared__ uint32_t szbuf[T];
+    __shared__ uint4 hbtab[2 * 64];
     quantize_d128_body<T, R, BK, LK, BV, LV, NIT, PAIR>(ak, av, nk, num_items, stage, colsum0, colsum1, wsh0, wsh1,
-                                                        multsh, outbuf, szbuf);
+                                                        multsh, outbuf, szbuf, hbtab);
 }
 
 bool quantize_d128_supported(int D, int T, const QuantArgs &a) {
