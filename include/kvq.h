@@ -48,6 +48,9 @@
 extern "C" {
 #endif
 
+/* Element types. Calls take them (and kvq_status_str its code) as int32_t: any
+ * value may arrive through the C ABI, and an out-of-range one returns KVQ_EINVAL
+ * (a parameter of enum type holding it would be undefined behaviour in C++). */
 typedef enum { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 } kvq_dtype;
 
 typedef enum {
@@ -125,7 +128,7 @@ size_t kvq_cache_bytes(const kvq_format *fmt, int32_t num_pages, int32_t num_hea
  *   or h = 1; R = 0, or R a multiple of 8 with bf16/f16/f32 input.
  * Errors: KVQ_EINVAL (nulls, negative counts, H != dst->num_heads ...),
  *   KVQ_EUNSUPPORTED (outside the list above), KVQ_ELAUNCH. */
-kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+kvq_status kv_quantize(const kvq_cache *dst, const void *src, int32_t src_dtype, int64_t stride_token,
                        int64_t stride_head, int32_t num_tiles, const int32_t *tile_src_token,
                        const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
                        hipStream_t stream);
@@ -141,7 +144,7 @@ kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtyp
  * iters and number of heads. Otherwise KVQ_EUNSUPPORTED and nothing is launched
  * (two kv_quantize calls do the work). Errors as for kv_quantize. */
 kvq_status kv_quantize_kv(const kvq_cache *k_dst, const kvq_cache *v_dst, const void *k_src, const void *v_src,
-                          kvq_dtype src_dtype, int64_t k_stride_token, int64_t k_stride_head, int64_t v_stride_token,
+                          int32_t src_dtype, int64_t k_stride_token, int64_t k_stride_head, int64_t v_stride_token,
                           int64_t v_stride_head, int32_t num_tiles, const int32_t *tile_src_token,
                           const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
                           hipStream_t stream);
@@ -150,7 +153,7 @@ kvq_status kv_quantize_kv(const kvq_cache *k_dst, const kvq_cache *v_dst, const 
  * dst (device): [num_tiles][H][T][D + R] in dst_dtype (f32, f16 or bf16); rows
  * t >= tile_valid[i] are written as zero. tile_page, tile_valid: device int32. */
 kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t *tile_page,
-                         const int32_t *tile_valid, void *dst, kvq_dtype dst_dtype, hipStream_t stream);
+                         const int32_t *tile_valid, void *dst, int32_t dst_dtype, hipStream_t stream);
 
 /* Number of split-K partitions kv_decode_attn uses when num_splits == 0 for
  * these caches (k, v as passed to kv_decode_attn; host structs, device arrays
@@ -182,7 +185,7 @@ size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (layouts: K token-major, V channel-major,
  * MLA latent token-major; T in {16, 32, 64, 128}; num_seqs above 65535 except
  * for MLA), KVQ_EWORKSPACE, KVQ_ELAUNCH. */
-kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+kvq_status kv_decode_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                           const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
                           int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
                           float sm_scale, int32_t num_splits, void *workspace, size_t workspace_bytes,
@@ -205,7 +208,7 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
  * kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, Dv, splits), exceed
  * KVQ_NOALLOC_SCRATCH_BYTES (nothing is launched); KVQ_ELAUNCH when the runtime
  * does not give the array's device address. */
-kvq_status kv_decode_attn_noalloc(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+kvq_status kv_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                                   const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
                                   int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
                                   float sm_scale, int32_t num_splits, float *out, hipStream_t stream);
@@ -235,7 +238,7 @@ kvq_status kv_decode_attn_noalloc(const void *q, kvq_dtype q_dtype, int32_t num_
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (as kv_quantize), KVQ_EWORKSPACE,
  * KVQ_ELAUNCH. Calls on one stream are ordered; two appends to one sequence
  * must not run concurrently. */
-kvq_status kv_append(const kvq_cache *dst, void *tail, kvq_dtype dtype, const void *new_tokens,
+kvq_status kv_append(const kvq_cache *dst, void *tail, int32_t dtype, const void *new_tokens,
                      int64_t new_stride_seq, int64_t new_stride_head, int32_t num_seqs,
                      const int32_t *seq_lens, const int32_t *block_table, int32_t block_table_stride,
                      void *workspace, size_t workspace_bytes, uint32_t *status_flags, hipStream_t stream);
@@ -248,7 +251,7 @@ size_t kv_append_workspace_bytes(int32_t num_seqs);
  * "quantize_t16_kernel", "quantize_d512_kernel" (specialised tile shapes) or
  * "quantize_kernel" (any supported format). NULL where kv_quantize would
  * reject the arguments. The string is static. For profilers and benchmarks. */
-const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_dtype src_dtype,
+const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, int32_t src_dtype,
                                     int64_t stride_token, int64_t stride_head);
 
 /* Name of the main GPU kernel kv_decode_attn runs for this query pointer and
@@ -280,7 +283,7 @@ const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const 
  *   num_splits: 0 = kv_prefill_attn_default_splits(...).
  * Other arguments and errors as kv_decode_attn; KVQ_EUNSUPPORTED when
  * num_seqs * chunk_len exceeds 2^24. */
-kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t chunk_len,
+kvq_status kv_prefill_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t chunk_len,
                            int32_t num_q_heads, const kvq_cache *k, const kvq_cache *v,
                            const int32_t *block_table, int32_t block_table_stride, const int32_t *seq_lens,
                            int32_t max_seq_len, float sm_scale, int32_t num_splits, void *workspace,
@@ -302,7 +305,7 @@ const char *kv_prefill_attn_kernel_name(const void *q, const kvq_cache *k, const
                                         int32_t num_q_heads);
 
 /* Static description of a status code. */
-const char *kvq_status_str(kvq_status s);
+const char *kvq_status_str(int32_t s);
 
 #ifdef __cplusplus
 }

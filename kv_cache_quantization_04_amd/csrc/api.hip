@@ -90,7 +90,7 @@ kvq_status decode_layout(const kvq_cache *k, const kvq_cache *v, int32_t num_q_h
 }
 
 // checks of kv_quantize's cache and source arguments
-kvq_status check_quantize_source(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+kvq_status check_quantize_source(const kvq_cache *dst, const void *src, int32_t src_dtype, int64_t stride_token,
                                  int64_t stride_head) {
     kvq_status st = check_cache(dst);
     if (st != KVQ_OK) return st;
@@ -99,7 +99,7 @@ kvq_status check_quantize_source(const kvq_cache *dst, const void *src, kvq_dtyp
     return KVQ_OK;
 }
 
-kvq::QuantArgs quant_args(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+kvq::QuantArgs quant_args(const kvq_cache *dst, const void *src, int32_t src_dtype, int64_t stride_token,
                           int64_t stride_head, const int32_t *tile_src_token, const int32_t *tile_valid,
                           const int32_t *tile_dst_page, uint32_t *status_flags) {
     const kvq_format &f = dst->fmt;
@@ -145,7 +145,7 @@ void *scratch_for(hipStream_t stream) {
 
 // kv_decode_attn after its workspace is known (nullptr with `have_ws` false: the
 // noalloc scratch, resolved after every host-side check has passed)
-kvq_status decode_attn_impl(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+kvq_status decode_attn_impl(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                             const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
                             int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
                             int32_t num_splits, void *workspace, size_t workspace_bytes, bool have_ws, float *out,
@@ -155,7 +155,7 @@ kvq_status decode_attn_impl(const void *q, kvq_dtype q_dtype, int32_t num_seqs, 
 
 extern "C" {
 
-const char *kvq_status_str(kvq_status s) {
+const char *kvq_status_str(int32_t s) {
     switch (s) {
     case KVQ_OK: return "ok";
     case KVQ_EINVAL: return "invalid argument";
@@ -184,7 +184,7 @@ size_t kvq_cache_bytes(const kvq_format *f, int32_t num_pages, int32_t num_heads
     return ph * (T * D * f->bits / 8 + T * (D / f->group) * 4 + D * 2 + T * f->rope_dim * 2);
 }
 
-kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+kvq_status kv_quantize(const kvq_cache *dst, const void *src, int32_t src_dtype, int64_t stride_token,
                        int64_t stride_head, int32_t num_tiles, const int32_t *tile_src_token,
                        const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
                        hipStream_t stream) {
@@ -201,7 +201,7 @@ kvq_status kv_quantize(const kvq_cache *dst, const void *src, kvq_dtype src_dtyp
 }
 
 kvq_status kv_quantize_kv(const kvq_cache *k_dst, const kvq_cache *v_dst, const void *k_src, const void *v_src,
-                          kvq_dtype src_dtype, int64_t k_stride_token, int64_t k_stride_head, int64_t v_stride_token,
+                          int32_t src_dtype, int64_t k_stride_token, int64_t k_stride_head, int64_t v_stride_token,
                           int64_t v_stride_head, int32_t num_tiles, const int32_t *tile_src_token,
                           const int32_t *tile_valid, const int32_t *tile_dst_page, uint32_t *status_flags,
                           hipStream_t stream) {
@@ -223,7 +223,7 @@ kvq_status kv_quantize_kv(const kvq_cache *k_dst, const kvq_cache *v_dst, const 
     return launched();
 }
 
-const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_dtype src_dtype, int64_t stride_token,
+const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, int32_t src_dtype, int64_t stride_token,
                                     int64_t stride_head) {
     if (check_quantize_source(dst, src, src_dtype, stride_token, stride_head) != KVQ_OK) return nullptr;
     const kvq::QuantArgs a =
@@ -232,7 +232,7 @@ const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, kvq_d
 }
 
 kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t *tile_page, const int32_t *tile_valid,
-                         void *dst, kvq_dtype dst_dtype, hipStream_t stream) {
+                         void *dst, int32_t dst_dtype, hipStream_t stream) {
     kvq_status st = check_cache(src);
     if (st != KVQ_OK) return st;
     if (!dst || num_tiles < 0 || !valid_dtype(dst_dtype)) return KVQ_EINVAL;
@@ -250,7 +250,7 @@ size_t kv_append_workspace_bytes(int32_t num_seqs) {
     return (size_t)3 * num_seqs * sizeof(int32_t);
 }
 
-kvq_status kv_append(const kvq_cache *dst, void *tail, kvq_dtype dtype, const void *new_tokens,
+kvq_status kv_append(const kvq_cache *dst, void *tail, int32_t dtype, const void *new_tokens,
                      int64_t new_stride_seq, int64_t new_stride_head, int32_t num_seqs, const int32_t *seq_lens,
                      const int32_t *block_table, int32_t block_table_stride, void *workspace, size_t workspace_bytes,
                      uint32_t *status_flags, hipStream_t stream) {
@@ -305,7 +305,7 @@ size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
     return (size_t)num_seqs * num_q_heads * num_splits * (head_dim_v + 2) * sizeof(float);
 }
 
-kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads, const kvq_cache *k,
+kvq_status kv_decode_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads, const kvq_cache *k,
                           const kvq_cache *v, const int32_t *block_table, int32_t block_table_stride,
                           const int32_t *seq_lens, int32_t max_seq_len, float sm_scale, int32_t num_splits,
                           void *workspace, size_t workspace_bytes, float *out, hipStream_t stream) {
@@ -313,7 +313,7 @@ kvq_status kv_decode_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, in
                             max_seq_len, sm_scale, num_splits, workspace, workspace_bytes, true, out, stream);
 }
 
-kvq_status kv_decode_attn_noalloc(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+kvq_status kv_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                                   const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
                                   int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len,
                                   float sm_scale, int32_t num_splits, float *out, hipStream_t stream) {
@@ -352,7 +352,7 @@ const char *kv_prefill_attn_kernel_name(const void *q, const kvq_cache *k, const
     return kvq::prefill_kernel_name(a);
 }
 
-kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t chunk_len, int32_t num_q_heads,
+kvq_status kv_prefill_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t chunk_len, int32_t num_q_heads,
                            const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
                            int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
                            int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
@@ -398,7 +398,7 @@ kvq_status kv_prefill_attn(const void *q, kvq_dtype q_dtype, int32_t num_seqs, i
 
 namespace {
 
-kvq_status decode_attn_impl(const void *q, kvq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+kvq_status decode_attn_impl(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                             const kvq_cache *k, const kvq_cache *v, const int32_t *block_table,
                             int32_t block_table_stride, const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
                             int32_t num_splits, void *workspace, size_t workspace_bytes, bool have_ws, float *out,

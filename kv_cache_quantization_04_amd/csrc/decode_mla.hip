@@ -517,10 +517,14 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
     // ---- split partial of the lane's head: o' (channels 16 mc + 4 lq + i of this half), m (natural log), l
     if (!hq_ok) return;
     l_run = lq_sum(l_run);
+    // a partial row is XD + 2 = 514 floats: rows start 8-byte aligned only, so the stores are float2
     float *wsr = a.ws + (((int64_t)s * a.Hq + hq) * a.splits + split) * (XD + 2);
 #pragma unroll
-    for (int m2 = 0; m2 < 16; ++m2)
-        *reinterpret_cast<float4 *>(wsr + 16 * (16 * half + m2) + 4 * lq) = float4{o[m2][0], o[m2][1], o[m2][2], o[m2][3]};
+    for (int m2 = 0; m2 < 16; ++m2) {
+        float2 *dst = reinterpret_cast<float2 *>(wsr + 16 * (16 * half + m2) + 4 * lq);
+        dst[0] = float2{o[m2][0], o[m2][1]};
+        dst[1] = float2{o[m2][2], o[m2][3]};
+    }
     if (lq == 0 && half == 0) {
         wsr[XD] = m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f;
         wsr[XD + 1] = l_run;

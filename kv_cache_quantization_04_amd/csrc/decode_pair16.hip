@@ -25,6 +25,7 @@
 #include "common.h"
 #include "decode_mfma.h"
 #include "launch.h"
+#include "xlane.h"
 
 namespace kvq {
 
@@ -146,12 +147,22 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
         const float s16 = (lq & 1) ? -1.f : 1.f, s32 = (lq & 2) ? -1.f : 1.f;
         const float qscale = 1.0f / sqrtf((float)a.kh);
         const bool x16 = a.kh > 32, x32 = a.kh > 64;
+        // channel bits 5 and 6 across lanes 16 and 32 apart (permlane swaps: lo + s hi is the
+        // butterfly, s = -1 on the odd / upper member)
         if (x16)
 #pragma unroll
-            for (int i = 0; i < 32; ++i) qv[i] = __builtin_fmaf(s16, qv[i], __shfl_xor(qv[i], 16, 64));
+            for (int i = 0; i < 32; ++i) {
+                float lo, hi;
+                pair16(qv[i], lo, hi);
+                qv[i] = __builtin_fmaf(s16, hi, lo);
+            }
         if (x32)
 #pragma unroll
-            for (int i = 0; i < 32; ++i) qv[i] = __builtin_fmaf(s32, qv[i], __shfl_xor(qv[i], 32, 64));
+            for (int i = 0; i < 32; ++i) {
+                float lo, hi;
+                pair32(qv[i], lo, hi);
+                qv[i] = __builtin_fmaf(s32, hi, lo);
+            }
 #pragma unroll
         for (int i = 0; i < 32; ++i) qv[i] *= qscale;
     }
@@ -329,8 +340,11 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
             const bool upper = lq >= 2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const _Float16 hu = (_Float16)__shfl_xor((float)phi[i], 32, 64);
-                const _Float16 lu = (_Float16)__shfl_xor((float)plo[i], 32, 64);
+                // the partner's (hi, lo) pair, 32 lanes apart: one permlane swap of the packed pair
+                const half2v mine = {phi[i], plo[i]};
+                const auto sw = __builtin_amdgcn_permlane32_swap(as_u(mine), as_u(mine), false, false);
+                const half2v other = as_h2(upper ? sw[0] : sw[1]);
+                const _Float16 hu = other.x, lu = other.y;
                 const _Float16 z = (_Float16)0.f;
                 pbh[2 * i] = act ? (upper ? hu : phi[i]) : z;
                 pbh[2 * i + 1] = act ? (upper ? phi[i] : hu) : z;

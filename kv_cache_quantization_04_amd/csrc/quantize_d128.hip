@@ -287,7 +287,9 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
     // 1 / (sqrt(128) c16); a column whose sum of squares is 0 or not finite keeps c = 1
     constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
     if (tid < QD) {
-        const float csq = (iters > 0 && n > 0 && t_own > 0.f && t_own < INFINITY) ? t_own / fn : 1.f;
+        // mean over the n valid rows by a reciprocal of n (exact for a full tile, n a
+        // power of two; within an ulp of the quotient otherwise)
+        const float csq = (iters > 0 && n > 0 && t_own > 0.f && t_own < INFINITY) ? t_own * __builtin_amdgcn_rcpf(fn) : 1.f;
         const uint16_t c16 = float_to_half_bits(sqrtf(csq));
         const float cv = half_bits_to_float(c16);
         if (!(cv > 0.f && cv < INFINITY)) sideov = true;

@@ -7,8 +7,8 @@
 // as the A operand, and receives the rotated rows 4 (l >> 4) .. + 3 at channels
 // 16 j + (l & 15), j = 0..7. The 16 lanes of a DPP row thus cover one token's 128
 // channels, and all per-token reductions are row operations. Column sums finish
-// inside the wave (permlane swaps across the four row groups) and come back to the
-// lanes through a small per-wave LDS array. Codes go to a per-wave LDS byte image in
+// inside the wave (permlane swaps across the four row groups) and the per-channel
+// factors go back to the four row groups by the reverse swaps (no LDS round trip). Codes go to a per-wave LDS byte image in
 // bitstream order (token-major t * 128 + j, channel-major j * 16 + t); each lane then
 // packs 32 consecutive codes into the little-endian bitstream, and the block leaves
 // with one store per lane. The next tile is loaded into registers meanwhile.
@@ -47,12 +47,24 @@ __device__ __forceinline__ Rows load_rows(const QuantArgs &a, int item, int lane
     return r;
 }
 
+// The values of the lane's 8 local channels (t = 0..7, channel 16 t + (lane & 15)) from
+// their owners: after the column-sum swaps, lane (cc, rr) holds local channels 2 rr and
+// 2 rr + 1 (o0, o1). The swaps of rows 16 lanes apart give every lane of a 32-lane
+// half h its four channels 4 h + {0, 1, 2, 3}; those 32 lanes apart, all eight.
+__device__ __forceinline__ void bcast_owned(float o0, float o1, float (&v)[8]) {
+    float q[4];
+    pair16(o0, q[0], q[2]);  // local 4 h, 4 h + 2
+    pair16(o1, q[1], q[3]);  // local 4 h + 1, 4 h + 3
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pair32(q[m], v[m], v[4 + m]);
+}
+
 }  // namespace
 
 template <int BITS, int LAYOUT, int NIT>
 __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int num_items) {
-    __shared__ float chv[4][ZD];                                // per wave: one value per channel
     __shared__ __attribute__((aligned(16))) uint8_t img[4][ZT * ZD];  // per wave: codes in stream order
+    __shared__ uint4 hbtab[2 * 64];  // the two per-lane Hadamard operand patterns, read per item
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -60,8 +72,12 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
     constexpr float TINY = 1e-30f;
     constexpr float INV_SQRT_H = 0.08838834764831845f;  // 1 / sqrt(128)
     const int iters = NIT >= 0 ? NIT : a.iters;
-    const Had128B hb = had128_operands(lane);
-    float *cv = chv[wave];
+    if (threadIdx.x < 64) {
+        const Had128B hb = had128_operands(lane);
+        hbtab[lane] = hb.p0;
+        hbtab[64 + lane] = hb.p1;
+    }
+    __syncthreads();
     uint8_t *im = img[wave];
 
     int item = blockIdx.x * 4 + wave;
@@ -83,6 +99,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
         float y[4][8];
         {
             f32x4 xr[8];
+            const Had128B hb{hbtab[ol], hbtab[64 + ol]};  // held across the loop, the patterns spill
             had128_rows16(nxt.v, hb, xr);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -158,30 +175,30 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
                 t_own[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // channel 16 (2 rr + j) + cc
             }
             // a zero column keeps a large finite w (its A entries are all zero)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) cv[16 * (2 * rr + j) + cc] = fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[j], TINY));
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w[j] = cv[16 * j + cc];
+            bcast_owned(fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[0], TINY)),
+                        fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[1], TINY)), w);
         }
 
         // ---- fp16 normalizer c16 of the lane's two channels and the multiplier
         // 1 / (sqrt(128) c16); a column whose sum of squares is 0 or not finite keeps c = 1
+        float mult[8];
         {
+            float m2[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float tj = t_own[j];
-                const float csq = (iters > 0 && n > 0 && tj > 0.f && tj < INFINITY) ? tj / fn : 1.f;
+                // mean over the n valid rows by a reciprocal of n (exact for a full tile,
+                // n = 16; within an ulp of the quotient otherwise)
+                const float csq = (iters > 0 && n > 0 && tj > 0.f && tj < INFINITY) ? tj * __builtin_amdgcn_rcpf(fn) : 1.f;
                 const uint16_t c16 = float_to_half_bits(sqrtf(csq));
                 const float cvj = half_bits_to_float(c16);
                 if (!(cvj > 0.f && cvj < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
                 const int ch = 16 * (2 * rr + j) + cc;
                 a.cnorm[blk * ZD + ch] = c16;
-                cv[ch] = INV_SQRT_H / cvj;
+                m2[j] = INV_SQRT_H / cvj;
             }
+            bcast_owned(m2[0], m2[1], mult);
         }
-        float mult[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mult[j] = cv[16 * j + cc];
 
         // ---- per token: asymmetric RTN with fp16 (S, Z); byte codes into the image
         uint32_t cm[8];  // channel-major: bytes of rows 4 rr .. + 3 of channel 16 j + cc
@@ -246,15 +263,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
             const uint4 b1 = *reinterpret_cast<const uint4 *>(&im[32 * ol + 16]);
             const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
             uint32_t out[BITS];
-#pragma unroll
-            for (int d = 0; d < BITS; ++d) out[d] = 0;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                const uint32_t c = (bw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-                const int bit = BITS * i;
-                out[bit >> 5] |= c << (bit & 31);
-                if ((bit & 31) + BITS > 32) out[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-            }
+            pack32_codes<BITS>(bw, out);
             uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + blk * (ZT * ZD * BITS / 8)) + BITS * ol;
             if constexpr (BITS == 4) *reinterpret_cast<uint4 *>(dst) = uint4{out[0], out[1], out[2], out[3]};
             else if constexpr (BITS == 2) *reinterpret_cast<uint2 *>(dst) = uint2{out[0], out[1]};

@@ -162,4 +162,25 @@ __device__ __forceinline__ float row_max16(float s) {
     return fmaxf(s, dpp<DPP_QUAD_XOR1>(s));
 }
 
+// 32 byte codes (each < 2^BITS) in stream order, four per word (code 4 i + b in byte
+// b of bw[i]) -> the BITS words of their little-endian bitstream. Within a word the
+// four codes are joined in parallel (SWAR): (w | w >> (8 - BITS)) puts bytes 1 and 3
+// next to bytes 0 and 2, the mask keeps the two 2 BITS-bit fields, and a shift by
+// 16 - 2 BITS joins them: 4 BITS bits per word in four instructions.
+template <int BITS>
+__device__ __forceinline__ void pack32_codes(const uint32_t (&bw)[8], uint32_t (&out)[BITS]) {
+    constexpr uint32_t F = (1u << (2 * BITS)) - 1u;
+#pragma unroll
+    for (int d = 0; d < BITS; ++d) out[d] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t v = (bw[i] | (bw[i] >> (8 - BITS))) & (F * 0x00010001u);
+        const uint32_t x = (v & F) | (v >> (16 - 2 * BITS));
+        constexpr int W = 4 * BITS;  // bits per word of codes
+        const int pos = W * i;       // compile-time after unrolling
+        out[pos >> 5] |= x << (pos & 31);
+        if ((pos & 31) + W > 32) out[(pos >> 5) + 1] |= x >> (32 - (pos & 31));
+    }
+}
+
 }  // namespace kvq

@@ -34,7 +34,8 @@ class OrcCache(ctypes.Structure):
 def lib():
     global _LIB
     if _LIB is None:
-        path = os.path.join(_HERE, "liboracle.so")
+        # KVQ_ORACLE_LIB: another build of oracle.cpp (e.g. with sanitizers), same ABI
+        path = os.environ.get("KVQ_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
         L = ctypes.CDLL(path)

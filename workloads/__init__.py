@@ -41,7 +41,8 @@ _LIB = None
 def lib():
     global _LIB
     if _LIB is None:
-        path = os.path.join(_HERE, "libsynth.so")
+        # KVQ_SYNTH_LIB: another build of synth.c (e.g. with sanitizers), same ABI
+        path = os.environ.get("KVQ_SYNTH_LIB") or os.path.join(_HERE, "libsynth.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
         L = ctypes.CDLL(path)
