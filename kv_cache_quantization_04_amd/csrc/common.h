@@ -46,6 +46,10 @@ __device__ __forceinline__ V load_const(const V *p, int64_t i) {
     return ((const __attribute__((address_space(4))) V *)(uintptr_t)p)[i];
 }
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, no
+// stride): loads at offsets past num_records bytes return zero.
+constexpr int BUF_DWORD3 = 0x00020000;
+
 // Butterfly partner exchange inside a group of lanes (xor pattern).
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, WAVE); }
 

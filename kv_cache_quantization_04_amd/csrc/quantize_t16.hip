@@ -33,18 +33,29 @@ struct Rows {
     uint4 v[4];  // token lane & 15: 8 bf16 channels 32 s + 8 (lane >> 4) .. + 7 for s = 0..3
 };
 
-// The lane's A operands of an item (a token row >= nv reads as zero).
+// The lane's A operands of an item. The loads go through a buffer resource that
+// covers the tile's nv valid rows only (nv row strides from its first row; a row
+// stride is at least 128 channels), so a row >= nv falls outside it and reads as zero
+// without a branch.
 __device__ __forceinline__ Rows load_rows(const QuantArgs &a, int item, int lane) {
     Rows r;
     const int tl = item / a.H, hd = item % a.H;
     const int nv = load_const(a.tile_valid, tl);
-    const int row = lane & 15;
-    const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src) + hd * a.stride_head +
-                          ((int64_t)load_const(a.tile_src_token, tl) + row) * a.stride_token + 8 * (lane >> 4);
+    const uint16_t *base = reinterpret_cast<const uint16_t *>(a.src) + hd * a.stride_head +
+                           (int64_t)load_const(a.tile_src_token, tl) * a.stride_token;
+    const int rec = (int)(nv * a.stride_token * 2);  // bytes; < 2^31 (checked at launch)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, rec,
+                                                                        BUF_DWORD3);
+    const int off = (int)((lane & 15) * a.stride_token * 2) + 16 * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        r.v[s] = row < nv ? *reinterpret_cast<const uint4 *>(src + 32 * s) : uint4{0, 0, 0, 0};
+    for (int s = 0; s < 4; ++s) r.v[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * s, 0, 0));
     return r;
+}
+
+// Value of lane K of the lane's 16-lane row (ds_swizzle broadcast: LDS crossbar, no VALU slot).
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x10 | (K << 5)));
 }
 
 // The values of the lane's 8 local channels (t = 0..7, channel 16 t + (lane & 15)) from
@@ -195,7 +206,10 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
                 if (!(cvj > 0.f && cvj < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
                 const int ch = 16 * (2 * rr + j) + cc;
                 a.cnorm[blk * ZD + ch] = c16;
-                m2[j] = INV_SQRT_H / cvj;
+                // 1 / (sqrt(128) c16): reciprocal, then one Newton correction of the quotient
+                // (Markstein), within an ulp of the rounded quotient
+                const float rc = __builtin_amdgcn_rcpf(cvj), q0 = INV_SQRT_H * rc;
+                m2[j] = __builtin_fmaf(__builtin_fmaf(-cvj, q0, INV_SQRT_H), rc, q0);
             }
             bcast_owned(m2[0], m2[1], mult);
         }
@@ -220,30 +234,45 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
             mxr[k] = mx;
         }
         row_minmax16_x4(mnr, mxr);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int row = 4 * rr + k;
-            const float mn = mnr[k], mx = mxr[k];
+        // per token: lane cc = k of each row group computes (S16, Z16) of its row 4 rr + k
+        // (k < 4) and stores them; the rows' 1 / S and -Z / S return to the 16 lanes by
+        // broadcasts. The other lanes' results are not used.
+        float inv4[4], zi4[4];
+        bool clamp;
+        {
+            const float mn = cc == 0 ? mnr[0] : cc == 1 ? mnr[1] : cc == 2 ? mnr[2] : mnr[3];
+            const float mx = cc == 0 ? mxr[0] : cc == 1 ? mxr[1] : cc == 2 ? mxr[2] : mxr[3];
+            const int row = 4 * rr + (cc & 3);
             uint16_t S16 = 0, Z16 = 0;
             if (row < n) {
                 S16 = float_to_half_bits((mx - mn) * (1.0f / LEVELS));
                 Z16 = float_to_half_bits(mn);
             }
             const float Sv = half_bits_to_float(S16), Zv = half_bits_to_float(Z16);
-            if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
+            const bool own = cc < 4;
+            if (own && (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY))) bad |= KVQ_FLAG_SIDE_OVERFLOW;
             const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
             const float zi = -Zv * inv;
+            if (own) reinterpret_cast<uint32_t *>(a.sz)[blk * ZT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
             // (y - Z) / S; cvt_pk_u8 rounds to nearest even and clamps below at 0. The upper
             // clamp changes a code only for a value at or above LEVELS + 1/2, and the map
-            // is monotone (inv >= 0), so only when the row's largest value gets there
+            // is monotone (inv >= 0), so only when a row's largest value gets there; it is
+            // then applied to the whole wave (it leaves every other code as it is)
+            clamp = __ballot(bad != 0 || (own && !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))) != 0;
+            inv4[0] = row_bcast<0>(inv), zi4[0] = row_bcast<0>(zi);
+            inv4[1] = row_bcast<1>(inv), zi4[1] = row_bcast<1>(zi);
+            inv4[2] = row_bcast<2>(inv), zi4[2] = row_bcast<2>(zi);
+            inv4[3] = row_bcast<3>(inv), zi4[3] = row_bcast<3>(zi);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = 4 * rr + k;
             float q[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[k][j], inv, zi);
-            if (bad || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))
+            for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[k][j], inv4[k], zi4[k]);
+            if (clamp)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) q[j] = fminf(q[j], LEVELS);
-            if (cc == 0)
-                reinterpret_cast<uint32_t *>(a.sz)[blk * ZT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
             if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) im[row * ZD + 16 * j + cc] = (uint8_t)__builtin_amdgcn_cvt_pk_u8_f32(q[j], 0, 0);
@@ -284,7 +313,8 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
 bool quantize_t16_supported(int D, int T, const QuantArgs &a) {
     return D == ZD && T == ZT && a.h == ZD && a.G == ZD && a.R == 0 && a.dtype == KVQ_BF16 && a.center == 0 &&
            (a.bits == 2 || a.bits == 3 || a.bits == 4) &&
-           (a.layout == KVQ_TOKEN_MAJOR || a.layout == KVQ_CHANNEL_MAJOR) && a.stride_token < (int64_t(1) << 40) &&
+           (a.layout == KVQ_TOKEN_MAJOR || a.layout == KVQ_CHANNEL_MAJOR) && a.stride_token >= ZD &&
+           a.stride_token < (int64_t(1) << 26) &&
            ((uintptr_t)a.codes & 15) == 0 && ((uintptr_t)a.cnorm & 3) == 0;
 }
 
