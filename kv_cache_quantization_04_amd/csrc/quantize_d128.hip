@@ -293,7 +293,10 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
         const uint16_t c16 = float_to_half_bits(sqrtf(csq));
         const float cv = half_bits_to_float(c16);
         if (!(cv > 0.f && cv < INFINITY)) sideov = true;
-        multsh[tid] = INV_SQRT_H / cv;
+        // reciprocal, then one Newton correction of the quotient (Markstein): within an
+        // ulp of the rounded quotient
+        const float rc = __builtin_amdgcn_rcpf(cv), q0 = INV_SQRT_H * rc;
+        multsh[tid] = __builtin_fmaf(__builtin_fmaf(-cv, q0, INV_SQRT_H), rc, q0);
         // thread id made opaque: the store address is formed here, not hoisted out of
         // the item loop (with two caches' addresses held, they would spill, and a spill
         // reload waits for the prefetch in flight)
@@ -334,31 +337,47 @@ __device__ __forceinline__ void quantize_d128_body(const QuantArgs &ak, const Qu
         mxr[k] = mx;
     }
     row_minmax16_x4(mnr, mxr);
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const int row = rg * R + k;
-        const float mn = mnr[k], mx = mxr[k];
+    // per token: lane cc = k of each row group computes (S16, Z16) of its row rg R + k
+    // and writes them; the rows' 1 / S and -Z / S return to the 16 lanes by broadcasts
+    // (the other lanes' results are not used)
+    float inv4[R], zi4[R];
+    bool clamp;
+    {
+        const float mn = cc == 0 ? mnr[0] : cc == 1 ? mnr[1] : cc == 2 ? mnr[2] : mnr[3];
+        const float mx = cc == 0 ? mxr[0] : cc == 1 ? mxr[1] : cc == 2 ? mxr[2] : mxr[3];
+        const int row = rg * R + (cc & 3);
+        const bool own = cc < 4;
         uint16_t S16 = 0, Z16 = 0;
         if (row < n) {
             S16 = float_to_half_bits((mx - mn) * (1.0f / LEVELS));
             Z16 = float_to_half_bits(mn);
         }
         const float Sv = half_bits_to_float(S16), Zv = half_bits_to_float(Z16);
-        if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) sideov = true;
+        if (own && (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY))) sideov = true;
         const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
         const float zi = -Zv * inv;
+        if (own) szbuf[row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         // (y - Z) / S; cvt_pk_u8 rounds to nearest even and clamps below at 0. The upper
         // clamp changes a code only for a value at or above LEVELS + 1/2 (below it the
         // rounding gives at most LEVELS), and the map is monotone (inv >= 0), so only when
-        // the row's largest value gets there: fp16 rounding of S and Z far larger than
-        // usual (an offset much larger than the range), or a non-finite value
+        // a row's largest value gets there: fp16 rounding of S and Z far larger than
+        // usual (an offset much larger than the range), or a non-finite value. It is then
+        // applied to the whole wave (it leaves every other code as it is).
+        clamp = __ballot(nonfinite || sideov || (own && !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))) != 0;
+        inv4[0] = row_bcast<0>(inv), zi4[0] = row_bcast<0>(zi);
+        inv4[1] = row_bcast<1>(inv), zi4[1] = row_bcast<1>(zi);
+        inv4[2] = row_bcast<2>(inv), zi4[2] = row_bcast<2>(zi);
+        inv4[3] = row_bcast<3>(inv), zi4[3] = row_bcast<3>(zi);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int row = rg * R + k;
         float q[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[k][j], inv, zi);
-        if (nonfinite || sideov || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))
+        for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[k][j], inv4[k], zi4[k]);
+        if (clamp)
 #pragma unroll
             for (int j = 0; j < 8; ++j) q[j] = fminf(q[j], LEVELS);
-        if (cc == 0) szbuf[row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         if constexpr (LAYOUT == KVQ_TOKEN_MAJOR) {
             // the lane's channel pairs 32 u + 2 cc + {0, 1}: one byte each (4-bit, the
             // even channel in the low nibble); 2-bit: the pair's nibble, joined with the

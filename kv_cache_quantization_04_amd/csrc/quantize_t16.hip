@@ -52,12 +52,6 @@ __device__ __forceinline__ Rows load_rows(const QuantArgs &a, int item, int lane
     return r;
 }
 
-// Value of lane K of the lane's 16-lane row (ds_swizzle broadcast: LDS crossbar, no VALU slot).
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x10 | (K << 5)));
-}
-
 // The values of the lane's 8 local channels (t = 0..7, channel 16 t + (lane & 15)) from
 // their owners: after the column-sum swaps, lane (cc, rr) holds local channels 2 rr and
 // 2 rr + 1 (o0, o1). The swaps of rows 16 lanes apart give every lane of a 32-lane

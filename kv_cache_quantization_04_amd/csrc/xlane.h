@@ -22,6 +22,13 @@ __device__ __forceinline__ float swz_xor(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
 }
 
+// Value of lane K of the lane's 16-lane row (ds_swizzle broadcast mode: and-mask 0x10,
+// or-mask K within each 32-lane group).
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x10 | (K << 5)));
+}
+
 // Walsh-Hadamard butterflies over the 16 lanes of a DPP row, all in DPP-fused
 // FMAs, t <- t + s partner: stage 1 pairs lane l with l ^ 15 (row mirror, s = -1
 // on lanes with bit 3 set), stage 2 with l ^ 7 (half-row mirror, bit 2), stage 3
