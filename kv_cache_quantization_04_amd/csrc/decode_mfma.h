@@ -3,6 +3,8 @@
 // images and their prefetch.
 #pragma once
 
+#include "xlane.h"
+
 #include "common.h"
 #include "launch.h"
 
@@ -73,16 +75,10 @@ __device__ __forceinline__ void split_prod(float a, float b, _Float16 &hi, _Floa
     lo = (_Float16)__builtin_fmaf(a, b, -(float)hi);
 }
 
-__device__ __forceinline__ float xlane_sum_q(float v) {  // sum over the 4 lanes sharing lane & 15
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-__device__ __forceinline__ float xlane_max_q(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
-}
+// Sum / max over the 4 lanes sharing lane & 15, by permlane swaps (VALU, no LDS
+// round trip on the dependency chain); every lane gets the same bits.
+__device__ __forceinline__ float xlane_sum_q(float v) { return sum_x4rows(v); }
+__device__ __forceinline__ float xlane_max_q(float v) { return max_x4rows(v); }
 
 // The 24 bits of eight 3-bit codes starting at byte-aligned bit `bit0`
 // (three byte loads: never reads past the chunk).
@@ -139,28 +135,42 @@ struct Chunks {
     uint4 v[N];
 };
 
-// This lane's 16-byte chunks lane + 64 k of the page image of block `blk`
-// (branch-free sources; lanes past the image re-read its last chunk, unused).
+// Where this lane's 16-byte chunks lane + 64 k of a page image come from: chunk k of
+// block blk is at base[k] + blk * stride[k] (the region the chunk falls in, resolved
+// once per kernel; lanes past the image re-read its last chunk, unused).
 template <int T, int KB, int VB>
-__device__ __forceinline__ Chunks<PageImage<T, KB, VB>::NPRE> fetch_page(const DecodeArgs &a, int64_t blk, int lane) {
+struct PageSrc {
+    static constexpr int N = PageImage<T, KB, VB>::NPRE;
+    uint64_t base[N];
+    uint32_t stride[N];
+};
+template <int T, int KB, int VB>
+__device__ __forceinline__ PageSrc<T, KB, VB> page_src(const DecodeArgs &a, int lane) {
     using PI = PageImage<T, KB, VB>;
-    const uint8_t *kc = a.kcodes + blk * PI::KC, *vc = a.vcodes + blk * PI::VC;
-    const uint8_t *ksz = reinterpret_cast<const uint8_t *>(a.ksz) + blk * PI::SZ;
-    const uint8_t *vsz = reinterpret_cast<const uint8_t *>(a.vsz) + blk * PI::SZ;
-    const uint8_t *kcn = reinterpret_cast<const uint8_t *>(a.kcn) + blk * PI::CN;
-    const uint8_t *vcn = reinterpret_cast<const uint8_t *>(a.vcn) + blk * PI::CN;
-    Chunks<PI::NPRE> r;
+    PageSrc<T, KB, VB> r;
 #pragma unroll
     for (int k = 0; k < PI::NPRE; ++k) {
         const int off = min(1024 * k + 16 * lane, PI::BYTES - 16);
-        uintptr_t src = (uintptr_t)(kc + off);
-        src = off >= PI::O_KSZ ? (uintptr_t)(ksz + (off - PI::O_KSZ)) : src;
-        src = off >= PI::O_KCN ? (uintptr_t)(kcn + (off - PI::O_KCN)) : src;
-        src = off >= PI::O_VC ? (uintptr_t)(vc + (off - PI::O_VC)) : src;
-        src = off >= PI::O_VSZ ? (uintptr_t)(vsz + (off - PI::O_VSZ)) : src;
-        src = off >= PI::O_VCN ? (uintptr_t)(vcn + (off - PI::O_VCN)) : src;
-        r.v[k] = *reinterpret_cast<const uint4 *>(src);
+        uintptr_t src = (uintptr_t)(a.kcodes + off);
+        uint32_t st = PI::KC;
+        if (off >= PI::O_KSZ) src = (uintptr_t)a.ksz + (off - PI::O_KSZ), st = PI::SZ;
+        if (off >= PI::O_KCN) src = (uintptr_t)a.kcn + (off - PI::O_KCN), st = PI::CN;
+        if (off >= PI::O_VC) src = (uintptr_t)a.vcodes + (off - PI::O_VC), st = PI::VC;
+        if (off >= PI::O_VSZ) src = (uintptr_t)a.vsz + (off - PI::O_VSZ), st = PI::SZ;
+        if (off >= PI::O_VCN) src = (uintptr_t)a.vcn + (off - PI::O_VCN), st = PI::CN;
+        r.base[k] = src;
+        r.stride[k] = st;
     }
+    return r;
+}
+
+// This lane's chunks of the page image of block `blk` (blk < 2^32, checked at launch).
+template <int T, int KB, int VB>
+__device__ __forceinline__ Chunks<PageImage<T, KB, VB>::NPRE> fetch_page(const PageSrc<T, KB, VB> &ps, uint32_t blk) {
+    Chunks<PageImage<T, KB, VB>::NPRE> r;
+#pragma unroll
+    for (int k = 0; k < PageImage<T, KB, VB>::NPRE; ++k)
+        r.v[k] = *reinterpret_cast<const uint4 *>(ps.base[k] + (uint64_t)blk * ps.stride[k]);
     return r;
 }
 

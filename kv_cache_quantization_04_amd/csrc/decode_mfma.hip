@@ -68,6 +68,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     float(*red_ml)[16][2] = reinterpret_cast<float(*)[16][2]>(pool + RED_O);
 
     const int tid = threadIdx.x, lane = tid & 63;
+    const PageSrc<T, KB, VB> psrc = page_src<T, KB, VB>(a, lane);  // staged path: chunk sources
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint8_t *stg = pool + wave * (LDSPAGE ? PI::BYTES : 0);  // this wave's page image
     uint8_t *stg2 = pool2 + wave * (DB ? PI::BYTES : 0);     // its second image (DB)
@@ -140,7 +141,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     // the compiler cannot count the outstanding loads past a conditional request)
     if constexpr (STAGED) {
         if (pi < p1) {
-            pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);
+            pre = fetch_page(psrc, (uint32_t)(page_of(pi) * a.Hkv + hk));
             wait_vm_upto<PI::NPRE>();
         } else {
             wait_vm_upto<0>();
@@ -260,7 +261,7 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
                     *reinterpret_cast<uint4 *>(&wrk[wave][16 * c4]) = r;
                 }
             }
-            if (pi < p1) pre = fetch_page<T, KB, VB>(a, (int64_t)page_of(pi) * a.Hkv + hk, lane);  // travels meanwhile
+            if (pi < p1) pre = fetch_page(psrc, (uint32_t)(page_of(pi) * a.Hkv + hk));  // travels meanwhile
         }
         const int rows = min(T, Lc - cur * T);  // valid tokens of this column (may be <= 0 in PF)
         const int64_t kblk = (int64_t)page * a.Hkv + hk;
@@ -582,6 +583,7 @@ bool decode_mfma_supported(const DecodeArgs &a) {
     if (a.grp > 16 || 16 % a.grp != 0 || a.hc != a.grp) return false;
     if (a.klayout != KVQ_TOKEN_MAJOR || a.vlayout != KVQ_CHANNEL_MAJOR || a.vH != a.Hkv) return false;
     if (!(a.kbits >= 2 && a.kbits <= 4) || !(a.vbits >= 2 && a.vbits <= 4)) return false;
+    if ((int64_t)a.num_pages * a.Hkv >= (int64_t(1) << 31)) return false;  // 32-bit block ids
     return a.T == 16 || a.T == 32 || a.T == 64 || a.T == 128;
 }
 

@@ -43,6 +43,7 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
     float(*red_ml)[16][2] = reinterpret_cast<float(*)[16][2]>(pool + RED_O);
 
     const int tid = threadIdx.x, lane = tid & 63;
+    const PageSrc<T, KB, VB> psrc = page_src<T, KB, VB>(a, lane);  // chunk sources of a page image
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint8_t *img0 = pool + wave * 2 * PI::BYTES;  // page A image; page B's follows it
     const int l16 = lane & 15, lq = lane >> 4;
@@ -87,9 +88,9 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
     int pb = pa < p1 ? next_valid(pa + 4) : p1;
     Chunks<PI::NPRE> preA{}, preB{};
     if (pa < p1) {
-        preA = fetch_page<T, KB, VB>(a, (int64_t)page_of(pa) * a.Hkv + hk, lane);
+        preA = fetch_page(psrc, (uint32_t)(page_of(pa) * a.Hkv + hk));
         if (pb < p1) {
-            preB = fetch_page<T, KB, VB>(a, (int64_t)page_of(pb) * a.Hkv + hk, lane);
+            preB = fetch_page(psrc, (uint32_t)(page_of(pb) * a.Hkv + hk));
             wait_vm_upto<2 * PI::NPRE>();
         } else {
             preB = preA;
@@ -205,8 +206,8 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
                 }
         }
         if (pa < p1) {  // the next pair travels meanwhile
-            preA = fetch_page<T, KB, VB>(a, (int64_t)page_of(pa) * a.Hkv + hk, lane);
-            if (pb < p1) preB = fetch_page<T, KB, VB>(a, (int64_t)page_of(pb) * a.Hkv + hk, lane);
+            preA = fetch_page(psrc, (uint32_t)(page_of(pa) * a.Hkv + hk));
+            if (pb < p1) preB = fetch_page(psrc, (uint32_t)(page_of(pb) * a.Hkv + hk));
             else preB = preA;
         }
         // valid tokens of this lane's column page (0: the missing page B)
