@@ -30,7 +30,7 @@
 namespace kvq {
 
 template <int KB, int VB>
-__global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     constexpr int T = 16;
     using PI = PageImage<T, KB, VB>;
     constexpr int KCB = 32 * KB / 8;  // bytes of one lane's 32-channel K chunk
@@ -205,11 +205,6 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
                     *reinterpret_cast<uint4 *>(&wrk[wave][h2][16 * c4]) = r;
                 }
         }
-        if (pa < p1) {  // the next pair travels meanwhile
-            preA = fetch_page(psrc, (uint32_t)(page_of(pa) * a.Hkv + hk));
-            if (pb < p1) preB = fetch_page(psrc, (uint32_t)(page_of(pb) * a.Hkv + hk));
-            else preB = preA;
-        }
         // valid tokens of this lane's column page (0: the missing page B)
         const int rows = half ? (curB < p1 ? min(T, L - curB * T) : 0) : min(T, L - curA * T);
         const uint8_t *own = img0 + half * PI::BYTES;  // the column's page image
@@ -222,43 +217,42 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < KB; ++i) kw[h2][i] = reinterpret_cast<const uint32_t *>(row)[i];
         }
-        // c_K of the lane's 32 channels on its column's page
-        uint32_t cw[16];
-        {
-            const uint4 *cp = reinterpret_cast<const uint4 *>(&own[PI::O_KCN + 64 * lq]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = cp[i];
-                cw[4 * i] = v.x; cw[4 * i + 1] = v.y; cw[4 * i + 2] = v.z; cw[4 * i + 3] = v.w;
-            }
-        }
-        // q' = qbar o c_K for the column's page, scaled by 2^sq, as fp16 hi + lo
-        float qt[32];
+        // q' = qbar o c_K for the column's page (c_K of the lane's 32 channels), scaled by
+        // 2^sq, as fp16 hi + lo: one pass for sum_j q'_j and max |q'_j| (the scale), a
+        // second that recomputes each product for its split (no array of q' kept live)
+        const uint4 *cp = reinterpret_cast<const uint4 *>(&own[PI::O_KCN + 64 * lq]);
         float qc = 0.f, qmax = 0.f;
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+        for (int st = 0; st < 4; ++st) {
+            const uint4 v = cp[st];
+            const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const half2v c2 = as_h2(cw[st * 4 + (e >> 1)]);
+                const half2v c2 = as_h2(cw[e >> 1]);
                 const float x = mul_h((e & 1) ? c2.y : c2.x, qv[st * 8 + e]);
-                qt[st * 8 + e] = x;
                 qc += x;
                 qmax = fmaxf(qmax, fabsf(x));
             }
+        }
         qc = xlane_sum_q(qc);
         const float qsc = pow2_scale_for(xlane_max_q(qmax));
         const float qinv = pow2_over<CODE_EXP<KB>>(qsc);
         half8 qhi[4], qlo[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+        for (int st = 0; st < 4; ++st) {
+            uint4 v = cp[st];
+            asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));  // not merged with the first pass
+            const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const int e = (kk >> 1) + 4 * (kk & 1);
+                const half2v c2 = as_h2(cw[e >> 1]);
                 _Float16 hi, lo;
-                split_prod(qt[st * 8 + e], qsc, hi, lo);
+                split_prod(mul_h((e & 1) ? c2.y : c2.x, qv[st * 8 + e]), qsc, hi, lo);
                 qhi[st][kk] = hi;
                 qlo[st][kk] = lo;
             }
+        }
 
         // ---- scores: one MFMA chain per page; each column keeps its own page's
         f32x4 scp[2];
@@ -282,6 +276,13 @@ __global__ void __launch_bounds__(MNT) decode_pair16_kernel(DecodeArgs a) {
         f32x4 sc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[i] = half ? scp[1][i] : scp[0][i];
+        // the next pair travels during the softmax and the value product (issued here,
+        // after the query fold, so that its registers are not live across the fold)
+        if (pa < p1) {
+            preA = fetch_page(psrc, (uint32_t)(page_of(pa) * a.Hkv + hk));
+            if (pb < p1) preB = fetch_page(psrc, (uint32_t)(page_of(pb) * a.Hkv + hk));
+            else preB = preA;
+        }
 
         // ---- online softmax over the column's page
         const float a_s = sml2 * qinv, a_z = sml2 * qc;
