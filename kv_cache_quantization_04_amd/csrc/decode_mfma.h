@@ -169,8 +169,13 @@ template <int T, int KB, int VB>
 __device__ __forceinline__ Chunks<PageImage<T, KB, VB>::NPRE> fetch_page(const PageSrc<T, KB, VB> &ps, uint32_t blk) {
     Chunks<PageImage<T, KB, VB>::NPRE> r;
 #pragma unroll
-    for (int k = 0; k < PageImage<T, KB, VB>::NPRE; ++k)
-        r.v[k] = *reinterpret_cast<const uint4 *>(ps.base[k] + (uint64_t)blk * ps.stride[k]);
+    for (int k = 0; k < PageImage<T, KB, VB>::NPRE; ++k) {
+        // a global-memory load (an integer address alone would make it a flat load, which
+        // also holds the LDS counter until it returns)
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)(ps.base[k] + (uint64_t)blk * ps.stride[k]);
+        r.v[k] = uint4{v.x, v.y, v.z, v.w};
+    }
     return r;
 }
 
