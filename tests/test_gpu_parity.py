@@ -108,6 +108,52 @@ def test_quantize_centered_every_element(gpu, case):
     check_quantize_case(gpu, case, center=1)
 
 
+# Source rows just past a tile's valid ones hold NaN (and the latent tiles' rope part
+# too): a kernel that read them would change codes or side data or raise a flag.
+POISON = [
+    (128, 16, 3, 128, 128, 2, "bf16", 0, 0),
+    (128, 16, 3, 128, 128, 2, "bf16", 1, 0),
+    (128, 128, 4, 128, 128, 4, "bf16", 0, 0),
+    (128, 64, 2, 128, 128, 2, "bf16", 1, 0),
+    (512, 128, 4, 512, 512, 4, "bf16", 0, 64),
+    (64, 64, 4, 64, 64, 4, "f32", 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", POISON, ids=lambda c: "D{}T{}b{}G{}h{}N{}{}L{}R{}".format(*c))
+def test_quantize_ignores_rows_past_the_valid_ones(gpu, case):
+    D, T, bits, G, h, iters, dtype, layout, R = case
+    log("poisoned padding rows", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 7)
+    f = W.Fmt(D, R, T, h, G, bits, iters, layout)
+    H = 2
+    lens = [T + 5, 1, T - 1, 2 * T + 3]
+    tst, tv, tp = [], [], []
+    rows, start = [], 0
+    for L in lens:  # each sequence followed by T rows of NaN
+        x = heavy(rng, L, H, D)
+        if R:
+            x = np.concatenate([x, rng.standard_normal((L, H, R))], axis=2)
+        rows += [x, np.full((T, H, D + R), np.nan)]
+        for p0 in range(0, L, T):
+            tst.append(start + p0)
+            tv.append(min(T, L - p0))
+        start += L + T
+    src = make_src(np.concatenate(rows, axis=0), dtype)
+    tst, tv = np.array(tst), np.array(tv)
+    tp = rng.permutation(len(tst))
+    P = len(tp)
+    flags = torch.zeros(1, dtype=torch.int32, device=gpu)
+    log("  kernel", K.kv_quantize_kernel_name(K.DeviceCache(kfmt(f), P, H), to_dev(src, dtype)))
+    dc = gpu_quantize(f, src, dtype, tst, tv, tp, P, flags=flags)
+    torch.cuda.synchronize()
+    hc, fl = orc_quantize(f, src, dtype, tst, tv, tp, P)
+    st = compare_blocks(host_copy(dc, f), hc, range(P))
+    log("  stats", st)
+    assert_block_parity(st, str(case))
+    assert int(flags.item()) == fl == 0
+
+
 def check_quantize_case(gpu, case, center=0):
     D, T, bits, G, h, iters, dtype, layout, R = case
     log("quantize case", case, "center", center)
