@@ -167,6 +167,12 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) qv[i] *= qscale;
     }
+    // max |qbar| of the lane's head (all 128 channels): with the page's largest c_K it
+    // bounds max |q'|, which sets the power-of-two scaling of the query fold
+    float qvmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qvmax = fmaxf(qvmax, fabsf(qv[i]));
+    qvmax = xlane_max_q(qvmax);
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     float m_run = -INFINITY, l_run = 0.f;
@@ -218,41 +224,45 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
             for (int i = 0; i < KB; ++i) kw[h2][i] = reinterpret_cast<const uint32_t *>(row)[i];
         }
         // q' = qbar o c_K for the column's page (c_K of the lane's 32 channels), scaled by
-        // 2^sq, as fp16 hi + lo: one pass for sum_j q'_j and max |q'_j| (the scale), a
-        // second that recomputes each product for its split (no array of q' kept live)
+        // 2^sq so that the bound max |qbar| max c_K lands in [2^14, 2^15), as fp16 hi + lo;
+        // sum_j q'_j accumulates on the way. The normalizers are >= 0: their largest is the
+        // largest fp16 bit pattern (packed u16 maxima).
         const uint4 *cp = reinterpret_cast<const uint4 *>(&own[PI::O_KCN + 64 * lq]);
-        float qc = 0.f, qmax = 0.f;
+        float cmax;
+        {
+            u16x2 m = {0, 0};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint4 v = cp[st];
-            const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const half2v c2 = as_h2(cw[e >> 1]);
-                const float x = mul_h((e & 1) ? c2.y : c2.x, qv[st * 8 + e]);
-                qc += x;
-                qmax = fmaxf(qmax, fabsf(x));
+            for (int st = 0; st < 4; ++st) {
+                const uint4 v = cp[st];
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.x));
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.y));
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.z));
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.w));
             }
+            cmax = xlane_max_q(half_bits_to_float(m.x > m.y ? m.x : m.y));
         }
-        qc = xlane_sum_q(qc);
-        const float qsc = pow2_scale_for(xlane_max_q(qmax));
+        const float qsc = pow2_scale_for(qvmax * cmax);
         const float qinv = pow2_over<CODE_EXP<KB>>(qsc);
+        float qc = 0.f;
         half8 qhi[4], qlo[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             uint4 v = cp[st];
-            asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));  // not merged with the first pass
+            asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));  // re-read: not held from the maximum
             const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const int e = (kk >> 1) + 4 * (kk & 1);
                 const half2v c2 = as_h2(cw[e >> 1]);
+                const float x = mul_h((e & 1) ? c2.y : c2.x, qv[st * 8 + e]);
+                qc += x;
                 _Float16 hi, lo;
-                split_prod(mul_h((e & 1) ? c2.y : c2.x, qv[st * 8 + e]), qsc, hi, lo);
+                split_prod(x, qsc, hi, lo);
                 qhi[st][kk] = hi;
                 qlo[st][kk] = lo;
             }
         }
+        qc = xlane_sum_q(qc);
 
         // ---- scores: one MFMA chain per page; each column keeps its own page's
         f32x4 scp[2];
