@@ -8,10 +8,12 @@
 // 16 j + (l & 15), j = 0..7. The 16 lanes of a DPP row thus cover one token's 128
 // channels, and all per-token reductions are row operations. Column sums finish
 // inside the wave (permlane swaps across the four row groups) and the per-channel
-// factors go back to the four row groups by the reverse swaps (no LDS round trip). Codes go to a per-wave LDS byte image in
-// bitstream order (token-major t * 128 + j, channel-major j * 16 + t); each lane then
-// packs 32 consecutive codes into the little-endian bitstream, and the block leaves
-// with one store per lane. The next tile is loaded into registers meanwhile.
+// factors go back to the four row groups by the reverse swaps (no LDS round trip).
+// Per-token scale and zero are computed by one lane per row and broadcast. Codes go
+// to a per-wave LDS byte image in bitstream order (token-major t * 128 + j,
+// channel-major j * 16 + t); each lane then packs 32 consecutive codes into the
+// little-endian bitstream, and the block leaves with one store per lane. The next
+// tile is loaded into registers meanwhile.
 //
 // Method: "KVarN" project review, Key Features ("Variance-Normalized
 // Quantization Pipeline"): rotate, run row/column RMS normalization rounds,
