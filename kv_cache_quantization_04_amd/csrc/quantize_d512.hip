@@ -263,7 +263,10 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
             const uint16_t c16 = float_to_half_bits(sqrtf(csq));
             const float cv = half_bits_to_float(c16);
             if (!(cv > 0.f && cv < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
-            lds_store_f32(&multsh[pch(tid)], INV_SQRT_H / cv);
+            // reciprocal, then one Newton correction of the quotient (Markstein): within an
+            // ulp of the rounded quotient
+            const float rc = __builtin_amdgcn_rcpf(cv), q0 = INV_SQRT_H * rc;
+            lds_store_f32(&multsh[pch(tid)], __builtin_fmaf(__builtin_fmaf(-cv, q0, INV_SQRT_H), rc, q0));
             a.cnorm[blk * LD + tid] = c16;
         }
         lds_barrier();
@@ -293,28 +296,46 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
             mxr[k] = mx;
         }
         row_minmax16_x4(mnr, mxr);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int row = 4 * rg + k;
-            const float mn = mnr[k], mx = mxr[k];
+        // per token: lane cc = k of each row group computes (S16, Z16) of its row 4 rg + k
+        // (k < 4) and writes them; the rows' 1 / S and -Z / S return to the 16 lanes by
+        // broadcasts (the other lanes' results are not used)
+        float inv4[4], zi4[4];
+        bool clamp;
+        {
+            const float mn = cc == 0 ? mnr[0] : cc == 1 ? mnr[1] : cc == 2 ? mnr[2] : mnr[3];
+            const float mx = cc == 0 ? mxr[0] : cc == 1 ? mxr[1] : cc == 2 ? mxr[2] : mxr[3];
+            const int row = 4 * rg + (cc & 3);
+            const bool own = cc < 4;
             uint16_t S16 = 0, Z16 = 0;
             if (row < n) {
                 S16 = float_to_half_bits((mx - mn) * (1.0f / LEVELS));
                 Z16 = float_to_half_bits(mn);
             }
             const float Sv = half_bits_to_float(S16), Zv = half_bits_to_float(Z16);
-            if (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
+            if (own && (!(Sv < INFINITY) || !(fabsf(Zv) < INFINITY))) bad |= KVQ_FLAG_SIDE_OVERFLOW;
             const float inv = Sv != 0.f ? __builtin_amdgcn_rcpf(Sv) : 0.f;
             const float zi = -Zv * inv;
+            if (own) reinterpret_cast<uint32_t *>(a.sz)[blk * LT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
             // (y - Z) / S; v_cvt_pk_u8_f32 rounds to nearest even and clamps below at 0.
             // The upper clamp changes a code only for a value at or above LEVELS + 1/2, and
-            // the map is monotone (inv >= 0), so only when the row's largest value gets there
+            // the map is monotone (inv >= 0), so only when a row's largest value gets there
             // (fp16 rounding of S and Z far larger than usual, or a non-finite value): the
-            // packing runs in one of two copies, with and without it
-            auto pack_row = [&](auto clamp) {
+            // packing runs in one of two copies, with and without it, chosen for the whole
+            // wave (the clamp leaves every other code as it is)
+            clamp = __ballot(bad != 0 || (own && !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f))) != 0;
+            inv4[0] = row_bcast<0>(inv), zi4[0] = row_bcast<0>(zi);
+            inv4[1] = row_bcast<1>(inv), zi4[1] = row_bcast<1>(zi);
+            inv4[2] = row_bcast<2>(inv), zi4[2] = row_bcast<2>(zi);
+            inv4[3] = row_bcast<3>(inv), zi4[3] = row_bcast<3>(zi);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = 4 * rg + k;
+            const float inv = inv4[k], zi = zi4[k];
+            auto pack_row = [&](auto clamp_c) {
                 auto code = [&](float v) {
                     const float q = __builtin_fmaf(v, inv, zi);
-                    return decltype(clamp)::value ? fminf(q, LEVELS) : q;
+                    return decltype(clamp_c)::value ? fminf(q, LEVELS) : q;
                 };
                 uint32_t word[BITS];
                 if constexpr (BITS == 4) {
@@ -343,9 +364,8 @@ __device__ __forceinline__ void quantize_d512_body(const QuantArgs &a, int num_i
                     *reinterpret_cast<uint2 *>(codes + row * (LD / 4) + 8 * pcc) = uint2{word[0], word[1]};
                 }
             };
-            if (bad || !(__builtin_fmaf(mx, inv, zi) < LEVELS + 0.5f)) pack_row(std::true_type{});
+            if (clamp) pack_row(std::true_type{});
             else pack_row(std::false_type{});
-            if (cc == 0) reinterpret_cast<uint32_t *>(a.sz)[blk * LT + row] = (uint32_t)S16 | ((uint32_t)Z16 << 16);
         }
         if (a.R == 64) {
 #pragma unroll
