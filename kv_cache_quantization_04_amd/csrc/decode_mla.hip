@@ -1,7 +1,7 @@
-// Split-K decode attention over a quantized MLA latent cache with MFMA (gfx950):
-// 512 latent channels (4-bit codes, token-major, one scale group per token),
-// a 64-channel bf16 rope part, 128-token pages, and query heads that share one
-// latent per kv head (absorbed MLA: the latent is both key and value).
+// Split-K decode attention over a quantized MLA latent cache on the int8 matrix
+// cores (gfx950): 512 latent channels (4-bit codes, token-major, one scale group
+// per token), a 64-channel bf16 rope part, 128-token pages, and query heads that
+// share one latent per kv head (absorbed MLA: the latent is both key and value).
 //
 // Method: "KVarN" project review, Key Features (rotation, normalization rounds,
 // asymmetric RTN with fp16 scale/zero/normalizer); the decode folds the rotation
@@ -10,22 +10,35 @@
 // Per page, with qbar = q Q over the latent, q'_j = qbar_j c_j (c of this page):
 //   score_t = sm * ( S_t * [A . q']_t + Z_t * sum_j q'_j + <q_rope, k_rope_t> )
 //   o'_j   += c_j * ( [A^T . P~]_j + sum_t p_t Z_t ),  P~_t = p_t S_t
-// with A the codes, exact in fp16 (as subnormals n 2^-18). Both products run as
-// v_mfma_f32_16x16x32_f16 with q' and P~ split into fp16 hi + lo parts after a
-// power-of-two scaling; the rope product runs as v_mfma_f32_16x16x32_bf16 with
-// the query's rope part split into bf16 hi + lo.
+// with A the codes (integers 0..15). Both products run on
+// v_mfma_i32_16x16x64_i8: the codes are exact int8 operands, and q' and P~ enter
+// as 16-bit fixed-point integers (a power-of-two scale per page puts the largest
+// possible magnitude just under 2^15 for q', 2^14 for P~) split into two signed
+// int8 limbs x = 256 s1 + s0, each limb its own product, the two joined in int32
+// (exact). One mixed-precision FMA against the constant 1.5 2^23 (+128) rounds
+// a product to that integer and leaves it, biased by 128, in the low 16 bits of
+// the result: its bytes are the limbs. sum_j q'_j is taken from the same rounded
+// integers (v_dot4 on the limbs), so the rounding enters the score as
+// sum_j d_j (S_t a_tj + Z_t), an error on the centered key. The rope product runs
+// as v_mfma_f32_16x16x32_bf16 (query rope part split into bf16 hi + lo unless
+// the query is bf16).
+//
+// Per page the workgroup unpacks the 4-bit codes once into an int8 image in LDS
+// (token rows of 512 bytes, 16-byte slots XOR-swizzled); the score product reads
+// it row-wise (16 channels of one token per lane), the value product through
+// ds_read_b64_tr_b8 (8 tokens of one channel per lane and read), both without
+// unpacking in the waves.
 //
 // Work split: a workgroup (8 waves) serves 64 query heads of one (sequence,
-// kv head, page range). Waves w and w + 4 own the same 16 heads, which form the
-// N dimension of every tile, and split the latent: wave half h = w / 4 takes
-// channels 256 h .. 256 h + 255 of the score product (and rope half h), and the
-// same channels of the value product. The two partial scores meet through LDS;
-// both waves then run the same softmax. Scores are computed transposed (tokens
-// x heads), so the probability tile lands, lane for lane, in the B operand of
-// the value product (latent x heads); that product's A operand (the latent
-// transposed to 16 tokens of one channel per lane) comes from LDS by
-// ds_read_b64_tr_b4. Each thread prefetches its share of the next page into
-// registers while the current page is processed from LDS.
+// kv head, page range). Waves w and w + 4 own the same 16 heads (the N dimension
+// of every tile) and split the latent: wave half h = w / 4 takes channels
+// 256 h .. 256 h + 255 of both products (and rope half h). The two partial scores
+// meet through LDS; both waves then run the same softmax. Scores are computed
+// transposed (tokens x heads): lane (head l16, group lq) holds tokens
+// 16 j + 4 lq + i of tile j, which is the B operand layout of the value product
+// with K-step k taking tiles 4 k .. 4 k + 3. The next page's codes, scales and
+// normalizers are copied HBM -> LDS staging by direct-to-LDS loads during the
+// current page's scores, its rope part after them.
 #include "common.h"
 #include "launch.h"
 #include "xlane.h"
@@ -39,31 +52,12 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// a * b with a an fp16 value: one mixed-precision FMA (v_fma_mix_f32) instead of a
-// conversion and a multiply
-__device__ __forceinline__ float mul_h(_Float16 a, float b) { return __builtin_fmaf((float)a, b, 0.f); }
-// fp16 hi + lo parts of the product a b: hi = f16(a b), lo = f16(a b - hi). Each is
-// one mixed-precision FMA (v_fma_mixlo/mixhi_f16: b may be an fp16 value, the product
-// is formed exactly inside the FMA), so lo carries the exact residual of hi.
-__device__ __forceinline__ void split_prod(float a, float b, _Float16 &hi, _Float16 &lo) {
-    hi = (_Float16)__builtin_fmaf(a, b, 0.f);
-    lo = (_Float16)__builtin_fmaf(a, b, -(float)hi);
-}
-// largest of the fp16 values (all >= 0) in the low and high halves of four words,
-// taken on the bit patterns (the order of non-negative fp16 values)
-__device__ __forceinline__ float max_h8(const uint32_t (&w)[4]) {
-    u16x2 m = __builtin_bit_cast(u16x2, w[0]);
-#pragma unroll
-    for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i]));
-    return half_bits_to_float(m.x > m.y ? m.x : m.y);
-}
 
 constexpr int XD = 512;    // latent channels
 constexpr int XR = 64;     // rope channels
@@ -71,56 +65,96 @@ constexpr int XT = 128;    // tokens per page
 constexpr int XNT = 512;   // threads per workgroup (8 waves)
 constexpr int XHG = 64;    // query heads per workgroup
 
-// LDS image of one page (bytes). Codes: token row r (256 B) holds its 16-byte
-// chunk g at slot g ^ swz(r); rope: row r (128 B) holds chunk g at slot g ^ rswz(r);
-// (S, Z) pairs and the normalizer in natural order.
-constexpr int L_CODES = 0;
-constexpr int L_ROPE = XT * XD / 2;             // 32768
-constexpr int L_SZ = L_ROPE + XT * XR * 2;      // 49152
-constexpr int L_CN = L_SZ + XT * 4;             // 49664
-constexpr int L_BYTES = L_CN + XD * 2;          // 50688
-constexpr int NCHUNK = L_BYTES / 16;            // 3168 16-byte chunks per page
-constexpr int CPT = (NCHUNK + XNT - 1) / XNT;   // 7 chunks per thread in the staging copy
-constexpr int NDMA = (NCHUNK + 63) / 64;        // 50 wave-wide direct-to-LDS copies per page
-// shared memory: staging image (natural chunk order, written by direct-to-LDS
-// copies), working image (swizzled), score exchange [pair][33][64] floats, and
-// each wave's rope query (bf16 hi / lo words, lane-major): 151552 bytes
-constexpr int XCH_WORDS = 33 * 64;
+// Staging image of the next page (direct-to-LDS copies, natural chunk order):
+// codes (token rows of 256 B), (S, Z) fp16 pairs per token, normalizer c.
+constexpr int S_SZ = XT * XD / 2;           // 32768
+constexpr int S_CN = S_SZ + XT * 4;         // 33280
+constexpr int S_BYTES = S_CN + XD * 2;      // 34304
+constexpr int S_CHUNKS = S_BYTES / 16;      // 2144 16-byte chunks
+constexpr int S_COPIES = (S_CHUNKS + 63) / 64;  // 34 wave-wide copies
+// Rope image (bf16 rows of 128 B; chunk g of row r at slot g ^ rswz(r), placed by
+// the copy's source addresses): 1024 chunks, 16 wave-wide copies.
+constexpr int R_BYTES = XT * XR * 2;
+constexpr int R_COPIES = R_BYTES / 1024;
+// Working image: int8 codes (token rows of 512 B, 16-channel slot g of row r at
+// g ^ i8swz(r), bytes of a slot in channel order pi), (S, Z), normalizer in the
+// same per-16-channel order pi.
+constexpr int W_SZ = XT * XD;               // 65536
+constexpr int W_CN = W_SZ + XT * 4;         // 66048
+constexpr int W_BYTES = W_CN + XD * 2;      // 67072
+constexpr int XCH_WORDS = 32 * 64;          // partial scores of one wave pair (32 per lane)
 
-// Slot swizzle of a code row: the 16 rows read together by either product land
-// in 16 different 16-byte slots (rows 4b + i + 16 q of a score tile, and rows
-// 16 lq + i of a transposed read).
-__device__ __forceinline__ int swz(int r) { return (r & 15) ^ ((r >> 2) & 12); }
-// Rope rows are 128 B, two to a bank window: the 16 rows of a score tile (rows
-// 4 b + i + 16 q) differ in (r & 1, rswz(r)).
-__device__ __forceinline__ int rswz(int r) { return ((r >> 1) & 1) | ((r >> 3) & 6); }
+// Byte p of an int8 slot holds channel pi(p) of its 16 (the 4-bit unpack of a
+// dword gives the even channels, then the odd ones):
+// pi = 0 2 4 6 1 3 5 7 8 10 12 14 9 11 13 15.
+__host__ __device__ constexpr int pi16(int p) { return 8 * (p >> 3) + 2 * (p & 3) + ((p >> 2) & 1); }
+
+// Slot swizzle of an int8 code row. A score read takes one slot of 16 rows
+// 16 j + 0..15; a transposing read takes one slot of the 8 rows r0 + {0,1,2,3,16,
+// 17,18,19} in each 16-lane group: both land in distinct slots modulo 16.
+__device__ __forceinline__ int i8swz(int r) { return (r & 3) | ((((r >> 2) & 3) ^ (((r >> 4) & 1) * 3)) << 2); }
+// Rope rows are 128 B, two to a 256-byte bank window: the 16 rows of a score tile
+// differ in (r & 1, rswz(r)).
+__device__ __forceinline__ int rswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
-// Eight 4-bit codes of one dword -> half8 in MFMA element order kk, element kk
-// holding nibble e(kk) = (kk >> 1) + 4 (kk & 1). Each code n becomes the fp16 bit
-// pattern n << 6, the subnormal n * 2^-18, which the matrix cores take exactly
-// (with the bare pattern n * 2^-24 their accumulation loses low-order bits); the
-// factor 2^18 goes into the fp32 scale of the product.
-__device__ __forceinline__ half8 unpack8_4(uint32_t w) {
-    constexpr uint32_t M = 0x000F000Fu << 6;
-    const uint32_t p0 = (w << 6) & M, p1 = (w << 2) & M, p2 = (w >> 2) & M, p3 = (w >> 6) & M;
-    return __builtin_bit_cast(half8, uint4{p0, p1, p2, p3});
+// v_perm_b32: byte k of the result is byte sel_k of the pair (lo: bytes 0..3,
+// hi: bytes 4..7)
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
 }
-constexpr int CODE_EXP = 18;  // unpacked code n is n * 2^-18
 
-// 2^(14 - floor(log2 m)) for m > 0 (1 for m == 0 or not finite).
-__device__ __forceinline__ float pow2_scale(float m) {
+// The two int8 limbs of four integers x_k, each given as y_k with (x_k + 128) in
+// its low 16 bits: limb 1 (byte 1 of y_k) = (x_k + 128) >> 8, limb 0 = low byte
+// of y_k minus 128 (byte k of each result word is element k).
+__device__ __forceinline__ void limbs4(float y0, float y1, float y2, float y3, uint32_t &l1, uint32_t &l0) {
+    const uint32_t p01 = perm(__float_as_uint(y1), __float_as_uint(y0), 0x05010400u);  // y0.b0 y1.b0 y0.b1 y1.b1
+    const uint32_t p23 = perm(__float_as_uint(y3), __float_as_uint(y2), 0x05010400u);
+    l0 = perm(p23, p01, 0x05040100u) ^ 0x80808080u;
+    l1 = perm(p23, p01, 0x07060302u);
+}
+
+// The three int8 limbs of four integers 0 <= x_k < 2^19, each given as y_k with
+// (x_k + 32896) in its low mantissa bits: with u = x + 32896, limb 2 = u >> 16
+// (byte 2 of y minus 64), limb 1 = byte 1 of u minus 128, limb 0 = byte 0 minus 128.
+__device__ __forceinline__ void limbs4x3(float y0, float y1, float y2, float y3, uint32_t &l2, uint32_t &l1,
+                                         uint32_t &l0) {
+    const uint32_t p01 = perm(__float_as_uint(y1), __float_as_uint(y0), 0x05010400u);  // y0.b0 y1.b0 y0.b1 y1.b1
+    const uint32_t p23 = perm(__float_as_uint(y3), __float_as_uint(y2), 0x05010400u);
+    const uint32_t q01 = perm(__float_as_uint(y1), __float_as_uint(y0), 0x0c0c0602u);  // y0.b2 y1.b2 0 0
+    const uint32_t q23 = perm(__float_as_uint(y3), __float_as_uint(y2), 0x0c0c0602u);
+    l0 = perm(p23, p01, 0x05040100u) ^ 0x80808080u;
+    l1 = perm(p23, p01, 0x07060302u) ^ 0x80808080u;
+    l2 = perm(q23, q01, 0x05040100u) ^ 0x40404040u;
+}
+
+// 1.5 2^23 + 128: an FMA result near this constant has an ulp of 1 and holds
+// round(product) + 128 in its low mantissa bits (for |product| < 2^22)
+constexpr float MAGIC_B = 12583040.0f;
+// 1.5 2^23 + 32896: the same with the bias of the three-limb split
+constexpr float MAGIC_P = 12615808.0f;
+
+// Scale 2^k of the query fold: the largest power of two with b 2^k <= 32639, so
+// that |x| + 128 stays below 2^15 (1 for b == 0 or not finite)
+__device__ __forceinline__ float qfold_scale(float b) {
+    const uint32_t u = __float_as_uint(b);
+    const int e = (int)((u >> 23) & 0xffu);
+    if (e == 0 || e == 0xff) return 1.f;
+    int k = 141 - e;                           // b 2^k in [2^14, 2^15)
+    if ((u & 0x7fffffu) > 0x7EFE00u) k -= 1;   // mantissa above 32639 / 16384
+    k = max(-100, min(100, k));
+    return __uint_as_float((uint32_t)(127 + k) << 23);
+}
+// 2^(18 - floor(log2 m)) for m > 0 (1 for m == 0 or not finite): m times it is below 2^19
+__device__ __forceinline__ float pfold_scale(float m) {
     const int e = (int)((__float_as_uint(m) >> 23) & 0xffu);
     if (e == 0 || e == 0xff) return 1.f;
-    const int se = min(254, 268 - e);
-    return __uint_as_float((uint32_t)se << 23);
+    const int k = max(-100, min(100, 145 - e));
+    return __uint_as_float((uint32_t)(127 + k) << 23);
 }
-
-// 2^CODE_EXP / x for x a power of two from pow2_scale (exact; saturates at 2^127)
-__device__ __forceinline__ float code_over(float x) {
-    return __uint_as_float((uint32_t)min(254, 254 + CODE_EXP - (int)(__float_as_uint(x) >> 23)) << 23);
-}
+// 1 / x for x a power of two from the two functions above (exact)
+__device__ __forceinline__ float pow2_inv(float x) { return __uint_as_float((uint32_t)(254 - (int)(__float_as_uint(x) >> 23)) << 23); }
 
 __device__ __forceinline__ float lq_sum(float v) { return sum_x4rows(v); }  // the 4 lanes sharing lane & 15
 __device__ __forceinline__ float lq_max(float v) { return max_x4rows(v); }
@@ -129,6 +163,16 @@ __device__ __forceinline__ uint16_t bf16_rn(float f) {  // fp32 -> bf16 bits, ne
     uint32_t u = __float_as_uint(f);
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+// largest fp16 value (all >= 0) among the low halves (lo) and among the high halves
+// with their sign bits cleared (hi) of four words
+__device__ __forceinline__ void max_h4_words(const uint32_t (&w)[4], float &lo, float &hi) {
+    u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7fff7fffu);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+    lo = half_bits_to_float(m.x);
+    hi = half_bits_to_float(m.y);
 }
 
 }  // namespace
@@ -140,14 +184,15 @@ __device__ __forceinline__ float load_q(const void *q, int64_t i) {
     else return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(q)[i]);
 }
 
-// One workgroup's pages. The three shared-memory regions come in as restrict
-// pointers: after inlining, the compiler knows that the direct-to-LDS copies
-// into `stage` touch neither `work` nor `xch`, and lets them stay in flight while
+// One workgroup's pages. The shared-memory regions come in as restrict pointers:
+// after inlining, the compiler knows that the direct-to-LDS copies into `stage`
+// and `ropeb` touch neither `work` nor `xch`, and lets them stay in flight while
 // the current page is processed.
 template <int QDT>
 __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg, uint8_t *__restrict__ stage,
-                                         uint8_t *__restrict__ work, float *__restrict__ xch,
-                                         uint32_t *__restrict__ qrl_lds) {
+                                         uint8_t *__restrict__ ropeb, uint8_t *__restrict__ work,
+                                         float *__restrict__ xch) {
+    constexpr bool QLO = QDT != KVQ_BF16;  // the rope query needs a bf16 lo part
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hs = wave & 3, half = wave >> 2;
@@ -173,24 +218,34 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
     const bool hq_ok = active && hl0 + l16 < a.grp;
     const int hq = hk * a.grp + hl0 + l16;                  // this lane's head (columns of every tile)
 
-    // ---- page copy HBM -> staging image: wave w issues wave-wide copies w, w + 8, ...;
-    // lane l of copy k moves chunk 64 k + l
-    auto fetch = [&](int pi) {
+    auto page_blk = [&](int pi) {
         const int page = load_const(a.bt, (int64_t)s * a.bt_stride + pi);
-        const int64_t blk = (int64_t)page * a.Hkv + hk;
+        return (int64_t)page * a.Hkv + hk;
+    };
+    // codes, (S, Z) and normalizer of page pi -> staging image: wave w issues
+    // wave-wide copies w, w + 8, ...; lane l of copy k moves chunk 64 k + l
+    auto fetch_codes = [&](int pi) {
+        const int64_t blk = page_blk(pi);
         const uint8_t *gcodes = a.kcodes + blk * (XT * XD / 2);
-        const uint8_t *grope = reinterpret_cast<const uint8_t *>(a.krope + blk * (XT * XR));
         const uint8_t *gsz = reinterpret_cast<const uint8_t *>(a.ksz + blk * (XT * 2));
         const uint8_t *gcn = reinterpret_cast<const uint8_t *>(a.kcn + blk * XD);
-        for (int k = wave; k < NDMA; k += 8) {
+        for (int k = wave; k < S_COPIES; k += 8) {
             const int c = 64 * k + lane;
-            const uint8_t *src = c < 2048 ? gcodes + 16 * c
-                               : c < 3072 ? grope + 16 * (c - 2048)
-                               : c < 3104 ? gsz + 16 * (c - 3072)
-                                          : gcn + 16 * (c - 3104);
-            if (c < NCHUNK)
+            const uint8_t *src = c < 2048 ? gcodes + 16 * c : c < 2080 ? gsz + 16 * (c - 2048) : gcn + 16 * (c - 2080);
+            if (c < S_CHUNKS)
                 __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(stage + 1024 * k),
                                                  16, 0, 0);
+        }
+    };
+    // rope part of page pi -> rope image, swizzled: LDS chunk p (row p >> 3, slot
+    // p & 7) takes the row's chunk (p & 7) ^ rswz(row)
+    auto fetch_rope = [&](int pi) {
+        const uint8_t *grope = reinterpret_cast<const uint8_t *>(a.krope + page_blk(pi) * (XT * XR));
+        for (int k = wave; k < R_COPIES; k += 8) {
+            const int p = 64 * k + lane, r = p >> 3;
+            const uint8_t *src = grope + 128 * r + 16 * ((p & 7) ^ rswz(r));
+            __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(ropeb + 1024 * k),
+                                             16, 0, 0);
         }
     };
     auto page_ok = [&](int pi) {
@@ -199,20 +254,23 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
     };
     int pi = p0;
     while (pi < p1 && !page_ok(pi)) ++pi;
-    if (pi < p1) fetch(pi);
+    if (pi < p1) {
+        fetch_codes(pi);
+        fetch_rope(pi);
+    }
 
-    // ---- rotated query of the lane's head over all 512 channels (c = 32 st + 8 lq + e);
-    // the wave keeps its half: qv[st'][e] = qbar[256 half + 32 st' + 8 lq + e] / sqrt(512)
-    float qv[8][8];
-    uint32_t *qr = qrl_lds + wave * 8 * 64 + lane;  // rope dims 32 half + 8 lq + 0..7: bf16 hi words 0..3, lo 4..7
+    // ---- rotated query of the lane's head over all 512 channels (c = 64 ks + 16 lq + f);
+    // the wave keeps its half: qv[ks][f] = qbar[256 half + 64 ks + 16 lq + f] / sqrt(512)
+    float qv[4][16];
+    uint32_t qrh[4], qrl[4];  // rope dims 32 half + 8 lq + 0..7 as bf16 pairs: hi, lo
     float qmax = 0.f;
     {
         const int64_t qb = ((int64_t)s * a.Hq + hq) * (XD + XR);
-        float q[16][8];
+        float q[8][16];
 #pragma unroll
-        for (int st = 0; st < 16; ++st)
+        for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[st][e] = hq_ok ? load_q<QDT>(a.q, qb + 32 * st + 8 * lq + e) : 0.f;
+            for (int f = 0; f < 16; ++f) q[ks][f] = hq_ok ? load_q<QDT>(a.q, qb + 64 * ks + 16 * lq + f) : 0.f;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
             uint32_t hw = 0, lw = 0;
@@ -224,171 +282,191 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                 hw |= (uint32_t)hb << (16 * h);
                 lw |= (uint32_t)lb << (16 * h);
             }
-            qr[e2 * 64] = hw;
-            qr[(4 + e2) * 64] = lw;
+            qrh[e2] = hw;
+            qrl[e2] = lw;
         }
-        // Walsh-Hadamard transform: bits of e and st in registers, bits of lq
+        // Walsh-Hadamard transform: bits of f and ks in registers, bits of lq
         // across lanes (lane bits 4 and 5)
-#pragma unroll
-        for (int b = 1; b < 8; b <<= 1)
-#pragma unroll
-            for (int st = 0; st < 16; ++st)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (!(e & b)) {
-                        const float x = q[st][e], y = q[st][e | b];
-                        q[st][e] = x + y;
-                        q[st][e | b] = x - y;
-                    }
 #pragma unroll
         for (int b = 1; b < 16; b <<= 1)
 #pragma unroll
-            for (int st = 0; st < 16; ++st)
-                if (!(st & b))
+            for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float x = q[st][e], y = q[st | b][e];
-                        q[st][e] = x + y;
-                        q[st | b][e] = x - y;
+                for (int f = 0; f < 16; ++f)
+                    if (!(f & b)) {
+                        const float x = q[ks][f], y = q[ks][f | b];
+                        q[ks][f] = x + y;
+                        q[ks][f | b] = x - y;
+                    }
+#pragma unroll
+        for (int b = 1; b < 8; b <<= 1)
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                if (!(ks & b))
+#pragma unroll
+                    for (int f = 0; f < 16; ++f) {
+                        const float x = q[ks][f], y = q[ks | b][f];
+                        q[ks][f] = x + y;
+                        q[ks | b][f] = x - y;
                     }
         const float s16 = (lq & 1) ? -1.f : 1.f, s32 = (lq & 2) ? -1.f : 1.f;
         constexpr float INV_SQRT = 0.04419417382415922f;  // 1 / sqrt(512)
 #pragma unroll
-        for (int st = 0; st < 16; ++st)
+        for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = q[st][e], lo, hi;
+            for (int f = 0; f < 16; ++f) {
+                float v = q[ks][f], lo, hi;
                 pair16(v, lo, hi);
                 v = __builtin_fmaf(s16, hi, lo);
                 pair32(v, lo, hi);
                 v = __builtin_fmaf(s32, hi, lo);
                 v *= INV_SQRT;
                 qmax = fmaxf(qmax, fabsf(v));
-                q[st][e] = v;
+                q[ks][f] = v;
             }
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qv[st][e] = half ? q[st + 8][e] : q[st][e];
+            for (int f = 0; f < 16; ++f) qv[ks][f] = half ? q[ks + 4][f] : q[ks][f];
     }
     qmax = lq_max(qmax);
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     float m_run = -INFINITY, l_run = 0.f;
+    float psc_run = 1.f;  // o holds the page-weighted sums times psc_run
     f32x4 o[16];
 #pragma unroll
     for (int mc = 0; mc < 16; ++mc) o[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
     float *xp = xch + hs * XCH_WORDS;  // this pair's exchange slot
-    const uint16_t *cn = reinterpret_cast<const uint16_t *>(work + L_CN);
 
     while (pi < p1) {
         const int cur = pi;
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into the staging image have landed
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into the staging and rope images have landed
         lds_barrier();                  // every wave's, and every wave is done with the working image
-        // staging -> working image, swizzled
+        // ---- staging -> working image: 4-bit code chunks unpacked to int8 slots;
+        // (S, Z) copied; the normalizer rearranged to the slot channel order
+        {
+            const int r0 = tid >> 4, g = tid & 15;  // chunk tid + 512 k: row r0 + 32 k, 32 channels 32 g ..
+            const int sw = i8swz(r0);               // rows 32 apart share the swizzle
+            const int off0 = r0 * 512 + 16 * ((2 * g) ^ sw), off1 = r0 * 512 + 16 * ((2 * g + 1) ^ sw);
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int c = tid + XNT * k;
-            if (c < NCHUNK) {
-                int off;
-                if (c < 2048) {
-                    const int r = c >> 4, g = c & 15;
-                    off = L_CODES + r * 256 + 16 * (g ^ swz(r));
-                } else if (c < 3072) {
-                    const int r = (c - 2048) >> 3, g = (c - 2048) & 7;
-                    off = L_ROPE + r * 128 + 16 * (g ^ rswz(r));
-                } else {
-                    off = L_SZ + 16 * (c - 3072);  // (S, Z) then normalizer, contiguous
-                }
-                *reinterpret_cast<uint4 *>(work + off) = *reinterpret_cast<const uint4 *>(stage + 16 * c);
+            for (int k = 0; k < 4; ++k) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(stage + 16 * (tid + 512 * k));
+                constexpr uint32_t M = 0x0F0F0F0Fu;
+                *reinterpret_cast<uint4 *>(work + off0 + 16384 * k) = uint4{w.x & M, (w.x >> 4) & M, w.y & M, (w.y >> 4) & M};
+                *reinterpret_cast<uint4 *>(work + off1 + 16384 * k) = uint4{w.z & M, (w.z >> 4) & M, w.w & M, (w.w >> 4) & M};
+            }
+            if (tid < 32) {
+                *reinterpret_cast<uint4 *>(work + W_SZ + 16 * tid) = *reinterpret_cast<const uint4 *>(stage + S_SZ + 16 * tid);
+            } else if (tid < 96) {
+                // eight channels 8 q .. 8 q + 7 stay in their 16 bytes: halves 0 2 4 6 1 3 5 7
+                const int qk = tid - 32;
+                const uint4 w = *reinterpret_cast<const uint4 *>(stage + S_CN + 16 * qk);
+                *reinterpret_cast<uint4 *>(work + W_CN + 16 * qk) =
+                    uint4{perm(w.y, w.x, 0x05040100u), perm(w.w, w.z, 0x05040100u), perm(w.y, w.x, 0x07060302u),
+                          perm(w.w, w.z, 0x07060302u)};
             }
         }
         lds_barrier();  // working image complete, staging image free
-        const int rows = min(XT, L - cur * XT);
-        // Per-lane byte addresses of the code rows this lane reads, made opaque here
-        // so that the per-K-step addresses below are formed next to their reads
-        // rather than hoisted out of the page loop (64 live registers otherwise).
-        // Score tile j reads row r = 64 pi2 + 16 q + 4 b + i: address r * 256 + 4 lq,
-        // XOR 16 (chunk ^ swz(r)); the transposed reads use rows 64 pi2 + 16 lq + l16.
-        int lo = lane;  // the lane id, opaque: addresses derived from it stay inside the loop
-        asm volatile("" : "+v"(lo));
-        const int ol16 = lo & 15, olq = lo >> 4;
-        // rows 64 apart share the swizzle, so the second half of the page is a
-        // constant 16 KB further (an immediate offset of the read)
-        int sbase[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int r = 16 * (ol16 >> 2) + 4 * b + (ol16 & 3);
-            sbase[b] = L_CODES + r * 256 + 16 * swz(r) + 4 * olq;
-        }
-        const int tr0 = 16 * olq + ol16;
-        const int tbase = L_CODES + tr0 * 256 + 16 * swz(tr0);
-
-        // page-wide bound of the query-side scaling: max c
-        float cmax = 0.f;
-        {
-            const uint4 cw = *reinterpret_cast<const uint4 *>(work + L_CN + 16 * lane);
-            const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
-            cmax = max_x4rows(row_max16(max_h8(w4)));  // all 64 lanes (normalizers are > 0)
-        }
-        const float qsc = pow2_scale(qmax * cmax);
-        const float qinv = code_over(qsc);  // undoes the query scaling and the code unit
-        // the next valid page, copied into the staging image while this one is processed
+        // the next valid page's codes and side data travel during this page's scores
         ++pi;
         while (pi < p1 && !page_ok(pi)) ++pi;
-        if (pi < p1) fetch(pi);
+        const bool more = pi < p1;
+        if (more) fetch_codes(pi);
+        const int rows = min(XT, L - cur * XT);
 
-        // ---- partial scores^T over this wave's latent half: tile j = (pi2 = j >> 2, b = j & 3)
-        // holds tokens 64 pi2 + 16 q + 4 b + i (row 4 q + i); A rows come from lane l16 = 4 q + i
+        // Per-lane byte offsets, made opaque here so that the per-step addresses
+        // below are formed next to their reads rather than hoisted out of the loop.
+        int lo = lane;
+        asm volatile("" : "+v"(lo));
+        const int ol16 = lo & 15, olq = lo >> 4;
+        // score read of tile j, K-step ks: row 16 j + l16, slot (16 half | 4 ks | lq) ^ i8swz(row)
+        const int ibase = 512 * ol16 + 16 * ((16 * half + olq) ^ ol16);
+        // rope read of tile j: row 16 j + l16, chunk 4 half + lq
+        const int rbase = 128 * ol16 + 16 * ((4 * half + olq) ^ ((ol16 & 7) ^ (ol16 >> 3)));
+        // transposing read (K-step kk, read rr, channel tile mc): this lane supplies row
+        // 64 kk + 32 rr + 16 (l16 >> 3) + 4 lq + ((l16 >> 1) & 3), half (l16 & 1) of slot
+        // (16 half + mc) ^ i8swz(row)
+        const int trow = 16 * (ol16 >> 3) + 4 * olq + ((ol16 >> 1) & 3);
+        const int tsw = ((ol16 >> 1) & 3) | ((olq ^ (3 * (ol16 >> 3))) << 2);
+        const int tbase = 512 * trow + 16 * ((16 * half) ^ tsw) + 8 * (ol16 & 1);
+
+        // page bounds: the largest normalizer (query fold scale), the largest scale
+        // and |zero point| (value fold scale); every lane takes two words of each
+        float cmax, smax, zmax;
+        {
+            const uint4 cw = *reinterpret_cast<const uint4 *>(work + W_CN + 16 * lane);
+            const uint32_t c4[4] = {cw.x, cw.y, cw.z, cw.w};
+            float c0, c1;
+            max_h4_words(c4, c0, c1);
+            cmax = max_x4rows(row_max16(fmaxf(c0, c1)));
+            const uint2 zw = *reinterpret_cast<const uint2 *>(work + W_SZ + 8 * lane);
+            const uint32_t z4[4] = {zw.x, zw.y, zw.x, zw.y};
+            float s0, z0;
+            max_h4_words(z4, s0, z0);
+            smax = max_x4rows(row_max16(s0));
+            zmax = max_x4rows(row_max16(z0));
+        }
+        const float qsc = qfold_scale(qmax * cmax), qinv = pow2_inv(qsc);
+        const float magic_q = MAGIC_B * qinv;
+
         f32x4 sc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float qc = 0.f;
         if (active) {
+            // ---- fold: q' = qbar o c for the wave's 256 channels as int8 limbs (B
+            // operands of the four K-steps); sum_j x_j from the same limbs
+            v4i B1[4], B0[4];
+            int qc1 = 0, qc0 = 0;
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const int chunk = 8 * half + st;  // 16-byte chunk of a code row: channels 32 chunk ..
-                const uint4 cw = *reinterpret_cast<const uint4 *>(work + L_CN + 2 * (32 * chunk + 8 * lq));
-                const uint32_t c4[4] = {cw.x, cw.y, cw.z, cw.w};
-                half8 bh, bl;
+            for (int ks = 0; ks < 4; ++ks) {
+                const uint8_t *cp = work + W_CN + 32 * (16 * half + 4 * ks + olq);
+                const uint4 cwa = *reinterpret_cast<const uint4 *>(cp), cwb = *reinterpret_cast<const uint4 *>(cp + 16);
+                const uint32_t cw[8] = {cwa.x, cwa.y, cwa.z, cwa.w, cwb.x, cwb.y, cwb.z, cwb.w};
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int e = (kk >> 1) + 4 * (kk & 1);
-                    const half2v c2 = as_h2(c4[e >> 1]);
-                    const float x = mul_h((e & 1) ? c2.y : c2.x, qv[st][e]);
-                    qc += x;
-                    _Float16 hi, lo;
-                    split_prod(x, qsc, hi, lo);
-                    bh[kk] = hi;
-                    bl[kk] = lo;
+                for (int d = 0; d < 4; ++d) {
+                    float y[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int p = 4 * d + i;
+                        const half2v c2 = as_h2(cw[p >> 1]);
+                        y[i] = __builtin_fmaf((float)((p & 1) ? c2.y : c2.x), qv[ks][pi16(p)], magic_q);
+                    }
+                    uint32_t l1, l0;
+                    limbs4(y[0], y[1], y[2], y[3], l1, l0);
+                    B1[ks][d] = (int)l1;
+                    B0[ks][d] = (int)l0;
+                    qc1 = __builtin_amdgcn_sdot4((int)l1, 0x01010101, qc1, false);
+                    qc0 = __builtin_amdgcn_sdot4((int)l0, 0x01010101, qc0, false);
                 }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t w =
-                        *reinterpret_cast<const uint32_t *>(work + (sbase[j & 3] ^ (16 * chunk)) + 16384 * (j >> 2));
-                    const half8 av = unpack8_4(w);
-                    sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, sc[j], 0, 0, 0);
-                    sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, sc[j], 0, 0, 0);
-                }
-                // keep the next K-step's operands from being hoisted here (register pressure)
-                __builtin_amdgcn_sched_barrier(0);
             }
-            // rope half, then y = S qinv sc + rope
-            const bf16x8 bh = __builtin_bit_cast(bf16x8, uint4{qr[0], qr[64], qr[128], qr[192]});
-            const bf16x8 bl = __builtin_bit_cast(bf16x8, uint4{qr[256], qr[320], qr[384], qr[448]});
+            const float qcs = lq_sum((float)(256 * qc1 + qc0)) * qinv;  // sum_j q'_j of the half, dot units
+
+            const bf16x8 rqh = __builtin_bit_cast(bf16x8, uint4{qrh[0], qrh[1], qrh[2], qrh[3]});
+            const bf16x8 rql = __builtin_bit_cast(bf16x8, uint4{qrl[0], qrl[1], qrl[2], qrl[3]});
+            // ---- partial scores^T: tile j holds tokens 16 j + row; y = S qinv R + Z qinv sum q' + rope
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int r = 64 * (j >> 2) + 16 * (ol16 >> 2) + 4 * (j & 3) + (ol16 & 3);
-                const uint4 rw = *reinterpret_cast<const uint4 *>(work + L_ROPE + r * 128 + 16 * ((4 * half + olq) ^ rswz(r)));
-                const bf16x8 av = __builtin_bit_cast(bf16x8, rw);
-                f32x4 rp = {0.f, 0.f, 0.f, 0.f};
-                rp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, rp, 0, 0, 0);
-                rp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, rp, 0, 0, 0);
-                const int t0 = 64 * (j >> 2) + 16 * olq + 4 * (j & 3);
-                const uint4 zw = *reinterpret_cast<const uint4 *>(work + L_SZ + 4 * t0);
-                const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+                v4i a1 = {0, 0, 0, 0}, a0 = {0, 0, 0, 0};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[j][i] = __builtin_fmaf((float)as_h2(z4[i]).x, qinv * sc[j][i], rp[i]);  // qinv: a power of two
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int off = 8192 * j + (ibase ^ ((64 * ks) ^ (192 * (j & 1))));
+                    const v4i av = *reinterpret_cast<const v4i *>(work + off);
+                    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, B1[ks], a1, 0, 0, 0);
+                    a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, B0[ks], a0, 0, 0, 0);
+                }
+                const uint4 zw = *reinterpret_cast<const uint4 *>(work + W_SZ + 4 * (16 * j + 4 * olq));
+                const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+                f32x4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const half2v sz = as_h2(z4[i]);  // (S, Z)
+                    const float rf = (float)((a1[i] << 8) + a0[i]);
+                    y[i] = __builtin_fmaf((float)sz.x * qinv, rf, (float)sz.y * qcs);
+                }
+                const bf16x8 ar = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(ropeb + rbase + 2048 * j));
+                y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, rqh, y, 0, 0, 0);
+                if constexpr (QLO) y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, rql, y, 0, 0, 0);
+                sc[j] = y;
+                __builtin_amdgcn_sched_barrier(0);  // one tile's operands in flight at a time
             }
             // the low half publishes its partial sums
             if (half == 0) {
@@ -396,10 +474,11 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                 for (int j = 0; j < 8; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) xp[(4 * j + i) * 64 + lane] = sc[j][i];
-                xp[32 * 64 + lane] = qc;
             }
         }
         lds_barrier();
+        // every wave's rope reads are done: the next page's rope part may land
+        if (more) fetch_rope(pi);
         if (active && half == 1) {  // the high half completes the sums and publishes them
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -408,8 +487,6 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                     sc[j][i] += xp[(4 * j + i) * 64 + lane];
                     xp[(4 * j + i) * 64 + lane] = sc[j][i];
                 }
-            qc += xp[32 * 64 + lane];
-            xp[32 * 64 + lane] = qc;
         }
         lds_barrier();
         if (!active) continue;
@@ -418,113 +495,101 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             for (int j = 0; j < 8; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[j][i] = xp[(4 * j + i) * 64 + lane];
-            qc = xp[32 * 64 + lane];
         }
-        qc = lq_sum(qc);
 
-        // ---- online softmax; lane (head l16, lq) holds tokens 64 pi2 + 16 lq + 4 b + i of tile (pi2, b)
-        // scales are >= 0: their largest is the largest fp16 bit pattern (packed u16
-        // maxima; the zero points in the upper halves are ignored)
-        uint32_t smaxw = 0;
-        float pmax = -INFINITY;
-        const float a_z = sml2 * qc;
+        // ---- online softmax; lane (head l16, lq) holds tokens 16 j + 4 lq + i
+        if (rows < XT) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t0 = 64 * (j >> 2) + 16 * olq + 4 * (j & 3);
-            const uint4 zw = *reinterpret_cast<const uint4 *>(work + L_SZ + 4 * t0);
-            const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                smaxw = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, smaxw),
-                                                                               __builtin_bit_cast(u16x2, z4[i])));
-                float x = __builtin_fmaf((float)as_h2(z4[i]).y, a_z, sml2 * sc[j][i]);
-                if (t0 + i >= rows) x = -INFINITY;
-                sc[j][i] = x;
-                pmax = fmaxf(pmax, x);
-            }
+                for (int i = 0; i < 4; ++i)
+                    if (16 * j + 4 * olq + i >= rows) sc[j][i] = -INFINITY;
         }
-        pmax = lq_max(pmax);
-        const float smax = lq_max(half_bits_to_float(smaxw & 0x7fffu));
+        float pmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pmax = fmaxf(pmax, sc[j][i]);
+        pmax = lq_max(pmax) * sml2;
         const float m_new = fmaxf(m_run, pmax);
         const float alpha = exp2_fast(m_run - m_new);
-        // the rescaling of o' runs only when some head's running maximum moved (most
-        // pages once the first few are seen leave every alpha at exactly 1)
-        const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
         m_run = m_new;
-        const float psc = pow2_scale(smax), pinv = code_over(psc);
-        // the scaling enters the exponent: ps = p psc = 2^(score - m + log2 psc), and the
-        // sums over ps are scaled back once (powers of two: the same values as unscaled)
+        // P~ = p S psc below 2^19 (three limbs); the zero-point sum sum_t p Z psc stays
+        // below 2^29 in the int32 accumulator (|Z| / 8 enters the bound)
+        const float psc = pfold_scale(fmaxf(smax, zmax * 0.125f));
+        // the scaling enters the exponent: ps = p psc = 2^(score - m + log2 psc)
         const float m_ps = m_new - (float)((int)(__float_as_uint(psc) >> 23) - 127);
-        const float pscinv = __uint_as_float((uint32_t)(254 - (int)(__float_as_uint(psc) >> 23)) << 23);
         float psum = 0.f, zs = 0.f;
-        // P~ = p S psc straight into the B operand of the value product: K-step
-        // kap = 2 pi2 + beta covers tokens 64 pi2 + 16 lq + 8 beta + e(kk); element
-        // kk = 2 i + (j & 1) comes from tile j = 4 pi2 + 2 beta + (j & 1), row i
-        half8 pbh[4], pbl[4];
+        uint32_t pl2[8], pl1[8], pl0[8];  // P~ limbs of tile j, elements i in bytes i
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int t0 = 64 * (j >> 2) + 16 * olq + 4 * (j & 3);
-            const int kap = 2 * (j >> 2) + ((j >> 1) & 1);
-            const uint4 zw = *reinterpret_cast<const uint4 *>(work + L_SZ + 4 * t0);
+            const uint4 zw = *reinterpret_cast<const uint4 *>(work + W_SZ + 4 * (16 * j + 4 * olq));
             const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+            float y[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const half2v sz = as_h2(z4[i]);  // (S, Z)
-                const float ps = exp2_fast(sc[j][i] - m_ps);
+                const float ps = exp2_fast(__builtin_fmaf(sc[j][i], sml2, -m_ps));
                 psum += ps;
                 zs = __builtin_fmaf((float)sz.y, ps, zs);
-                _Float16 hi, lo;
-                split_prod(ps, (float)sz.x, hi, lo);
-                pbh[kap][2 * i + (j & 1)] = hi;
-                pbl[kap][2 * i + (j & 1)] = lo;
+                y[i] = __builtin_fmaf(ps, (float)sz.x, MAGIC_P);
             }
+            limbs4x3(y[0], y[1], y[2], y[3], pl2[j], pl1[j], pl0[j]);
         }
-        l_run = __builtin_fmaf(l_run, alpha, psum * pscinv);
-        zs = lq_sum(zs) * pscinv;
+        l_run = __builtin_fmaf(l_run, alpha, psum * pow2_inv(psc));
+        const int zi = (int)rintf(lq_sum(zs));
+        // o' is kept times the page's psc: rescaled when a head's maximum moved or psc changed
+        const float beta = alpha * (psc * pow2_inv(psc_run));
+        psc_run = psc;
+        if (__builtin_amdgcn_ballot_w64(beta != 1.f) != 0)
+#pragma unroll
+            for (int mc = 0; mc < 16; ++mc)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[mc][i] *= beta;
 
-        if (rescale)
+        // ---- values^T over this wave's latent half: tile mc has channels 256 half + 16 mc
+        // + pi(row) as A rows (rows 4 lq + i of the lane: cnp entries 16 mc + 4 lq + i);
+        // K-step kk takes tokens 64 kk .. 64 kk + 63 in the order of score tiles 4 kk .. 4 kk + 3
+        const v4i P2[2] = {{(int)pl2[0], (int)pl2[1], (int)pl2[2], (int)pl2[3]}, {(int)pl2[4], (int)pl2[5], (int)pl2[6], (int)pl2[7]}};
+        const v4i P1[2] = {{(int)pl1[0], (int)pl1[1], (int)pl1[2], (int)pl1[3]}, {(int)pl1[4], (int)pl1[5], (int)pl1[6], (int)pl1[7]}};
+        const v4i P0[2] = {{(int)pl0[0], (int)pl0[1], (int)pl0[2], (int)pl0[3]}, {(int)pl0[4], (int)pl0[5], (int)pl0[6], (int)pl0[7]}};
+        const v4i zi4 = {zi, zi, zi, zi};
+        const uint8_t *cnp = work + W_CN + 2 * (256 * half + 4 * olq);
 #pragma unroll
-            for (int m2 = 0; m2 < 16; ++m2)
+        for (int mc = 0; mc < 16; ++mc) {
+            v4i a2 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a0 = zi4;
+            const int toff = tbase ^ (16 * mc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[m2][i] *= alpha;
-        // ---- values^T over this wave's latent half: tile mc (channels 16 mc + l16 as A rows);
-        // the transposed read gives lane (l16, lq) channel 16 mc + l16 of tokens 64 pi2 + 16 lq + 0..15
-#pragma unroll
-        for (int m2 = 0; m2 < 16; ++m2) {
-            const int mc = 16 * half + m2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p2 = 0; p2 < 2; ++p2) {
-                const int off = (tbase ^ (16 * (mc >> 1))) + 16384 * p2 + 8 * (mc & 1);  // this lane's row of the group's read
-                const v2i tw = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(work + off));
-#pragma unroll
-                for (int beta = 0; beta < 2; ++beta) {
-                    const half8 av = unpack8_4((uint32_t)tw[beta]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbh[2 * p2 + beta], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbl[2 * p2 + beta], acc, 0, 0, 0);
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                const v2i t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i *)(work + toff + 32768 * kk));
+                const v2i t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i *)(work + toff + 32768 * kk + 16384));
+                const v4i av = {t0.x, t0.y, t1.x, t1.y};
+                a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, P2[kk], a2, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, P1[kk], a1, 0, 0, 0);
+                a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, P0[kk], a0, 0, 0, 0);
             }
-            // fold (o' rescaled above): rows 4 lq + i of tile mc are channels 16 mc + 4 lq + i
-            const uint2 cv2 = *reinterpret_cast<const uint2 *>(cn + 16 * mc + 4 * lq);
+            const uint2 cv2 = *reinterpret_cast<const uint2 *>(cnp + 32 * mc);
             const half2v c01 = as_h2(cv2.x), c23 = as_h2(cv2.y);
             const _Float16 cvv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[m2][i] = __builtin_fmaf((float)cvv[i], __builtin_fmaf(acc[i], pinv, zs), o[m2][i]);
-            if (m2 & 1) __builtin_amdgcn_sched_barrier(0);  // at most two tiles' operands in flight
+            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf((float)cvv[i], (float)((a2[i] << 16) + (a1[i] << 8) + a0[i]), o[mc][i]);
+            if (mc & 1) __builtin_amdgcn_sched_barrier(0);  // at most two tiles' operands in flight
         }
     }
 
-    // ---- split partial of the lane's head: o' (channels 16 mc + 4 lq + i of this half), m (natural log), l
+    // ---- split partial of the lane's head: o' (channels 256 half + 16 mc + pi(4 lq + i)),
+    // m (natural log), l
     if (!hq_ok) return;
     l_run = lq_sum(l_run);
-    // a partial row is XD + 2 = 514 floats: rows start 8-byte aligned only, so the stores are float2
+    const float oinv = pow2_inv(psc_run);
+    // a partial row is XD + 2 = 514 floats
     float *wsr = a.ws + (((int64_t)s * a.Hq + hq) * a.splits + split) * (XD + 2);
 #pragma unroll
-    for (int m2 = 0; m2 < 16; ++m2) {
-        float2 *dst = reinterpret_cast<float2 *>(wsr + 16 * (16 * half + m2) + 4 * lq);
-        dst[0] = float2{o[m2][0], o[m2][1]};
-        dst[1] = float2{o[m2][2], o[m2][3]};
-    }
+    for (int mc = 0; mc < 16; ++mc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsr[256 * half + 16 * mc + pi16(4 * lq + i)] = o[mc][i] * oinv;
     if (lq == 0 && half == 0) {
         wsr[XD] = m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f;
         wsr[XD + 1] = l_run;
@@ -534,13 +599,13 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 template <int QDT>
 __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int units, int nhg) {
     // Separate LDS variables: each gets its own alias scope, which lets the
-    // compiler keep the direct-to-LDS copies into `stage` in flight across the
-    // accesses to the others.
-    __shared__ __attribute__((aligned(16))) uint8_t stage[L_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t work[L_BYTES];
+    // compiler keep the direct-to-LDS copies into `stage` and `ropeb` in flight
+    // across the accesses to the others.
+    __shared__ __attribute__((aligned(16))) uint8_t stage[S_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ropeb[R_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t work[W_BYTES];
     __shared__ float xch[4 * XCH_WORDS];
-    __shared__ uint32_t qr[8 * 8 * 64];
-    mla_body<QDT>(a, units, nhg, stage, work, xch, qr);
+    mla_body<QDT>(a, units, nhg, stage, ropeb, work, xch);
 }
 
 bool decode_mla_supported(const DecodeArgs &a) {
