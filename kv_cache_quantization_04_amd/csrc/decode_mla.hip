@@ -156,6 +156,12 @@ __device__ __forceinline__ float pfold_scale(float m) {
 // 1 / x for x a power of two from the two functions above (exact)
 __device__ __forceinline__ float pow2_inv(float x) { return __uint_as_float((uint32_t)(254 - (int)(__float_as_uint(x) >> 23)) << 23); }
 
+// both bf16 halves of w times a power of two (exact for finite results)
+__device__ __forceinline__ uint32_t bf16x2_scale(uint32_t w, float f) {
+    const float lo = __uint_as_float(w << 16) * f, hi = __uint_as_float(w & 0xffff0000u) * f;
+    return perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 __device__ __forceinline__ float lq_sum(float v) { return sum_x4rows(v); }  // the 4 lanes sharing lane & 15
 __device__ __forceinline__ float lq_max(float v) { return max_x4rows(v); }
 
@@ -191,7 +197,7 @@ __device__ __forceinline__ float load_q(const void *q, int64_t i) {
 template <int QDT>
 __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg, uint8_t *__restrict__ stage,
                                          uint8_t *__restrict__ ropeb, uint8_t *__restrict__ work,
-                                         float *__restrict__ xch) {
+                                         float *__restrict__ xch, uint32_t *__restrict__ qrl_lds) {
     constexpr bool QLO = QDT != KVQ_BF16;  // the rope query needs a bf16 lo part
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -262,7 +268,10 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
     // ---- rotated query of the lane's head over all 512 channels (c = 64 ks + 16 lq + f);
     // the wave keeps its half: qv[ks][f] = qbar[256 half + 64 ks + 16 lq + f] / sqrt(512)
     float qv[4][16];
-    uint32_t qrh[4], qrl[4];  // rope dims 32 half + 8 lq + 0..7 as bf16 pairs: hi, lo
+    // rope dims 32 half + 8 lq + 0..7 as bf16 pairs: hi words in LDS (wave-major, then
+    // word, then lane), lo words in registers (bf16 queries have none)
+    uint32_t *qrw = qrl_lds + wave * 4 * 64 + lane;
+    uint32_t qrl[4];
     float qmax = 0.f;
     {
         const int64_t qb = ((int64_t)s * a.Hq + hq) * (XD + XR);
@@ -282,7 +291,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                 hw |= (uint32_t)hb << (16 * h);
                 lw |= (uint32_t)lb << (16 * h);
             }
-            qrh[e2] = hw;
+            qrw[e2 * 64] = hw;
             qrl[e2] = lw;
         }
         // Walsh-Hadamard transform: bits of f and ks in registers, bits of lq
@@ -438,11 +447,10 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                     qc0 = __builtin_amdgcn_sdot4((int)l0, 0x01010101, qc0, false);
                 }
             }
-            const float qcs = lq_sum((float)(256 * qc1 + qc0)) * qinv;  // sum_j q'_j of the half, dot units
+            const float qcx = lq_sum((float)(256 * qc1 + qc0));  // sum_j x_j of the half (units of 2^-k)
 
-            const bf16x8 rqh = __builtin_bit_cast(bf16x8, uint4{qrh[0], qrh[1], qrh[2], qrh[3]});
-            const bf16x8 rql = __builtin_bit_cast(bf16x8, uint4{qrl[0], qrl[1], qrl[2], qrl[3]});
-            // ---- partial scores^T: tile j holds tokens 16 j + row; y = S qinv R + Z qinv sum q' + rope
+            // ---- partial scores^T in units of 2^-k: tile j holds tokens 16 j + row;
+            // y = S R + Z sum x, then + 2^k rope
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 v4i a1 = {0, 0, 0, 0}, a0 = {0, 0, 0, 0};
@@ -455,18 +463,26 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
                 }
                 const uint4 zw = *reinterpret_cast<const uint4 *>(work + W_SZ + 4 * (16 * j + 4 * olq));
                 const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
-                f32x4 y;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const half2v sz = as_h2(z4[i]);  // (S, Z)
                     const float rf = (float)((a1[i] << 8) + a0[i]);
-                    y[i] = __builtin_fmaf((float)sz.x * qinv, rf, (float)sz.y * qcs);
+                    sc[j][i] = __builtin_fmaf((float)sz.x, rf, (float)sz.y * qcx);
                 }
-                const bf16x8 ar = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(ropeb + rbase + 2048 * j));
-                y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, rqh, y, 0, 0, 0);
-                if constexpr (QLO) y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, rql, y, 0, 0, 0);
-                sc[j] = y;
                 __builtin_amdgcn_sched_barrier(0);  // one tile's operands in flight at a time
+            }
+            // the rope query times 2^k, so that the rope product lands in the same units
+            const bf16x8 rqh = __builtin_bit_cast(bf16x8, uint4{bf16x2_scale(qrw[0], qsc), bf16x2_scale(qrw[64], qsc),
+                                                                 bf16x2_scale(qrw[128], qsc), bf16x2_scale(qrw[192], qsc)});
+            bf16x8 rql;
+            if constexpr (QLO)
+                rql = __builtin_bit_cast(bf16x8, uint4{bf16x2_scale(qrl[0], qsc), bf16x2_scale(qrl[1], qsc),
+                                                        bf16x2_scale(qrl[2], qsc), bf16x2_scale(qrl[3], qsc)});
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bf16x8 ar = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(ropeb + rbase + 2048 * j));
+                sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, rqh, sc[j], 0, 0, 0);
+                if constexpr (QLO) sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, rql, sc[j], 0, 0, 0);
             }
             // the low half publishes its partial sums
             if (half == 0) {
@@ -510,13 +526,17 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) pmax = fmaxf(pmax, sc[j][i]);
-        pmax = lq_max(pmax) * sml2;
+        const float sml2q = sml2 * qinv;  // scores are in units of 2^-k
+        pmax = lq_max(pmax) * sml2q;
         const float m_new = fmaxf(m_run, pmax);
         const float alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
         // P~ = p S psc below 2^19 (three limbs); the zero-point sum sum_t p Z psc stays
         // below 2^29 in the int32 accumulator (|Z| / 8 enters the bound)
-        const float psc = pfold_scale(fmaxf(smax, zmax * 0.125f));
+        // kept from page to page unless this page needs a smaller one or allows one 4x larger
+        // (each change rescales o')
+        const float psc_pg = pfold_scale(fmaxf(smax, zmax * 0.125f));
+        const float psc = (psc_pg < psc_run || psc_pg >= 4.f * psc_run) ? psc_pg : psc_run;
         // the scaling enters the exponent: ps = p psc = 2^(score - m + log2 psc)
         const float m_ps = m_new - (float)((int)(__float_as_uint(psc) >> 23) - 127);
         float psum = 0.f, zs = 0.f;
@@ -529,7 +549,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const half2v sz = as_h2(z4[i]);  // (S, Z)
-                const float ps = exp2_fast(__builtin_fmaf(sc[j][i], sml2, -m_ps));
+                const float ps = exp2_fast(__builtin_fmaf(sc[j][i], sml2q, -m_ps));
                 psum += ps;
                 zs = __builtin_fmaf((float)sz.y, ps, zs);
                 y[i] = __builtin_fmaf(ps, (float)sz.x, MAGIC_P);
@@ -574,7 +594,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             const half2v c01 = as_h2(cv2.x), c23 = as_h2(cv2.y);
             const _Float16 cvv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf((float)cvv[i], (float)((a2[i] << 16) + (a1[i] << 8) + a0[i]), o[mc][i]);
+            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf((float)cvv[i], (float)((((a2[i] << 8) + a1[i]) << 8) + a0[i]), o[mc][i]);
             if (mc & 1) __builtin_amdgcn_sched_barrier(0);  // at most two tiles' operands in flight
         }
     }
@@ -605,7 +625,8 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
     __shared__ __attribute__((aligned(16))) uint8_t ropeb[R_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t work[W_BYTES];
     __shared__ float xch[4 * XCH_WORDS];
-    mla_body<QDT>(a, units, nhg, stage, ropeb, work, xch);
+    __shared__ uint32_t qr[8 * 4 * 64];
+    mla_body<QDT>(a, units, nhg, stage, ropeb, work, xch, qr);
 }
 
 bool decode_mla_supported(const DecodeArgs &a) {
