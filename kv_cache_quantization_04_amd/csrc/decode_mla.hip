@@ -58,6 +58,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
 constexpr int XD = 512;    // latent channels
 constexpr int XR = 64;     // rope channels
@@ -99,11 +100,29 @@ __device__ __forceinline__ int rswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
+// a * b with a an fp16 value: one mixed-precision FMA (v_fma_mix_f32)
+__device__ __forceinline__ float mul_h(_Float16 a, float b) { return __builtin_fmaf((float)a, b, 0.f); }
+// fp16 hi + lo parts of the product a b: hi = f16(a b), lo = f16(a b - hi), each one
+// mixed-precision FMA (the product is formed exactly inside it)
+__device__ __forceinline__ void split_prod(float a, float b, _Float16 &hi, _Float16 &lo) {
+    hi = (_Float16)__builtin_fmaf(a, b, 0.f);
+    lo = (_Float16)__builtin_fmaf(a, b, -(float)hi);
+}
+
 // v_perm_b32: byte k of the result is byte sel_k of the pair (lo: bytes 0..3,
 // hi: bytes 4..7)
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
+
+// Eight int8 codes (two words) -> fp16 operands code 2^-18 (the bit pattern code << 6,
+// a subnormal the matrix cores take exactly): each code byte becomes the low byte of a
+// half (v_perm with zero bytes), and one shift moves both halves' codes up by 6 bits
+__device__ __forceinline__ half8 codes_sub18(uint32_t w0, uint32_t w1) {
+    return __builtin_bit_cast(half8, uint4{perm(0u, w0, 0x0C010C00u) << 6, perm(0u, w0, 0x0C030C02u) << 6,
+                                           perm(0u, w1, 0x0C010C00u) << 6, perm(0u, w1, 0x0C030C02u) << 6});
+}
+constexpr float CODE_UNIT_INV = 262144.f;  // 2^18
 
 // The two int8 limbs of four integers x_k, each given as y_k with (x_k + 128) in
 // its low 16 bits: limb 1 (byte 1 of y_k) = (x_k + 128) >> 8, limb 0 = low byte
@@ -269,8 +288,9 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
     // the wave keeps its half: qv[ks][f] = qbar[256 half + 64 ks + 16 lq + f] / sqrt(512)
     float qv[4][16];
     // rope dims 32 half + 8 lq + 0..7 as bf16 pairs: hi words in LDS (wave-major, then
-    // word, then lane), lo words in registers (bf16 queries have none)
-    uint32_t *qrw = qrl_lds + wave * 4 * 64 + lane;
+    // word, then lane; a fifth word holds the lane's mean square of qbar), lo words in
+    // registers (bf16 queries have none)
+    uint32_t *qrw = qrl_lds + wave * 5 * 64 + lane;
     uint32_t qrl[4];
     float qmax = 0.f;
     {
@@ -339,6 +359,14 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             for (int f = 0; f < 16; ++f) qv[ks][f] = half ? q[ks + 4][f] : q[ks][f];
     }
     qmax = lq_max(qmax);
+    // mean square of qbar over the head's 512 channels (the score product's range test)
+    float qms = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int f = 0; f < 16; ++f) qms = __builtin_fmaf(qv[ks][f], qv[ks][f], qms);
+    qms = lq_sum(qms);  // this half's 256 channels
+    qrw[4 * 64] = __float_as_uint(qms);  // kept in LDS beside the rope query words (registers are tight)
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     float m_run = -INFINITY, l_run = 0.f;
@@ -402,13 +430,21 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 
         // page bounds: the largest normalizer (query fold scale), the largest scale
         // and |zero point| (value fold scale); every lane takes two words of each
-        float cmax, smax, zmax;
+        float cmax, smax, zmax, cms;
         {
             const uint4 cw = *reinterpret_cast<const uint4 *>(work + W_CN + 16 * lane);
             const uint32_t c4[4] = {cw.x, cw.y, cw.z, cw.w};
             float c0, c1;
             max_h4_words(c4, c0, c1);
             cmax = max_x4rows(row_max16(fmaxf(c0, c1)));
+            float cs = 0.f;  // sum of c^2 over the page's 512 channels (eight per lane)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half2v c2 = as_h2(c4[i]);
+                cs = __builtin_fmaf((float)c2.x, (float)c2.x, cs);
+                cs = __builtin_fmaf((float)c2.y, (float)c2.y, cs);
+            }
+            cms = lq_sum(row_sum16(cs));
             const uint2 zw = *reinterpret_cast<const uint2 *>(work + W_SZ + 8 * lane);
             const uint32_t z4[4] = {zw.x, zw.y, zw.x, zw.y};
             float s0, z0;
@@ -421,55 +457,106 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
 
         f32x4 sc[8];
         if (active) {
-            // ---- fold: q' = qbar o c for the wave's 256 channels as int8 limbs (B
-            // operands of the four K-steps); sum_j x_j from the same limbs
-            v4i B1[4], B0[4];
-            int qc1 = 0, qc0 = 0;
+            // Range test: the fixed-point fold gives every channel the page's one scale 2^k,
+            // set by max |qbar| max c; channels far below that bound (a latent with a large
+            // mean puts one rotated channel's normalizer far above the rest) keep few bits.
+            // Pages where the bound exceeds 16 times rms(qbar) rms(c) take the fp16 product.
+            const bool fp16 = __builtin_amdgcn_ballot_w64(qmax * qmax * cmax * cmax > 256.f * (__uint_as_float(qrw[4 * 64]) * (1.f / 256.f)) * (cms * (1.f / 512.f))) != 0;
+            if (fp16) {
+                // ---- scores^T from fp16 products: K-step ks2 takes 32 channels, lane lq the
+                // eight of slot (16 half | 4 (ks2 >> 1) | lq), half ks2 & 1; the codes enter as
+                // code 2^-18, the query as fp16 hi + lo of x 2^k
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const uint8_t *cp = work + W_CN + 32 * (16 * half + 4 * ks + olq);
-                const uint4 cwa = *reinterpret_cast<const uint4 *>(cp), cwb = *reinterpret_cast<const uint4 *>(cp + 16);
-                const uint32_t cw[8] = {cwa.x, cwa.y, cwa.z, cwa.w, cwb.x, cwb.y, cwb.z, cwb.w};
+                for (int j = 0; j < 8; ++j) sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                float qc = 0.f;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    float y[4];
+                for (int ks2 = 0; ks2 < 8; ++ks2) {
+                    const int ks = ks2 >> 1, hh = ks2 & 1;
+                    const uint4 cw = *reinterpret_cast<const uint4 *>(work + W_CN + 32 * (16 * half + 4 * ks + olq) + 16 * hh);
+                    const uint32_t c4[4] = {cw.x, cw.y, cw.z, cw.w};
+                    half8 bh, bl;
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const half2v c2 = as_h2(c4[p >> 1]);
+                        const float x = mul_h((p & 1) ? c2.y : c2.x, qv[ks][pi16(8 * hh + p)]);
+                        qc += x;
+                        _Float16 hi, lo;
+                        split_prod(x, qsc, hi, lo);
+                        bh[p] = hi;
+                        bl[p] = lo;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int off = 8192 * j + (ibase ^ ((64 * ks) ^ (192 * (j & 1)))) + 8 * hh;
+                        const uint2 w = *reinterpret_cast<const uint2 *>(work + off);
+                        const half8 av = codes_sub18(w.x, w.y);
+                        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, sc[j], 0, 0, 0);
+                        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, sc[j], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // one K-step's operands in flight at a time
+                }
+                const float qcx = lq_sum(qc) * qsc;  // sum_j x_j 2^k of the half
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint4 zw = *reinterpret_cast<const uint4 *>(work + W_SZ + 4 * (16 * j + 4 * olq));
+                    const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int p = 4 * d + i;
-                        const half2v c2 = as_h2(cw[p >> 1]);
-                        y[i] = __builtin_fmaf((float)((p & 1) ? c2.y : c2.x), qv[ks][pi16(p)], magic_q);
+                        const half2v sz = as_h2(z4[i]);  // (S, Z)
+                        sc[j][i] = __builtin_fmaf((float)sz.x * CODE_UNIT_INV, sc[j][i], (float)sz.y * qcx);
                     }
-                    uint32_t l1, l0;
-                    limbs4(y[0], y[1], y[2], y[3], l1, l0);
-                    B1[ks][d] = (int)l1;
-                    B0[ks][d] = (int)l0;
-                    qc1 = __builtin_amdgcn_sdot4((int)l1, 0x01010101, qc1, false);
-                    qc0 = __builtin_amdgcn_sdot4((int)l0, 0x01010101, qc0, false);
                 }
-            }
-            const float qcx = lq_sum((float)(256 * qc1 + qc0));  // sum_j x_j of the half (units of 2^-k)
-
-            // ---- partial scores^T in units of 2^-k: tile j holds tokens 16 j + row;
-            // y = S R + Z sum x, then + 2^k rope
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                v4i a1 = {0, 0, 0, 0}, a0 = {0, 0, 0, 0};
+            } else {
+                // ---- fold: q' = qbar o c for the wave's 256 channels as int8 limbs (B
+                // operands of the four K-steps); sum_j x_j from the same limbs
+                v4i B1[4], B0[4];
+                int qc1 = 0, qc0 = 0;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const int off = 8192 * j + (ibase ^ ((64 * ks) ^ (192 * (j & 1))));
-                    const v4i av = *reinterpret_cast<const v4i *>(work + off);
-                    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, B1[ks], a1, 0, 0, 0);
-                    a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, B0[ks], a0, 0, 0, 0);
-                }
-                const uint4 zw = *reinterpret_cast<const uint4 *>(work + W_SZ + 4 * (16 * j + 4 * olq));
-                const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+                    const uint8_t *cp = work + W_CN + 32 * (16 * half + 4 * ks + olq);
+                    const uint4 cwa = *reinterpret_cast<const uint4 *>(cp), cwb = *reinterpret_cast<const uint4 *>(cp + 16);
+                    const uint32_t cw[8] = {cwa.x, cwa.y, cwa.z, cwa.w, cwb.x, cwb.y, cwb.z, cwb.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const half2v sz = as_h2(z4[i]);  // (S, Z)
-                    const float rf = (float)((a1[i] << 8) + a0[i]);
-                    sc[j][i] = __builtin_fmaf((float)sz.x, rf, (float)sz.y * qcx);
+                    for (int d = 0; d < 4; ++d) {
+                        float y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int p = 4 * d + i;
+                            const half2v c2 = as_h2(cw[p >> 1]);
+                            y[i] = __builtin_fmaf((float)((p & 1) ? c2.y : c2.x), qv[ks][pi16(p)], magic_q);
+                        }
+                        uint32_t l1, l0;
+                        limbs4(y[0], y[1], y[2], y[3], l1, l0);
+                        B1[ks][d] = (int)l1;
+                        B0[ks][d] = (int)l0;
+                        qc1 = __builtin_amdgcn_sdot4((int)l1, 0x01010101, qc1, false);
+                        qc0 = __builtin_amdgcn_sdot4((int)l0, 0x01010101, qc0, false);
+                    }
                 }
-                __builtin_amdgcn_sched_barrier(0);  // one tile's operands in flight at a time
+                const float qcx = lq_sum((float)(256 * qc1 + qc0));  // sum_j x_j of the half (units of 2^-k)
+
+                // ---- partial scores^T in units of 2^-k: tile j holds tokens 16 j + row;
+                // y = S R + Z sum x, then + 2^k rope
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    v4i a1 = {0, 0, 0, 0}, a0 = {0, 0, 0, 0};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int off = 8192 * j + (ibase ^ ((64 * ks) ^ (192 * (j & 1))));
+                        const v4i av = *reinterpret_cast<const v4i *>(work + off);
+                        a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, B1[ks], a1, 0, 0, 0);
+                        a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, B0[ks], a0, 0, 0, 0);
+                    }
+                    const uint4 zw = *reinterpret_cast<const uint4 *>(work + W_SZ + 4 * (16 * j + 4 * olq));
+                    const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const half2v sz = as_h2(z4[i]);  // (S, Z)
+                        const float rf = (float)((a1[i] << 8) + a0[i]);
+                        sc[j][i] = __builtin_fmaf((float)sz.x, rf, (float)sz.y * qcx);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // one tile's operands in flight at a time
+                }
             }
             // the rope query times 2^k, so that the rope product lands in the same units
             const bf16x8 rqh = __builtin_bit_cast(bf16x8, uint4{bf16x2_scale(qrw[0], qsc), bf16x2_scale(qrw[64], qsc),
@@ -625,7 +712,7 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
     __shared__ __attribute__((aligned(16))) uint8_t ropeb[R_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t work[W_BYTES];
     __shared__ float xch[4 * XCH_WORDS];
-    __shared__ uint32_t qr[8 * 4 * 64];
+    __shared__ uint32_t qr[8 * 5 * 64];
     mla_body<QDT>(a, units, nhg, stage, ropeb, work, xch, qr);
 }
 

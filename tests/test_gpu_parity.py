@@ -440,14 +440,14 @@ def test_append_skips_invalid_destinations(gpu):
 
 # ----------------------------------------------------------------------------- dequantize and decode, small
 def small_paged(seed, D=128, T=16, Hq=8, Hkv=2, lens=(300, 1, 77, 16), kbits=4, vbits=3, iters=2, G=None, mla=False,
-                R=0, dtype="bf16", qscale=1.0):
+                R=0, dtype="bf16", qscale=1.0, kshift=0.0):
     rng = np.random.default_rng(seed)
     G = G or D
     fk = W.Fmt(D, R, T, D, G, kbits, iters, 0)
     fv = None if mla else W.Fmt(D, 0, T, D, G, vbits, iters, 1)
     tst, tv, tp, tok = tiles_for(list(lens), T, rng)
     P = len(tp)
-    kx = heavy(rng, tok, Hkv, D)
+    kx = heavy(rng, tok, Hkv, D) + kshift
     if R:
         kx = np.concatenate([kx, rng.standard_normal((tok, Hkv, R))], axis=2)
     ks = make_src(kx, dtype)
@@ -495,6 +495,14 @@ DEC_SMALL = [
     dict(G=32, lens=(100, 33)),
     dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(700, 128, 1), iters=4),
     dict(mla=True, D=512, R=64, T=128, Hq=128, Hkv=1, lens=(300,), iters=4),
+    # the MLA kernel with fp32 and fp16 queries (rope query in bf16 hi + lo)
+    dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(300, 129), iters=4, dtype="f32"),
+    dict(mla=True, D=512, R=64, T=128, Hq=32, Hkv=1, lens=(260,), iters=4, dtype="f16"),
+    # MLA latent far from zero mean (zero points large against the scales), a nearly flat
+    # and a sharply peaked softmax: the fixed-point ranges of the int8 products
+    dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(400, 3), iters=4, kshift=20.0),
+    dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(2000,), iters=4, qscale=0.01),
+    dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(700,), iters=4, qscale=6.0),
     # 8-bit codes (test width) on the general decode kernel
     dict(T=32, lens=(250, 33, 31), kbits=8, vbits=8, iters=3),
     dict(T=128, lens=(300, 5), kbits=8, vbits=4, iters=4, Hq=16, Hkv=2),
