@@ -503,6 +503,11 @@ DEC_SMALL = [
     dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(400, 3), iters=4, kshift=20.0),
     dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(2000,), iters=4, qscale=0.01),
     dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(700,), iters=4, qscale=6.0),
+    # keys with a large mean (one rotated channel's normalizer far above the rest) on the
+    # GQA, paired-page and generic kernels
+    dict(T=128, lens=(600, 131), kbits=4, vbits=4, iters=4, kshift=20.0),
+    dict(T=16, lens=(1000, 17), kbits=3, vbits=3, Hq=16, Hkv=2, kshift=20.0),
+    dict(T=32, lens=(250, 33, 31), kbits=2, vbits=4, iters=3, kshift=20.0),
     # 8-bit codes (test width) on the general decode kernel
     dict(T=32, lens=(250, 33, 31), kbits=8, vbits=8, iters=3),
     dict(T=128, lens=(300, 5), kbits=8, vbits=4, iters=4, Hq=16, Hkv=2),
