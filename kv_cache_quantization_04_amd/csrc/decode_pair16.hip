@@ -29,6 +29,18 @@
 
 namespace kvq {
 
+// One Walsh-Hadamard stage on channel bit 4 K of a query row held four channels per lane
+// (lane u of a 32-lane group holds channels 4 u .. 4 u + 3): the lower member of each
+// pair takes own + partner, the upper one partner - own (stages at or above h skipped)
+template <int K>
+__device__ __forceinline__ void hstage(float (&x)[4], int u, int h) {
+    if (4 * K < h) {
+        const float sg = (u & K) ? -1.f : 1.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(sg, x[e], swz_xor<K>(x[e]));
+    }
+}
+
 template <int KB, int VB>
 __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     constexpr int T = 16;
@@ -39,6 +51,8 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     constexpr int IMG_BYTES = 4 * 2 * PI::BYTES;
     __shared__ __attribute__((aligned(16))) uint8_t pool[IMG_BYTES > RED_BYTES ? IMG_BYTES : RED_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t wrk[4][2][VB == 3 ? PI::VCW : 16];
+    // the rotated query of the (up to 8) heads, then max |qbar| of each head
+    __shared__ __attribute__((aligned(16))) float qlds[8 * MD + 8];
     float(*red_o)[16][MD + 1] = reinterpret_cast<float(*)[16][MD + 1]>(pool);
     float(*red_ml)[16][2] = reinterpret_cast<float(*)[16][2]>(pool + RED_O);
 
@@ -67,20 +81,18 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
         return p1;
     };
 
-    // the query's raw words, loaded before the first pages are requested
-    uint4 qraw[8];
-    {
-        const int64_t qb = ((int64_t)s * a.Hq + hk * g + (hv ? hh : 0)) * MD + lq * 32;
-        if (a.q_dtype == KVQ_F32) {
-            const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.q) + qb);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qraw[i] = p4[i];
-        } else {
-            const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qraw[i] = p4[i];
-#pragma unroll
-            for (int i = 4; i < 8; ++i) qraw[i] = uint4{0, 0, 0, 0};
+    // The query is rotated once per workgroup: thread t takes head t >> 5 (< g) and its
+    // channels 4 (t & 31) .. + 3, whose raw words are loaded before the first pages are
+    // requested (the vector-memory counter is in order: waiting for them leaves the
+    // page loads in flight).
+    const int qh = tid >> 5, qu = tid & 31;
+    uint4 qraw = {0, 0, 0, 0};
+    if (qh < g) {
+        const int64_t qb = ((int64_t)s * a.Hq + hk * g + qh) * MD + 4 * qu;
+        if (a.q_dtype == KVQ_F32) qraw = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.q) + qb);
+        else {
+            const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
+            qraw = uint4{v.x, v.y, 0, 0};
         }
     }
     asm volatile("" ::: "memory");  // keep the query loads ahead of the page requests
@@ -100,79 +112,63 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
         wait_vm_upto<0>();
     }
 
-    // ---- rotated query of head hh (columns of both halves hold the same head): lane
-    // (column l16, chunk lq), K-step st covers channels lq*32 + st*8 + e(kk)
-    float qv[32];
+    // ---- rotated query, once per workgroup: the Walsh-Hadamard butterflies on channel
+    // bits 0 and 1 run in registers, bits 2..6 across the head's 32 lanes (xor swizzles
+    // in groups of 32); blocks of h channels rotate separately
     {
+        float x[4];
         if (a.q_dtype == KVQ_F32) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 v = qraw[i];
-                qv[4 * i] = __uint_as_float(v.x); qv[4 * i + 1] = __uint_as_float(v.y);
-                qv[4 * i + 2] = __uint_as_float(v.z); qv[4 * i + 3] = __uint_as_float(v.w);
-            }
+            x[0] = __uint_as_float(qraw.x); x[1] = __uint_as_float(qraw.y);
+            x[2] = __uint_as_float(qraw.z); x[3] = __uint_as_float(qraw.w);
+        } else if (a.q_dtype == KVQ_BF16) {
+            x[0] = __uint_as_float(qraw.x << 16); x[1] = __uint_as_float(qraw.x & 0xffff0000u);
+            x[2] = __uint_as_float(qraw.y << 16); x[3] = __uint_as_float(qraw.y & 0xffff0000u);
         } else {
-            uint32_t w[16];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = qraw[i];
-                w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-            }
-            if (a.q_dtype == KVQ_BF16) {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    qv[2 * k] = __uint_as_float(w[k] << 16);
-                    qv[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    qv[2 * k] = half_bits_to_float(w[k] & 0xffffu);
-                    qv[2 * k + 1] = half_bits_to_float(w[k] >> 16);
-                }
-            }
+            x[0] = half_bits_to_float(qraw.x & 0xffffu); x[1] = half_bits_to_float(qraw.x >> 16);
+            x[2] = half_bits_to_float(qraw.y & 0xffffu); x[3] = half_bits_to_float(qraw.y >> 16);
         }
-        if (!hv)
-#pragma unroll
-            for (int i = 0; i < 32; ++i) qv[i] = 0.f;
-#pragma unroll
-        for (int b = 1; b < 32; b <<= 1)
-            if (b < a.kh)
-#pragma unroll
-                for (int i = 0; i < 32; ++i)
-                    if (!(i & b)) {
-                        const float x = qv[i], y = qv[i | b];
-                        qv[i] = x + y;
-                        qv[i | b] = x - y;
-                    }
-        const float s16 = (lq & 1) ? -1.f : 1.f, s32 = (lq & 2) ? -1.f : 1.f;
+        if (1 < a.kh) {
+            const float y0 = x[0], y2 = x[2];
+            x[0] = y0 + x[1]; x[1] = y0 - x[1];
+            x[2] = y2 + x[3]; x[3] = y2 - x[3];
+        }
+        if (2 < a.kh) {
+            const float y0 = x[0], y1 = x[1];
+            x[0] = y0 + x[2]; x[2] = y0 - x[2];
+            x[1] = y1 + x[3]; x[3] = y1 - x[3];
+        }
+        hstage<1>(x, qu, a.kh);
+        hstage<2>(x, qu, a.kh);
+        hstage<4>(x, qu, a.kh);
+        hstage<8>(x, qu, a.kh);
+        hstage<16>(x, qu, a.kh);
         const float qscale = 1.0f / sqrtf((float)a.kh);
-        const bool x16 = a.kh > 32, x32 = a.kh > 64;
-        // channel bits 5 and 6 across lanes 16 and 32 apart (permlane swaps: lo + s hi is the
-        // butterfly, s = -1 on the odd / upper member)
-        if (x16)
+        float m = 0.f;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                float lo, hi;
-                pair16(qv[i], lo, hi);
-                qv[i] = __builtin_fmaf(s16, hi, lo);
-            }
-        if (x32)
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                float lo, hi;
-                pair32(qv[i], lo, hi);
-                qv[i] = __builtin_fmaf(s32, hi, lo);
-            }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) qv[i] *= qscale;
+        for (int e = 0; e < 4; ++e) {
+            x[e] *= qscale;
+            m = fmaxf(m, fabsf(x[e]));
+        }
+        m = fmaxf(m, swz_xor<1>(m));
+        m = fmaxf(m, swz_xor<2>(m));
+        m = fmaxf(m, swz_xor<4>(m));
+        m = fmaxf(m, swz_xor<8>(m));
+        m = fmaxf(m, swz_xor<16>(m));
+        *reinterpret_cast<float4 *>(&qlds[qh * MD + 4 * qu]) = float4{x[0], x[1], x[2], x[3]};
+        if (qu == 0) qlds[8 * MD + qh] = m;
     }
-    // max |qbar| of the lane's head (all 128 channels): with the page's largest c_K it
-    // bounds max |q'|, which sets the power-of-two scaling of the query fold
-    float qvmax = 0.f;
+    lds_barrier();  // the page loads stay in flight
+    // lane (column l16, chunk lq), K-step st covers channels lq*32 + st*8 + e(kk): columns
+    // of both halves hold the same head; max |qbar| of the lane's head (all 128 channels)
+    // with the page's largest c_K bounds max |q'|, which sets the power-of-two scaling of
+    // the query fold
+    float qv[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qvmax = fmaxf(qvmax, fabsf(qv[i]));
-    qvmax = xlane_max_q(qvmax);
+    for (int i = 0; i < 8; ++i) {
+        const float4 v = *reinterpret_cast<const float4 *>(&qlds[hh * MD + lq * 32 + 4 * i]);
+        qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+    }
+    const float qvmax = qlds[8 * MD + hh];
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     float m_run = -INFINITY, l_run = 0.f;
