@@ -37,6 +37,19 @@
 
 namespace kvq {
 
+// One Walsh-Hadamard stage on channel bit 3 + log2 K of a query row held eight channels
+// per lane (lane u of a 16-lane group holds channels 8 u .. 8 u + 7): the lower member
+// of each pair takes own + partner, the upper one partner - own (stages at or above h
+// skipped)
+template <int K>
+__device__ __forceinline__ void qstage(float (&x)[8], int u, int h) {
+    if (8 * K < h) {
+        const float sg = (u & K) ? -1.f : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(sg, x[e], swz_xor<K>(x[e]));
+    }
+}
+
 template <int T, int KB, int VB, bool PF, bool DB>
 __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = T / 16;                 // 16-token M-tiles of the score product
@@ -64,6 +77,13 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t pool[IMG_BYTES > RED_BYTES ? IMG_BYTES : RED_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t pool2[DB ? 4 * PI::BYTES : 16];
     __shared__ __attribute__((aligned(16))) uint8_t wrk[4][STAGED ? PI::VCW : 16];
+    // the rotated query of the workgroup's 16 columns (row stride padded against bank
+    // conflicts); with two images per wave it borrows the second ones, which receive
+    // nothing before the page walk
+    constexpr int QLD = MD + 4;
+    static_assert(!DB || 4 * PI::BYTES >= 16 * QLD * 4, "query rows fit the second images");
+    __shared__ __attribute__((aligned(16))) float qlds_own[DB ? 4 : 16 * QLD];
+    float *qlds = DB ? reinterpret_cast<float *>(pool2) : qlds_own;
     float(*red_o)[16][MD + 1] = reinterpret_cast<float(*)[16][MD + 1]>(pool);
     float(*red_ml)[16][2] = reinterpret_cast<float(*)[16][2]>(pool + RED_O);
 
@@ -112,24 +132,26 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         const int page = page_of(q);
         return page >= 0 && page < a.num_pages;
     };
-    // The query's raw words are loaded before the first page is requested: the vector-
-    // memory counter is in order, so waiting for the query then leaves the page's loads
-    // in flight while the query is converted and rotated.
-    uint4 qraw[8];
+    // The query rows are loaded before the first page is requested: the vector-memory
+    // counter is in order, so waiting for the query then leaves the page's loads in
+    // flight while the query is converted and rotated. The workgroup rotates each of
+    // its 16 columns once (all four waves read the same columns): thread t holds
+    // channels 8 (t mod 16) .. + 7 of column t / 16.
+    const int qcol = tid >> 4, qu = tid & 15;
+    uint4 qraw[2];
+    const int qpos = PF ? cb * ppb + qcol / g : 0;
+    const bool qok = PF ? qpos < a.Lq : qcol < g;
     {
-        const int64_t qrow = PF ? (int64_t)s * a.Lq + (hv ? pos : 0) : s;
-        const int64_t qb = (qrow * a.Hq + hk * g + (hv ? hh : 0)) * MD + lq * 32;
-        // 32 consecutive channels: 16-byte loads under one (uniform) dtype branch
+        const int qhh = PF ? qcol - (qcol / g) * g : qcol;
+        const int64_t qrow = PF ? (int64_t)s * a.Lq + (qok ? qpos : 0) : s;
+        const int64_t qb = (qrow * a.Hq + hk * g + (qok ? qhh : 0)) * MD + 8 * qu;
         if (a.q_dtype == KVQ_F32) {
             const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.q) + qb);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qraw[i] = p4[i];
+            qraw[0] = p4[0];
+            qraw[1] = p4[1];
         } else {
-            const uint4 *p4 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qraw[i] = p4[i];
-#pragma unroll
-            for (int i = 4; i < 8; ++i) qraw[i] = uint4{0, 0, 0, 0};
+            qraw[0] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
+            qraw[1] = uint4{0, 0, 0, 0};
         }
     }
     asm volatile("" ::: "memory");  // keep the query loads ahead of the page requests
@@ -171,66 +193,64 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
         }
     }
 
-    // ---- rotated query qbar = q Q of head l16 (< g; other lanes hold zeros) in the
-    // B-operand layout: lane (head l16, chunk lq), K-step st covers channels
-    // lq*32 + st*8 + e(kk); qv[st*8 + e] = qbar[lq*32 + st*8 + e] / sqrt(h). The
-    // Walsh-Hadamard butterflies on channel bits 0..4 run in registers, bits 5 and 6
-    // across lanes 16 and 32 apart; blocks of h channels rotate separately.
-    float qv[32];
+    // ---- rotated query qbar = q Q / sqrt(h), once per workgroup: the Walsh-Hadamard
+    // butterflies on channel bits 0..2 run in registers, bits 3..6 across the column's
+    // 16 lanes (xor swizzles); blocks of h channels rotate separately. Columns without a
+    // query (no head, or past the chunk) are zero.
     {
+        float x[8];
         if (a.q_dtype == KVQ_F32) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 v = qraw[i];
-                qv[4 * i] = __uint_as_float(v.x); qv[4 * i + 1] = __uint_as_float(v.y);
-                qv[4 * i + 2] = __uint_as_float(v.z); qv[4 * i + 3] = __uint_as_float(v.w);
-            }
+            x[0] = __uint_as_float(qraw[0].x); x[1] = __uint_as_float(qraw[0].y);
+            x[2] = __uint_as_float(qraw[0].z); x[3] = __uint_as_float(qraw[0].w);
+            x[4] = __uint_as_float(qraw[1].x); x[5] = __uint_as_float(qraw[1].y);
+            x[6] = __uint_as_float(qraw[1].z); x[7] = __uint_as_float(qraw[1].w);
         } else {
-            uint32_t w[16];
+            const uint32_t w[4] = {qraw[0].x, qraw[0].y, qraw[0].z, qraw[0].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = qraw[i];
-                w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-            }
-            if (a.q_dtype == KVQ_BF16) {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    qv[2 * k] = __uint_as_float(w[k] << 16);
-                    qv[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    qv[2 * k] = half_bits_to_float(w[k] & 0xffffu);
-                    qv[2 * k + 1] = half_bits_to_float(w[k] >> 16);
+            for (int k = 0; k < 4; ++k) {
+                if (a.q_dtype == KVQ_BF16) {
+                    x[2 * k] = __uint_as_float(w[k] << 16);
+                    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+                } else {
+                    x[2 * k] = half_bits_to_float(w[k] & 0xffffu);
+                    x[2 * k + 1] = half_bits_to_float(w[k] >> 16);
                 }
             }
         }
-        if (!hv)
+        if (!qok)
 #pragma unroll
-            for (int i = 0; i < 32; ++i) qv[i] = 0.f;
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
 #pragma unroll
-        for (int b = 1; b < 32; b <<= 1)
+        for (int b = 1; b < 8; b <<= 1)
             if (b < a.kh)
 #pragma unroll
-                for (int i = 0; i < 32; ++i)
+                for (int i = 0; i < 8; ++i)
                     if (!(i & b)) {
-                        const float x = qv[i], y = qv[i | b];
-                        qv[i] = x + y;
-                        qv[i | b] = x - y;
+                        const float y0 = x[i], y1 = x[i | b];
+                        x[i] = y0 + y1;
+                        x[i | b] = y0 - y1;
                     }
-        const float s16 = (lq & 1) ? -1.f : 1.f, s32 = (lq & 2) ? -1.f : 1.f;
+        qstage<1>(x, qu, a.kh);
+        qstage<2>(x, qu, a.kh);
+        qstage<4>(x, qu, a.kh);
+        qstage<8>(x, qu, a.kh);
         const float qscale = 1.0f / sqrtf((float)a.kh);
-        const bool x16 = a.kh > 32, x32 = a.kh > 64;
-        if (x16)
 #pragma unroll
-            for (int i = 0; i < 32; ++i) qv[i] = __builtin_fmaf(s16, qv[i], __shfl_xor(qv[i], 16, 64));
-        if (x32)
-#pragma unroll
-            for (int i = 0; i < 32; ++i) qv[i] = __builtin_fmaf(s32, qv[i], __shfl_xor(qv[i], 32, 64));
-#pragma unroll
-        for (int i = 0; i < 32; ++i) qv[i] *= qscale;
+        for (int e = 0; e < 8; ++e) x[e] *= qscale;
+        float *qd = &qlds[qcol * QLD + 8 * qu];
+        *reinterpret_cast<float4 *>(qd) = float4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<float4 *>(qd + 4) = float4{x[4], x[5], x[6], x[7]};
     }
+    lds_barrier();  // the page loads stay in flight
+    // B-operand layout: lane (column l16, chunk lq), K-step st covers channels
+    // lq*32 + st*8 + e(kk); qv[st*8 + e] = qbar[lq*32 + st*8 + e]
+    float qv[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 v = *reinterpret_cast<const float4 *>(&qlds[l16 * QLD + lq * 32 + 4 * i]);
+        qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+    }
+    if constexpr (DB) lds_barrier();  // every wave has its rows before the next pages' copies land
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     float m_run = -INFINITY, l_run = 0.f;
