@@ -360,8 +360,7 @@ def run_config(ci, args, torch, K, W, dev):
               if cfg.fv is not None else [None] * ring)
     max_len = int(cfg.seq_lens.max())
     splits = K.kv_decode_attn_default_splits(kcache[0], vcache[0], cfg.num_seqs, cfg.num_q_heads, max_len)
-    ws = torch.empty(K.kv_decode_attn_workspace_bytes(cfg.num_seqs, cfg.num_q_heads, cfg.dv, splits),
-                     dtype=torch.uint8, device=dev)
+    ws = K.decode_workspace(K.kv_decode_attn_workspace_bytes(cfg.num_seqs, cfg.num_q_heads, cfg.dv, splits), dev)
     out = torch.empty((cfg.num_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device=dev)
     # K and V in one launch (kv_quantize_kv) where the library takes the pair of formats
     pair = False

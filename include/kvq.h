@@ -164,7 +164,13 @@ kvq_status kv_dequantize(const kvq_cache *src, int32_t num_tiles, const int32_t 
 int32_t kv_decode_attn_default_splits(const kvq_cache *k, const kvq_cache *v, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_seq_len);
 
-/* Workspace bytes kv_decode_attn needs for these sizes (num_splits >= 1). */
+/* Bytes at the head of a kv_decode_attn workspace that hold split-merge arrival
+ * counters (one 32-bit counter per sequence and kv head, up to 16384 of them). */
+#define KVQ_DECODE_COUNTER_BYTES (64u << 10)
+
+/* Workspace bytes kv_decode_attn needs for these sizes (num_splits >= 1):
+ * KVQ_DECODE_COUNTER_BYTES plus num_seqs * num_q_heads * num_splits *
+ * (head_dim_v + 2) floats of split partials. */
 size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,
                                       int32_t num_splits);
 
@@ -179,7 +185,18 @@ size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  *   block_table (device int32): [num_seqs][block_table_stride].
  *   seq_lens (device int32): [num_seqs], each in [0, max_seq_len].
  *   out (device fp32): [num_seqs][num_q_heads][Dv], Dv = (v ? v : k)->fmt.head_dim.
- *   workspace (device): at least kv_decode_attn_workspace_bytes(...) bytes.
+ *   workspace (device): at least kv_decode_attn_workspace_bytes(...) bytes,
+ *     4-byte aligned. Its first KVQ_DECODE_COUNTER_BYTES bytes are counters that
+ *     must be zero when the workspace is first used (a zero-filled allocation, or
+ *     one clear after allocating it); every call leaves them zero, and
+ *     kv_prefill_attn never writes them, so a workspace stays ready between calls
+ *     of both. Other writes to those bytes require clearing them again. The rest
+ *     is overwritten. On the matrix-core kernels (128-channel K and V), when the
+ *     grid of num_seqs * H * splits workgroups is at most 512 (one round on the
+ *     chip), the last workgroup to finish among the splits of each (sequence,
+ *     kv head) merges them (it counts arrivals there); larger grids and the other
+ *     kernels merge in a second kernel. Calls that overlap in time must use
+ *     different workspaces.
  * The score rotation and normalizer fold is exact in real arithmetic; in fp32
  * the result differs from fp64 dequantize-then-attention by rounding only.
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (layouts: K token-major, V channel-major,
@@ -201,9 +218,10 @@ kvq_status kv_decode_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int3
  * until the process ends) instead of a caller workspace. The call allocates
  * nothing; the caller still passes q, the caches, the tables and out.
  * The first call on a device looks up that device's copy of the array (with the
- * device current); later calls reuse the address. The array keeps the last call's
- * partials: calls on one GPU that overlap in time (different streams, or host
- * threads) race on it and must be ordered by the caller.
+ * device current) and clears its split-merge counters (a kernel on `stream`,
+ * ahead of the decode); later calls reuse the address. The array keeps the last
+ * call's partials: calls on one GPU that overlap in time (different streams, or
+ * host threads) race on it and must be ordered by the caller.
  * Errors: as kv_decode_attn; KVQ_EWORKSPACE when the partials,
  * kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, Dv, splits), exceed
  * KVQ_NOALLOC_SCRATCH_BYTES (nothing is launched); KVQ_ELAUNCH when the runtime
@@ -279,7 +297,8 @@ const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const 
  *   out (device fp32): [num_seqs][chunk_len][num_q_heads][Dv].
  *   workspace (device): at least kv_prefill_attn_workspace_bytes(...) bytes,
  *     256-byte aligned; holds the split partials, the virtual block table and
- *     the virtual lengths.
+ *     the virtual lengths after KVQ_DECODE_COUNTER_BYTES bytes that it leaves
+ *     untouched (kv_decode_attn's counters, when the workspace also serves it).
  *   num_splits: 0 = kv_prefill_attn_default_splits(...).
  * Other arguments and errors as kv_decode_attn; KVQ_EUNSUPPORTED when
  * num_seqs * chunk_len exceeds 2^24. */

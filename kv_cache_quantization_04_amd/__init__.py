@@ -11,7 +11,8 @@ libkvq.so. PyTorch supplies device memory (tensor.data_ptr()) and the stream
     kv_quantize_kernel_name, kv_decode_attn_kernel_name,
     kv_prefill_attn_kernel_name, kvq_status_str
 
-plus ``DeviceCache``, a holder of the four device arrays of one cache.
+plus ``DeviceCache``, a holder of the four device arrays of one cache, and
+``decode_workspace``, a workspace for kv_decode_attn with its counters cleared.
 Importing this module fails if libkvq.so has not been built: there is no
 fallback implementation.
 """
@@ -282,8 +283,22 @@ def kv_prefill_attn_kernel_name(q, k: DeviceCache, v: Optional[DeviceCache]) -> 
     return r.decode() if r is not None else None
 
 
+# bytes at the head of a decode workspace holding the split-merge arrival counters:
+# zero when the workspace is first used, left zero by every call
+KVQ_DECODE_COUNTER_BYTES = 64 << 10
+
+
 def kv_decode_attn_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim_v: int, num_splits: int) -> int:
     return int(_lib.kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, head_dim_v, num_splits))
+
+
+def decode_workspace(num_bytes: int, device):
+    """A decode workspace of `num_bytes` bytes, ready for kv_decode_attn (its counter
+    bytes cleared) and for kv_prefill_attn."""
+    torch = _torch()
+    ws = torch.empty(max(int(num_bytes), KVQ_DECODE_COUNTER_BYTES), dtype=torch.uint8, device=device)
+    ws[:KVQ_DECODE_COUNTER_BYTES].zero_()
+    return ws
 
 
 def kv_decode_attn(q, k: DeviceCache, v: Optional[DeviceCache], block_table, seq_lens, max_seq_len: int,
@@ -295,7 +310,7 @@ def kv_decode_attn(q, k: DeviceCache, v: Optional[DeviceCache], block_table, seq
         num_splits = kv_decode_attn_default_splits(k, v, B, Hq, max_seq_len)
     need = kv_decode_attn_workspace_bytes(B, Hq, dv, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(need, q.device)
     if out is None:
         out = torch.empty((B, Hq, dv), dtype=torch.float32, device=q.device)
     _check(_lib.kv_decode_attn(_ptr(q), _dtype_code(q), B, Hq, ctypes.byref(k.struct),

@@ -112,9 +112,15 @@ kvq::QuantArgs quant_args(const kvq_cache *dst, const void *src, int32_t src_dty
 // per GPU the library runs on, held until the process ends. In host code `scratch`
 // names a host-side stand-in, never the device memory: the per-device address comes
 // from hipGetSymbolAddress (taken once per device, with that device current) and only
-// that address is passed to kernels. No kernel reads a partial it has not written, so
-// nothing in it needs clearing between calls.
+// that address is passed to kernels. Its head holds the split-merge arrival counters,
+// cleared on the device's first call (by a kernel on the caller's stream) and left at
+// zero by every call; no kernel reads a partial it has not written.
 static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+__global__ void clear_words_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
 
 constexpr int SCRATCH_MAX_DEVICES = 64;
 std::mutex scratch_mu;
@@ -137,6 +143,11 @@ void *scratch_for(hipStream_t stream) {
     if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
     void *ptr = nullptr;
     const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && ptr) {
+        // (a launch error surfaces in the caller's launch check)
+        constexpr int nw = KVQ_DECODE_COUNTER_BYTES / 4;
+        hipLaunchKernelGGL(clear_words_kernel, dim3((nw + 255) / 256), dim3(256), 0, stream, (uint32_t *)ptr, nw);
+    }
     if (dev != cur) (void)hipSetDevice(cur);
     if (e != hipSuccess || !ptr) return nullptr;
     scratch_ptr[dev] = ptr;
@@ -302,7 +313,7 @@ const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const 
 size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,
                                       int32_t num_splits) {
     if (num_seqs < 0 || num_q_heads <= 0 || head_dim_v <= 0 || num_splits <= 0) return 0;
-    return (size_t)num_seqs * num_q_heads * num_splits * (head_dim_v + 2) * sizeof(float);
+    return KVQ_DECODE_COUNTER_BYTES + (size_t)num_seqs * num_q_heads * num_splits * (head_dim_v + 2) * sizeof(float);
 }
 
 kvq_status kv_decode_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads, const kvq_cache *k,
@@ -388,7 +399,9 @@ kvq_status kv_prefill_attn(const void *q, int32_t q_dtype, int32_t num_seqs, int
     a.seq_lens = vlens;
     a.sm = sm_scale;
     a.splits = splits;
-    a.ws = (float *)workspace;
+    // the counter bytes at the head stay untouched (a workspace may also serve decode)
+    a.ws = (float *)((char *)workspace + KVQ_DECODE_COUNTER_BYTES);
+    a.cnt = nullptr;
     a.out = out;
     if (!kvq::launch_prefill(p, a, stream)) return KVQ_EUNSUPPORTED;
     return launched();
@@ -416,7 +429,7 @@ kvq_status decode_attn_impl(const void *q, int32_t q_dtype, int32_t num_seqs, in
     const int splits = num_splits > 0 ? num_splits : kvq::decode_default_splits(a, max_seq_len);
     if (workspace_bytes < kv_decode_attn_workspace_bytes(num_seqs, num_q_heads, a.Dv, splits)) return KVQ_EWORKSPACE;
     if (have_ws) {
-        if (!workspace) return KVQ_EWORKSPACE;
+        if (!workspace || ((uintptr_t)workspace & 3)) return KVQ_EWORKSPACE;
     } else if (!(workspace = scratch_for(stream))) {
         return KVQ_ELAUNCH;
     }
@@ -427,7 +440,8 @@ kvq_status decode_attn_impl(const void *q, int32_t q_dtype, int32_t num_seqs, in
     a.seq_lens = seq_lens;
     a.sm = sm_scale;
     a.splits = splits;
-    a.ws = (float *)workspace;
+    a.cnt = (uint32_t *)workspace;
+    a.ws = (float *)((char *)workspace + KVQ_DECODE_COUNTER_BYTES);
     a.out = out;
     a.max_len = max_seq_len;
     if (!kvq::launch_decode(a, stream)) return KVQ_EUNSUPPORTED;

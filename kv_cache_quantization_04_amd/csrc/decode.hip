@@ -8,6 +8,7 @@
 // Grid: (split, kv head x head chunk, sequence); each workgroup walks its page
 // range through the block table and writes (m, l, o') to the workspace.
 #include "common.h"
+#include "decode_merge.h"
 #include "launch.h"
 #include "xlane.h"
 
@@ -178,162 +179,6 @@ __global__ void __launch_bounds__(DEC_NT) decode_generic_kernel(DecodeArgs a) {
     }
 }
 
-// Merge the split partials of one (sequence, query head), normalize, rotate back.
-// One wave per (sequence, query head), no workgroup barriers: lane l owns the
-// E = Dv / 64 consecutive channels E l .. E l + E - 1. The lanes load the split
-// maxima and sums in parallel (split i on lane i mod 64), reduce them across the
-// wave, and leave the weights exp(m_i - M) in a wave-private LDS array; the
-// output pass then streams the partial outputs with independent loads. The
-// inverse rotation runs in registers (channel bits below E) and across lanes.
-constexpr int RED_MAX_SPLITS = 1024;
-constexpr int RED_WAVES = 4;
-
-__device__ __forceinline__ float wave_max(float v) {
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-// Up to RED_FAST splits with at most two channels per lane: every load in one round
-// (split i's maximum and sum on lane i, all partial outputs on every lane), the
-// maxima and sums reduced over the first 16 lanes with DPP row operations and read
-// back as wave-uniform values; the outputs accumulate in split order, as below.
-constexpr int RED_FAST = 16;
-
-template <int E>
-__device__ __forceinline__ void reduce_weights_fast(const float *w, int S, int lane, float (&part)[RED_FAST][E],
-                                                    float (&e)[RED_FAST], float &l) {
-    constexpr int Dv = 64 * E;
-    float mi = -INFINITY, li = 0.f;
-    if (lane < S) {
-        mi = w[(int64_t)lane * (Dv + 2) + Dv];
-        li = w[(int64_t)lane * (Dv + 2) + Dv + 1];
-    }
-#pragma unroll
-    for (int i = 0; i < RED_FAST; ++i) {
-        if (i < S) {  // uniform
-            const float *wi = w + (int64_t)i * (Dv + 2) + E * lane;
-            if constexpr (E == 1) part[i][0] = wi[0];
-            else {
-                const float2 v = *reinterpret_cast<const float2 *>(wi);
-                part[i][0] = v.x;
-                part[i][1] = v.y;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < E; ++k) part[i][k] = 0.f;
-        }
-    }
-    const float Mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_max16(mi))));
-    const float ei = mi == -INFINITY ? 0.f : __expf(mi - Mx);
-    l = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_sum16(ei * li))));
-#pragma unroll
-    for (int i = 0; i < RED_FAST; ++i) e[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ei), i));
-}
-
-template <int E>
-__device__ __forceinline__ void reduce_one(const DecodeArgs &a, int s, int hq, int lane, float *wgt) {
-    constexpr int Dv = 64 * E;
-    const float *w = a.ws + ((int64_t)s * a.Hq + hq) * a.splits * (Dv + 2);
-    float acc[E];
-#pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] = 0.f;
-    float l = 0.f;
-    if (E <= 2 && a.splits <= RED_FAST) {
-        float part[RED_FAST][E], e[RED_FAST];
-        reduce_weights_fast<E>(w, a.splits, lane, part, e, l);
-#pragma unroll
-        for (int i = 0; i < RED_FAST; ++i)
-            if (i < a.splits)
-#pragma unroll
-                for (int k = 0; k < E; ++k) acc[k] = __builtin_fmaf(e[i], part[i][k], acc[k]);
-    } else {
-    float M = -INFINITY;
-    for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, w[(int64_t)i * (Dv + 2) + Dv]);
-    M = wave_max(M);
-    for (int i = lane; i < a.splits; i += 64) {
-        const float mi = w[(int64_t)i * (Dv + 2) + Dv];
-        const float e = mi == -INFINITY ? 0.f : __expf(mi - M);
-        wgt[i] = e;
-        l = __builtin_fmaf(e, w[(int64_t)i * (Dv + 2) + Dv + 1], l);
-    }
-    l = wave_sum(l);  // the weights' LDS writes are ordered before the reads below (one wave)
-#pragma unroll 4
-    for (int i = 0; i < a.splits; ++i) {
-        const float *wi = w + (int64_t)i * (Dv + 2) + E * lane;
-        const float e = wgt[i];
-#pragma unroll
-        for (int k = 0; k < E; k += (E > 1 ? 2 : 1)) {
-            if constexpr (E == 1) acc[0] = __builtin_fmaf(e, wi[0], acc[0]);
-            else {
-                const float2 v = *reinterpret_cast<const float2 *>(wi + k);
-                acc[k] = __builtin_fmaf(e, v.x, acc[k]);
-                acc[k + 1] = __builtin_fmaf(e, v.y, acc[k + 1]);
-            }
-        }
-    }
-    }
-    const float invl = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] *= invl;
-    // Walsh-Hadamard over blocks of vh channels: channel c = E lane + k. Two channels
-    // per lane and one block of 128 (head_dim 128): the lane stages by DPP, the LDS
-    // crossbar (ds_swizzle, no memory) and permlane swaps instead of LDS permutes
-    if (E == 2 && a.vh == 128) {
-        {
-            const float x = acc[0], y = acc[E - 1];
-            acc[0] = x + y;
-            acc[E - 1] = x - y;
-        }
-        auto stage = [&](auto pv_of, int m) {
-            const bool upper = (lane & m) != 0;
-#pragma unroll
-            for (int k = 0; k < E; ++k) {
-                const float pv = pv_of(acc[k]);
-                acc[k] = upper ? pv - acc[k] : acc[k] + pv;
-            }
-        };
-        stage([](float v) { return dpp<DPP_QUAD_XOR1>(v); }, 1);
-        stage([](float v) { return dpp<DPP_QUAD_XOR2>(v); }, 2);
-        stage([](float v) { return swz_xor<4>(v); }, 4);
-        stage([](float v) { return swz_xor<8>(v); }, 8);
-#pragma unroll
-        for (int k = 0; k < E; ++k) {
-            float lo, hi;
-            pair16(acc[k], lo, hi);
-            acc[k] = (lane & 16) ? lo - hi : lo + hi;
-            pair32(acc[k], lo, hi);
-            acc[k] = (lane & 32) ? lo - hi : lo + hi;
-        }
-    } else
-    for (int len = 1; len < a.vh; len <<= 1) {
-        if (len < E) {
-#pragma unroll
-            for (int k = 0; k < E; ++k)
-                if (!(k & len) && (k | len) < E) {
-                    const float x = acc[k], y = acc[k | len];
-                    acc[k] = x + y;
-                    acc[k | len] = x - y;
-                }
-        } else {
-            const int m = len / E;  // partner lane
-            const bool upper = (lane & m) != 0;
-#pragma unroll
-            for (int k = 0; k < E; ++k) {
-                const float pv = __shfl_xor(acc[k], m, 64);
-                acc[k] = upper ? pv - acc[k] : acc[k] + pv;
-            }
-        }
-    }
-    const float scl = 1.0f / sqrtf((float)a.vh);
-    float *out = a.out + ((int64_t)s * a.Hq + hq) * Dv + E * lane;
-#pragma unroll
-    for (int k = 0; k < E; ++k) out[k] = acc[k] * scl;
-}
-
 __global__ void __launch_bounds__(64 * RED_WAVES) decode_reduce_kernel(DecodeArgs a) {
     __shared__ float wgt[RED_WAVES][RED_MAX_SPLITS];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -418,7 +263,9 @@ const char *decode_kernel_name(const DecodeArgs &a) {
 
 // chunked prefill on the MFMA kernel: a.B real sequences of a.Lq positions; the
 // split partials, the reduce and the output cover a.B * a.Lq rows
-bool launch_decode_chunk(const DecodeArgs &a, hipStream_t stream) {
+bool launch_decode_chunk(const DecodeArgs &a_in, hipStream_t stream) {
+    DecodeArgs a = a_in;
+    a.cnt = nullptr;
     if (a.splits > RED_MAX_SPLITS || a.Lq <= 0 || !decode_mfma_supported(a)) return false;
     if (!launch_decode_mfma(a, stream)) return false;
     DecodeArgs r = a;
@@ -428,7 +275,21 @@ bool launch_decode_chunk(const DecodeArgs &a, hipStream_t stream) {
     return true;
 }
 
-bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
+// The matrix-core GQA kernels merge the splits themselves (the last workgroup of each
+// sequence and kv head, counted in a.cnt) when the grid is one round of workgroups on
+// the chip (at most two per compute unit): the merge then replaces the reduce kernel's
+// launch and ramp with a few memory round trips at the end of the last workgroups.
+// Larger grids keep the reduce kernel: every workgroup would wait for its partial
+// stores to complete before counting its arrival, and with several rounds of
+// workgroups those waits add up to more than the launch they save. Grids beyond the
+// counters, and the other kernels, use the reduce kernel too.
+constexpr int64_t MERGE_MAX_WORKGROUPS = 512;
+
+bool launch_decode(const DecodeArgs &a_in, hipStream_t stream) {
+    DecodeArgs a = a_in;
+    const bool counters = a.cnt && (int64_t)a.B * a.Hkv <= MERGE_COUNTERS &&
+                          (int64_t)a.B * a.Hkv * a.splits <= MERGE_MAX_WORKGROUPS;
+    a.cnt = nullptr;
     if (a.splits > RED_MAX_SPLITS) return false;
     if (decode_mla_supported(a)) {
         if (!launch_decode_mla(a, stream)) return false;
@@ -437,8 +298,9 @@ bool launch_decode(const DecodeArgs &a, hipStream_t stream) {
     }
     if (a.B > 65535) return false;  // the grids below put sequences on z
     if (decode_mfma_supported(a)) {
+        if (counters) a.cnt = a_in.cnt;
         if (!launch_decode_mfma(a, stream)) return false;
-        launch_reduce(a, stream);
+        if (!a.cnt) launch_reduce(a, stream);
         return true;
     }
     const size_t smem = sizeof(float) * (2 * a.hc * a.D + a.hc * (a.D / a.kG) + a.hc * a.R + a.hc * a.T + 3 * a.hc);

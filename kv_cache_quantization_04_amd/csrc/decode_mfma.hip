@@ -32,6 +32,7 @@
 // and with long splits (DB) into two alternating images, the next page's copies
 // travelling while the current page is computed.
 #include "common.h"
+#include "decode_merge.h"
 #include "decode_mfma.h"
 #include "launch.h"
 
@@ -585,12 +586,21 @@ __global__ void __launch_bounds__(MNT) decode_mfma_kernel(DecodeArgs a) {
             }
         }
         float *wsr = a.ws + (wrow * a.splits + split) * (MD + 2);
-        wsr[j] = acc;
+        // device-coherent stores when the last workgroup of the unit reads them
+        auto put = [&](int i, float v) {
+            if (a.cnt) store_dev(wsr + i, v);
+            else wsr[i] = v;
+        };
+        put(j, acc);
         if (j == 0) {
             // partial max stored in natural-log units for the merge kernel
-            wsr[MD] = M == -INFINITY ? -INFINITY : M * 0.6931471805599453f;
-            wsr[MD + 1] = lsum;
+            put(MD, M == -INFINITY ? -INFINITY : M * 0.6931471805599453f);
+            put(MD + 1, lsum);
         }
+    }
+    if constexpr (!PF) {
+        static_assert(sizeof(pool) >= 4 * RED_MAX_SPLITS * sizeof(float), "merge weights fit the pool");
+        if (a.cnt) merge_if_last<MNT, MD / 64>(a, s, hk, reinterpret_cast<float *>(pool));
     }
 }
 

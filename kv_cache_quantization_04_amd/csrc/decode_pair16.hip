@@ -23,6 +23,7 @@
 // and written to the wave's two LDS images at the top of the next pair; a wave with an
 // odd number of pages ends with page B a copy of page A whose tokens are all masked.
 #include "common.h"
+#include "decode_merge.h"
 #include "decode_mfma.h"
 #include "launch.h"
 #include "xlane.h"
@@ -424,12 +425,19 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
                 }
             }
         float *wsr = a.ws + (wrow * a.splits + split) * (MD + 2);
-        wsr[j] = acc;
+        // device-coherent stores when the last workgroup of the unit reads them
+        auto put = [&](int i, float v) {
+            if (a.cnt) store_dev(wsr + i, v);
+            else wsr[i] = v;
+        };
+        put(j, acc);
         if (j == 0) {
-            wsr[MD] = M == -INFINITY ? -INFINITY : M * 0.6931471805599453f;
-            wsr[MD + 1] = lsum;
+            put(MD, M == -INFINITY ? -INFINITY : M * 0.6931471805599453f);
+            put(MD + 1, lsum);
         }
     }
+    static_assert(sizeof(pool) >= 4 * RED_MAX_SPLITS * sizeof(float), "merge weights fit the pool");
+    if (a.cnt) merge_if_last<MNT, MD / 64>(a, s, hk, reinterpret_cast<float *>(pool));
 }
 
 bool decode_mfma_supported(const DecodeArgs &a);

@@ -46,6 +46,9 @@ struct DecodeArgs {
     float sm;
     int splits;
     float *ws;
+    // arrival counters of the in-kernel split merge, one per (sequence, kv head), zero
+    // between calls; null: the reduce kernel merges
+    uint32_t *cnt;
     float *out;
     // chunked prefill on the MFMA kernel: Lq > 0 query positions per sequence (q rows
     // [B][Lq][Hq]), position i attending to tokens 0 .. seq_lens[b] - Lq + i; the

@@ -120,7 +120,9 @@ def test_decode_argument_errors():
     assert st(ws=None) == K.KVQ_EWORKSPACE
     assert st(kk=vc, vv=kc) == K.KVQ_EUNSUPPORTED    # layouts swapped
     need = K.kv_decode_attn_workspace_bytes(2, 8, 128, 3)
-    assert need == 2 * 8 * 3 * 130 * 4
+    assert need == K.KVQ_DECODE_COUNTER_BYTES + 2 * 8 * 3 * 130 * 4  # counters, then (m, l, o) per split
+    assert K.KVQ_DECODE_COUNTER_BYTES == 64 << 10 == K._lib.kv_decode_attn_workspace_bytes(0, 1, 1, 1)
+    assert st(ws=FAKE + 2) == K.KVQ_EWORKSPACE       # counters need 4-byte alignment
     assert st(splits=3, ws_bytes=need - 1) == K.KVQ_EWORKSPACE
     assert st(splits=1025) == K.KVQ_EUNSUPPORTED     # more split partials than the merge takes
     # no sequences: nothing to do, nothing launched (block table and workspace not needed)
@@ -242,8 +244,9 @@ def test_prefill_argument_errors():
     fk = K.make_format(128, 0, 16, 128, 128, 4, 2, K.KVQ_TOKEN_MAJOR)
     fv = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_CHANNEL_MAJOR)
     need = K._lib.kv_prefill_attn_workspace_bytes(2, 4, 8, 128, 1, 4)
-    # decode partials for 8 virtual sequences (256-byte rounded) + virtual table and lengths
-    assert need == ((8 * 8 * 1 * 130 * 4 + 255) // 256) * 256 + 8 * 4 * 4 + 8 * 4
+    # decode counters (left untouched) and partials for 8 virtual sequences (256-byte
+    # rounded) + virtual table and lengths
+    assert need == K.KVQ_DECODE_COUNTER_BYTES + ((8 * 8 * 1 * 130 * 4 + 255) // 256) * 256 + 8 * 4 * 4 + 8 * 4
     assert K._lib.kv_prefill_attn_workspace_bytes(2, 0, 8, 128, 1, 4) == 0
     assert prefill_status(fk, fv, num_seqs=0) == K.KVQ_OK
     assert prefill_status(fk, fv, chunk=0) == K.KVQ_EINVAL

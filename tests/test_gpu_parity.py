@@ -617,6 +617,57 @@ def test_decode_closed_forms(gpu):
     assert np.all(out[1] == 0)
 
 
+def decode_inputs(w):
+    dk = gpu_quantize(w["fk"], w["ks"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
+    dv = gpu_quantize(w["fv"], w["vs"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"]) if w["fv"] is not None else None
+    return dk, dv, to_dev(w["q"], w["dtype"]), i32(w["bt"]), i32(w["lens"]), int(w["lens"].max())
+
+
+def test_decode_workspace_counters_reused(gpu):
+    """One workspace across decode calls of different shapes, split counts and kernels,
+    and a prefill call: each result is bit-identical to the same call on a fresh
+    workspace, and the counter bytes are zero after every call."""
+    cases = [dict(T=16, lens=(300, 1, 77, 16), Hq=8, Hkv=2),                      # paired pages
+             dict(T=128, lens=(600, 131, 40), kbits=4, vbits=4, iters=4, Hq=16, Hkv=4),  # matrix-core GQA
+             dict(T=32, lens=(250, 33), kbits=3, vbits=2, Hq=4, Hkv=4),
+             dict(mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(300, 7), iters=4)]  # reduce kernel
+    ws = K.decode_workspace(64 << 20, gpu)
+    ins = [decode_inputs(small_paged(300 + i, **kw)) for i, kw in enumerate(cases)]
+    for rnd, (ci, splits) in enumerate([(0, 3), (1, 40), (0, 1), (2, 7), (3, 2), (1, 0), (0, 100), (2, 1)]):
+        dk, dv, q, bt, sl, L = ins[ci]
+        log("workspace reuse: case", ci, "splits", splits)
+        fresh = K.kv_decode_attn(q, dk, dv, bt, sl, L, 0.1, num_splits=splits)
+        out = K.kv_decode_attn(q, dk, dv, bt, sl, L, 0.1, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, fresh), (ci, splits)
+        assert int(ws[:K.KVQ_DECODE_COUNTER_BYTES].count_nonzero()) == 0
+        if rnd == 3:  # a prefill on the same workspace leaves the counters alone
+            dk1, dv1, *_ = ins[1]
+            w1 = small_paged(301, **cases[1])
+            qp = to_dev(np.repeat(w1["q"][:, None], 5, axis=1), w1["dtype"])
+            K.kv_prefill_attn(qp, dk1, dv1, ins[1][3], ins[1][4], ins[1][5], 0.1, num_splits=3, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(ws[:K.KVQ_DECODE_COUNTER_BYTES].count_nonzero()) == 0
+
+
+def test_decode_merge_beyond_the_counters(gpu):
+    """More (sequence, kv head) pairs than counters: the reduce kernel merges, and the
+    rows equal those of a small batch (one round of workgroups) merged inside the
+    decode kernel."""
+    Hkv = 8
+    B = K.KVQ_DECODE_COUNTER_BYTES // 4 // Hkv + 1
+    lens = tuple(int(x) for x in np.random.default_rng(5).integers(1, 40, B))
+    w = small_paged(404, T=16, lens=lens, Hq=32, Hkv=Hkv, kbits=4, vbits=2)
+    dk, dv, q, bt, sl, L = decode_inputs(w)
+    log("beyond the counters: B", B, "pages", w["P"])
+    big = K.kv_decode_attn(q, dk, dv, bt, sl, L, 0.1, num_splits=2)
+    n = 16
+    small = K.kv_decode_attn(q[:n].contiguous(), dk, dv, bt[:n].contiguous(), sl[:n].contiguous(), L, 0.1,
+                             num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:n], small)
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(T=128, lens=(300, 5), kbits=4, vbits=2, iters=4),
                                 dict(mla=True, D=512, R=64, T=128, Hkv=1, Hq=4, lens=(260,), iters=4),
                                 dict(mla=True, D=512, R=64, T=64, G=128, Hkv=1, Hq=4, lens=(150,), iters=4),
