@@ -413,6 +413,7 @@ def run_config(ci, args, torch, K, W, dev):
     qnames = sorted({K.kv_quantize_kernel_name(kcache[0], ksrc[0])} |
                     ({K.kv_quantize_kernel_name(vcache[0], vsrc[0])} if vsrc[0] is not None else set()))
     dname = K.kv_decode_attn_kernel_name(qd, kcache[0], vcache[0])
+    mname = K.kv_decode_attn_merge_kernel_name(qd, kcache[0], vcache[0], splits, max_len)
     qops = quantize_valu_ops(cfg, cfg.fk, cfg.width) + (quantize_valu_ops(cfg, cfg.fv, cfg.dv)
                                                         if cfg.fv is not None else 0)
     positions = int(cfg.seq_lens.sum())
@@ -427,7 +428,7 @@ def run_config(ci, args, torch, K, W, dev):
         "quantize_tokens_per_s": round((2 if cfg.fv is not None else 1) * cfg.total_tokens * cfg.num_kv_heads /
                                        (tq * 1e-3), 1),
         "quantize_valu_frac": round(qops / (tq * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
-        "decode_kernel": dname + " + decode_reduce_kernel", "decode_splits": splits, "decode_us": round(td * 1e3, 2),
+        "decode_kernel": dname + (" + " + mname if mname else " (split merge inside)"), "decode_splits": splits, "decode_us": round(td * 1e3, 2),
         "decode_GBps": round(d_gbs, 2), "decode_frac_hbm": round(d_gbs / HBM_PEAK_GBS, 4),
         "decode_positions_per_s": round(positions / (td * 1e-3), 1),
         "decode_tokens_per_s": round(cfg.num_seqs / (td * 1e-3), 1),

@@ -273,13 +273,21 @@ const char *kv_quantize_kernel_name(const kvq_cache *dst, const void *src, int32
                                     int64_t stride_token, int64_t stride_head);
 
 /* Name of the main GPU kernel kv_decode_attn runs for this query pointer and
- * these caches (the split-merge pass, "decode_reduce_kernel", follows it):
- * "decode_mla_kernel", "decode_pair16_kernel" (16-token pages, at most 8 query
- * heads per kv head: two pages per matrix-core pass), "decode_mfma_kernel" or
- * "decode_generic_kernel". NULL
- * for invalid arguments. The string is static. For profilers and benchmarks. */
+ * these caches: "decode_mla_kernel", "decode_pair16_kernel" (16-token pages, at
+ * most 8 query heads per kv head: two pages per matrix-core pass),
+ * "decode_mfma_kernel" or "decode_generic_kernel". NULL for invalid arguments.
+ * The string is static. For profilers and benchmarks. */
 const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v,
                                        int32_t num_q_heads);
+
+/* Name of the split-merge kernel kv_decode_attn launches after the main kernel
+ * for these arguments (num_splits as passed to it, 0 = the default rule for
+ * max_seq_len): "decode_reduce_kernel", or "" when the main kernel merges the
+ * splits itself (see kv_decode_attn's workspace). NULL for invalid arguments.
+ * The string is static. For profilers and benchmarks. */
+const char *kv_decode_attn_merge_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v,
+                                             int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                                             int32_t max_seq_len);
 
 /* Chunked prefill attention over the paged quantized cache. Each sequence b
  * ends with a chunk of chunk_len query positions whose keys and values are

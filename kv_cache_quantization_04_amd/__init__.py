@@ -9,7 +9,7 @@ libkvq.so. PyTorch supplies device memory (tensor.data_ptr()) and the stream
     kv_decode_attn, kv_append, kv_append_workspace_bytes, kv_prefill_attn,
     kv_prefill_attn_workspace_bytes, kv_prefill_attn_default_splits,
     kv_quantize_kernel_name, kv_decode_attn_kernel_name,
-    kv_prefill_attn_kernel_name, kvq_status_str
+    kv_decode_attn_merge_kernel_name, kv_prefill_attn_kernel_name, kvq_status_str
 
 plus ``DeviceCache``, a holder of the four device arrays of one cache, and
 ``decode_workspace``, a workspace for kv_decode_attn with its counters cleared.
@@ -44,7 +44,8 @@ KVQ_FLAG_NONFINITE, KVQ_FLAG_SIDE_OVERFLOW = 1, 2
 EXPORTS = ("kvq_format_from_preset", "kvq_cache_bytes", "kv_quantize", "kv_quantize_kv", "kv_dequantize",
            "kv_decode_attn_default_splits", "kv_decode_attn_workspace_bytes", "kv_decode_attn", "kv_decode_attn_noalloc", "kv_append", "kv_append_workspace_bytes", "kv_prefill_attn",
            "kv_prefill_attn_workspace_bytes", "kv_prefill_attn_default_splits",
-           "kv_quantize_kernel_name", "kv_decode_attn_kernel_name", "kv_prefill_attn_kernel_name", "kvq_status_str")
+           "kv_quantize_kernel_name", "kv_decode_attn_kernel_name", "kv_decode_attn_merge_kernel_name",
+           "kv_prefill_attn_kernel_name", "kvq_status_str")
 
 
 class kvq_format(ctypes.Structure):
@@ -84,6 +85,8 @@ _sig = {
     "kv_prefill_attn_default_splits": (_i32, [ctypes.c_void_p, ctypes.c_void_p, _i32, _i32, _i32, _i32]),
     "kv_quantize_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(kvq_cache), _vp, _i32, _i64, _i64]),
     "kv_decode_attn_kernel_name": (ctypes.c_char_p, [_vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _i32]),
+    "kv_decode_attn_merge_kernel_name": (ctypes.c_char_p, [_vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _i32,
+                                                           _i32, _i32, _i32]),
     "kv_prefill_attn_kernel_name": (ctypes.c_char_p, [_vp, ctypes.POINTER(kvq_cache), ctypes.POINTER(kvq_cache), _i32]),
     "kvq_status_str": (ctypes.c_char_p, [_i32]),
 }
@@ -273,6 +276,16 @@ def kv_decode_attn_kernel_name(q, k: DeviceCache, v: Optional[DeviceCache]) -> O
     """Main kernel kv_decode_attn(q, k, v, ...) runs, or None for invalid arguments."""
     r = _lib.kv_decode_attn_kernel_name(_ptr(q), ctypes.byref(k.struct), ctypes.byref(v.struct) if v is not None else None,
                                         q.shape[1])
+    return r.decode() if r is not None else None
+
+
+def kv_decode_attn_merge_kernel_name(q, k: DeviceCache, v: Optional[DeviceCache], num_splits: int,
+                                     max_seq_len: int) -> Optional[str]:
+    """Split-merge kernel that follows the main kernel of kv_decode_attn(q, k, v, ...),
+    "" when the main kernel merges the splits itself, None for invalid arguments."""
+    r = _lib.kv_decode_attn_merge_kernel_name(_ptr(q), ctypes.byref(k.struct),
+                                              ctypes.byref(v.struct) if v is not None else None, q.shape[0], q.shape[1],
+                                              num_splits, max_seq_len)
     return r.decode() if r is not None else None
 
 

@@ -7,6 +7,11 @@
 
 #include "launch.h"
 
+namespace kvq {
+// the decode kernel merges its split partials itself (no reduce kernel follows)
+bool decode_merges_in_kernel(const DecodeArgs &a);
+}  // namespace kvq
+
 namespace {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -308,6 +313,18 @@ const char *kv_decode_attn_kernel_name(const void *q, const kvq_cache *k, const 
         return nullptr;
     a.q = q;
     return kvq::decode_kernel_name(a);
+}
+
+const char *kv_decode_attn_merge_kernel_name(const void *q, const kvq_cache *k, const kvq_cache *v, int32_t num_seqs,
+                                             int32_t num_q_heads, int32_t num_splits, int32_t max_seq_len) {
+    kvq::DecodeArgs a{};
+    if (!q || num_seqs <= 0 || num_splits < 0 || max_seq_len < 0 || check_cache(k) != KVQ_OK ||
+        (v && check_cache(v) != KVQ_OK) || decode_layout(k, v, num_q_heads, a) != KVQ_OK)
+        return nullptr;
+    a.q = q;
+    a.B = num_seqs;
+    a.splits = num_splits > 0 ? num_splits : kvq::decode_default_splits(a, max_seq_len);
+    return kvq::decode_merges_in_kernel(a) ? "" : "decode_reduce_kernel";
 }
 
 size_t kv_decode_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim_v,

@@ -285,10 +285,14 @@ bool launch_decode_chunk(const DecodeArgs &a_in, hipStream_t stream) {
 // counters, and the other kernels, use the reduce kernel too.
 constexpr int64_t MERGE_MAX_WORKGROUPS = 512;
 
+bool decode_merges_in_kernel(const DecodeArgs &a) {
+    return !decode_mla_supported(a) && decode_mfma_supported(a) && a.B <= 65535 && a.splits <= RED_MAX_SPLITS &&
+           (int64_t)a.B * a.Hkv <= MERGE_COUNTERS && (int64_t)a.B * a.Hkv * a.splits <= MERGE_MAX_WORKGROUPS;
+}
+
 bool launch_decode(const DecodeArgs &a_in, hipStream_t stream) {
     DecodeArgs a = a_in;
-    const bool counters = a.cnt && (int64_t)a.B * a.Hkv <= MERGE_COUNTERS &&
-                          (int64_t)a.B * a.Hkv * a.splits <= MERGE_MAX_WORKGROUPS;
+    const bool counters = a.cnt && decode_merges_in_kernel(a);
     a.cnt = nullptr;
     if (a.splits > RED_MAX_SPLITS) return false;
     if (decode_mla_supported(a)) {

@@ -206,6 +206,35 @@ def test_decode_kernel_name():
     assert decode_kernel(fk, fv, 32, 8, q=None) is None
 
 
+def merge_kernel(fk, fv, num_seqs, num_q_heads, num_kv_heads, splits, max_len=4096, q=FAKE):
+    kc = cache_struct(fk, heads=num_kv_heads, rope=FAKE if fk.rope_dim else None)
+    vc = cache_struct(fv, heads=num_kv_heads) if fv is not None else None
+    r = K._lib.kv_decode_attn_merge_kernel_name(q, ctypes.byref(kc), ctypes.byref(vc) if vc is not None else None,
+                                                num_seqs, num_q_heads, splits, max_len)
+    return r.decode() if r is not None else None
+
+
+def test_decode_merge_kernel_name():
+    """The matrix-core kernels merge inside when sequences x kv heads x splits <= 512
+    workgroups (and the pairs fit the 16384 counters); every other case names the
+    reduce kernel."""
+    fk = K.make_format(128, 0, 128, 128, 128, 4, 4, K.KVQ_TOKEN_MAJOR)
+    fv = K.make_format(128, 0, 128, 128, 128, 2, 4, K.KVQ_CHANNEL_MAJOR)
+    assert merge_kernel(fk, fv, 8, 32, 8, 8) == ""                        # 512 workgroups
+    assert merge_kernel(fk, fv, 8, 32, 8, 9) == "decode_reduce_kernel"    # 576
+    assert merge_kernel(fk, fv, 8, 32, 8, 0) == ""                        # default rule: 8 splits
+    assert merge_kernel(fk, fv, 1, 32, 8, 64) == ""
+    assert merge_kernel(fk, fv, 8, 32 * 8, 8, 1) == "decode_reduce_kernel"  # generic kernel (32 heads per kv head)
+    f16k = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_TOKEN_MAJOR)
+    f16v = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_CHANNEL_MAJOR)
+    assert merge_kernel(f16k, f16v, 4, 64, 8, 16) == ""                   # paired pages
+    assert merge_kernel(f16k, f16v, 64, 64, 8, 8) == "decode_reduce_kernel"
+    fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)
+    assert merge_kernel(fm, None, 1, 128, 1, 1) == "decode_reduce_kernel"  # MLA
+    assert merge_kernel(fk, fv, 8, 30, 8, 8) is None
+    assert merge_kernel(fk, fv, 0, 32, 8, 8) is None
+
+
 def append_status(fmt, tail=FAKE, new=FAKE, num_seqs=2, ws_bytes=None, ws=FAKE, dtype=2, bt_stride=4):
     c = cache_struct(fmt, rope=FAKE if fmt.rope_dim else None)
     if ws_bytes is None:
