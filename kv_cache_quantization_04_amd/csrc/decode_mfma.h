@@ -40,8 +40,11 @@ __device__ __forceinline__ half8 unpack8(uint32_t lo) {
     constexpr int K = 10 - B;
     constexpr uint32_t M = ((1u << B) - 1u) * 0x00010001u << K;
     uint32_t s = lo;
-    if constexpr (B == 2) s = (lo & 0xFFu) | ((lo & 0xFF00u) << 8);   // codes 4..7 to bits 16..
-    if constexpr (B == 3) s = (lo & 0xFFFu) | ((lo & 0xFFF000u) << 4);  // codes 4..7 to bits 16..
+    // codes 4..7 to bits 16..: one bitfield insert; the other bits it leaves above the
+    // low codes (copies of lower codes, or of bits past the chunk) are never shifted
+    // into the mask below
+    if constexpr (B == 2) s = (lo & 0xFFu) | ((lo << 8) & ~0xFFu);
+    if constexpr (B == 3) s = (lo & 0xFFFu) | ((lo << 4) & ~0xFFFu);
     uint32_t p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
