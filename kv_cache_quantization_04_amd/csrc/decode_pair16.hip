@@ -181,6 +181,10 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     // row l16 of an M-tile is token ktok of its page (the order that makes the score
     // tile the value product's B operand without a transpose)
     const int tok0 = 8 * (lq & 1) + 4 * (lq >> 1);
+    // P~ operand selectors (byte permutes of the swapped pairs): the low halves, or the
+    // high halves, of both words; all zero for the other page's tokens
+    const bool pact = (lq >> 1) == half;
+    const uint32_t psel_h = pact ? 0x01000504u : 0x0C0C0C0Cu, psel_l = pact ? 0x03020706u : 0x0C0C0C0Cu;
     const int ktok = 8 * ((l16 >> 2) & 1) + 4 * (l16 >> 3) + (l16 & 3);
 
     while (pa < p1) {
@@ -345,21 +349,20 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
         // other 4 come from lane ^ 32
         half8 pbh, pbl;
         {
-            const bool act = (lq >> 1) == half;
-            const bool upper = lq >= 2;
+            // the partner's (hi, lo) pair, 32 lanes apart, by one permlane swap of the packed
+            // pair; the swap leaves the lower lane's pair in its first result and the upper
+            // lane's in its second, so one byte permute per word puts the two hi (lo) parts
+            // in token order on both sides (selectors fixed per lane, zero off the page)
+            uint32_t hw[4], lw[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // the partner's (hi, lo) pair, 32 lanes apart: one permlane swap of the packed pair
                 const half2v mine = {phi[i], plo[i]};
                 const auto sw = __builtin_amdgcn_permlane32_swap(as_u(mine), as_u(mine), false, false);
-                const half2v other = as_h2(upper ? sw[0] : sw[1]);
-                const _Float16 hu = other.x, lu = other.y;
-                const _Float16 z = (_Float16)0.f;
-                pbh[2 * i] = act ? (upper ? hu : phi[i]) : z;
-                pbh[2 * i + 1] = act ? (upper ? phi[i] : hu) : z;
-                pbl[2 * i] = act ? (upper ? lu : plo[i]) : z;
-                pbl[2 * i + 1] = act ? (upper ? plo[i] : lu) : z;
+                hw[i] = __builtin_amdgcn_perm(sw[0], sw[1], psel_h);
+                lw[i] = __builtin_amdgcn_perm(sw[0], sw[1], psel_l);
             }
+            pbh = __builtin_bit_cast(half8, uint4{hw[0], hw[1], hw[2], hw[3]});
+            pbl = __builtin_bit_cast(half8, uint4{lw[0], lw[1], lw[2], lw[3]});
         }
 
         // ---- values: channel tiles mc; lane (channel 16 mc + l16, page lq >> 1, tokens
