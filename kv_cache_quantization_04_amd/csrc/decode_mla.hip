@@ -109,6 +109,14 @@ __device__ __forceinline__ void split_prod(float a, float b, _Float16 &hi, _Floa
     lo = (_Float16)__builtin_fmaf(a, b, -(float)hi);
 }
 
+// ((a << 8) + b) << 8 + c as two shift-adds: the inner sum made opaque, so that the
+// compiler does not re-associate it into a << 16 + b << 8 + c (three instructions)
+__device__ __forceinline__ int limbs3_combine(int a, int b, int c) {
+    int t = (a << 8) + b;
+    asm("" : "+v"(t));
+    return (t << 8) + c;
+}
+
 // v_perm_b32: byte k of the result is byte sel_k of the pair (lo: bytes 0..3,
 // hi: bytes 4..7)
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -681,7 +689,7 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
             const half2v c01 = as_h2(cv2.x), c23 = as_h2(cv2.y);
             const _Float16 cvv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf((float)cvv[i], (float)((((a2[i] << 8) + a1[i]) << 8) + a0[i]), o[mc][i]);
+            for (int i = 0; i < 4; ++i) o[mc][i] = __builtin_fmaf((float)cvv[i], (float)limbs3_combine(a2[i], a1[i], a0[i]), o[mc][i]);
             if (mc & 1) __builtin_amdgcn_sched_barrier(0);  // at most two tiles' operands in flight
         }
     }
