@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
                 // mean over the n valid rows by a reciprocal of n (exact for a full tile,
                 // n = 16; within an ulp of the quotient otherwise)
                 const float csq = (iters > 0 && n > 0 && tj > 0.f && tj < INFINITY) ? tj * __builtin_amdgcn_rcpf(fn) : 1.f;
-                const uint16_t c16 = float_to_half_bits(sqrtf(csq));
+                const uint16_t c16 = float_to_half_bits(__builtin_amdgcn_sqrtf(csq));
                 const float cvj = half_bits_to_float(c16);
                 if (!(cvj > 0.f && cvj < INFINITY)) bad |= KVQ_FLAG_SIDE_OVERFLOW;
                 const int ch = 16 * (2 * rr + j) + cc;
