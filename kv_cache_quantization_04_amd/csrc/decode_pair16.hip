@@ -42,6 +42,39 @@ __device__ __forceinline__ void hstage(float (&x)[4], int u, int h) {
     }
 }
 
+// Workgroups take their sequence in order of decreasing page count: grid row z gets the
+// sequence of rank z (ties by index). Workgroups are dispatched in grid order, so the
+// splits of the longest sequences start in the first rounds and the shortest fill in at
+// the end: greedy list scheduling with the longest jobs first, whose tail is at most one
+// short job, where the natural order can leave a long sequence's splits for last. Up to
+// MNT sequences (one per thread); more keep the natural order. keys: MNT + 4 ints of LDS.
+template <int T>
+__device__ __forceinline__ int sequence_of_row(const DecodeArgs &a, int z, int *keys) {
+    if (a.B > MNT) return z;
+    const int t = threadIdx.x, n4 = (a.B + 3) >> 2;
+    int np = 0;
+    if (t < a.B) {
+        const int L = a.seq_lens[t];
+        np = min((L + T - 1) / T, a.bt_stride);  // the page walk's own count
+        keys[t] = np;
+    } else if (t < 4 * n4) {
+        keys[t] = -2147483647 - 1;  // padding: below every page count (which is > INT32_MIN)
+    }
+    lds_barrier();
+    if (t < a.B) {
+        int r = 0;
+        for (int u4 = 0; u4 < n4; ++u4) {
+            const int4 p = *reinterpret_cast<const int4 *>(&keys[4 * u4]);
+            const int u = 4 * u4;
+            r += (p.x > np || (p.x == np && u < t)) + (p.y > np || (p.y == np && u + 1 < t)) +
+                 (p.z > np || (p.z == np && u + 2 < t)) + (p.w > np || (p.w == np && u + 3 < t));
+        }
+        if (r == z) keys[MNT] = t;  // the ranks are a permutation of 0 .. B - 1
+    }
+    lds_barrier();
+    return __builtin_amdgcn_readfirstlane(keys[MNT]);
+}
+
 template <int KB, int VB>
 __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     constexpr int T = 16;
@@ -64,7 +97,8 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     const int l16 = lane & 15, lq = lane >> 4;
     const int half = l16 >> 3;  // this lane's column: page A (0) or B (1) of the pair
     const int g = a.grp;
-    const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
+    __shared__ __attribute__((aligned(16))) int seq_keys[MNT + 4];
+    const int split = blockIdx.x, hk = blockIdx.y, s = sequence_of_row<T>(a, blockIdx.z, seq_keys);
     const int hh = l16 & 7;  // column head
     const bool hv = hh < g;
     const int L = load_const(a.seq_lens, s);
