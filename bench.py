@@ -359,7 +359,7 @@ def run_config(ci, args, torch, K, W, dev):
     vcache = ([K.DeviceCache(kfmt(cfg.fv), cfg.num_pages, cfg.num_kv_heads, device=dev) for _ in range(ring)]
               if cfg.fv is not None else [None] * ring)
     max_len = int(cfg.seq_lens.max())
-    splits = K.kv_decode_attn_default_splits(kcache[0], vcache[0], cfg.num_seqs, cfg.num_q_heads, max_len)
+    splits = args.splits or K.kv_decode_attn_default_splits(kcache[0], vcache[0], cfg.num_seqs, cfg.num_q_heads, max_len)
     ws = K.decode_workspace(K.kv_decode_attn_workspace_bytes(cfg.num_seqs, cfg.num_q_heads, cfg.dv, splits), dev)
     out = torch.empty((cfg.num_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device=dev)
     # K and V in one launch (kv_quantize_kv) where the library takes the pair of formats
@@ -468,6 +468,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--splits", type=int, default=0, help="decode split count (0: the library's default rule)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--configs", default="1,2,3,4", help="workload indices timed in this run")
     ap.add_argument("--headline", type=int, default=3,

@@ -229,11 +229,15 @@ int decode_default_splits(const DecodeArgs &a, int max_seq_len) {
     // larger wins: at least 512 workgroups (two per compute unit), and at most 2048
     // tokens of the longest sequence per split (512 per wave), so that with unequal
     // lengths the longest sequences do not trail; each wave keeps at least one page.
+    // The paired 16-token kernel starts the longest sequences first (up to 256, one per
+    // thread of its workgroup), which keeps them from trailing with splits twice as
+    // long: 4096 tokens (64 sequences of 512..16384 tokens: 4 splits 238-240 us, 8 splits 262 us).
     // (Measured on the GQA workloads against 2..256 splits: best or within 2% of it.)
     const int64_t units = (int64_t)a.B * a.Hkv;
     if (units < 1) return 1;
     int64_t sp = (512 + units - 1) / units;
-    const int64_t by_len = ((int64_t)max_seq_len + 2047) / 2048;
+    const int64_t split_tokens = decode_pair16_supported(a) && a.B <= 256 ? 4096 : 2048;
+    const int64_t by_len = ((int64_t)max_seq_len + split_tokens - 1) / split_tokens;
     if (sp < by_len) sp = by_len;
     sp = splits_for(1, sp, pages, 4);
     // Long splits of 64- and 128-token pages (4 or more pages per wave): one workgroup

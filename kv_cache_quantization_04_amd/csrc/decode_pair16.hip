@@ -50,6 +50,7 @@ __device__ __forceinline__ void hstage(float (&x)[4], int u, int h) {
 // MNT sequences (one per thread); more keep the natural order. keys: MNT + 4 ints of LDS.
 template <int T>
 __device__ __forceinline__ int sequence_of_row(const DecodeArgs &a, int z, int *keys) {
+    static_assert(MNT == 256, "the split rule assumes ordering up to 256 sequences");
     if (a.B > MNT) return z;
     const int t = threadIdx.x, n4 = (a.B + 3) >> 2;
     int np = 0;

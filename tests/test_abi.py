@@ -151,8 +151,13 @@ def test_default_splits():
     f16k = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_TOKEN_MAJOR)
     f16v = K.make_format(128, 0, 16, 128, 128, 3, 2, K.KVQ_CHANNEL_MAJOR)
     assert default_splits(f16k, f16v, 1, 8, 1, 5) == 1
-    # 64 sequences up to 16384 tokens in 16-token pages: the length bound
-    assert default_splits(f16k, f16v, 64, 64, 8, 16384) == 8
+    # 64 sequences up to 16384 tokens in 16-token pages: the length bound, 4096 tokens
+    # per split for the paired kernel, which starts the longest sequences first
+    assert default_splits(f16k, f16v, 64, 64, 8, 16384) == 4
+    # more than 256 sequences keep the natural order and 2048 tokens per split
+    assert default_splits(f16k, f16v, 300, 64, 8, 16384) == 8
+    # more than 8 query heads per kv head: the one-page kernel, 2048 tokens per split
+    assert default_splits(f16k, f16v, 64, 128, 8, 16384) == 8
     # MLA latent (512 + 64 rope, 4-bit): one workgroup per compute unit over
     # (sequence, 64 query heads, split): 32 sequences x 2 head groups x 4 splits
     fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)

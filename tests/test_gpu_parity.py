@@ -586,6 +586,27 @@ def test_decode_small(gpu, kw, splits):
     assert err <= DECODE_RTOL
 
 
+# The paired 16-token kernel starts the sequences in order of decreasing page count
+# (ranked inside every workgroup, ties by index) up to 256 sequences; more keep the
+# natural order. Equal lengths, lengths whose page counts tie, and 260 sequences.
+DEC_ORDER = [
+    dict(T=16, lens=(50, 7, 50, 1, 7, 50, 33, 16, 17, 49), kbits=3, vbits=3, Hq=8, Hkv=1),
+    dict(T=16, lens=tuple(int(x) for x in np.random.default_rng(5).integers(1, 90, 260)), kbits=3, vbits=3,
+         Hq=4, Hkv=1),
+]
+
+
+@pytest.mark.parametrize("kw", DEC_ORDER, ids=["ties", "260_seqs"])
+@pytest.mark.parametrize("splits", [0, 2, 5])
+def test_decode_longest_first_order(gpu, kw, splits):
+    log("decode order case", len(kw["lens"]), "sequences, splits", splits)
+    w = small_paged(23 + len(kw["lens"]), **kw)
+    out, ref, *_ = run_decode_case(gpu, w, 1.0 / math.sqrt(w["fk"].head_dim), splits)
+    err = rel_rowwise(out, ref)
+    log("  decode rel err", err)
+    assert err <= DECODE_RTOL
+
+
 DEC_DB = [
     dict(T=128, lens=(9000, 4100, 130), kbits=4, vbits=2, iters=4),   # 71, 33 and 2 pages, ragged last pages
     dict(T=64, lens=(5000, 70), kbits=3, vbits=4, Hq=16, Hkv=2),      # 79 and 2 pages, g = 8
