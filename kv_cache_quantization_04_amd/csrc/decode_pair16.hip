@@ -21,7 +21,7 @@
 // wave's even and odd pages); the workgroup merge combines them with the other waves'.
 // The next pair's page images are prefetched into registers while a pair is computed
 // and written to the wave's two LDS images at the top of the next pair; a wave with an
-// odd number of pages ends with page B a copy of page A whose tokens are all masked.
+// odd number of pages ends with page A loaded again as page B, whose tokens are all masked.
 #include "common.h"
 #include "decode_merge.h"
 #include "decode_mfma.h"
@@ -135,15 +135,12 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     int pa = next_valid(p0 + wave);
     int pb = pa < p1 ? next_valid(pa + 4) : p1;
     Chunks<PI::NPRE> preA{}, preB{};
+    // A missing page B is page A loaded a second time (its tokens are masked): a register
+    // copy of page A would wait for A's loads where it is made.
     if (pa < p1) {
         preA = fetch_page(psrc, (uint32_t)(page_of(pa) * a.Hkv + hk));
-        if (pb < p1) {
-            preB = fetch_page(psrc, (uint32_t)(page_of(pb) * a.Hkv + hk));
-            wait_vm_upto<2 * PI::NPRE>();
-        } else {
-            preB = preA;
-            wait_vm_upto<PI::NPRE>();
-        }
+        preB = fetch_page(psrc, (uint32_t)(page_of(pb < p1 ? pb : pa) * a.Hkv + hk));
+        wait_vm_upto<2 * PI::NPRE>();
     } else {
         wait_vm_upto<0>();
     }
@@ -326,8 +323,7 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
         // after the query fold, so that its registers are not live across the fold)
         if (pa < p1) {
             preA = fetch_page(psrc, (uint32_t)(page_of(pa) * a.Hkv + hk));
-            if (pb < p1) preB = fetch_page(psrc, (uint32_t)(page_of(pb) * a.Hkv + hk));
-            else preB = preA;
+            preB = fetch_page(psrc, (uint32_t)(page_of(pb < p1 ? pb : pa) * a.Hkv + hk));
         }
 
         // ---- online softmax over the column's page
