@@ -210,11 +210,36 @@ __device__ __forceinline__ void max_h4_words(const uint32_t (&w)[4], float &lo, 
 
 }  // namespace
 
+// Raw words of 8 consecutive query elements from element offset i (16-byte aligned for
+// 16-bit types: 32 bytes of fp32 as two loads)
 template <int QDT>
-__device__ __forceinline__ float load_q(const void *q, int64_t i) {
-    if constexpr (QDT == KVQ_F32) return reinterpret_cast<const float *>(q)[i];
-    else if constexpr (QDT == KVQ_F16) return half_bits_to_float(reinterpret_cast<const uint16_t *>(q)[i]);
-    else return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(q)[i]);
+struct Q8 {
+    uint4 w[QDT == KVQ_F32 ? 2 : 1];
+};
+template <int QDT>
+__device__ __forceinline__ Q8<QDT> load_q8(const void *q, int64_t i) {
+    Q8<QDT> r;
+    if constexpr (QDT == KVQ_F32) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(q) + i);
+        r.w[0] = p[0];
+        r.w[1] = p[1];
+    } else {
+        r.w[0] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q) + i);
+    }
+    return r;
+}
+template <int QDT>
+__device__ __forceinline__ float q8_at(const Q8<QDT> &r, int e) {
+    if constexpr (QDT == KVQ_F32) {
+        const uint4 w = r.w[e >> 2];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+        return __uint_as_float(u[e & 3]);
+    } else {
+        const uint4 w = r.w[0];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+        const uint32_t b = (e & 1) ? u[e >> 1] >> 16 : u[e >> 1] & 0xffffu;
+        return QDT == KVQ_F16 ? half_bits_to_float((uint16_t)b) : __uint_as_float(b << 16);
+    }
 }
 
 // One workgroup's pages. The shared-memory regions come in as restrict pointers:
@@ -285,6 +310,20 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
         const int page = load_const(a.bt, (int64_t)s * a.bt_stride + pi);
         return page >= 0 && page < a.num_pages;
     };
+    // The lane's query words are requested before the first page: 16 wide loads, issued
+    // together, ahead of the page copies (the vector-memory count is in order, so waiting
+    // for them leaves the copies in flight). Lanes past the kv group's heads read the
+    // group's first head and use zeros.
+    Q8<QDT> qraw[8][2], rraw;
+    {
+        const int64_t qb = ((int64_t)s * a.Hq + (hq_ok ? hq : hk * a.grp)) * (XD + XR);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) qraw[ks][h] = load_q8<QDT>(a.q, qb + 64 * ks + 16 * lq + 8 * h);
+        rraw = load_q8<QDT>(a.q, qb + XD + 32 * half + 8 * lq);
+    }
+    asm volatile("" ::: "memory");  // keep the query loads ahead of the page requests
     int pi = p0;
     while (pi < p1 && !page_ok(pi)) ++pi;
     if (pi < p1) {
@@ -302,18 +341,17 @@ __device__ __forceinline__ void mla_body(const DecodeArgs &a, int units, int nhg
     uint32_t qrl[4];
     float qmax = 0.f;
     {
-        const int64_t qb = ((int64_t)s * a.Hq + hq) * (XD + XR);
         float q[8][16];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-            for (int f = 0; f < 16; ++f) q[ks][f] = hq_ok ? load_q<QDT>(a.q, qb + 64 * ks + 16 * lq + f) : 0.f;
+            for (int f = 0; f < 16; ++f) q[ks][f] = hq_ok ? q8_at<QDT>(qraw[ks][f >> 3], f & 7) : 0.f;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
             uint32_t hw = 0, lw = 0;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const float x = hq_ok ? load_q<QDT>(a.q, qb + XD + 32 * half + 8 * lq + 2 * e2 + h) : 0.f;
+                const float x = hq_ok ? q8_at<QDT>(rraw, 2 * e2 + h) : 0.f;
                 const uint16_t hb = bf16_rn(x);
                 const uint16_t lb = bf16_rn(x - bf16_bits_to_float(hb));
                 hw |= (uint32_t)hb << (16 * h);
@@ -726,7 +764,7 @@ __global__ void __launch_bounds__(XNT, 1) decode_mla_kernel(DecodeArgs a, int un
 
 bool decode_mla_supported(const DecodeArgs &a) {
     auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
-    return al16(a.kcodes) && al16(a.ksz) && al16(a.kcn) && al16(a.krope) && a.D == XD && a.R == XR && a.Dv == XD && a.T == XT && a.kbits == 4 && a.kG == XD && a.kh == XD &&
+    return al16(a.q) && al16(a.kcodes) && al16(a.ksz) && al16(a.kcn) && al16(a.krope) && a.D == XD && a.R == XR && a.Dv == XD && a.T == XT && a.kbits == 4 && a.kG == XD && a.kh == XD &&
            a.klayout == KVQ_TOKEN_MAJOR && a.vcodes == a.kcodes && a.grp % 16 == 0 && a.krope != nullptr;
 }
 
