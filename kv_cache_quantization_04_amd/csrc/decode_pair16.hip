@@ -121,10 +121,14 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
     // channels 4 (t & 31) .. + 3, whose raw words are loaded before the first pages are
     // requested (the vector-memory counter is in order: waiting for them leaves the
     // page loads in flight).
+    // The load is unconditional (threads past the group's g heads read its first head and
+    // use zeros below): a load under a divergent condition is waited for where the branch
+    // joins, before the page requests.
     const int qh = tid >> 5, qu = tid & 31;
-    uint4 qraw = {0, 0, 0, 0};
-    if (qh < g) {
-        const int64_t qb = ((int64_t)s * a.Hq + hk * g + qh) * MD + 4 * qu;
+    const bool qok = qh < g;
+    uint4 qraw;
+    {
+        const int64_t qb = ((int64_t)s * a.Hq + hk * g + (qok ? qh : 0)) * MD + 4 * qu;
         if (a.q_dtype == KVQ_F32) qraw = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.q) + qb);
         else {
             const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.q) + qb);
@@ -160,6 +164,7 @@ __global__ void __launch_bounds__(MNT, 3) decode_pair16_kernel(DecodeArgs a) {
             x[0] = half_bits_to_float(qraw.x & 0xffffu); x[1] = half_bits_to_float(qraw.x >> 16);
             x[2] = half_bits_to_float(qraw.y & 0xffffu); x[3] = half_bits_to_float(qraw.y >> 16);
         }
+        if (!qok) x[0] = x[1] = x[2] = x[3] = 0.f;
         if (1 < a.kh) {
             const float y0 = x[0], y2 = x[2];
             x[0] = y0 + x[1]; x[1] = y0 - x[1];
