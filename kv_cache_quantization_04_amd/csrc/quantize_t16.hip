@@ -8,7 +8,7 @@
 // 16 j + (l & 15), j = 0..7. The 16 lanes of a DPP row thus cover one token's 128
 // channels, and all per-token reductions are row operations. Column sums finish
 // inside the wave (permlane swaps across the four row groups) and the per-channel
-// factors go back to the four row groups by the reverse swaps (no LDS round trip).
+// factors go back to the four row groups through a small per-wave LDS buffer.
 // Per-token scale and zero are computed by one lane per row and broadcast. Codes go
 // to a per-wave LDS byte image in bitstream order (token-major t * 128 + j,
 // channel-major j * 16 + t); each lane then packs 32 consecutive codes into the
@@ -56,14 +56,17 @@ __device__ __forceinline__ Rows load_rows(const QuantArgs &a, int item, int lane
 
 // The values of the lane's 8 local channels (t = 0..7, channel 16 t + (lane & 15)) from
 // their owners: after the column-sum swaps, lane (cc, rr) holds local channels 2 rr and
-// 2 rr + 1 (o0, o1). The swaps of rows 16 lanes apart give every lane of a 32-lane
-// half h its four channels 4 h + {0, 1, 2, 3}; those 32 lanes apart, all eight.
-__device__ __forceinline__ void bcast_owned(float o0, float o1, float (&v)[8]) {
-    float q[4];
-    pair16(o0, q[0], q[2]);  // local 4 h, 4 h + 2
-    pair16(o1, q[1], q[3]);  // local 4 h + 1, 4 h + 3
-#pragma unroll
-    for (int m = 0; m < 4; ++m) pair32(q[m], v[m], v[4 + m]);
+// 2 rr + 1 (o0, o1).
+// Through the wave's own 512-byte LDS buffer: lane (cc, rr) writes its pair to row cc,
+// slots 2 rr, 2 rr + 1, and reads row cc back (a wave's LDS operations run in order, so
+// no barrier is needed). The permlane swaps would do it in registers, but a swap of a
+// value with itself first needs a register copy: 12 VALU instructions against none.
+__device__ __forceinline__ void bcast_owned(float o0, float o1, float (&v)[8], float *buf, int cc, int rr) {
+    *reinterpret_cast<float2 *>(&buf[8 * cc + 2 * rr]) = float2{o0, o1};
+    const float4 lo = *reinterpret_cast<const float4 *>(&buf[8 * cc]);
+    const float4 hi = *reinterpret_cast<const float4 *>(&buf[8 * cc + 4]);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
 }
 
 }  // namespace
@@ -72,6 +75,7 @@ template <int BITS, int LAYOUT, int NIT>
 __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int num_items) {
     __shared__ __attribute__((aligned(16))) uint8_t img[4][ZT * ZD];  // per wave: codes in stream order
     __shared__ uint4 hbtab[2 * 64];  // the two per-lane Hadamard operand patterns, read per item
+    __shared__ __attribute__((aligned(16))) float bcb[4][16 * 8];  // per wave: channel factors, row cc = lane & 15
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,7 +187,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
             }
             // a zero column keeps a large finite w (its A entries are all zero)
             bcast_owned(fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[0], TINY)),
-                        fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[1], TINY)), w);
+                        fn_d * __builtin_amdgcn_rcpf(fmaxf(t_own[1], TINY)), w, bcb[wave], cc, rr);
         }
 
         // ---- fp16 normalizer c16 of the lane's two channels and the multiplier
@@ -207,7 +211,7 @@ __global__ void __launch_bounds__(ZNT, 4) quantize_t16_kernel(QuantArgs a, int n
                 const float rc = __builtin_amdgcn_rcpf(cvj), q0 = INV_SQRT_H * rc;
                 m2[j] = __builtin_fmaf(__builtin_fmaf(-cvj, q0, INV_SQRT_H), rc, q0);
             }
-            bcast_owned(m2[0], m2[1], mult);
+            bcast_owned(m2[0], m2[1], mult, bcb[wave], cc, rr);
         }
 
         // ---- per token: asymmetric RTN with fp16 (S, Z); byte codes into the image
