@@ -207,6 +207,7 @@ def test_decode_kernel_name():
     assert decode_kernel(fk, fv, 32 * 8, 8) == "decode_generic_kernel"          # 32 query heads per kv head
     fm = K.make_format(512, 64, 128, 512, 512, 4, 4, K.KVQ_TOKEN_MAJOR)
     assert decode_kernel(fm, None, 128, 1) == "decode_mla_kernel"
+    assert decode_kernel(fm, None, 128, 1, q=FAKE + 4) == "decode_generic_kernel"  # MLA: q not 16-byte aligned
     assert decode_kernel(fk, fv, 30, 8) is None
     assert decode_kernel(fk, fv, 32, 8, q=None) is None
 

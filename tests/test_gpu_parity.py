@@ -463,7 +463,9 @@ def small_paged(seed, D=128, T=16, Hq=8, Hkv=2, lens=(300, 1, 77, 16), kbits=4, 
                 Hq=Hq, Hkv=Hkv)
 
 
-def run_decode_case(gpu, w, sm, splits=0):
+def run_decode_case(gpu, w, sm, splits=0, q_offset=0):
+    """q_offset > 0: the query starts that many elements into a larger buffer (a pointer
+    that is not 16-byte aligned selects the generic kernel)."""
     kc, _ = orc_quantize(w["fk"], w["ks"], w["dtype"], w["tst"], w["tv"], w["tp"], w["P"])
     vc = None
     if w["fv"] is not None:
@@ -475,7 +477,12 @@ def run_decode_case(gpu, w, sm, splits=0):
     if vc is not None:
         dv = K.DeviceCache(kfmt(w["fv"]), w["P"], w["Hkv"])
         upload(vc, dv)
-    out = K.kv_decode_attn(to_dev(w["q"], w["dtype"]), dk, dv, i32(w["bt"]), i32(w["lens"]), int(w["lens"].max()), sm,
+    qd = to_dev(w["q"], w["dtype"])
+    if q_offset:
+        buf = torch.empty(qd.numel() + q_offset, dtype=qd.dtype, device=qd.device)
+        buf[q_offset:] = qd.reshape(-1)
+        qd = buf[q_offset:].view(qd.shape)
+    out = K.kv_decode_attn(qd, dk, dv, i32(w["bt"]), i32(w["lens"]), int(w["lens"].max()), sm,
                            num_splits=splits)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), ref, kc, vc, dk, dv
@@ -583,6 +590,17 @@ def test_decode_small(gpu, kw, splits):
     out, ref, *_ = run_decode_case(gpu, w, 1.0 / math.sqrt(w["fk"].head_dim + w["fk"].rope_dim), splits)
     err = rel_rowwise(out, ref)
     log("  decode rel err", err)
+    assert err <= DECODE_RTOL
+
+
+def test_decode_mla_query_not_16_byte_aligned(gpu):
+    """The MLA kernel loads the query 16 bytes at a time; a query pointer off 16-byte
+    alignment runs the generic kernel, with the same result."""
+    w = small_paged(41, mla=True, D=512, R=64, T=128, Hq=16, Hkv=1, lens=(300, 129), iters=4)
+    sm = 1.0 / math.sqrt(512 + 64)
+    out, ref, *_ = run_decode_case(gpu, w, sm, q_offset=1)
+    err = rel_rowwise(out, ref)
+    log("  decode rel err (generic kernel, unaligned query)", err)
     assert err <= DECODE_RTOL
 
 
